@@ -1,0 +1,240 @@
+/*
+ * idx.h -- C ABI of libidx, an MI355X (gfx950) implementation of the
+ * DeepSeek-V3.2 DSA lightning-indexer path with IndexCache layer reuse.
+ *
+ * Sources (web pages; cited by title and snippet / section):
+ *   [blog]  "IndexCache: cross-layer index reuse in DeepSeek sparse attention"
+ *           (atomage.cn) -- vLLM snippets DeepseekV32IndexerCache,
+ *           DeepseekV32IndexerBackend, Indexer.forward, SparseAttnIndexer,
+ *           the op body, DeepseekV32IndexerMetadata, the skip_topk schedule,
+ *           the top-k buffer allocation, the MLA forward.
+ *   [pr]    "PR #37735 report: [Feature]: IndexCache support for DSA models"
+ *           (prhub.com.cn) -- Implementation, Key source snippets, Risks & impact.
+ *   [group] vLLM API page "vllm.v1.attention.backends.mla.index_group" --
+ *           SparseMLAIndexGroup, SparseMLAIndexGroupBuilder.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; scratch memory is passed in as
+ *     a caller-owned workspace whose size the *_workspace_size calls report.
+ *   - Every call validates its arguments on the host first.  A non-zero
+ *     status means nothing was enqueued.  Otherwise the kernels are enqueued
+ *     on `stream` and the call returns at once; a failure inside a kernel
+ *     surfaces at the caller's next synchronisation as a HIP error.
+ *   - Kernels bound every memory access by the host-side sizes they are given
+ *     (num_blocks, block_table_stride, max_seq_len, strides).  Device metadata
+ *     that disagrees with them (a block id outside the pool, a sequence longer
+ *     than max_seq_len) gives unspecified values for the affected positions
+ *     but no out-of-bounds access.
+ *   - Supported shapes: n_heads == 64, head_dim == 128, block_size == 64,
+ *     1 <= k <= 2048.  Anything else returns IDX_ERR_UNSUPPORTED.
+ *   - Calls are stream-ordered; calls on different streams that share a
+ *     cache, buffer or workspace race.
+ */
+#ifndef IDX_H_
+#define IDX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum idx_status {
+  IDX_OK = 0,
+  IDX_ERR_INVALID_ARG = -1,  /* null pointer, negative size, stride too small, misaligned */
+  IDX_ERR_UNSUPPORTED = -2,  /* a shape outside the supported set above */
+  IDX_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+  IDX_ERR_LAUNCH = -4        /* the HIP runtime refused a launch */
+} idx_status_t;
+
+/* Static, NUL-terminated description of a status code. */
+const char* idx_status_str(idx_status_t s);
+
+/* Library version string, e.g. "idx 0.1 gfx950". */
+const char* idx_version(void);
+
+/*
+ * Paged indexer K cache ([blog] DeepseekV32IndexerCache,
+ * DeepseekV32IndexerBackend.get_kv_cache_shape, "FP8 naive cache"):
+ * uint8 [num_blocks, block_size, 132], one shared K per position (no V,
+ * one KV head).  Byte order inside a block of B = block_size * 132 bytes:
+ *   bytes [0, block_size*128)           128 E4M3 codes of offsets 0..block_size-1
+ *   bytes [block_size*128, B)           one fp32 (little-endian) scale per offset
+ * so the token at slot = block * block_size + off has its codes at
+ * block*B + off*128 and its scale at block*B + block_size*128 + off*4.
+ */
+typedef struct idx_kcache {
+  uint8_t* data;        /* device, num_blocks * block_size * 132 bytes, 16-byte aligned */
+  int64_t num_blocks;
+  int32_t block_size;   /* must be 64 */
+} idx_kcache_t;
+
+/*
+ * One batch of query tokens ([blog] DeepseekV32IndexerMetadata: seq_lens,
+ * max_seq_len, slot_mapping, decode/prefill counts; the paged backend's block
+ * table).  Request r has seq_lens[r] positions in total, of which the last
+ * n_r = query_start_loc[r+1] - query_start_loc[r] are this step's new
+ * tokens; query token t = query_start_loc[r] + i sits at position
+ * p_t = seq_lens[r] - n_r + i and is scored against positions 0..p_t.
+ */
+typedef struct idx_batch {
+  const int32_t* seq_lens;         /* device [num_reqs] */
+  const int32_t* query_start_loc;  /* device [num_reqs + 1], query_start_loc[0] == 0 */
+  const int32_t* block_table;      /* device [num_reqs, block_table_stride] physical block ids */
+  int64_t block_table_stride;      /* >= ceil(max_seq_len / block_size) */
+  int32_t num_reqs;                /* >= 1 */
+  int32_t num_tokens;              /* host copy of query_start_loc[num_reqs] */
+  int32_t max_seq_len;             /* host copy of max(seq_lens) */
+  int32_t max_query_len;           /* host copy of max(n_r) */
+} idx_batch_t;
+
+/*
+ * Quantise new K rows to E4M3 with one power-of-two fp32 scale per row and
+ * scatter them into the paged cache ([blog] op body:
+ * ops.indexer_k_quant_and_cache(k, kv_cache, slot_mapping, quant_block_size,
+ * scale_fmt); "FP8 naive cache": 128 bytes + 4-byte fp32 scale).
+ *   k_bf16        device bf16 bit patterns, row i at k_bf16 + i*k_row_stride,
+ *                 head_dim values; 8-byte aligned, k_row_stride % 4 == 0
+ *   slot_mapping  device int64 [num_tokens]; slot < 0 = padding, skipped;
+ *                 slot >= num_blocks*block_size is skipped too
+ * Per row: amax = max(max|x|, 1e-4); scale = smallest 2^e with
+ * amax <= 448 * 2^e; code_i = E4M3(x_i / scale) rounded to nearest, ties to
+ * even, sign of zero kept.  Only the bytes of the written slots change.
+ * num_tokens == 0 is a no-op.
+ */
+idx_status_t idx_quant_write_k(const uint16_t* k_bf16, int64_t num_tokens, int32_t head_dim,
+                               int64_t k_row_stride, const int64_t* slot_mapping,
+                               idx_kcache_t cache, hipStream_t stream);
+
+/*
+ * Quantise q per (token, head) group of 128 with power-of-two scales and fold
+ * the weights ([blog] Indexer.forward: per_token_group_quant_fp8(...,
+ * use_ue8m0=True), then weights * q_scale * softmax_scale * n_head^-0.5).
+ *   q_bf16        device bf16 bits [num_tokens, n_heads, head_dim], contiguous
+ *   w_raw         device fp32 [num_tokens, n_heads]
+ *   q_fp8         device out uint8 [num_tokens, n_heads, head_dim]
+ *   w_folded      device out fp32 [num_tokens, n_heads]:
+ *                 ((w_raw * q_scale) * softmax_scale) * n_heads^-0.5, fp32
+ *   q_scale_out   device out fp32 [num_tokens, n_heads], or NULL
+ * The quantiser is the one idx_quant_write_k uses.
+ */
+idx_status_t idx_quant_q_fold_w(const uint16_t* q_bf16, const float* w_raw, int64_t num_tokens,
+                                int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                uint8_t* q_fp8, float* w_folded, float* q_scale_out,
+                                hipStream_t stream);
+
+/*
+ * Lightning-indexer scores ([blog] SparseAttnIndexer / op body: fp8 q of 64
+ * heads, one shared fp8 K per position, folded fp32 weights):
+ *   logits[t*logits_stride + s] = ks[s] * sum_h w[t,h] * max(0, q8[t,h,:] . k8[s,:])
+ * for s in 0..p_t; entries with s > p_t are not written.
+ *   q_fp8   device uint8 [num_tokens, 64, 128], 16-byte aligned
+ *   w       device fp32 [num_tokens, 64] (q_scale etc. already folded in)
+ *   logits  device fp32, logits_stride >= max_seq_len
+ * Sums are fp32 (fp8 x fp8 products accumulated by the matrix cores).
+ */
+idx_status_t idx_logits(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
+                        idx_kcache_t cache, const idx_batch_t* batch,
+                        float* logits, int64_t logits_stride, hipStream_t stream);
+
+/* Workspace bytes idx_topk needs for this batch and k (0 for an empty batch). */
+size_t idx_topk_workspace_size(const idx_batch_t* batch, int32_t k);
+
+/*
+ * Top-k positions per query token into the persistent buffer ([blog] the
+ * buffer-allocation snippet: int32 [max_num_batched_tokens, index_topk]; the
+ * op body: entries not produced are -1).
+ * Row t considers positions 0..p_t of logits row t and keeps the k largest,
+ * ties broken by the lower position, -0.0 equal to +0.0.  The row holds the
+ * min(k, p_t + 1) selected positions in ascending order, then -1 up to k.
+ *   topk       device int32, row t at topk + t*topk_stride, topk_stride >= k
+ *   workspace  device, >= idx_topk_workspace_size(batch, k) bytes, 256-byte aligned
+ */
+idx_status_t idx_topk(const float* logits, int64_t logits_stride, const idx_batch_t* batch,
+                      int32_t k, int32_t* topk, int64_t topk_stride,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes idx_score_topk needs for this batch and k. */
+size_t idx_score_topk_workspace_size(const idx_batch_t* batch, int32_t k);
+
+/*
+ * idx_logits followed by idx_topk in one call; the scores live only in the
+ * workspace.  The selected rows are identical to idx_logits + idx_topk on
+ * the same inputs.
+ */
+idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
+                            idx_kcache_t cache, const idx_batch_t* batch, int32_t k,
+                            int32_t* topk, int64_t topk_stride,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * IndexCache schedule ([blog] skip_topk snippet; [pr] deepseek_v2.py snippet
+ * and Risks & impact).  Host-only.  is_full[l] = 1 for an F layer (runs the
+ * indexer, refreshes the top-k buffer), 0 for an S layer (reuses it).
+ *   use_index_cache == 0          every layer is F
+ *   pattern == NULL               F iff max(l - offset + 1, 0) % freq == 0
+ *   pattern != NULL               F iff pattern[l] == 'F'
+ * Returns IDX_ERR_INVALID_ARG if freq < 1, num_layers < 1, is_full is NULL,
+ * the pattern's length is not num_layers, it holds a character other than
+ * 'F' or 'S', or the resulting first layer is S (no producer would have
+ * written the buffer before it).
+ */
+idx_status_t idx_layer_schedule(int32_t use_index_cache, const char* pattern, int32_t freq,
+                                int32_t offset, int32_t num_layers, uint8_t* is_full);
+
+/*
+ * One indexer layer under IndexCache ([blog] MLA forward: the indexer runs
+ * only when the layer does not skip top-k; [pr] mla.py snippet).
+ * If is_full or write_k: idx_quant_write_k(layer->k_bf16 ...) into layer->cache.
+ * If is_full: idx_score_topk into topk.  An S layer leaves topk untouched, so
+ * its consumer reads the rows of the most recent F layer.
+ * layer->q_fp8 and layer->w may be NULL on S layers.
+ */
+typedef struct idx_layer_io {
+  const uint16_t* k_bf16;   /* new K rows [num_tokens, k_row_stride] bf16 bits */
+  int64_t k_row_stride;
+  idx_kcache_t cache;       /* this layer's K cache */
+  const uint8_t* q_fp8;     /* [num_tokens, 64, 128] */
+  const float* w;           /* [num_tokens, 64] */
+} idx_layer_io_t;
+
+idx_status_t idx_indexcache_layer(const idx_layer_io_t* layer, int32_t is_full, int32_t write_k,
+                                  const int64_t* slot_mapping, const idx_batch_t* batch, int32_t k,
+                                  int32_t* topk, int64_t topk_stride,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * A whole stack: idx_indexcache_layer for l = 0..num_layers-1 in order, with
+ * is_full from idx_layer_schedule (is_full[0] must be 1) and write_k_on_s
+ * choosing whether S layers still write their K rows.
+ */
+idx_status_t idx_indexcache_stack(const idx_layer_io_t* layers, int32_t num_layers,
+                                  const uint8_t* is_full, int32_t write_k_on_s,
+                                  const int64_t* slot_mapping, const idx_batch_t* batch, int32_t k,
+                                  int32_t* topk, int64_t topk_stride,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Logical -> physical top-k conversion ([group] SparseMLAIndexGroup,
+ * convert_logical_to_physical_topk / _convert_once): for token t of request
+ * r, physical = block_table[r][pos / block_size] * stride_rows + pos % block_size,
+ * -1 stays -1; valid_counts[t] = number of entries >= 0 in row t.
+ *   logical, physical   device int32 rows of k entries (strides >= k)
+ *   block_stride_rows   rows per physical block (0 = block_size)
+ *   valid_counts        device int32 [num_tokens] or NULL
+ * A logical position outside 0..p_t (or a block id outside the pool) gives -1.
+ */
+idx_status_t idx_topk_to_physical(const int32_t* logical, int64_t logical_stride,
+                                  const idx_batch_t* batch, int32_t block_size, int64_t num_blocks,
+                                  int32_t k, int64_t block_stride_rows,
+                                  int32_t* physical, int64_t physical_stride,
+                                  int32_t* valid_counts, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_H_ */

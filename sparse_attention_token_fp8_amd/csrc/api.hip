@@ -1,0 +1,279 @@
+// The C ABI of libidx: host-side argument checks, workspace carving and
+// kernel dispatch.  Nothing here allocates, frees or synchronises.
+
+#include <string.h>
+
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace idx;
+
+namespace {
+
+constexpr int kMaxTokens = 65535;  // grid y-extent used for per-token launches
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+idx_status_t check_cache(const idx_kcache_t& c) {
+  if (c.block_size != kBlock) return IDX_ERR_UNSUPPORTED;
+  if (c.num_blocks < 0) return IDX_ERR_INVALID_ARG;
+  if (c.num_blocks > 0 && (c.data == nullptr || !aligned(c.data, 16))) return IDX_ERR_INVALID_ARG;
+  return IDX_OK;
+}
+
+idx_status_t check_batch(const idx_batch_t* b) {
+  if (b == nullptr) return IDX_ERR_INVALID_ARG;
+  if (b->num_reqs < 1 || b->num_tokens < 0 || b->max_seq_len < 0 || b->max_query_len < 0)
+    return IDX_ERR_INVALID_ARG;
+  if (b->num_tokens > kMaxTokens) return IDX_ERR_UNSUPPORTED;
+  if (b->seq_lens == nullptr || b->query_start_loc == nullptr || b->block_table == nullptr)
+    return IDX_ERR_INVALID_ARG;
+  if (b->block_table_stride < (int64_t)(b->max_seq_len + kBlock - 1) / kBlock ||
+      b->block_table_stride < 1)
+    return IDX_ERR_INVALID_ARG;
+  if (b->max_query_len > b->num_tokens) return IDX_ERR_INVALID_ARG;
+  return IDX_OK;
+}
+
+BatchArgs to_args(const idx_batch_t* b) {
+  BatchArgs a;
+  a.seq_lens = b->seq_lens;
+  a.qsl = b->query_start_loc;
+  a.bt = b->block_table;
+  a.bt_stride = b->block_table_stride;
+  a.num_reqs = b->num_reqs;
+  a.num_tokens = b->num_tokens;
+  a.max_seq_len = b->max_seq_len;
+  a.max_query_len = b->max_query_len;
+  return a;
+}
+
+idx_status_t check_scoring(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                           int32_t head_dim, const idx_kcache_t& cache, const idx_batch_t* b) {
+  if (n_heads != kHeads || head_dim != kHeadDim) return IDX_ERR_UNSUPPORTED;
+  idx_status_t s = check_cache(cache);
+  if (s != IDX_OK) return s;
+  s = check_batch(b);
+  if (s != IDX_OK) return s;
+  if (b->num_tokens > 0 && (q_fp8 == nullptr || w == nullptr)) return IDX_ERR_INVALID_ARG;
+  if (!aligned(q_fp8, 16) || !aligned(w, 16)) return IDX_ERR_INVALID_ARG;
+  return IDX_OK;
+}
+
+idx_status_t check_k(int32_t k, int64_t topk_stride, const int32_t* topk, int32_t num_tokens) {
+  if (k < 1 || k > kMaxK) return IDX_ERR_UNSUPPORTED;
+  if (topk_stride < k) return IDX_ERR_INVALID_ARG;
+  if (num_tokens > 0 && topk == nullptr) return IDX_ERR_INVALID_ARG;
+  return IDX_OK;
+}
+
+int64_t fused_ld(const idx_batch_t* b) {
+  return (int64_t)align_up((size_t)std::max(b->max_seq_len, 1), (size_t)kBlock);
+}
+
+idx_status_t launched(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* idx_status_str(idx_status_t s) {
+  switch (s) {
+    case IDX_OK: return "ok";
+    case IDX_ERR_INVALID_ARG: return "invalid argument";
+    case IDX_ERR_UNSUPPORTED: return "unsupported shape";
+    case IDX_ERR_WORKSPACE: return "workspace missing or too small";
+    case IDX_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* idx_version(void) { return "idx 0.1 gfx950"; }
+
+idx_status_t idx_quant_write_k(const uint16_t* k_bf16, int64_t num_tokens, int32_t head_dim,
+                               int64_t k_row_stride, const int64_t* slot_mapping,
+                               idx_kcache_t cache, hipStream_t stream) {
+  if (head_dim != kHeadDim) return IDX_ERR_UNSUPPORTED;
+  idx_status_t s = check_cache(cache);
+  if (s != IDX_OK) return s;
+  if (num_tokens < 0) return IDX_ERR_INVALID_ARG;
+  if (num_tokens == 0) return IDX_OK;
+  if (k_bf16 == nullptr || slot_mapping == nullptr || cache.data == nullptr)
+    return IDX_ERR_INVALID_ARG;
+  if (k_row_stride < head_dim || (k_row_stride % 4) != 0 || !aligned(k_bf16, 8))
+    return IDX_ERR_INVALID_ARG;
+  return launched(launch_quant_write_k(k_bf16, num_tokens, k_row_stride, slot_mapping, cache.data,
+                                       cache.num_blocks * kBlock, stream));
+}
+
+idx_status_t idx_quant_q_fold_w(const uint16_t* q_bf16, const float* w_raw, int64_t num_tokens,
+                                int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                uint8_t* q_fp8, float* w_folded, float* q_scale_out,
+                                hipStream_t stream) {
+  if (n_heads != kHeads || head_dim != kHeadDim) return IDX_ERR_UNSUPPORTED;
+  if (num_tokens < 0) return IDX_ERR_INVALID_ARG;
+  if (num_tokens == 0) return IDX_OK;
+  if (q_bf16 == nullptr || w_raw == nullptr || q_fp8 == nullptr || w_folded == nullptr)
+    return IDX_ERR_INVALID_ARG;
+  if (!aligned(q_bf16, 8) || !aligned(q_fp8, 4)) return IDX_ERR_INVALID_ARG;
+  const float head_norm = (float)(1.0 / __builtin_sqrt((double)n_heads));
+  return launched(launch_quant_q_fold(q_bf16, w_raw, num_tokens * n_heads, softmax_scale,
+                                      head_norm, q_fp8, w_folded, q_scale_out, stream));
+}
+
+idx_status_t idx_logits(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
+                        idx_kcache_t cache, const idx_batch_t* batch, float* logits,
+                        int64_t logits_stride, hipStream_t stream) {
+  idx_status_t s = check_scoring(q_fp8, w, n_heads, head_dim, cache, batch);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens == 0) return IDX_OK;
+  if (logits == nullptr || logits_stride < batch->max_seq_len) return IDX_ERR_INVALID_ARG;
+  CacheArgs c{cache.data, cache.num_blocks};
+  return launched(launch_score(q_fp8, w, c, to_args(batch), logits, logits_stride, nullptr, 0,
+                               stream));
+}
+
+size_t idx_topk_workspace_size(const idx_batch_t* batch, int32_t k) {
+  if (batch == nullptr || batch->num_tokens <= 0 || k < 1) return 0;
+  return topk_workspace_layout(batch->num_tokens, k, 0, nullptr, nullptr);
+}
+
+idx_status_t idx_topk(const float* logits, int64_t logits_stride, const idx_batch_t* batch,
+                      int32_t k, int32_t* topk, int64_t topk_stride, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  idx_status_t s = check_batch(batch);
+  if (s != IDX_OK) return s;
+  s = check_k(k, topk_stride, topk, batch->num_tokens);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens == 0) return IDX_OK;
+  if (logits == nullptr || logits_stride < batch->max_seq_len) return IDX_ERR_INVALID_ARG;
+  const size_t need = idx_topk_workspace_size(batch, k);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+    return IDX_ERR_WORKSPACE;
+  TopkWorkspace ws;
+  topk_workspace_layout(batch->num_tokens, k, 0, workspace, &ws);
+  const BatchArgs b = to_args(batch);
+  hipError_t e = launch_topk_clear(ws, batch->num_tokens, stream);
+  if (e == hipSuccess) e = launch_topk_hist(logits, logits_stride, b, ws, k, stream);
+  if (e == hipSuccess) e = launch_topk_filter(logits, logits_stride, b, ws, k, topk, topk_stride, stream);
+  return launched(e);
+}
+
+size_t idx_score_topk_workspace_size(const idx_batch_t* batch, int32_t k) {
+  if (batch == nullptr || batch->num_tokens <= 0 || k < 1) return 0;
+  return topk_workspace_layout(batch->num_tokens, k, fused_ld(batch), nullptr, nullptr);
+}
+
+idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
+                            idx_kcache_t cache, const idx_batch_t* batch, int32_t k,
+                            int32_t* topk, int64_t topk_stride, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  idx_status_t s = check_scoring(q_fp8, w, n_heads, head_dim, cache, batch);
+  if (s != IDX_OK) return s;
+  s = check_k(k, topk_stride, topk, batch->num_tokens);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens == 0) return IDX_OK;
+  const size_t need = idx_score_topk_workspace_size(batch, k);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+    return IDX_ERR_WORKSPACE;
+  TopkWorkspace ws;
+  topk_workspace_layout(batch->num_tokens, k, fused_ld(batch), workspace, &ws);
+  const BatchArgs b = to_args(batch);
+  CacheArgs c{cache.data, cache.num_blocks};
+  hipError_t e = launch_topk_clear(ws, batch->num_tokens, stream);
+  const bool fused_hist = score_builds_hist(b);
+  if (e == hipSuccess)
+    e = launch_score(q_fp8, w, c, b, ws.logits, ws.ld, fused_hist ? &ws : nullptr, k, stream);
+  if (e == hipSuccess && !fused_hist) e = launch_topk_hist(ws.logits, ws.ld, b, ws, k, stream);
+  if (e == hipSuccess) e = launch_topk_filter(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
+  return launched(e);
+}
+
+idx_status_t idx_indexcache_layer(const idx_layer_io_t* layer, int32_t is_full, int32_t write_k,
+                                  const int64_t* slot_mapping, const idx_batch_t* batch, int32_t k,
+                                  int32_t* topk, int64_t topk_stride, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (layer == nullptr) return IDX_ERR_INVALID_ARG;
+  idx_status_t s = check_batch(batch);
+  if (s != IDX_OK) return s;
+  if (is_full) {
+    s = check_scoring(layer->q_fp8, layer->w, kHeads, kHeadDim, layer->cache, batch);
+    if (s != IDX_OK) return s;
+    s = check_k(k, topk_stride, topk, batch->num_tokens);
+    if (s != IDX_OK) return s;
+    if (batch->num_tokens > 0 &&
+        (workspace == nullptr || workspace_bytes < idx_score_topk_workspace_size(batch, k)))
+      return IDX_ERR_WORKSPACE;
+  }
+  if (is_full || write_k) {
+    s = idx_quant_write_k(layer->k_bf16, batch->num_tokens, kHeadDim, layer->k_row_stride,
+                          slot_mapping, layer->cache, stream);
+    if (s != IDX_OK) return s;
+  }
+  if (is_full)
+    return idx_score_topk(layer->q_fp8, layer->w, kHeads, kHeadDim, layer->cache, batch, k, topk,
+                          topk_stride, workspace, workspace_bytes, stream);
+  return IDX_OK;
+}
+
+idx_status_t idx_indexcache_stack(const idx_layer_io_t* layers, int32_t num_layers,
+                                  const uint8_t* is_full, int32_t write_k_on_s,
+                                  const int64_t* slot_mapping, const idx_batch_t* batch, int32_t k,
+                                  int32_t* topk, int64_t topk_stride, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (layers == nullptr || is_full == nullptr || num_layers < 1) return IDX_ERR_INVALID_ARG;
+  if (!is_full[0]) return IDX_ERR_INVALID_ARG;
+  // check every layer before enqueueing anything
+  idx_status_t s = check_batch(batch);
+  if (s != IDX_OK) return s;
+  for (int l = 0; l < num_layers; ++l) {
+    const idx_layer_io_t& L = layers[l];
+    s = check_cache(L.cache);
+    if (s != IDX_OK) return s;
+    if (is_full[l]) {
+      s = check_scoring(L.q_fp8, L.w, kHeads, kHeadDim, L.cache, batch);
+      if (s != IDX_OK) return s;
+    }
+    if ((is_full[l] || write_k_on_s) && batch->num_tokens > 0 &&
+        (L.k_bf16 == nullptr || L.k_row_stride < kHeadDim || (L.k_row_stride % 4) != 0 ||
+         !aligned(L.k_bf16, 8) || slot_mapping == nullptr || L.cache.data == nullptr))
+      return IDX_ERR_INVALID_ARG;
+  }
+  s = check_k(k, topk_stride, topk, batch->num_tokens);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens > 0 &&
+      (workspace == nullptr || workspace_bytes < idx_score_topk_workspace_size(batch, k) ||
+       !aligned(workspace, 256)))
+    return IDX_ERR_WORKSPACE;
+  for (int l = 0; l < num_layers; ++l) {
+    s = idx_indexcache_layer(&layers[l], is_full[l], write_k_on_s, slot_mapping, batch, k, topk,
+                             topk_stride, workspace, workspace_bytes, stream);
+    if (s != IDX_OK) return s;
+  }
+  return IDX_OK;
+}
+
+idx_status_t idx_topk_to_physical(const int32_t* logical, int64_t logical_stride,
+                                  const idx_batch_t* batch, int32_t block_size, int64_t num_blocks,
+                                  int32_t k, int64_t block_stride_rows, int32_t* physical,
+                                  int64_t physical_stride, int32_t* valid_counts,
+                                  hipStream_t stream) {
+  idx_status_t s = check_batch(batch);
+  if (s != IDX_OK) return s;
+  if (k < 1 || k > kMaxK) return IDX_ERR_UNSUPPORTED;
+  if (block_size < 1 || num_blocks < 0 || block_stride_rows < 0) return IDX_ERR_INVALID_ARG;
+  const int64_t stride_rows = block_stride_rows ? block_stride_rows : block_size;
+  if (stride_rows < block_size) return IDX_ERR_INVALID_ARG;
+  if (num_blocks * stride_rows > (int64_t)INT32_MAX) return IDX_ERR_UNSUPPORTED;
+  if (batch->block_table_stride * block_size < batch->max_seq_len) return IDX_ERR_INVALID_ARG;
+  if (logical_stride < k || physical_stride < k) return IDX_ERR_INVALID_ARG;
+  if (batch->num_tokens == 0) return IDX_OK;
+  if (logical == nullptr || physical == nullptr) return IDX_ERR_INVALID_ARG;
+  return launched(launch_topk_to_physical(logical, logical_stride, to_args(batch), block_size,
+                                          num_blocks, k, stride_rows, physical, physical_stride,
+                                          valid_counts, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Kernel launchers (internal).  Each enqueues on `stream` and returns the
+// launch status; argument checking happens in api.cpp before any of these.
+#pragma once
+
+#include "common.hpp"
+
+namespace idx {
+
+hipError_t launch_quant_write_k(const uint16_t* k, int64_t num_rows, int64_t stride,
+                                const int64_t* slots, uint8_t* cache, int64_t num_slots,
+                                hipStream_t stream);
+
+hipError_t launch_quant_q_fold(const uint16_t* q, const float* w_raw, int64_t num_rows,
+                               float softmax_scale, float head_norm, uint8_t* q8, float* w_out,
+                               float* qs_out, hipStream_t stream);
+
+// Scores into `logits` (row stride ld).  With `ws` non-null the decode kernel
+// also builds the level-1 histogram and picks each long row's threshold digit
+// (rows with more than k positions).
+hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cache,
+                        const BatchArgs& b, float* logits, int64_t ld, const TopkWorkspace* ws,
+                        int k, hipStream_t stream);
+
+// True if launch_score fills the histogram itself for this batch.
+bool score_builds_hist(const BatchArgs& b);
+
+hipError_t launch_topk_clear(const TopkWorkspace& ws, int64_t T, hipStream_t stream);
+hipError_t launch_topk_hist(const float* logits, int64_t ld, const BatchArgs& b,
+                            const TopkWorkspace& ws, int k, hipStream_t stream);
+hipError_t launch_topk_filter(const float* logits, int64_t ld, const BatchArgs& b,
+                              const TopkWorkspace& ws, int k, int32_t* out, int64_t ldo,
+                              hipStream_t stream);
+
+hipError_t launch_topk_to_physical(const int32_t* logical, int64_t ldl, const BatchArgs& b,
+                                   int block_size, int64_t num_blocks, int k, int64_t stride_rows,
+                                   int32_t* physical, int64_t ldp, int32_t* valid,
+                                   hipStream_t stream);
+
+}  // namespace idx

@@ -1,0 +1,251 @@
+"""GPU parity of each entry point against the oracle on small, ragged shapes.
+
+Sizes span several tiles, blocks and work-groups with ragged tails; every
+comparison is element by element against the CPU oracle on the same seeded
+raw inputs.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import quant as oquant, topk as otopk
+from synth import f32_to_bf16_bits, random_batch
+from tests.fp8_bruteforce import all_finite_bf16_bits
+from tests.gpu_helpers import (check_logits_row, check_topk_band, device_batch, device_layer,
+                               oracle_batch, oracle_layer, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_token_fp8_amd as m
+    return m, torch
+
+
+# ------------------------------------------------------------ quantiser --
+
+def _special_rows(rng):
+    rows = rng.standard_normal((40, 128)).astype(np.float32)
+    rows[0] = 0.0
+    rows[1] = -0.0
+    rows[2] = 1e-6                     # below the amax floor
+    rows[3, :] = 0.0
+    rows[3, 7] = 448.0 * 4             # amax exactly on a power-of-two boundary
+    rows[4] *= 1e30
+    rows[5] *= 1e-30                   # bf16 subnormals
+    rows[6] = np.float32(2.0 ** -130)
+    rows[7, ::2] = -rows[7, ::2] * 1e-8  # mixed tiny magnitudes that round to (signed) zero
+    return f32_to_bf16_bits(rows)
+
+
+def test_quant_write_k_bitexact(env):
+    m, torch = env
+    rng = np.random.default_rng(1001)
+    bits = np.concatenate([_special_rows(rng),
+                           f32_to_bf16_bits(rng.standard_normal((1000, 128)).astype(np.float32))])
+    nb = 20
+    slots = rng.permutation(nb * 64)[:bits.shape[0]].astype(np.int64)
+    slots[::17] = -1                   # padding tokens
+    say("quant_write_k: rows", bits.shape[0], "pool", nb)
+    cache = m.KCache(nb, fill=0xA5)
+    m.idx_quant_write_k(torch.from_numpy(bits.view(np.int16)).cuda(),
+                        torch.from_numpy(slots).cuda(), cache)
+    got = cache.tensor.cpu().numpy()
+    want = np.full((nb, 64, 132), 0xA5, np.uint8)
+    oquant.quant_write_k(want, bits, slots)
+    assert np.array_equal(got, want)
+
+
+def test_quant_write_k_strided_rows(env):
+    m, torch = env
+    rng = np.random.default_rng(1002)
+    full = f32_to_bf16_bits(rng.standard_normal((300, 192)).astype(np.float32))  # kw[:, :128] view
+    slots = np.arange(300, dtype=np.int64)
+    cache = m.KCache(5, fill=0)
+    t = torch.from_numpy(full.view(np.int16)).cuda()
+    m.idx_quant_write_k(t[:, :128], torch.from_numpy(slots).cuda(), cache)
+    want = np.zeros((5, 64, 132), np.uint8)
+    oquant.quant_write_k(want, np.ascontiguousarray(full[:, :128]), slots)
+    assert np.array_equal(cache.tensor.cpu().numpy(), want)
+
+
+def test_quant_all_finite_bf16_patterns(env):
+    m, torch = env
+    bits = all_finite_bf16_bits()
+    pad = (-bits.size) % 128
+    bits = np.concatenate([bits, np.zeros(pad, np.uint16)])
+    rng = np.random.default_rng(1003)
+    for arrangement in ("sorted", "shuffled"):
+        b = bits if arrangement == "sorted" else rng.permutation(bits)
+        rows = b.reshape(-1, 128)
+        nb = -(-rows.shape[0] // 64)
+        slots = np.arange(rows.shape[0], dtype=np.int64)
+        cache = m.KCache(nb, fill=0)
+        m.idx_quant_write_k(torch.from_numpy(rows.view(np.int16)).cuda(),
+                            torch.from_numpy(slots).cuda(), cache)
+        want = np.zeros((nb, 64, 132), np.uint8)
+        oquant.quant_write_k(want, rows, slots)
+        assert np.array_equal(cache.tensor.cpu().numpy(), want), arrangement
+
+
+def test_quant_q_fold_bitexact(env):
+    m, torch = env
+    rng = np.random.default_rng(1004)
+    x = rng.standard_normal((37, 64, 128)).astype(np.float32)
+    x[3, 5] = 0.0
+    x[4, 9] *= 1e5
+    qb = f32_to_bf16_bits(x)
+    w_raw = rng.standard_normal((37, 64)).astype(np.float32)
+    q8, w, qs = m.idx_quant_q_fold_w(torch.from_numpy(qb.view(np.int16)).cuda(),
+                                     torch.from_numpy(w_raw).cuda())
+    oq8, oqs = oquant.quantize_q(qb)
+    ow = oquant.fold_weights(w_raw, oqs)
+    assert np.array_equal(q8.cpu().numpy(), oq8)
+    assert np.array_equal(qs.cpu().numpy(), oqs)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+
+
+# --------------------------------------------------------------- scores --
+
+def _run_logits(m, torch, wl, seed_note):
+    dev = device_layer(m, torch, wl, 0, with_new=True)
+    orc = oracle_layer(wl, 0)
+    # the device cache must equal the oracle's byte for byte before scores are compared
+    assert np.array_equal(dev["cache"].tensor.cpu().numpy(), orc["cache"]), seed_note
+    assert np.array_equal(dev["q8"].cpu().numpy(), orc["q8"])
+    batch = device_batch(m, wl)
+    logits = torch.full((wl.num_tokens, wl.max_seq_len + 5), float("nan"), device="cuda")
+    m.idx_logits(dev["q8"], dev["w"], dev["cache"], batch, logits=logits)
+    got = logits.cpu().numpy()
+    want = oracle.logits.logits(orc["q8"], orc["w"], orc["cache"], oracle_batch(wl))
+    for t, row in want.items():
+        n = row.shape[0]
+        check_logits_row(got[t, :n], row, f"{seed_note} token {t}")
+        assert np.all(np.isnan(got[t, n:])), f"{seed_note} token {t}: wrote past p_t"
+    return dev, orc, batch, got, want
+
+
+def test_logits_decode_ragged(env):
+    m, torch = env
+    wl = random_batch(2001, [1, 63, 64, 65, 127, 1000, 3000, 4097], 1, k=64)
+    say("logits decode ragged", wl.seq_lens.tolist())
+    _run_logits(m, torch, wl, "decode")
+
+
+def test_logits_prefill_ragged(env):
+    m, torch = env
+    wl = random_batch(2002, [100, 1500, 64, 700], [100, 37, 10, 1], k=64)
+    say("logits prefill ragged", wl.seq_lens.tolist(), wl.new_tokens.tolist())
+    _run_logits(m, torch, wl, "prefill")
+
+
+def test_decode_and_prefill_kernels_agree_bitwise(env):
+    m, torch = env
+    L = 2000
+    wl1 = random_batch(2003, [L], 1, k=64)
+    wl3 = random_batch(2003, [L], 3, k=64)       # same draws; three new tokens, the last at L-1
+    d1 = device_layer(m, torch, wl1, 0, with_new=True)
+    d3 = device_layer(m, torch, wl3, 0, with_new=True)
+    assert np.array_equal(d1["cache"].tensor.cpu().numpy(), d3["cache"].tensor.cpu().numpy())
+    q8 = d3["q8"].clone()
+    w = d3["w"].clone()
+    q8[2] = d1["q8"][0]
+    w[2] = d1["w"][0]
+    a = m.idx_logits(d1["q8"], d1["w"], d1["cache"], device_batch(m, wl1))
+    b = m.idx_logits(q8, w, d3["cache"], device_batch(m, wl3))
+    assert np.array_equal(a[0].cpu().numpy().view(np.uint32), b[2].cpu().numpy().view(np.uint32))
+
+
+# ---------------------------------------------------------------- top-k --
+
+def _topk_case(m, torch, lengths, k, gen):
+    wl = random_batch(3000 + len(lengths), lengths, 1, k=k)
+    T = wl.num_tokens
+    L = wl.max_seq_len
+    scores = np.full((T, L), np.nan, np.float32)
+    for t, n in enumerate(wl.seq_lens):
+        scores[t, :n] = gen(t, int(n))
+    batch = device_batch(m, wl)
+    got = m.idx_topk(torch.from_numpy(scores).cuda(), batch, k).cpu().numpy()
+    for t, n in enumerate(wl.seq_lens):
+        want = otopk.topk_row(scores[t, :n].astype(np.float64), k)
+        assert np.array_equal(got[t], want), f"row {t} n={n} k={k}"
+
+
+def test_topk_exact_random(env):
+    m, torch = env
+    rng = np.random.default_rng(3001)
+    lengths = [1, 5, 64, 255, 256, 257, 1000, 4095, 4096, 4097, 9000, 40000]
+    _topk_case(m, torch, lengths, 256, lambda t, n: rng.standard_normal(n).astype(np.float32))
+    _topk_case(m, torch, lengths, 2048, lambda t, n: rng.standard_normal(n).astype(np.float32))
+
+
+def test_topk_exact_with_ties(env):
+    m, torch = env
+    rng = np.random.default_rng(3002)
+    lengths = [300, 2049, 5000, 20000]
+    # coarse values: many exact ties at the threshold, signed zeros mixed in
+    def gen(t, n):
+        v = (rng.integers(-20, 21, n) * 0.25).astype(np.float32)
+        v[rng.random(n) < 0.1] = -0.0
+        return v
+    _topk_case(m, torch, lengths, 100, gen)
+    _topk_case(m, torch, lengths, 2048, gen)
+
+
+def test_topk_candidate_overflow_path(env):
+    m, torch = env
+    # every score equal: the threshold bin holds the whole row (beyond the list capacity)
+    _topk_case(m, torch, [10000, 70000], 100, lambda t, n: np.full(n, 1.5, np.float32))
+    rng = np.random.default_rng(3003)
+    _topk_case(m, torch, [9000], 2000,
+               lambda t, n: (1.0 + rng.integers(0, 4, n) * 2.0 ** -20).astype(np.float32))
+
+
+def test_score_topk_fused_equals_unfused(env):
+    m, torch = env
+    for wl in (random_batch(4001, [100, 3000, 5000, 20000], 1, k=512),
+               random_batch(4002, [3000, 900], [300, 50], k=256)):
+        dev = device_layer(m, torch, wl, 0, with_new=True)
+        batch = device_batch(m, wl)
+        lg = m.idx_logits(dev["q8"], dev["w"], dev["cache"], batch)
+        a = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+        b = m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], batch, wl.k).cpu().numpy()
+        assert np.array_equal(a, b)
+
+
+def test_score_topk_vs_oracle(env):
+    m, torch = env
+    for wl in (random_batch(4003, [70, 2100, 5000, 9000], 1, k=2048),
+               random_batch(4004, [1200, 3000], [200, 40], k=300)):
+        dev = device_layer(m, torch, wl, 0, with_new=True)
+        orc = oracle_layer(wl, 0)
+        got = m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], device_batch(m, wl), wl.k).cpu().numpy()
+        want = oracle.logits.logits(orc["q8"], orc["w"], orc["cache"], oracle_batch(wl))
+        for t, sc in want.items():
+            check_topk_band(got[t], sc, wl.k, f"token {t}")
+
+
+def test_topk_to_physical(env):
+    m, torch = env
+    wl = random_batch(5001, [100, 700, 64], [2, 1, 3], k=32, pool_factor=2.0)
+    rng = np.random.default_rng(5002)
+    pos = wl.token_pos()
+    logical = np.full((wl.num_tokens, 32), -1, np.int32)
+    for t in range(wl.num_tokens):
+        n = int(pos[t]) + 1
+        c = rng.choice(n, min(n, 20), replace=False)
+        logical[t, :c.size] = c
+    logical[0, 25] = 10 ** 6                 # outside the causal range -> -1
+    batch = device_batch(m, wl)
+    phys, valid = m.idx_topk_to_physical(torch.from_numpy(logical).cuda(), batch, wl.num_blocks)
+    lg = logical.copy()
+    lg[0, 25] = -1
+    want, wv = oracle.physical.to_physical(lg, wl.token_req(), wl.block_table, 64)
+    assert np.array_equal(phys.cpu().numpy(), want)
+    assert np.array_equal(valid.cpu().numpy(), wv)
