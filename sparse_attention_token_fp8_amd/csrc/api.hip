@@ -131,13 +131,12 @@ idx_status_t idx_logits(const uint8_t* q_fp8, const float* w, int32_t n_heads, i
   if (batch->num_tokens == 0) return IDX_OK;
   if (logits == nullptr || logits_stride < batch->max_seq_len) return IDX_ERR_INVALID_ARG;
   CacheArgs c{cache.data, cache.num_blocks};
-  return launched(launch_score(q_fp8, w, c, to_args(batch), logits, logits_stride, nullptr, 0,
-                               stream));
+  return launched(launch_score(q_fp8, w, c, to_args(batch), logits, logits_stride, stream));
 }
 
 size_t idx_topk_workspace_size(const idx_batch_t* batch, int32_t k) {
   if (batch == nullptr || batch->num_tokens <= 0 || k < 1) return 0;
-  return topk_workspace_layout(batch->num_tokens, k, 0, nullptr, nullptr);
+  return topk_workspace_layout(batch->num_tokens, batch->max_seq_len, 0, nullptr, nullptr);
 }
 
 idx_status_t idx_topk(const float* logits, int64_t logits_stride, const idx_batch_t* batch,
@@ -153,17 +152,15 @@ idx_status_t idx_topk(const float* logits, int64_t logits_stride, const idx_batc
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
     return IDX_ERR_WORKSPACE;
   TopkWorkspace ws;
-  topk_workspace_layout(batch->num_tokens, k, 0, workspace, &ws);
-  const BatchArgs b = to_args(batch);
-  hipError_t e = launch_topk_clear(ws, batch->num_tokens, stream);
-  if (e == hipSuccess) e = launch_topk_hist(logits, logits_stride, b, ws, k, stream);
-  if (e == hipSuccess) e = launch_topk_filter(logits, logits_stride, b, ws, k, topk, topk_stride, stream);
-  return launched(e);
+  topk_workspace_layout(batch->num_tokens, batch->max_seq_len, 0, workspace, &ws);
+  return launched(launch_topk(logits, logits_stride, to_args(batch), ws, k, topk, topk_stride,
+                              stream));
 }
 
 size_t idx_score_topk_workspace_size(const idx_batch_t* batch, int32_t k) {
   if (batch == nullptr || batch->num_tokens <= 0 || k < 1) return 0;
-  return topk_workspace_layout(batch->num_tokens, k, fused_ld(batch), nullptr, nullptr);
+  return topk_workspace_layout(batch->num_tokens, batch->max_seq_len, fused_ld(batch), nullptr,
+                               nullptr);
 }
 
 idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
@@ -179,15 +176,11 @@ idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_head
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
     return IDX_ERR_WORKSPACE;
   TopkWorkspace ws;
-  topk_workspace_layout(batch->num_tokens, k, fused_ld(batch), workspace, &ws);
+  topk_workspace_layout(batch->num_tokens, batch->max_seq_len, fused_ld(batch), workspace, &ws);
   const BatchArgs b = to_args(batch);
   CacheArgs c{cache.data, cache.num_blocks};
-  hipError_t e = launch_topk_clear(ws, batch->num_tokens, stream);
-  const bool fused_hist = score_builds_hist(b);
-  if (e == hipSuccess)
-    e = launch_score(q_fp8, w, c, b, ws.logits, ws.ld, fused_hist ? &ws : nullptr, k, stream);
-  if (e == hipSuccess && !fused_hist) e = launch_topk_hist(ws.logits, ws.ld, b, ws, k, stream);
-  if (e == hipSuccess) e = launch_topk_filter(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
+  hipError_t e = launch_score(q_fp8, w, c, b, ws.logits, ws.ld, stream);
+  if (e == hipSuccess) e = launch_topk(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
   return launched(e);
 }
 

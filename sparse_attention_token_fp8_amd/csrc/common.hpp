@@ -17,8 +17,7 @@ constexpr int kBlockBytes = kBlock * kTokenBytes;  // 8448
 constexpr int kCodeBytes = kBlock * kHeadDim;      // 8192: the scales follow the codes
 constexpr int kMaxK = 2048;
 
-// Top-k radix digits: bits [31:21] of the order key (level 1, also the
-// histogram the scoring kernels build), then [20:10], then [9:0].
+// Top-k radix digits of the order key: bits [31:21], then [20:10], then [9:0].
 constexpr int kBins1 = 2048;
 constexpr int kShift1 = 21;
 constexpr int kBins2 = 2048;
@@ -45,61 +44,49 @@ struct CacheArgs {
   int64_t num_blocks;
 };
 
-// Per-row top-k bookkeeping in the workspace (64 bytes per row).
-struct RowState {
-  uint32_t done_hist;    // producer work-groups finished (histogram complete when == chunks)
-  uint32_t done_filter;  // filter work-groups finished
-  uint32_t b1;           // level-1 threshold digit
-  uint32_t need;         // k - #(digit > b1)
-  uint32_t n_above;      // append counter of the above list
-  uint32_t n_cand;       // append counter of the candidate list
-  uint32_t cand_total;   // hist[b1]
-  uint32_t pad[9];
-};
-
-// Workspace carve-up shared by the host sizing code and the launchers.
+// Top-k workspace (device, caller-owned).  The fused entry point keeps the
+// scores in `logits`; the long-row launch shape keeps each (row, 4096-position
+// chunk) candidate slot in `cand` with its count in `counts`.
 struct TopkWorkspace {
-  RowState* state;     // [T]
-  uint32_t* hist;      // [T][kBins1]
-  int32_t* above;      // [T][k]
-  uint32_t* cand;      // [T][cap][2] (key, position)
   float* logits;       // [T][ld] (fused path only)
+  uint32_t* cand;      // [T][nchunks][4096][2] (key, position)
+  uint32_t* counts;    // [T][nchunks]
   int64_t ld;
-  int32_t cap;
-  int32_t k;
+  int32_t nchunks;
+  int32_t pad;
 };
-
-constexpr int kCandCap = 4096;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Layout of a top-k workspace for T rows; returns total bytes.  When base is
-// non-null also fills `ws`.
-inline size_t topk_workspace_layout(int64_t T, int32_t k, int64_t logits_ld, void* base,
+bool topk_uses_long_rows(int64_t T, int max_seq_len);
+int topk_nchunks(int max_seq_len);
+int topk_chunk();
+
+// Layout of the workspace for T rows of up to max_seq_len positions; returns
+// the total bytes.  When base is non-null also fills `ws`.  logits_ld is 0 for
+// idx_topk (scores come from the caller).
+inline size_t topk_workspace_layout(int64_t T, int max_seq_len, int64_t logits_ld, void* base,
                                     TopkWorkspace* ws) {
+  const bool lr = topk_uses_long_rows(T, max_seq_len);
+  const int64_t nch = lr ? topk_nchunks(max_seq_len) : 0;
   size_t off = 0;
-  const size_t o_state = off;  off = align_up(off + sizeof(RowState) * (size_t)T, 256);
-  const size_t o_hist = off;   off = align_up(off + sizeof(uint32_t) * kBins1 * (size_t)T, 256);
-  const size_t o_above = off;  off = align_up(off + sizeof(int32_t) * (size_t)k * (size_t)T, 256);
-  const size_t o_cand = off;   off = align_up(off + 2 * sizeof(uint32_t) * kCandCap * (size_t)T, 256);
-  const size_t o_logits = off; off = align_up(off + sizeof(float) * (size_t)logits_ld * (size_t)T, 256);
+  const size_t o_logits = off;
+  off = align_up(off + sizeof(float) * (size_t)logits_ld * (size_t)T, 256);
+  const size_t o_cand = off;
+  off = align_up(off + 2 * sizeof(uint32_t) * (size_t)topk_chunk() * (size_t)nch * (size_t)T, 256);
+  const size_t o_counts = off;
+  off = align_up(off + sizeof(uint32_t) * (size_t)nch * (size_t)T, 256);
+  if (off == 0) off = 256;
   if (base && ws) {
     char* b = static_cast<char*>(base);
-    ws->state = reinterpret_cast<RowState*>(b + o_state);
-    ws->hist = reinterpret_cast<uint32_t*>(b + o_hist);
-    ws->above = reinterpret_cast<int32_t*>(b + o_above);
-    ws->cand = reinterpret_cast<uint32_t*>(b + o_cand);
     ws->logits = logits_ld ? reinterpret_cast<float*>(b + o_logits) : nullptr;
+    ws->cand = reinterpret_cast<uint32_t*>(b + o_cand);
+    ws->counts = reinterpret_cast<uint32_t*>(b + o_counts);
     ws->ld = logits_ld;
-    ws->cap = kCandCap;
-    ws->k = k;
+    ws->nchunks = (int32_t)nch;
+    ws->pad = 0;
   }
   return off;
-}
-
-// Bytes the per-call clear must zero (state + histograms).
-inline size_t topk_workspace_clear_bytes(int64_t T) {
-  return align_up(sizeof(RowState) * (size_t)T, 256) + sizeof(uint32_t) * kBins1 * (size_t)T;
 }
 
 // ---------------------------------------------------------------- device --
@@ -143,11 +130,6 @@ __device__ __forceinline__ int64_t phys_block(const BatchArgs& b, const CacheArg
   if (lb < 0 || lb >= b.bt_stride) return -1;
   const int64_t blk = b.bt[(int64_t)r * b.bt_stride + lb];
   return (blk >= 0 && blk < c.num_blocks) ? blk : -1;
-}
-
-// Agent-scope loads of values other work-groups updated with atomics.
-__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace idx

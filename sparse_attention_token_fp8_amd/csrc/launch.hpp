@@ -14,22 +14,13 @@ hipError_t launch_quant_q_fold(const uint16_t* q, const float* w_raw, int64_t nu
                                float softmax_scale, float head_norm, uint8_t* q8, float* w_out,
                                float* qs_out, hipStream_t stream);
 
-// Scores into `logits` (row stride ld).  With `ws` non-null the decode kernel
-// also builds the level-1 histogram and picks each long row's threshold digit
-// (rows with more than k positions).
+// Scores into `logits` (row stride ld).
 hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cache,
-                        const BatchArgs& b, float* logits, int64_t ld, const TopkWorkspace* ws,
-                        int k, hipStream_t stream);
+                        const BatchArgs& b, float* logits, int64_t ld, hipStream_t stream);
 
-// True if launch_score fills the histogram itself for this batch.
-bool score_builds_hist(const BatchArgs& b);
-
-hipError_t launch_topk_clear(const TopkWorkspace& ws, int64_t T, hipStream_t stream);
-hipError_t launch_topk_hist(const float* logits, int64_t ld, const BatchArgs& b,
-                            const TopkWorkspace& ws, int k, hipStream_t stream);
-hipError_t launch_topk_filter(const float* logits, int64_t ld, const BatchArgs& b,
-                              const TopkWorkspace& ws, int k, int32_t* out, int64_t ldo,
-                              hipStream_t stream);
+// Top-k rows from scores (row stride ld) into out (row stride ldo).
+hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, const TopkWorkspace& ws,
+                       int k, int32_t* out, int64_t ldo, hipStream_t stream);
 
 hipError_t launch_topk_to_physical(const int32_t* logical, int64_t ldl, const BatchArgs& b,
                                    int block_size, int64_t num_blocks, int k, int64_t stride_rows,

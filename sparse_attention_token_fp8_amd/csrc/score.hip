@@ -20,7 +20,6 @@
 
 #include "common.hpp"
 #include "launch.hpp"
-#include "topk_device.hpp"
 
 namespace idx {
 namespace {
@@ -115,10 +114,9 @@ __device__ __forceinline__ const uint8_t* block_base(const BatchArgs& b, const C
 // consecutive 64-position blocks of its causal range and its four waves take
 // every fourth block.  Each wave keeps the next block's loads in flight while
 // it scores the current one.
-template <bool kHist>
 __global__ __launch_bounds__(256) void score_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    float* __restrict__ logits, int64_t ld, TopkWorkspace ws, int k, int chunk_blocks) {
+    float* __restrict__ logits, int64_t ld, int chunk_blocks) {
   const int t = blockIdx.y;
   const TokenPos tp = token_pos(b, t);
   const int n = tp.n;
@@ -127,14 +125,6 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   const int nblk = min(chunk_blocks, (n - lb0 * kBlock + kBlock - 1) / kBlock);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, G = lane >> 4;
-  const bool hist = kHist && n > k;
-
-  __shared__ uint32_t lhist[kHist ? kBins1 : 1];
-  __shared__ uint32_t scratch[8];
-  if (hist) {
-    for (int i = threadIdx.x; i < kBins1; i += kThreads) lhist[i] = 0;
-    __syncthreads();
-  }
 
   QFrag f;
   load_q(f, q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
@@ -150,16 +140,9 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
     for (int tl = 0; tl < 4; ++tl) {
       const float v = tile_score(f, cur.b[tl]) * cur.ks[tl];
       const int s = sb + tl * 16 + c;
-      if (G == 0 && s < n) {
-        out[s] = v;
-        if (hist) atomicAdd(&lhist[order_key(v) >> kShift1], 1u);
-      }
+      if (G == 0 && s < n) out[s] = v;
     }
     if (more) cur = nxt;
-  }
-  if (hist) {
-    const int chunks = (n + chunk_blocks * kBlock - 1) / (chunk_blocks * kBlock);
-    finish_hist(ws, t, k, chunks, lhist, scratch);
   }
 }
 
@@ -244,24 +227,15 @@ int prefill_chunk_blocks(const BatchArgs& b) {
 
 }  // namespace
 
-bool score_builds_hist(const BatchArgs& b) { return b.max_query_len <= 1; }
-
 hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cache,
-                        const BatchArgs& b, float* logits, int64_t ld, const TopkWorkspace* ws,
-                        int k, hipStream_t stream) {
+                        const BatchArgs& b, float* logits, int64_t ld, hipStream_t stream) {
   if (b.num_tokens == 0 || b.max_seq_len == 0) return hipSuccess;
   if (b.max_query_len <= 1) {
     const int cb = kDecodeChunkBlocks;
     const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
     const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
-    if (ws) {
-      hipLaunchKernelGGL(score_decode_kernel<true>, grid, dim3(256), 0, stream, q8, w, cache, b,
-                         logits, ld, *ws, k, cb);
-    } else {
-      TopkWorkspace none{};
-      hipLaunchKernelGGL(score_decode_kernel<false>, grid, dim3(256), 0, stream, q8, w, cache, b,
-                         logits, ld, none, k, cb);
-    }
+    hipLaunchKernelGGL(score_decode_kernel, grid, dim3(256), 0, stream, q8, w, cache, b, logits,
+                       ld, cb);
   } else {
     const int cb = prefill_chunk_blocks(b);
     const int gpr = (b.max_query_len + 4 * kPrefillTPW - 1) / (4 * kPrefillTPW);

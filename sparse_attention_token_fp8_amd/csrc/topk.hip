@@ -1,24 +1,16 @@
-// Radix top-k select over the causal scores of each query token.
+// Top-k select over the causal scores of each query token (see
+// topk_device.hpp for the rule and the method).  Two launch shapes:
 //
-// Pages: IndexCache blog post -- the persistent topk_indices_buffer is int32
-// [max_num_batched_tokens, index_topk] and entries not produced hold -1 (the op
-// body and the buffer-allocation snippet).  Selection rule: the k largest
-// scores of positions 0..p_t, ties to the lower position, -0 == +0; a row lists
-// the selected positions in ascending order, then -1.
+//   many rows    one 1024-thread work-group per row: tau from the row's sample,
+//                candidates (key >= tau) compacted into LDS, exact select,
+//                ordered write-out.  No global scratch, no atomics outside LDS.
+//   few long rows  filter: work-groups of 4096 positions compact their
+//                candidates into a private slot of the workspace (no atomics,
+//                nothing to clear); resolve: one work-group per row gathers
+//                the slots and finishes as above.
 //
-// Scores map to order-preserving 32-bit keys.  Digits are bits [31:21],
-// [20:10], [9:0].
-//   1. level-1 histogram of the row (here, or fused into the decode scoring
-//      kernel); the last work-group of the row picks b1, the digit that holds
-//      the k-th largest key;
-//   2. filter: every key with digit > b1 is selected outright (fewer than k of
-//      them); keys with digit == b1 become candidates (key, position);
-//   3. the last filter work-group of the row resolves the candidates with two
-//      more LDS histograms to the exact k-th key K* and the number of keys equal
-//      to K* still to take (lowest positions first), then writes the row in
-//      ascending position order through an LDS bitmap, segment by segment.
-// When a row's candidate bin is larger than the workspace list, step 3 reads
-// the row itself instead of the list.
+// Neither shape uses device-scope atomics or fences: work-groups meet only at
+// kernel boundaries.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -27,269 +19,203 @@
 namespace idx {
 namespace {
 
-constexpr int kChunk = 4096;               // positions per work-group in hist / filter
-constexpr int kPerThread = kChunk / kThreads;
-constexpr int kSeg = 65536;                // positions per bitmap segment in the resolve
-constexpr int kSegWords = kSeg / 32;
-constexpr int kWordsPerThread = kSegWords / kThreads;
+constexpr int kRowThreads = 1024;
+constexpr int kCandCap = 8192;       // LDS candidate capacity per row
+constexpr int kBatch = 8;            // loads in flight per thread in the row kernel
 
-__global__ __launch_bounds__(256) void clear_kernel(uint4* __restrict__ p, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-    p[i] = make_uint4(0, 0, 0, 0);
+// Trivial rows (p_t + 1 <= k): every position, then -1.
+template <int NT>
+__device__ __forceinline__ void write_all(int32_t* out, int n, int k) {
+  for (int j = threadIdx.x; j < k; j += NT) out[j] = j < n ? j : -1;
 }
 
-__global__ __launch_bounds__(256) void hist_kernel(const float* __restrict__ logits, int64_t ld,
-                                                   BatchArgs b, TopkWorkspace ws, int k) {
-  const int t = blockIdx.y;
-  const int n = token_pos(b, t).n;
-  if (n <= k) return;
-  const int s0 = blockIdx.x * kChunk;
-  if (s0 >= n) return;
-  __shared__ uint32_t lhist[kBins1];
-  __shared__ uint32_t scratch[8];
-  for (int i = threadIdx.x; i < kBins1; i += kThreads) lhist[i] = 0;
-  __syncthreads();
-  const float* row = logits + (size_t)t * ld;
-#pragma unroll 4
-  for (int i = 0; i < kPerThread; ++i) {
-    const int s = s0 + threadIdx.x + i * kThreads;
-    if (s < n) atomicAdd(&lhist[order_key(row[s]) >> kShift1], 1u);
+// Append (key, pos) to an LDS candidate list with one LDS atomic per wave.
+__device__ __forceinline__ void append_wave(bool p, uint32_t key, int pos, uint32_t* count,
+                                            uint32_t* ckey, int32_t* cpos, uint32_t cap) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t m = __ballot(p);
+  uint32_t base = 0;
+  if (lane == 0 && m) base = atomicAdd(count, (uint32_t)__popcll(m));
+  base = (uint32_t)__shfl((int)base, 0);
+  if (p) {
+    const uint32_t slot = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+    if (slot < cap) { ckey[slot] = key; cpos[slot] = pos; }
   }
-  finish_hist(ws, t, k, (n + kChunk - 1) / kChunk, lhist, scratch);
 }
 
-// Visit the candidates of row t (digit == b1): from the list, or from the row.
-template <typename F>
-__device__ __forceinline__ void for_each_candidate(const TopkWorkspace& ws, const float* row, int n,
-                                                   int t, uint32_t b1, bool use_list,
-                                                   uint32_t n_list, F&& fn) {
-  if (use_list) {
-    const uint32_t* cl = ws.cand + (size_t)t * ws.cap * 2;
-    for (uint32_t i = threadIdx.x; i < n_list; i += kThreads) fn(cl[2 * i], (int)cl[2 * i + 1]);
+// Exact select over the candidates held in LDS (k <= C <= kCandCap), else over
+// the whole row, then the ordered write-out.
+template <int NT>
+__device__ __forceinline__ void finish_row(const float* __restrict__ row, int n, int k, uint32_t C,
+                                           const uint32_t* ckey, const int32_t* cpos,
+                                           int32_t* __restrict__ out, uint32_t* work,
+                                           uint32_t* scratch) {
+  uint32_t take;
+  if (C >= (uint32_t)k && C <= (uint32_t)kCandCap) {
+    auto visit = [&](auto&& fn) {
+      for (uint32_t i = threadIdx.x; i < C; i += NT) fn(ckey[i], cpos[i]);
+    };
+    const uint32_t kstar = radix_kth<NT>(visit, (uint32_t)k, &take, work, scratch);
+    emit_row<NT>(visit, n, kstar, take, k, out, work, scratch);
   } else {
-    for (int s = threadIdx.x; s < n; s += kThreads) {
-      const uint32_t key = order_key(row[s]);
-      if ((key >> kShift1) == b1) fn(key, s);
-    }
+    auto visit = [&](auto&& fn) {
+      for (int s = threadIdx.x; s < n; s += NT) fn(order_key(row[s]), s);
+    };
+    const uint32_t kstar = radix_kth<NT>(visit, (uint32_t)k, &take, work, scratch);
+    emit_row<NT>(visit, n, kstar, take, k, out, work, scratch);
   }
 }
 
-// Find the digit d (0..nb-1, searched from the top) with
-// #(digit > d) < need <= #(digit >= d) in an LDS histogram; returns d and
-// sets *above = #(digit > d).  All threads get the result.
-__device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32_t need,
-                                               uint32_t* above, uint32_t* scratch) {
-  const int per = nb / kThreads;  // 8 or 4
-  const int top = nb - 1 - per * (int)threadIdx.x;
-  uint32_t sum = 0;
-  for (int j = 0; j < per; ++j) sum += h[top - j];
-  uint32_t total;
-  const uint32_t before = block_exclusive_scan(sum, &total, scratch);
-  if (before < need && before + sum >= need) {
-    uint32_t cum = before;
-    for (int j = 0; j < per; ++j) {
-      const uint32_t c = h[top - j];
-      if (cum + c >= need) {
-        scratch[5] = (uint32_t)(top - j);
-        scratch[6] = cum;
-        break;
-      }
-      cum += c;
-    }
-  }
-  __syncthreads();
-  const uint32_t d = scratch[5];
-  *above = scratch[6];
-  __syncthreads();
-  return d;
-}
-
-__device__ void resolve_row(const TopkWorkspace& ws, const float* row, int n, int t, int k,
-                            int32_t* out, uint32_t* lds, uint32_t* scratch) {
-  RowState* st = ws.state + t;
-  const uint32_t b1 = st->b1;
-  const uint32_t n_above = min(load_agent(&st->n_above), (uint32_t)k);
-  const uint32_t cand_total = st->cand_total;
-  const bool use_list = cand_total <= (uint32_t)ws.cap;
-  const uint32_t n_list = use_list ? min(load_agent(&st->n_cand), (uint32_t)ws.cap) : 0u;
-  const uint32_t need = (uint32_t)k - n_above;   // >= 1
-
-  // level 2: digit [20:10] among the candidates
-  for (int i = threadIdx.x; i < kBins2; i += kThreads) lds[i] = 0;
-  __syncthreads();
-  for_each_candidate(ws, row, n, t, b1, use_list, n_list, [&](uint32_t key, int) {
-    atomicAdd(&lds[(key >> kShift2) & (kBins2 - 1)], 1u);
-  });
-  __syncthreads();
-  uint32_t above2;
-  const uint32_t b2 = find_digit(lds, kBins2, need, &above2, scratch);
-  const uint32_t need2 = need - above2;
-
-  // level 3: digit [9:0] among candidates with digits (b1, b2)
-  for (int i = threadIdx.x; i < kBins3; i += kThreads) lds[i] = 0;
-  __syncthreads();
-  for_each_candidate(ws, row, n, t, b1, use_list, n_list, [&](uint32_t key, int) {
-    if (((key >> kShift2) & (kBins2 - 1)) == b2) atomicAdd(&lds[key & (kBins3 - 1)], 1u);
-  });
-  __syncthreads();
-  uint32_t above3;
-  const uint32_t b3 = find_digit(lds, kBins3, need2, &above3, scratch);
-  const uint32_t take_eq = need2 - above3;        // keys equal to K* to take, lowest positions first
-  const uint32_t kstar = (b1 << kShift1) | (b2 << kShift2) | b3;
-
-  // emit in ascending position order, one bitmap segment at a time
-  uint32_t* sel = lds;
-  uint32_t* tie = lds + kSegWords;
-  const int32_t* al = ws.above + (size_t)t * k;
-  uint32_t written = 0, ties_taken = 0;
-  for (int g0 = 0; g0 < n; g0 += kSeg) {
-    for (int i = threadIdx.x; i < 2 * kSegWords; i += kThreads) lds[i] = 0;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < n_above; i += kThreads) {
-      const int s = al[i] - g0;
-      if (s >= 0 && s < kSeg) atomicOr(&sel[s >> 5], 1u << (s & 31));
-    }
-    for_each_candidate(ws, row, n, t, b1, use_list, n_list, [&](uint32_t key, int pos) {
-      const int s = pos - g0;
-      if (s < 0 || s >= kSeg) return;
-      if (key > kstar) atomicOr(&sel[s >> 5], 1u << (s & 31));
-      else if (key == kstar) atomicOr(&tie[s >> 5], 1u << (s & 31));
-    });
-    __syncthreads();
-    // ties: keep the first (take_eq - ties_taken) of this segment, in order
-    const int w0 = threadIdx.x * kWordsPerThread;
-    uint32_t my_ties = 0;
-    for (int j = 0; j < kWordsPerThread; ++j) my_ties += __popc(tie[w0 + j]);
-    uint32_t seg_ties;
-    uint32_t tie_before = ties_taken + block_exclusive_scan(my_ties, &seg_ties, scratch);
-    for (int j = 0; j < kWordsPerThread; ++j) {
-      uint32_t word = tie[w0 + j];
-      while (word) {
-        const uint32_t bit = word & (0u - word);
-        word ^= bit;
-        if (tie_before < take_eq) sel[w0 + j] |= bit;
-        ++tie_before;
-      }
-    }
-    ties_taken += seg_ties;
-    __syncthreads();
-    uint32_t my_sel = 0;
-    for (int j = 0; j < kWordsPerThread; ++j) my_sel += __popc(sel[w0 + j]);
-    uint32_t seg_sel;
-    uint32_t o = written + block_exclusive_scan(my_sel, &seg_sel, scratch);
-    for (int j = 0; j < kWordsPerThread; ++j) {
-      uint32_t word = sel[w0 + j];
-      while (word) {
-        const int bitpos = __ffs(word) - 1;
-        word &= word - 1;
-        if (o < (uint32_t)k) out[o] = g0 + (w0 + j) * 32 + bitpos;
-        ++o;
-      }
-    }
-    written += seg_sel;
-    __syncthreads();
-  }
-  for (uint32_t i = written + threadIdx.x; i < (uint32_t)k; i += kThreads) out[i] = -1;
-}
-
-__global__ __launch_bounds__(256) void filter_kernel(const float* __restrict__ logits, int64_t ld,
-                                                     BatchArgs b, TopkWorkspace ws, int k,
-                                                     int32_t* __restrict__ topk, int64_t ldo) {
-  const int t = blockIdx.y;
+__global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __restrict__ logits,
+                                                                int64_t ld, BatchArgs b, int k,
+                                                                int32_t* __restrict__ topk,
+                                                                int64_t ldo) {
+  const int t = blockIdx.x;
   const int n = token_pos(b, t).n;
   int32_t* out = topk + (size_t)t * ldo;
-  if (n <= k) {  // every causal position is selected
-    if (blockIdx.x == 0)
-      for (int j = threadIdx.x; j < k; j += kThreads) out[j] = j < n ? j : -1;
+  if (n <= k) {
+    write_all<kRowThreads>(out, n, k);
     return;
   }
-  const int s0 = blockIdx.x * kChunk;
-  if (s0 >= n) return;
-  __shared__ uint32_t lds[2 * kSegWords];
-  __shared__ uint32_t scratch[8];
+  __shared__ uint32_t ckey[kCandCap];
+  __shared__ int32_t cpos[kCandCap];
+  __shared__ uint32_t work[2 * kSegWords];
+  __shared__ uint32_t scratch[32];
+  __shared__ uint32_t count;
   const float* row = logits + (size_t)t * ld;
-  RowState* st = ws.state + t;
-  const uint32_t b1 = st->b1;
-  const bool use_list = st->cand_total <= (uint32_t)ws.cap;
+  const uint32_t tau = row_tau<kRowThreads>(row, n, k, kCandCap, work, scratch);
+  if (threadIdx.x == 0) count = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += kRowThreads * kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {
+      const int s = base + threadIdx.x + e * kRowThreads;
+      v[e] = s < n ? row[s] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {
+      const int s = base + threadIdx.x + e * kRowThreads;
+      const uint32_t key = order_key(v[e]);
+      append_wave(s < n && key >= tau, key, s, &count, ckey, cpos, kCandCap);
+    }
+  }
+  __syncthreads();
+  finish_row<kRowThreads>(row, n, k, count, ckey, cpos, out, work, scratch);
+}
 
-  uint32_t keys[kPerThread];
-  uint32_t na = 0, nc = 0;
+// ---------------------------------------------------------- long rows --
+constexpr int kChunk = 4096;          // positions per filter work-group
+constexpr int kPer = kChunk / kThreads;
+
+__global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __restrict__ logits,
+                                                               int64_t ld, BatchArgs b, int k,
+                                                               TopkWorkspace ws,
+                                                               int32_t* __restrict__ topk,
+                                                               int64_t ldo) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x;
+  const int n = token_pos(b, t).n;
+  if (n <= k) {
+    if (c == 0) write_all<kThreads>(topk + (size_t)t * ldo, n, k);
+    return;
+  }
+  const int s0 = c * kChunk;
+  if (s0 >= n) return;
+  __shared__ uint32_t work[kBins1];
+  __shared__ uint32_t scratch[16];
+  __shared__ uint32_t count;
+  const float* row = logits + (size_t)t * ld;
+  const uint32_t tau = row_tau<kThreads>(row, n, k, 4 * k, work, scratch);
+  if (threadIdx.x == 0) count = 0;
+  __syncthreads();
+  uint32_t* slot = ws.cand + ((size_t)t * ws.nchunks + c) * kChunk * 2;
+  float v[kPer];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int s = s0 + threadIdx.x + i * kThreads;
-    uint32_t key = 0;
-    if (s < n) {
-      key = order_key(row[s]);
-      const uint32_t d = key >> kShift1;
-      na += d > b1;
-      nc += (d == b1 && use_list);
-    }
-    keys[i] = key;
+  for (int e = 0; e < kPer; ++e) {
+    const int s = s0 + threadIdx.x + e * kThreads;
+    v[e] = s < n ? row[s] : 0.f;
   }
-  uint32_t tot;
-  const uint32_t pre = block_exclusive_scan(na | (nc << 16), &tot, scratch);
-  if (threadIdx.x == 0) {
-    scratch[4] = (tot & 0xFFFF) ? atomicAdd(&st->n_above, tot & 0xFFFF) : 0u;
-    scratch[5] = (tot >> 16) ? atomicAdd(&st->n_cand, tot >> 16) : 0u;
-  }
-  __syncthreads();
-  uint32_t ia = scratch[4] + (pre & 0xFFFF);
-  uint32_t ic = scratch[5] + (pre >> 16);
-  int32_t* al = ws.above + (size_t)t * k;
-  uint32_t* cl = ws.cand + (size_t)t * ws.cap * 2;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int s = s0 + threadIdx.x + i * kThreads;
-    if (s >= n) continue;
-    const uint32_t d = keys[i] >> kShift1;
-    if (d > b1) {
-      if (ia < (uint32_t)k) al[ia] = s;
-      ++ia;
-    } else if (d == b1 && use_list) {
-      if (ic < (uint32_t)ws.cap) { cl[2 * ic] = keys[i]; cl[2 * ic + 1] = (uint32_t)s; }
-      ++ic;
+  for (int e = 0; e < kPer; ++e) {
+    const int s = s0 + threadIdx.x + e * kThreads;
+    const uint32_t key = order_key(v[e]);
+    const bool p = s < n && key >= tau;
+    const uint64_t m = __ballot(p);
+    uint32_t base = 0;
+    if (lane == 0 && m) base = atomicAdd(&count, (uint32_t)__popcll(m));
+    base = (uint32_t)__shfl((int)base, 0);
+    if (p) {
+      const uint32_t i = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+      slot[2 * i] = key;
+      slot[2 * i + 1] = (uint32_t)s;
     }
   }
-  __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t chunks = (uint32_t)((n + kChunk - 1) / kChunk);
-    scratch[7] = (atomicAdd(&st->done_filter, 1u) == chunks - 1) ? 1u : 0u;
+  if (threadIdx.x == 0) ws.counts[(size_t)t * ws.nchunks + c] = count;
+}
+
+__global__ __launch_bounds__(kRowThreads) void topk_resolve_kernel(const float* __restrict__ logits,
+                                                                   int64_t ld, BatchArgs b, int k,
+                                                                   TopkWorkspace ws,
+                                                                   int32_t* __restrict__ topk,
+                                                                   int64_t ldo) {
+  const int t = blockIdx.x;
+  const int n = token_pos(b, t).n;
+  if (n <= k) return;                          // written by the filter
+  __shared__ uint32_t ckey[kCandCap];
+  __shared__ int32_t cpos[kCandCap];
+  __shared__ uint32_t work[2 * kSegWords];
+  __shared__ uint32_t scratch[32];
+  __shared__ uint32_t count;
+  const int nch = (n + kChunk - 1) / kChunk;
+  const uint32_t* cnts = ws.counts + (size_t)t * ws.nchunks;
+  uint32_t C = 0;
+  for (int c = 0; c < nch; ++c) C += cnts[c];
+  const float* row = logits + (size_t)t * ld;
+  int32_t* out = topk + (size_t)t * ldo;
+  if (C >= (uint32_t)k && C <= (uint32_t)kCandCap) {
+    // gather the chunk slots into LDS
+    uint32_t off = 0;
+    for (int c = 0; c < nch; ++c) {
+      const uint32_t cn = cnts[c];
+      const uint32_t* slot = ws.cand + ((size_t)t * ws.nchunks + c) * kChunk * 2;
+      for (uint32_t i = threadIdx.x; i < cn; i += kRowThreads) {
+        ckey[off + i] = slot[2 * i];
+        cpos[off + i] = (int32_t)slot[2 * i + 1];
+      }
+      off += cn;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (scratch[7]) {
-    __threadfence();
-    resolve_row(ws, row, n, t, k, out, lds, scratch);
-  }
+  (void)count;
+  finish_row<kRowThreads>(row, n, k, C, ckey, cpos, out, work, scratch);
 }
 
 }  // namespace
 
-hipError_t launch_topk_clear(const TopkWorkspace& ws, int64_t T, hipStream_t stream) {
-  const int64_t n16 = (int64_t)(topk_workspace_clear_bytes(T) / 16);
-  if (n16 == 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 4096);
-  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<uint4*>(ws.state), n16);
-  return hipGetLastError();
-}
+bool topk_uses_long_rows(int64_t T, int max_seq_len) { return T < 256 && max_seq_len > 8192; }
 
-hipError_t launch_topk_hist(const float* logits, int64_t ld, const BatchArgs& b,
-                            const TopkWorkspace& ws, int k, hipStream_t stream) {
-  if (b.num_tokens == 0 || b.max_seq_len <= k) return hipSuccess;
-  const dim3 grid((unsigned)((b.max_seq_len + kChunk - 1) / kChunk), (unsigned)b.num_tokens);
-  hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, stream, logits, ld, b, ws, k);
-  return hipGetLastError();
-}
+int topk_nchunks(int max_seq_len) { return (max_seq_len + kChunk - 1) / kChunk; }
 
-hipError_t launch_topk_filter(const float* logits, int64_t ld, const BatchArgs& b,
-                              const TopkWorkspace& ws, int k, int32_t* out, int64_t ldo,
-                              hipStream_t stream) {
+int topk_chunk() { return kChunk; }
+
+hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, const TopkWorkspace& ws,
+                       int k, int32_t* out, int64_t ldo, hipStream_t stream) {
   if (b.num_tokens == 0) return hipSuccess;
-  const int chunks = std::max(1, (b.max_seq_len + kChunk - 1) / kChunk);
-  const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
-  hipLaunchKernelGGL(filter_kernel, grid, dim3(256), 0, stream, logits, ld, b, ws, k, out, ldo);
+  if (topk_uses_long_rows(b.num_tokens, b.max_seq_len)) {
+    const dim3 grid((unsigned)std::max(1, topk_nchunks(b.max_seq_len)), (unsigned)b.num_tokens);
+    hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kThreads), 0, stream, logits, ld, b, k, ws,
+                       out, ldo);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_resolve_kernel, dim3((unsigned)b.num_tokens), dim3(kRowThreads), 0,
+                       stream, logits, ld, b, k, ws, out, ldo);
+  } else {
+    hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)b.num_tokens), dim3(kRowThreads), 0,
+                       stream, logits, ld, b, k, out, ldo);
+  }
   return hipGetLastError();
 }
 

