@@ -6,17 +6,22 @@
 // heads share one fp8 K per position, folded fp32 weights; the score's form is
 // the DSA lightning indexer's.)
 //
-// The head dot products are one v_mfma_f32_16x16x128_f8f6f4 per 16 heads x 16
-// positions: A = q rows of 16 heads (128 fp8 each), B = 16 K rows.  The MFMA
-// leaves D[head 4*(lane/16)+i][position lane%16] in lane `lane`, register i,
-// so the ReLU and the head weighting run in registers right after the MFMA,
-// each lane summing its 16 heads, and two cross-lane adds finish the 64-head
-// sum.  Both operands use the same byte->k assignment (lane group G = lane/16
-// holds k in [16G, 16G+16) and [64+16G, 64+16G+16)), so the contraction covers
-// all 128 dimensions whatever the hardware's own k order is.
+// Work unit: one token x one 64-position K block (four 16-position tiles).
+//  * Per tile, four v_mfma_f32_16x16x128_f8f6f4 (16 heads x 16 positions x 128
+//    dims each).  Lane `lane` receives D[head 4*(lane/16)+i][position lane%16]
+//    in register i.  Both operands use the same byte->k assignment (lane group
+//    G = lane/16 holds k in [16G, 16G+16) and [64+16G, 64+16G+16)), so the
+//    contraction covers all 128 dims whatever the hardware's k order is.
+//  * The ReLU and head weighting run in registers on the MFMA output; each lane
+//    sums its 16 heads of a tile.  Two accumulator sets alternate so the next
+//    tile's MFMAs run while the previous tile's epilogue executes.
+//  * The four per-tile partials (each split over the four lane groups) are
+//    reduced and transposed at once with v_permlane32_swap / v_permlane16_swap:
+//    afterwards lane `lane` holds the full 64-head sum of one position,
+//    16*tile(lane/16) + lane%16 with tile(r) = {0, 2, 1, 3}[r].
 //
 // Every kernel computes a score with exactly this sequence of operations, so
-// all kernels and all entry points give bit-identical scores.
+// all kernels and entry points give bit-identical scores.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -30,6 +35,22 @@ struct QFrag {
   v8i a[4];
   float w[16];
 };
+
+// One 64-position block: the four tiles' B operands and the scale of the
+// position this lane ends up holding.
+struct KBlock {
+  v8i b[4];
+  float ks;
+};
+
+struct TileAcc {
+  v4f d[4];
+};
+
+__device__ __forceinline__ int lane_pos(int lane) {
+  const int r = lane >> 4;
+  return 16 * (((r & 1) << 1) | (r >> 1)) + (lane & 15);
+}
 
 __device__ __forceinline__ v8i pack8(uint4 lo, uint4 hi) {
   v8i r;
@@ -61,37 +82,12 @@ __device__ __forceinline__ void zero_q(QFrag& f) {
   }
 }
 
-// Head-weighted ReLU sum for the 16 positions of one K tile; every lane of a
-// column (lane % 16) returns the same value.
-__device__ __forceinline__ float tile_score(const QFrag& f, const v8i& b) {
-  float part = 0.f;
-#pragma unroll
-  for (int hg = 0; hg < 4; ++hg) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.a[hg], b, acc, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part = fmaf(f.w[hg * 4 + i], fmaxf(acc[i], 0.f), part);
-  }
-  part += __shfl_xor(part, 16);
-  part += __shfl_xor(part, 32);
-  return part;
-}
-
-// The four 16-position tiles of one 64-position block: B operands and scales.
-struct KBlock {
-  v8i b[4];
-  float ks[4];
-};
-
-__device__ __forceinline__ void load_kblock(KBlock& kb, const uint8_t* __restrict__ base,
-                                            int lane) {
+__device__ __forceinline__ void load_kblock(KBlock& kb, const uint8_t* __restrict__ base, int lane) {
   const int c = lane & 15, G = lane >> 4;
   if (base == nullptr) {
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl) {
-      kb.b[tl] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      kb.ks[tl] = 0.f;
-    }
+    for (int tl = 0; tl < 4; ++tl) kb.b[tl] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    kb.ks = 0.f;
     return;
   }
 #pragma unroll
@@ -99,8 +95,56 @@ __device__ __forceinline__ void load_kblock(KBlock& kb, const uint8_t* __restric
     const uint8_t* row = base + (tl * 16 + c) * kHeadDim;
     kb.b[tl] = pack8(*reinterpret_cast<const uint4*>(row + 16 * G),
                      *reinterpret_cast<const uint4*>(row + 64 + 16 * G));
-    kb.ks[tl] = *reinterpret_cast<const float*>(base + kCodeBytes + (tl * 16 + c) * 4);
   }
+  kb.ks = *reinterpret_cast<const float*>(base + kCodeBytes + lane_pos(lane) * 4);
+}
+
+__device__ __forceinline__ void tile_mfma(TileAcc& acc, const QFrag& f, const v8i& b) {
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    acc.d[hg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.a[hg], b, zero, 0, 0, 0, 0, 0, 0);
+  }
+}
+
+// This lane's 16 heads of one tile: sum of w * max(d, 0) in a fixed order.
+__device__ __forceinline__ float tile_epilogue(const QFrag& f, const TileAcc& acc) {
+  float part = 0.f;
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part = fmaf(f.w[hg * 4 + i], fmaxf(acc.d[hg][i], 0.f), part);
+  return part;
+}
+
+// Reduce four per-tile partials over the lane groups and transpose, so that
+// each lane returns the complete sum of position lane_pos(lane).
+__device__ __forceinline__ float reduce_block(float p0, float p1, float p2, float p3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+  const float z = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p2), __float_as_uint(p3), false, false);
+  const float y = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(y), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Scores of one block for NT tokens: out[j] is token j's score at position
+// lane_pos(lane).  Work items (token, tile) are issued token-fastest and
+// pipelined two deep.
+template <int NT>
+__device__ __forceinline__ void block_scores(const QFrag* f, const KBlock& kb, float* out) {
+  constexpr int NI = 4 * NT;
+  float part[NT][4];
+  TileAcc acc[2];
+  tile_mfma(acc[0], f[0], kb.b[0]);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i + 1 < NI) tile_mfma(acc[(i + 1) & 1], f[(i + 1) % NT], kb.b[(i + 1) / NT]);
+    part[i % NT][i / NT] = tile_epilogue(f[i % NT], acc[i & 1]);
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+    out[j] = reduce_block(part[j][0], part[j][1], part[j][2], part[j][3]) * kb.ks;
 }
 
 __device__ __forceinline__ const uint8_t* block_base(const BatchArgs& b, const CacheArgs& c, int r,
@@ -112,8 +156,8 @@ __device__ __forceinline__ const uint8_t* block_base(const BatchArgs& b, const C
 // ------------------------------------------------------------- decode --
 // One query token per work-group; the work-group covers `chunk_blocks`
 // consecutive 64-position blocks of its causal range and its four waves take
-// every fourth block.  Each wave keeps the next block's loads in flight while
-// it scores the current one.
+// every fourth block.  Two block buffers alternate so the next block's loads
+// are in flight while the current one is scored.
 __global__ __launch_bounds__(256) void score_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int chunk_blocks) {
@@ -124,32 +168,32 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   if (lb0 * kBlock >= n) return;
   const int nblk = min(chunk_blocks, (n - lb0 * kBlock + kBlock - 1) / kBlock);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, G = lane >> 4;
+  const int lp = lane_pos(lane);
 
-  QFrag f;
-  load_q(f, q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
+  QFrag f[1];
+  load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
   float* out = logits + (size_t)t * ld;
 
-  KBlock cur, nxt;
-  if (wave < nblk) load_kblock(cur, block_base(b, cache, tp.r, lb0 + wave), lane);
-  for (int bi = wave; bi < nblk; bi += 4) {
-    const bool more = bi + 4 < nblk;
-    if (more) load_kblock(nxt, block_base(b, cache, tp.r, lb0 + bi + 4), lane);
-    const int sb = (lb0 + bi) * kBlock;
-#pragma unroll
-    for (int tl = 0; tl < 4; ++tl) {
-      const float v = tile_score(f, cur.b[tl]) * cur.ks[tl];
-      const int s = sb + tl * 16 + c;
-      if (G == 0 && s < n) out[s] = v;
-    }
-    if (more) cur = nxt;
+  KBlock k0, k1;
+  if (wave < nblk) load_kblock(k0, block_base(b, cache, tp.r, lb0 + wave), lane);
+  for (int bi = wave; bi < nblk; bi += 8) {
+    if (bi + 4 < nblk) load_kblock(k1, block_base(b, cache, tp.r, lb0 + bi + 4), lane);
+    float v;
+    block_scores<1>(f, k0, &v);
+    int s = (lb0 + bi) * kBlock + lp;
+    if (s < n) out[s] = v;
+    if (bi + 4 >= nblk) break;
+    if (bi + 8 < nblk) load_kblock(k0, block_base(b, cache, tp.r, lb0 + bi + 8), lane);
+    block_scores<1>(f, k1, &v);
+    s = (lb0 + bi + 4) * kBlock + lp;
+    if (s < n) out[s] = v;
   }
 }
 
 // ------------------------------------------------------------ prefill --
 // A work-group takes 4*TPW consecutive query tokens of one request (TPW per
 // wave) and `chunk_blocks` blocks of positions; all four waves walk the same
-// blocks, so each K tile is fetched from HBM once per work-group and reused
+// blocks, so each K block is fetched from HBM once per work-group and reused
 // from the caches by the other waves.
 template <int TPW>
 __global__ __launch_bounds__(256) void score_prefill_kernel(
@@ -174,7 +218,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
   if (lb0 * kBlock >= n_max) return;
   const int nblk = min(chunk_blocks, (n_max - lb0 * kBlock + kBlock - 1) / kBlock);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, G = lane >> 4;
+  const int lp = lane_pos(lane);
 
   QFrag f[TPW];
   int nt[TPW];
@@ -194,27 +238,37 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     }
   }
 
-  KBlock cur, nxt;
-  load_kblock(cur, block_base(b, cache, r, lb0), lane);
-  for (int bi = 0; bi < nblk; ++bi) {
-    const bool more = bi + 1 < nblk;
-    if (more) load_kblock(nxt, block_base(b, cache, r, lb0 + bi + 1), lane);
-    const int sb = (lb0 + bi) * kBlock;
+  KBlock k0, k1;
+  load_kblock(k0, block_base(b, cache, r, lb0), lane);
+  for (int bi = 0; bi < nblk; bi += 2) {
+    if (bi + 1 < nblk) load_kblock(k1, block_base(b, cache, r, lb0 + bi + 1), lane);
+    float v[TPW];
+    block_scores<TPW>(f, k0, v);
+    int s = (lb0 + bi) * kBlock + lp;
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl) {
-      const int s = sb + tl * 16 + c;
+    for (int j = 0; j < TPW; ++j)
+      if (s < nt[j]) out[j][s] = v[j];
+    if (bi + 1 >= nblk) break;
+    if (bi + 2 < nblk) load_kblock(k0, block_base(b, cache, r, lb0 + bi + 2), lane);
+    block_scores<TPW>(f, k1, v);
+    s = (lb0 + bi + 1) * kBlock + lp;
 #pragma unroll
-      for (int j = 0; j < TPW; ++j) {
-        const float v = tile_score(f[j], cur.b[tl]) * cur.ks[tl];
-        if (G == 0 && s < nt[j]) out[j][s] = v;
-      }
-    }
-    if (more) cur = nxt;
+    for (int j = 0; j < TPW; ++j)
+      if (s < nt[j]) out[j][s] = v[j];
   }
 }
 
-constexpr int kDecodeChunkBlocks = 16;   // 1024 positions per work-group
 constexpr int kPrefillTPW = 2;
+
+// Decode chunk: about three work-groups per CU over the whole batch, at least
+// 8 and at most 64 blocks per work-group.
+int decode_chunk_blocks(const BatchArgs& b) {
+  const int64_t blocks_per_row = (b.max_seq_len + kBlock - 1) / kBlock;
+  const int64_t total = blocks_per_row * b.num_tokens;
+  int64_t cb = (total + 767) / 768;
+  cb = (cb + 3) / 4 * 4;
+  return (int)std::min<int64_t>(64, std::max<int64_t>(8, cb));
+}
 
 int prefill_chunk_blocks(const BatchArgs& b) {
   // aim for a few thousand work-groups; never more blocks than the longest row needs
@@ -231,7 +285,7 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
                         const BatchArgs& b, float* logits, int64_t ld, hipStream_t stream) {
   if (b.num_tokens == 0 || b.max_seq_len == 0) return hipSuccess;
   if (b.max_query_len <= 1) {
-    const int cb = kDecodeChunkBlocks;
+    const int cb = decode_chunk_blocks(b);
     const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
     const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
     hipLaunchKernelGGL(score_decode_kernel, grid, dim3(256), 0, stream, q8, w, cache, b, logits,
