@@ -27,7 +27,7 @@ idx_status_t check_batch(const idx_batch_t* b) {
   if (b == nullptr) return IDX_ERR_INVALID_ARG;
   if (b->num_reqs < 1 || b->num_tokens < 0 || b->max_seq_len < 0 || b->max_query_len < 0)
     return IDX_ERR_INVALID_ARG;
-  if (b->num_tokens > kMaxTokens) return IDX_ERR_UNSUPPORTED;
+  if (b->num_tokens > kMaxTokens || b->max_seq_len > topk_max_seq_len()) return IDX_ERR_UNSUPPORTED;
   if (b->seq_lens == nullptr || b->query_start_loc == nullptr || b->block_table == nullptr)
     return IDX_ERR_INVALID_ARG;
   if (b->block_table_stride < (int64_t)(b->max_seq_len + kBlock - 1) / kBlock ||

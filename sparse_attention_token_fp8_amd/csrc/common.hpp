@@ -46,10 +46,11 @@ struct CacheArgs {
 
 // Top-k workspace (device, caller-owned).  The fused entry point keeps the
 // scores in `logits`; the long-row launch shape keeps each (row, 4096-position
-// chunk) candidate slot in `cand` with its count in `counts`.
+// chunk) candidate slot in `cand_key` / `cand_pos` with its count in `counts`.
 struct TopkWorkspace {
   float* logits;       // [T][ld] (fused path only)
-  uint32_t* cand;      // [T][nchunks][4096][2] (key, position)
+  uint32_t* cand_key;  // [T][nchunks][4096]
+  int32_t* cand_pos;   // [T][nchunks][4096]
   uint32_t* counts;    // [T][nchunks]
   int64_t ld;
   int32_t nchunks;
@@ -61,6 +62,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool topk_uses_long_rows(int64_t T, int max_seq_len);
 int topk_nchunks(int max_seq_len);
 int topk_chunk();
+int topk_max_seq_len();
 
 // Layout of the workspace for T rows of up to max_seq_len positions; returns
 // the total bytes.  When base is non-null also fills `ws`.  logits_ld is 0 for
@@ -72,15 +74,18 @@ inline size_t topk_workspace_layout(int64_t T, int max_seq_len, int64_t logits_l
   size_t off = 0;
   const size_t o_logits = off;
   off = align_up(off + sizeof(float) * (size_t)logits_ld * (size_t)T, 256);
-  const size_t o_cand = off;
-  off = align_up(off + 2 * sizeof(uint32_t) * (size_t)topk_chunk() * (size_t)nch * (size_t)T, 256);
+  const size_t o_ckey = off;
+  off = align_up(off + sizeof(uint32_t) * (size_t)topk_chunk() * (size_t)nch * (size_t)T, 256);
+  const size_t o_cpos = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)topk_chunk() * (size_t)nch * (size_t)T, 256);
   const size_t o_counts = off;
   off = align_up(off + sizeof(uint32_t) * (size_t)nch * (size_t)T, 256);
   if (off == 0) off = 256;
   if (base && ws) {
     char* b = static_cast<char*>(base);
     ws->logits = logits_ld ? reinterpret_cast<float*>(b + o_logits) : nullptr;
-    ws->cand = reinterpret_cast<uint32_t*>(b + o_cand);
+    ws->cand_key = reinterpret_cast<uint32_t*>(b + o_ckey);
+    ws->cand_pos = reinterpret_cast<int32_t*>(b + o_cpos);
     ws->counts = reinterpret_cast<uint32_t*>(b + o_counts);
     ws->ld = logits_ld;
     ws->nchunks = (int32_t)nch;

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restr
     cnt += o >= 0;
   }
   uint32_t total;
-  (void)block_exclusive_scan(cnt, &total, scratch);
+  (void)block_scan_excl<kThreads>(cnt, &total, scratch);
   if (valid && threadIdx.x == 0) valid[t] = (int32_t)total;
 }
 

@@ -156,8 +156,19 @@ __device__ __forceinline__ const uint8_t* block_base(const BatchArgs& b, const C
 // ------------------------------------------------------------- decode --
 // One query token per work-group; the work-group covers `chunk_blocks`
 // consecutive 64-position blocks of its causal range and its four waves take
-// every fourth block.  Two block buffers alternate so the next block's loads
-// are in flight while the current one is scored.
+// every fourth block.  A ring of NB block buffers keeps the loads of the next
+// NB-1 blocks in flight while the current one is scored.
+#ifndef IDX_DECODE_RING
+#define IDX_DECODE_RING 2
+#endif
+#ifndef IDX_PREFILL_RING
+#define IDX_PREFILL_RING 2
+#endif
+#ifndef IDX_PREFILL_TPW
+#define IDX_PREFILL_TPW 2
+#endif
+
+template <int NB>
 __global__ __launch_bounds__(256) void score_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int chunk_blocks) {
@@ -169,24 +180,29 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   const int nblk = min(chunk_blocks, (n - lb0 * kBlock + kBlock - 1) / kBlock);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lp = lane_pos(lane);
+  const int mine = nblk > wave ? (nblk - wave + 3) / 4 : 0;   // blocks of this wave
 
   QFrag f[1];
   load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
   float* out = logits + (size_t)t * ld;
+  auto blk = [&](int j) { return lb0 + wave + 4 * j; };
 
-  KBlock k0, k1;
-  if (wave < nblk) load_kblock(k0, block_base(b, cache, tp.r, lb0 + wave), lane);
-  for (int bi = wave; bi < nblk; bi += 8) {
-    if (bi + 4 < nblk) load_kblock(k1, block_base(b, cache, tp.r, lb0 + bi + 4), lane);
-    float v;
-    block_scores<1>(f, k0, &v);
-    int s = (lb0 + bi) * kBlock + lp;
-    if (s < n) out[s] = v;
-    if (bi + 4 >= nblk) break;
-    if (bi + 8 < nblk) load_kblock(k0, block_base(b, cache, tp.r, lb0 + bi + 8), lane);
-    block_scores<1>(f, k1, &v);
-    s = (lb0 + bi + 4) * kBlock + lp;
-    if (s < n) out[s] = v;
+  KBlock ring[NB];
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u)
+    if (u < mine) load_kblock(ring[u], block_base(b, cache, tp.r, blk(u)), lane);
+  for (int j0 = 0; j0 < mine; j0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int j = j0 + u;
+      if (j >= mine) break;
+      if (j + NB - 1 < mine)
+        load_kblock(ring[(u + NB - 1) % NB], block_base(b, cache, tp.r, blk(j + NB - 1)), lane);
+      float v;
+      block_scores<1>(f, ring[u], &v);
+      const int s = blk(j) * kBlock + lp;
+      if (s < n) out[s] = v;
+    }
   }
 }
 
@@ -195,7 +211,7 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
 // wave) and `chunk_blocks` blocks of positions; all four waves walk the same
 // blocks, so each K block is fetched from HBM once per work-group and reused
 // from the caches by the other waves.
-template <int TPW>
+template <int TPW, int NB>
 __global__ __launch_bounds__(256) void score_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int chunk_blocks, int groups_per_req) {
@@ -238,34 +254,39 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     }
   }
 
-  KBlock k0, k1;
-  load_kblock(k0, block_base(b, cache, r, lb0), lane);
-  for (int bi = 0; bi < nblk; bi += 2) {
-    if (bi + 1 < nblk) load_kblock(k1, block_base(b, cache, r, lb0 + bi + 1), lane);
-    float v[TPW];
-    block_scores<TPW>(f, k0, v);
-    int s = (lb0 + bi) * kBlock + lp;
+  KBlock ring[NB];
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
-      if (s < nt[j]) out[j][s] = v[j];
-    if (bi + 1 >= nblk) break;
-    if (bi + 2 < nblk) load_kblock(k0, block_base(b, cache, r, lb0 + bi + 2), lane);
-    block_scores<TPW>(f, k1, v);
-    s = (lb0 + bi + 1) * kBlock + lp;
+  for (int u = 0; u < NB - 1; ++u)
+    if (u < nblk) load_kblock(ring[u], block_base(b, cache, r, lb0 + u), lane);
+  for (int j0 = 0; j0 < nblk; j0 += NB) {
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
-      if (s < nt[j]) out[j][s] = v[j];
+    for (int u = 0; u < NB; ++u) {
+      const int j = j0 + u;
+      if (j >= nblk) break;
+      if (j + NB - 1 < nblk)
+        load_kblock(ring[(u + NB - 1) % NB], block_base(b, cache, r, lb0 + j + NB - 1), lane);
+      float v[TPW];
+      block_scores<TPW>(f, ring[u], v);
+      const int s = (lb0 + j) * kBlock + lp;
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj)
+        if (s < nt[jj]) out[jj][s] = v[jj];
+    }
   }
 }
 
-constexpr int kPrefillTPW = 2;
+constexpr int kPrefillTPW = IDX_PREFILL_TPW;
 
 // Decode chunk: about three work-groups per CU over the whole batch, at least
 // 8 and at most 64 blocks per work-group.
 int decode_chunk_blocks(const BatchArgs& b) {
   const int64_t blocks_per_row = (b.max_seq_len + kBlock - 1) / kBlock;
   const int64_t total = blocks_per_row * b.num_tokens;
-  int64_t cb = (total + 767) / 768;
+#ifndef IDX_DECODE_WG_PER_CU
+#define IDX_DECODE_WG_PER_CU 3
+#endif
+  const int64_t slots = 256 * IDX_DECODE_WG_PER_CU;
+  int64_t cb = (total + slots - 1) / slots;
   cb = (cb + 3) / 4 * 4;
   return (int)std::min<int64_t>(64, std::max<int64_t>(8, cb));
 }
@@ -274,7 +295,10 @@ int prefill_chunk_blocks(const BatchArgs& b) {
   // aim for a few thousand work-groups; never more blocks than the longest row needs
   const int gpr = (b.max_query_len + 4 * kPrefillTPW - 1) / (4 * kPrefillTPW);
   const int64_t groups = (int64_t)gpr * b.num_reqs;
-  int cb = 32;
+#ifndef IDX_PREFILL_MAX_CHUNK
+#define IDX_PREFILL_MAX_CHUNK 32
+#endif
+  int cb = IDX_PREFILL_MAX_CHUNK;
   while (cb > 4 && groups * ((b.max_seq_len + cb * kBlock - 1) / (cb * kBlock)) < 2048) cb >>= 1;
   return cb;
 }
@@ -288,14 +312,14 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
     const int cb = decode_chunk_blocks(b);
     const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
     const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
-    hipLaunchKernelGGL(score_decode_kernel, grid, dim3(256), 0, stream, q8, w, cache, b, logits,
+    hipLaunchKernelGGL(score_decode_kernel<IDX_DECODE_RING>, grid, dim3(256), 0, stream, q8, w, cache, b, logits,
                        ld, cb);
   } else {
     const int cb = prefill_chunk_blocks(b);
     const int gpr = (b.max_query_len + 4 * kPrefillTPW - 1) / (4 * kPrefillTPW);
     const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
     const dim3 grid((unsigned)chunks, (unsigned)(gpr * b.num_reqs));
-    hipLaunchKernelGGL(score_prefill_kernel<kPrefillTPW>, grid, dim3(256), 0, stream, q8, w, cache,
+    hipLaunchKernelGGL((score_prefill_kernel<kPrefillTPW, IDX_PREFILL_RING>), grid, dim3(256), 0, stream, q8, w, cache,
                        b, logits, ld, cb, gpr);
   }
   return hipGetLastError();

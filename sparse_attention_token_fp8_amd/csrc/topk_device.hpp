@@ -7,11 +7,12 @@
 //
 // Scores become order-preserving 32-bit keys.  The exact k-th largest key K*
 // among a candidate set is found with three LDS histogram passes over digits
-// [31:21], [20:10], [9:0].  Candidates are every key >= tau, where tau is the
-// j-th largest key of a fixed sample of the row chosen so that almost surely at
-// least k keys pass; if fewer do, the whole row is the candidate set, so the
-// result never depends on tau.  The row is written through an LDS bitmap:
-// keys > K* are set, keys == K* are set in position order until k are taken.
+// [31:21], [20:10], [9:0].  Candidates are every key >= tau, where tau comes
+// from a fixed sample of the row and is placed so that almost surely at least
+// k keys pass; if fewer do, the whole row is the candidate set, so the result
+// never depends on tau.  Candidates are kept in ascending position order, so
+// the row is written with one block-wide scan: a candidate's output slot is
+// #(earlier keys > K*) + min(#(earlier keys == K*), take_eq).
 #pragma once
 
 #include "common.hpp"
@@ -44,21 +45,37 @@ __device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* total,
   return before + incl - v;
 }
 
-// 256-thread form kept for the small kernels.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total,
-                                                         uint32_t* scratch) {
-  return block_scan_excl<kThreads>(v, total, scratch);
+// 64-bit form: `scratch` holds at least 2*NT/64 words.
+template <int NT>
+__device__ __forceinline__ uint64_t block_scan_excl64(uint64_t v, uint32_t* scratch) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)incl, off, 64);
+    const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(incl >> 32), off, 64);
+    if (lane >= off) incl += ((uint64_t)hi << 32) | lo;
+  }
+  __syncthreads();
+  if (lane == 63) { scratch[2 * wave] = (uint32_t)incl; scratch[2 * wave + 1] = (uint32_t)(incl >> 32); }
+  __syncthreads();
+  uint64_t before = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if (i < wave) before += ((uint64_t)scratch[2 * i + 1] << 32) | scratch[2 * i];
+  return before + incl - v;
 }
 
 // In an LDS histogram h[0..nb) find the digit d, searching from the top, with
 // #(digit > d) < need <= #(digit >= d).  Returns d to every thread and sets
 // *above = #(digit > d).  If the histogram holds fewer than `need` entries the
-// result is digit 0 with *above = total.
+// result is digit 0 with *above = total.  scratch: >= NT/64 + 3 words.
 template <int NT>
 __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32_t need,
                                                uint32_t* above, uint32_t* scratch) {
   const int per = nb / NT > 0 ? nb / NT : 1;
-  const int active = nb / per;            // threads that own digits
+  const int active = nb / per;
   const int top = nb - 1 - per * (int)threadIdx.x;
   uint32_t sum = 0;
   if ((int)threadIdx.x < active)
@@ -86,38 +103,38 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32
   return d;
 }
 
-// Exact `need`-th largest key (need >= 1) of the set visited by `visit(fn)`,
-// where fn(key, pos) is called once per element, spread over the block.
-// Returns K* and sets *take_eq = how many keys equal to K* belong to the top
-// `need` (the rest of the top set is every key > K*).  `hist` holds kBins1
-// words of LDS.
-template <int NT, typename V>
+// The `need`-th largest key (need >= 1) of the set visited by `visit(fn)`,
+// where fn(key) is called once per element, spread over the block.  With
+// LEVELS == 3 the result is exact and *take_eq = how many keys equal to it
+// belong to the top `need`; with LEVELS == 2 the result is the key rounded
+// down to a multiple of 2^10 (enough for placing a threshold).
+// `hist` holds kBins1 words of LDS.
+template <int NT, int LEVELS, typename V>
 __device__ __forceinline__ uint32_t radix_kth(V&& visit, uint32_t need, uint32_t* take_eq,
                                               uint32_t* hist, uint32_t* scratch) {
-  uint32_t prefix = 0;
-  // level 1: digit [31:21]
   for (int i = threadIdx.x; i < kBins1; i += NT) hist[i] = 0;
   __syncthreads();
-  visit([&](uint32_t key, int) { atomicAdd(&hist[key >> kShift1], 1u); });
+  visit([&](uint32_t key) { atomicAdd(&hist[key >> kShift1], 1u); });
   __syncthreads();
   uint32_t above;
   const uint32_t d1 = find_digit<NT>(hist, kBins1, need, &above, scratch);
   need -= above;
-  prefix = d1;
-  // level 2: digit [20:10] among keys with digit1 == d1
   for (int i = threadIdx.x; i < kBins2; i += NT) hist[i] = 0;
   __syncthreads();
-  visit([&](uint32_t key, int) {
-    if ((key >> kShift1) == prefix) atomicAdd(&hist[(key >> kShift2) & (kBins2 - 1)], 1u);
+  visit([&](uint32_t key) {
+    if ((key >> kShift1) == d1) atomicAdd(&hist[(key >> kShift2) & (kBins2 - 1)], 1u);
   });
   __syncthreads();
   const uint32_t d2 = find_digit<NT>(hist, kBins2, need, &above, scratch);
   need -= above;
-  prefix = (d1 << (kShift1 - kShift2)) | d2;
-  // level 3: digit [9:0] among keys with digits (d1, d2)
+  const uint32_t prefix = (d1 << (kShift1 - kShift2)) | d2;
+  if (LEVELS == 2) {
+    *take_eq = 0;
+    return prefix << kShift2;
+  }
   for (int i = threadIdx.x; i < kBins3; i += NT) hist[i] = 0;
   __syncthreads();
-  visit([&](uint32_t key, int) {
+  visit([&](uint32_t key) {
     if ((key >> kShift2) == prefix) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
   });
   __syncthreads();
@@ -126,62 +143,40 @@ __device__ __forceinline__ uint32_t radix_kth(V&& visit, uint32_t need, uint32_t
   return (prefix << kShift2) | d3;
 }
 
-constexpr int kSeg = 65536;             // positions per emission bitmap segment
-constexpr int kSegWords = kSeg / 32;
-
-// Write the selected positions of one row in ascending order: every visited
-// key > kstar, plus the first `take_eq` positions (in position order) whose key
-// equals kstar; then -1 up to k.  `bits` holds 2*kSegWords words of LDS.
-template <int NT, typename V>
-__device__ __forceinline__ void emit_row(V&& visit, int n, uint32_t kstar, uint32_t take_eq, int k,
-                                         int32_t* __restrict__ out, uint32_t* bits,
-                                         uint32_t* scratch) {
-  constexpr int kWordsPerThread = kSegWords / NT;
-  uint32_t* sel = bits;
-  uint32_t* tie = bits + kSegWords;
-  uint32_t written = 0, ties_taken = 0;
-  for (int g0 = 0; g0 < n; g0 += kSeg) {
-    for (int i = threadIdx.x; i < 2 * kSegWords; i += NT) bits[i] = 0;
-    __syncthreads();
-    visit([&](uint32_t key, int pos) {
-      const int s = pos - g0;
-      if (s < 0 || s >= kSeg) return;
-      if (key > kstar) atomicOr(&sel[s >> 5], 1u << (s & 31));
-      else if (key == kstar) atomicOr(&tie[s >> 5], 1u << (s & 31));
-    });
-    __syncthreads();
-    const int w0 = threadIdx.x * kWordsPerThread;
-    uint32_t my_ties = 0;
-    for (int j = 0; j < kWordsPerThread; ++j) my_ties += __popc(tie[w0 + j]);
-    uint32_t seg_ties;
-    uint32_t tb = ties_taken + block_scan_excl<NT>(my_ties, &seg_ties, scratch);
-    for (int j = 0; j < kWordsPerThread; ++j) {
-      uint32_t word = tie[w0 + j];
-      while (word) {
-        const uint32_t bit = word & (0u - word);
-        word ^= bit;
-        if (tb < take_eq) sel[w0 + j] |= bit;
-        ++tb;
-      }
-    }
-    ties_taken += seg_ties;
-    uint32_t my_sel = 0;
-    for (int j = 0; j < kWordsPerThread; ++j) my_sel += __popc(sel[w0 + j]);
-    uint32_t seg_sel;
-    uint32_t o = written + block_scan_excl<NT>(my_sel, &seg_sel, scratch);
-    for (int j = 0; j < kWordsPerThread; ++j) {
-      uint32_t word = sel[w0 + j];
-      while (word) {
-        const int bitpos = __ffs(word) - 1;
-        word &= word - 1;
-        if (o < (uint32_t)k) out[o] = g0 + (w0 + j) * 32 + bitpos;
-        ++o;
-      }
-    }
-    written += seg_sel;
-    __syncthreads();
+// Write one row: `get(i)` returns (key, position) of the i-th of `count`
+// elements, in ascending position order.  Keys > kstar are taken, and the
+// first take_eq keys == kstar; the rest of the k slots get -1.
+template <int NT, typename G>
+__device__ __forceinline__ void emit_ordered(G&& get, uint32_t count, uint32_t kstar, uint32_t take_eq,
+                                             int k, int32_t* __restrict__ out, uint32_t* scratch) {
+  const uint32_t per = (count + NT - 1) / NT;
+  const uint32_t i0 = min(count, per * threadIdx.x), i1 = min(count, i0 + per);
+  uint32_t gt = 0, eq = 0;
+  for (uint32_t i = i0; i < i1; ++i) {
+    const uint32_t key = get(i).x;
+    gt += key > kstar;
+    eq += key == kstar;
   }
+  const uint64_t pre = block_scan_excl64<NT>(((uint64_t)eq << 32) | gt, scratch);
+  uint32_t gb = (uint32_t)pre, eb = (uint32_t)(pre >> 32);
+  for (uint32_t i = i0; i < i1; ++i) {
+    const uint2 kp = get(i);
+    if (kp.x > kstar) {
+      const uint32_t o = gb + min(eb, take_eq);
+      if (o < (uint32_t)k) out[o] = (int32_t)kp.y;
+      ++gb;
+    } else if (kp.x == kstar) {
+      if (eb < take_eq && gb + eb < (uint32_t)k) out[gb + eb] = (int32_t)kp.y;
+      ++eb;
+    }
+  }
+  // every thread has the totals after the scan's last wave: recompute them
+  __syncthreads();
+  if (threadIdx.x == NT - 1) { scratch[0] = gb; scratch[1] = eb; }
+  __syncthreads();
+  const uint32_t written = min((uint32_t)k, scratch[0] + min(scratch[1], take_eq));
   for (uint32_t i = written + threadIdx.x; i < (uint32_t)k; i += NT) out[i] = -1;
+  __syncthreads();
 }
 
 // Sample of a row used to place tau: positions j*S + ((37*j + 11) & (S-1)),
@@ -204,35 +199,86 @@ __device__ __forceinline__ uint32_t sample_rank(int n, int ns, int k) {
 }
 
 // tau for one row: 0 (every key passes) when n <= all_below, else the
-// sample_rank-th largest sampled key.  Every thread of the block gets it.
+// sample_rank-th largest sampled key rounded down to a multiple of 2^10.
+// Every thread of the block gets it.
 template <int NT>
 __device__ __forceinline__ uint32_t row_tau(const float* __restrict__ row, int n, int k, int all_below,
                                             uint32_t* hist, uint32_t* scratch) {
   if (n <= all_below) return 0u;
   const int S = sample_stride(n);
   constexpr int kPer = (kMaxSample + NT - 1) / NT;
+  int ns = (n + S - 1) / S;
+  if (ns > 0 && sample_pos(ns - 1, S) >= n) --ns;
   uint32_t keys[kPer];
-  int ns = 0;
-  // number of sample positions inside the row
-  {
-    const int jmax = (n + S - 1) / S;
-    ns = jmax;
-    if (jmax > 0 && sample_pos(jmax - 1, S) >= n) ns = jmax - 1;
-  }
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int j = threadIdx.x + e * NT;
     keys[e] = j < ns ? order_key(row[sample_pos(j, S)]) : 0u;
   }
-  const uint32_t j = sample_rank(n, ns, k);
   uint32_t take;
-  return radix_kth<NT>([&](auto&& fn) {
+  return radix_kth<NT, 2>([&](auto&& fn) {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int jj = threadIdx.x + e * NT;
-      if (jj < ns) fn(keys[e], jj);
+    for (int e = 0; e < kPer; ++e)
+      if ((int)threadIdx.x + e * NT < ns) fn(keys[e]);
+  }, sample_rank(n, ns, k), &take, hist, scratch);
+}
+
+// Ordered compaction of one batch: element (e, thread) sits at position
+// base + e*NT + threadIdx.x; those with pass[e] are appended to (ckey, cpos)
+// after `*count` entries, in ascending position order.  `table` holds
+// E*NT/64 words of LDS.  Returns the batch's number of passing elements.
+template <int NT, int E>
+__device__ __forceinline__ uint32_t compact_ordered(const uint32_t* key, const bool* pass, int base,
+                                                    uint32_t start, uint32_t* ckey, int32_t* cpos,
+                                                    uint32_t cap, uint32_t* table) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t m[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    m[e] = __ballot(pass[e]);
+    if (lane == 0) table[e * NW + wave] = (uint32_t)__popcll(m[e]);
+  }
+  __syncthreads();
+  // exclusive prefix over the E*NW counts, in (e, wave) order, by wave 0
+  if (wave == 0) {
+    constexpr int PER = (E * NW + 63) / 64;
+    uint32_t v[PER];
+    uint32_t s = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = lane * PER + q;
+      v[q] = idx < E * NW ? table[idx] : 0u;
+      s += v[q];
     }
-  }, j, &take, hist, scratch);
+    uint32_t incl = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    uint32_t run = incl - s;
+    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = lane * PER + q;
+      if (idx < E * NW) table[idx] = run;
+      run += v[q];
+    }
+    if (lane == 0) table[E * NW] = total;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (pass[e]) {
+      const uint32_t slot = start + table[e * NW + wave] +
+                            (uint32_t)__popcll(m[e] & ((1ull << lane) - 1ull));
+      if (slot < cap) { ckey[slot] = key[e]; cpos[slot] = base + e * NT + (int)threadIdx.x; }
+    }
+  }
+  const uint32_t total = table[E * NW];
+  __syncthreads();
+  return total;
 }
 
 }  // namespace idx
