@@ -167,6 +167,12 @@ __device__ __forceinline__ const uint8_t* block_base(const BatchArgs& b, const C
 #ifndef IDX_PREFILL_TPW
 #define IDX_PREFILL_TPW 2
 #endif
+#ifndef IDX_PREFILL_LDS
+#define IDX_PREFILL_LDS 1
+#endif
+#ifndef IDX_PREFILL_WAVES
+#define IDX_PREFILL_WAVES 4
+#endif
 
 template <int NB>
 __global__ __launch_bounds__(256) void score_decode_kernel(
@@ -275,6 +281,133 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
   }
 }
 
+// ------------------------------------------------- prefill, LDS-staged --
+// Same work split as above, but each K block is fetched once per work-group:
+// the work-group copies it with contiguous 16-byte loads into LDS, two slots
+// alternating, and every wave reads its MFMA operands from there.  The 16-byte
+// chunk j of code row r sits at chunk (j ^ (r & 7)) of that row, so the
+// MFMA-layout reads (16 rows, one chunk each, per lane group) hit distinct
+// banks.
+template <int NW>
+struct StageRegs {
+  static constexpr int kChunks = kBlockBytes / 16;                  // 528
+  static constexpr int kPerThread = (kChunks + NW * 64 - 1) / (NW * 64);
+  uint4 v[kPerThread];
+};
+
+template <int NW>
+__device__ __forceinline__ int stage_src(int ci) {
+  // LDS chunk ci <- global byte offset
+  if (ci < kCodeBytes / 16) {
+    const int r = ci >> 3, slot = ci & 7;
+    return r * kHeadDim + ((slot ^ (r & 7)) << 4);
+  }
+  return ci << 4;                                                    // scales, unswizzled
+}
+
+template <int NW>
+__device__ __forceinline__ void stage_load(StageRegs<NW>& st, const uint8_t* __restrict__ base) {
+#pragma unroll
+  for (int u = 0; u < StageRegs<NW>::kPerThread; ++u) {
+    const int ci = threadIdx.x + u * NW * 64;
+    if (ci < StageRegs<NW>::kChunks)
+      st.v[u] = base ? *reinterpret_cast<const uint4*>(base + stage_src<NW>(ci)) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void stage_store(const StageRegs<NW>& st, uint8_t* slot) {
+#pragma unroll
+  for (int u = 0; u < StageRegs<NW>::kPerThread; ++u) {
+    const int ci = threadIdx.x + u * NW * 64;
+    if (ci < StageRegs<NW>::kChunks) *reinterpret_cast<uint4*>(slot + (ci << 4)) = st.v[u];
+  }
+}
+
+__device__ __forceinline__ void lds_kblock(KBlock& kb, const uint8_t* slot, int lane) {
+  const int c = lane & 15, G = lane >> 4;
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) {
+    const int r = tl * 16 + c;
+    const uint8_t* row = slot + r * kHeadDim;
+    kb.b[tl] = pack8(*reinterpret_cast<const uint4*>(row + ((G ^ (r & 7)) << 4)),
+                     *reinterpret_cast<const uint4*>(row + (((4 + G) ^ (r & 7)) << 4)));
+  }
+  kb.ks = *reinterpret_cast<const float*>(slot + kCodeBytes + lane_pos(lane) * 4);
+}
+
+template <int TPW, int NW>
+__global__ __launch_bounds__(NW * 64) void score_prefill_lds_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
+    float* __restrict__ logits, int64_t ld, int chunk_blocks, int groups_per_req) {
+  constexpr int TM = NW * TPW;
+  const int r = blockIdx.y / groups_per_req;
+  const int g = blockIdx.y % groups_per_req;
+  if (r >= b.num_reqs) return;
+  const int q0 = b.qsl[r];
+  const int nq = b.qsl[r + 1] - q0;
+  const int tb = g * TM;
+  if (tb >= nq) return;
+  const int L = b.seq_lens[r];
+  auto count = [&](int i) {
+    int n = L - nq + i + 1;
+    n = n < 0 ? 0 : n;
+    return n > b.max_seq_len ? b.max_seq_len : n;
+  };
+  const int n_max = count(min(tb + TM, nq) - 1);
+  const int lb0 = blockIdx.x * chunk_blocks;
+  if (lb0 * kBlock >= n_max) return;
+  const int nblk = min(chunk_blocks, (n_max - lb0 * kBlock + kBlock - 1) / kBlock);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lp = lane_pos(lane);
+
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kBlockBytes];
+
+  QFrag f[TPW];
+  int nt[TPW];
+  float* out[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int i = tb + wave * TPW + j;
+    const int t = q0 + i;
+    if (i < nq && t >= 0 && t < b.num_tokens) {
+      load_q(f[j], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
+      nt[j] = count(i);
+      out[j] = logits + (size_t)t * ld;
+    } else {
+      zero_q(f[j]);
+      nt[j] = 0;
+      out[j] = logits;
+    }
+  }
+
+  // Staging registers for blocks j+1 and j+2 alternate: block j+2's loads are
+  // issued while block j is scored and reach LDS one iteration later.
+  StageRegs<NW> st[2];
+  stage_load<NW>(st[0], block_base(b, cache, r, lb0));
+  stage_store<NW>(st[0], kbuf[0]);
+  if (nblk > 1) stage_load<NW>(st[1], block_base(b, cache, r, lb0 + 1));
+  if (nblk > 2) stage_load<NW>(st[0], block_base(b, cache, r, lb0 + 2));
+  for (int j0 = 0; j0 < nblk; j0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = j0 + u;
+      if (j >= nblk) break;
+      __syncthreads();                     // block j in slot j&1; slot (j+1)&1 free
+      if (j + 1 < nblk) stage_store<NW>(st[(u + 1) & 1], kbuf[(j + 1) & 1]);
+      if (j + 3 < nblk) stage_load<NW>(st[(u + 1) & 1], block_base(b, cache, r, lb0 + j + 3));
+      KBlock kb;
+      lds_kblock(kb, kbuf[j & 1], lane);
+      float v[TPW];
+      block_scores<TPW>(f, kb, v);
+      const int s = (lb0 + j) * kBlock + lp;
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj)
+        if (s < nt[jj]) out[jj][s] = v[jj];
+    }
+  }
+}
+
 constexpr int kPrefillTPW = IDX_PREFILL_TPW;
 
 // Decode chunk: about three work-groups per CU over the whole batch, at least
@@ -293,7 +426,8 @@ int decode_chunk_blocks(const BatchArgs& b) {
 
 int prefill_chunk_blocks(const BatchArgs& b) {
   // aim for a few thousand work-groups; never more blocks than the longest row needs
-  const int gpr = (b.max_query_len + 4 * kPrefillTPW - 1) / (4 * kPrefillTPW);
+  const int tm = (IDX_PREFILL_LDS ? IDX_PREFILL_WAVES : 4) * kPrefillTPW;
+  const int gpr = (b.max_query_len + tm - 1) / tm;
   const int64_t groups = (int64_t)gpr * b.num_reqs;
 #ifndef IDX_PREFILL_MAX_CHUNK
 #define IDX_PREFILL_MAX_CHUNK 32
@@ -316,11 +450,19 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
                        ld, cb);
   } else {
     const int cb = prefill_chunk_blocks(b);
-    const int gpr = (b.max_query_len + 4 * kPrefillTPW - 1) / (4 * kPrefillTPW);
     const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
-    const dim3 grid((unsigned)chunks, (unsigned)(gpr * b.num_reqs));
-    hipLaunchKernelGGL((score_prefill_kernel<kPrefillTPW, IDX_PREFILL_RING>), grid, dim3(256), 0, stream, q8, w, cache,
-                       b, logits, ld, cb, gpr);
+    if (IDX_PREFILL_LDS) {
+      constexpr int tm = IDX_PREFILL_WAVES * kPrefillTPW;
+      const int gpr = (b.max_query_len + tm - 1) / tm;
+      const dim3 grid((unsigned)chunks, (unsigned)(gpr * b.num_reqs));
+      hipLaunchKernelGGL((score_prefill_lds_kernel<kPrefillTPW, IDX_PREFILL_WAVES>), grid,
+                         dim3(IDX_PREFILL_WAVES * 64), 0, stream, q8, w, cache, b, logits, ld, cb, gpr);
+    } else {
+      const int gpr = (b.max_query_len + 4 * kPrefillTPW - 1) / (4 * kPrefillTPW);
+      const dim3 grid((unsigned)chunks, (unsigned)(gpr * b.num_reqs));
+      hipLaunchKernelGGL((score_prefill_kernel<kPrefillTPW, IDX_PREFILL_RING>), grid, dim3(256), 0,
+                         stream, q8, w, cache, b, logits, ld, cb, gpr);
+    }
   }
   return hipGetLastError();
 }

@@ -72,21 +72,29 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
   __shared__ uint32_t table[kBatch * kRowThreads / 64 + 1];
   __shared__ uint32_t scratch[40];
   const float* row = logits + (size_t)t * ld;
+  constexpr int kStep = kRowThreads * kBatch;
+  float v[kBatch];
+#pragma unroll
+  for (int e = 0; e < kBatch; ++e) {
+    const int s = e * kRowThreads + threadIdx.x;
+    v[e] = s < n ? row[s] : 0.f;
+  }
   const uint32_t tau = row_tau<kRowThreads>(row, n, k, kCandCap, hist, scratch);
   uint32_t C = 0;
-  for (int base = 0; base < n; base += kRowThreads * kBatch) {
-    float v[kBatch];
-#pragma unroll
-    for (int e = 0; e < kBatch; ++e) {
-      const int s = base + e * kRowThreads + threadIdx.x;
-      v[e] = s < n ? row[s] : 0.f;
-    }
+  for (int base = 0; base < n; base += kStep) {
     uint32_t key[kBatch];
     bool pass[kBatch];
 #pragma unroll
     for (int e = 0; e < kBatch; ++e) {
       key[e] = order_key(v[e]);
       pass[e] = base + e * kRowThreads + (int)threadIdx.x < n && key[e] >= tau;
+    }
+    if (base + kStep < n) {                     // next batch in flight during the compaction
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const int s = base + kStep + e * kRowThreads + threadIdx.x;
+        v[e] = s < n ? row[s] : 0.f;
+      }
     }
     C += compact_ordered<kRowThreads, kBatch>(key, pass, base, C, ckey, cpos, kCandCap, table);
   }
