@@ -121,13 +121,13 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
   __shared__ uint32_t table[kPer * kThreads / 64 + 1];
   __shared__ uint32_t scratch[16];
   const float* row = logits + (size_t)t * ld;
-  const uint32_t tau = row_tau<kThreads>(row, n, k, 4 * k, hist, scratch);
-  float v[kPer];
+  float v[kPer];                                // the chunk's loads fly while tau is placed
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int s = s0 + e * kThreads + threadIdx.x;
     v[e] = s < n ? row[s] : 0.f;
   }
+  const uint32_t tau = row_tau<kThreads>(row, n, k, 4 * k, hist, scratch);
   uint32_t key[kPer];
   bool pass[kPer];
 #pragma unroll
@@ -141,11 +141,15 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
   if (threadIdx.x == 0) ws.counts[(size_t)t * ws.nchunks + c] = cnt;
 }
 
-__global__ __launch_bounds__(kRowThreads) void topk_resolve_kernel(const float* __restrict__ logits,
-                                                                   int64_t ld, BatchArgs b, int k,
-                                                                   TopkWorkspace ws,
-                                                                   int32_t* __restrict__ topk,
-                                                                   int64_t ldo) {
+#ifndef IDX_RESOLVE_THREADS
+#define IDX_RESOLVE_THREADS 1024
+#endif
+constexpr int kResolveThreads = IDX_RESOLVE_THREADS;
+
+__global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
+    const float* __restrict__ logits, int64_t ld, BatchArgs b, int k, TopkWorkspace ws,
+    int32_t* __restrict__ topk, int64_t ldo) {
+  constexpr int NT = kResolveThreads;
   const int t = blockIdx.x;
   const int n = token_pos(b, t).n;
   if (n <= k) return;                          // written by the filter
@@ -156,14 +160,13 @@ __global__ __launch_bounds__(kRowThreads) void topk_resolve_kernel(const float* 
   __shared__ uint32_t scratch[40];
   const int nch = min((n + kChunk - 1) / kChunk, kMaxChunks);
   const uint32_t* cnts = ws.counts + (size_t)t * ws.nchunks;
-  // prefix of the chunk counts
   {
-    const int per = (nch + kRowThreads - 1) / kRowThreads;
+    const int per = (nch + NT - 1) / NT;
     const int c0 = min(nch, per * (int)threadIdx.x), c1 = min(nch, c0 + per);
     uint32_t s = 0;
     for (int c = c0; c < c1; ++c) s += cnts[c];
     uint32_t total;
-    uint32_t run = block_scan_excl<kRowThreads>(s, &total, scratch);
+    uint32_t run = block_scan_excl<NT>(s, &total, scratch);
     for (int c = c0; c < c1; ++c) { pre[c] = run; run += cnts[c]; }
     if (threadIdx.x == 0) pre[nch] = total;
   }
@@ -171,21 +174,38 @@ __global__ __launch_bounds__(kRowThreads) void topk_resolve_kernel(const float* 
   const uint32_t C = pre[nch];
   const float* row = logits + (size_t)t * ld;
   int32_t* out = topk + (size_t)t * ldo;
+  const size_t base = (size_t)t * ws.nchunks * kChunk;
+  auto at = [&](uint32_t i) {                   // workspace index of candidate i (position order)
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return base + (size_t)lo * kChunk + (i - pre[lo]);
+  };
   if (C >= (uint32_t)k && C <= (uint32_t)kCandCap) {
-    const size_t base = (size_t)t * ws.nchunks * kChunk;
-    for (uint32_t i = threadIdx.x; i < C; i += kRowThreads) {
-      int lo = 0, hi = nch - 1;               // chunk holding entry i
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= i) lo = mid; else hi = mid - 1;
-      }
-      const size_t at = base + (size_t)lo * kChunk + (i - pre[lo]);
-      ckey[i] = ws.cand_key[at];
-      cpos[i] = ws.cand_pos[at];
+    for (uint32_t i = threadIdx.x; i < C; i += NT) {
+      const size_t a = at(i);
+      ckey[i] = ws.cand_key[a];
+      cpos[i] = ws.cand_pos[a];
     }
     __syncthreads();
+    finish_row<NT>(row, n, k, C, ckey, cpos, out, hist, scratch);
+  } else if (C > (uint32_t)kCandCap) {          // too many for LDS: read the slots in place
+    uint32_t take;
+    const uint32_t kstar = radix_kth<NT, 3>([&](auto&& fn) {
+      for (int c = 0; c < nch; ++c) {
+        const size_t sb = base + (size_t)c * kChunk;
+        for (uint32_t i = threadIdx.x; i < cnts[c]; i += NT) fn(ws.cand_key[sb + i]);
+      }
+    }, (uint32_t)k, &take, hist, scratch);
+    emit_ordered<NT>([&](uint32_t i) {
+      const size_t a = at(i);
+      return make_uint2(ws.cand_key[a], (uint32_t)ws.cand_pos[a]);
+    }, C, kstar, take, k, out, scratch);
+  } else {
+    finish_row<NT>(row, n, k, C, ckey, cpos, out, hist, scratch);   // fewer than k: whole row
   }
-  finish_row<kRowThreads>(row, n, k, C, ckey, cpos, out, hist, scratch);
 }
 
 }  // namespace
@@ -207,7 +227,7 @@ hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, cons
                        out, ldo);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_resolve_kernel, dim3((unsigned)b.num_tokens), dim3(kRowThreads), 0,
+    hipLaunchKernelGGL(topk_resolve_kernel, dim3((unsigned)b.num_tokens), dim3(kResolveThreads), 0,
                        stream, logits, ld, b, k, ws, out, ldo);
   } else {
     hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)b.num_tokens), dim3(kRowThreads), 0,

@@ -191,10 +191,11 @@ __device__ __forceinline__ int sample_stride(int n) {
 
 __device__ __forceinline__ int sample_pos(int j, int S) { return j * S + ((37 * j + 11) & (S - 1)); }
 
-// Rank (1-based) of the sample key used as tau: about 2k of the n keys are
-// expected at or above it, plus a margin of 16 sample steps.
+// Rank (1-based) of the sample key used as tau: about 1.5k of the n keys are
+// expected at or above it, plus a margin of 16 sample steps (the count stays
+// several standard deviations above k for samples of a few hundred keys).
 __device__ __forceinline__ uint32_t sample_rank(int n, int ns, int k) {
-  const int64_t j = ((int64_t)2 * k * ns + n - 1) / n + 16;
+  const int64_t j = ((int64_t)3 * k * ns + 2 * (int64_t)n - 1) / (2 * (int64_t)n) + 16;
   return (uint32_t)(j < ns ? j : ns);
 }
 
