@@ -38,12 +38,10 @@ template <int NT>
 __device__ __forceinline__ void finish_row(const float* __restrict__ row, int n, int k, uint32_t C,
                                            const uint32_t* ckey, const int32_t* cpos,
                                            int32_t* __restrict__ out, uint32_t* hist,
-                                           uint32_t* scratch) {
+                                           uint32_t* bucket, uint32_t* scratch) {
   uint32_t take;
   if (C >= (uint32_t)k && C <= (uint32_t)kCandCap) {
-    const uint32_t kstar = radix_kth<NT, 3>([&](auto&& fn) {
-      for (uint32_t i = threadIdx.x; i < C; i += NT) fn(ckey[i]);
-    }, (uint32_t)k, &take, hist, scratch);
+    const uint32_t kstar = select_kth<NT>(ckey, C, (uint32_t)k, &take, hist, bucket, scratch);
     emit_ordered<NT>([&](uint32_t i) { return make_uint2(ckey[i], (uint32_t)cpos[i]); }, C, kstar,
                      take, k, out, scratch);
   } else {
@@ -70,16 +68,21 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
   __shared__ int32_t cpos[kCandCap];
   __shared__ uint32_t hist[kBins1];
   __shared__ uint32_t table[kBatch * kRowThreads / 64 + 1];
-  __shared__ uint32_t scratch[40];
+  __shared__ uint32_t bucket[64];
+  __shared__ uint32_t scratch[scratch_words<kRowThreads>()];
   const float* row = logits + (size_t)t * ld;
   constexpr int kStep = kRowThreads * kBatch;
+  const bool sampled = n > kCandCap;            // else every position is a candidate
+  float sv[sample_per<kRowThreads>()];
+  int ns = 0;
+  if (sampled) ns = sample_load<kRowThreads>(row, n, sv);   // first: tau waits on these only
   float v[kBatch];
 #pragma unroll
   for (int e = 0; e < kBatch; ++e) {
     const int s = e * kRowThreads + threadIdx.x;
     v[e] = s < n ? row[s] : 0.f;
   }
-  const uint32_t tau = row_tau<kRowThreads>(row, n, k, kCandCap, hist, scratch);
+  const uint32_t tau = sampled ? sample_tau<kRowThreads>(sv, ns, n, k, hist, scratch) : 0u;
   uint32_t C = 0;
   for (int base = 0; base < n; base += kStep) {
     uint32_t key[kBatch];
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
     }
     C += compact_ordered<kRowThreads, kBatch>(key, pass, base, C, ckey, cpos, kCandCap, table);
   }
-  finish_row<kRowThreads>(row, n, k, C, ckey, cpos, out, hist, scratch);
+  finish_row<kRowThreads>(row, n, k, C, ckey, cpos, out, hist, bucket, scratch);
 }
 
 // ---------------------------------------------------------- long rows --
@@ -119,15 +122,19 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
   if (s0 >= n) return;
   __shared__ uint32_t hist[kBins1];
   __shared__ uint32_t table[kPer * kThreads / 64 + 1];
-  __shared__ uint32_t scratch[16];
+  __shared__ uint32_t scratch[scratch_words<kThreads>()];
   const float* row = logits + (size_t)t * ld;
+  const bool sampled = n > 4 * k;               // else every position is a candidate
+  float sv[sample_per<kThreads>()];
+  int ns = 0;
+  if (sampled) ns = sample_load<kThreads>(row, n, sv);      // first: tau waits on these only
   float v[kPer];                                // the chunk's loads fly while tau is placed
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int s = s0 + e * kThreads + threadIdx.x;
     v[e] = s < n ? row[s] : 0.f;
   }
-  const uint32_t tau = row_tau<kThreads>(row, n, k, 4 * k, hist, scratch);
+  const uint32_t tau = sampled ? sample_tau<kThreads>(sv, ns, n, k, hist, scratch) : 0u;
   uint32_t key[kPer];
   bool pass[kPer];
 #pragma unroll
@@ -157,7 +164,8 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
   __shared__ int32_t cpos[kCandCap];
   __shared__ uint32_t hist[kBins1];
   __shared__ uint32_t pre[kMaxChunks + 1];
-  __shared__ uint32_t scratch[40];
+  __shared__ uint32_t bucket[64];
+  __shared__ uint32_t scratch[scratch_words<NT>()];
   const int nch = min((n + kChunk - 1) / kChunk, kMaxChunks);
   const uint32_t* cnts = ws.counts + (size_t)t * ws.nchunks;
   {
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
       cpos[i] = ws.cand_pos[a];
     }
     __syncthreads();
-    finish_row<NT>(row, n, k, C, ckey, cpos, out, hist, scratch);
+    finish_row<NT>(row, n, k, C, ckey, cpos, out, hist, bucket, scratch);
   } else if (C > (uint32_t)kCandCap) {          // too many for LDS: read the slots in place
     uint32_t take;
     const uint32_t kstar = radix_kth<NT, 3>([&](auto&& fn) {
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
       return make_uint2(ws.cand_key[a], (uint32_t)ws.cand_pos[a]);
     }, C, kstar, take, k, out, scratch);
   } else {
-    finish_row<NT>(row, n, k, C, ckey, cpos, out, hist, scratch);   // fewer than k: whole row
+    finish_row<NT>(row, n, k, C, ckey, cpos, out, hist, bucket, scratch);   // fewer than k: whole row
   }
 }
 

@@ -5,13 +5,15 @@
 // scores among positions 0..p_t, ties to the lower position, -0 == +0; the row
 // lists the selected positions ascending, then -1.
 //
-// Scores become order-preserving 32-bit keys.  The exact k-th largest key K*
-// among a candidate set is found with three LDS histogram passes over digits
-// [31:21], [20:10], [9:0].  Candidates are every key >= tau, where tau comes
-// from a fixed sample of the row and is placed so that almost surely at least
-// k keys pass; if fewer do, the whole row is the candidate set, so the result
-// never depends on tau.  Candidates are kept in ascending position order, so
-// the row is written with one block-wide scan: a candidate's output slot is
+// Scores become order-preserving 32-bit keys.  Candidates are every key >=
+// tau, where tau comes from a fixed sample of the row and is placed so that
+// almost surely at least k keys pass; if fewer do, the whole row is the
+// candidate set, so the result never depends on tau.  The exact k-th largest
+// key K* among the candidates comes from LDS histograms whose digits are taken
+// relative to the smallest candidate (a narrow score band then spreads over
+// the bins); once the band holding K* has at most 64 keys, one wave ranks them
+// directly.  Candidates are kept in ascending position order, so the row is
+// written with one block-wide scan: a candidate's output slot is
 // #(earlier keys > K*) + min(#(earlier keys == K*), take_eq).
 #pragma once
 
@@ -47,7 +49,7 @@ __device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* total,
 
 // 64-bit form: `scratch` holds at least 2*NT/64 words.
 template <int NT>
-__device__ __forceinline__ uint64_t block_scan_excl64(uint64_t v, uint32_t* scratch) {
+__device__ __forceinline__ uint64_t block_scan_excl64(uint64_t v, uint64_t* total, uint32_t* scratch) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint64_t incl = v;
@@ -60,27 +62,37 @@ __device__ __forceinline__ uint64_t block_scan_excl64(uint64_t v, uint32_t* scra
   __syncthreads();
   if (lane == 63) { scratch[2 * wave] = (uint32_t)incl; scratch[2 * wave + 1] = (uint32_t)(incl >> 32); }
   __syncthreads();
-  uint64_t before = 0;
+  uint64_t before = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < NW; ++i)
-    if (i < wave) before += ((uint64_t)scratch[2 * i + 1] << 32) | scratch[2 * i];
+  for (int i = 0; i < NW; ++i) {
+    const uint64_t s = ((uint64_t)scratch[2 * i + 1] << 32) | scratch[2 * i];
+    before += (i < wave) ? s : 0ull;
+    all += s;
+  }
+  *total = all;
   return before + incl - v;
 }
 
+// Words of LDS scratch the helpers below need for an NT-thread block.
+template <int NT>
+constexpr int scratch_words() { return 2 * (NT / 64) + 8; }
+
 // In an LDS histogram h[0..nb) find the digit d, searching from the top, with
 // #(digit > d) < need <= #(digit >= d).  Returns d to every thread and sets
-// *above = #(digit > d).  If the histogram holds fewer than `need` entries the
-// result is digit 0 with *above = total.  scratch: >= NT/64 + 3 words.
+// *above = #(digit > d) and *count = h[d].  If the histogram holds fewer than
+// `need` entries the result is digit 0 with *above = total.
 template <int NT>
 __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32_t need,
-                                               uint32_t* above, uint32_t* scratch) {
+                                               uint32_t* above, uint32_t* scratch,
+                                               uint32_t* count = nullptr) {
   const int per = nb / NT > 0 ? nb / NT : 1;
   const int active = nb / per;
   const int top = nb - 1 - per * (int)threadIdx.x;
   uint32_t sum = 0;
   if ((int)threadIdx.x < active)
     for (int j = 0; j < per; ++j) sum += h[top - j];
-  if (threadIdx.x == 0) { scratch[NT / 64 + 1] = 0u; scratch[NT / 64 + 2] = 0u; }
+  uint32_t* res = scratch + NT / 64;
+  if (threadIdx.x == 0) { res[1] = 0u; res[2] = 0u; res[3] = 0u; }
   uint32_t total;
   const uint32_t before = block_scan_excl<NT>(sum, &total, scratch);
   if ((int)threadIdx.x < active && before < need && before + sum >= need) {
@@ -88,16 +100,18 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32
     for (int j = 0; j < per; ++j) {
       const uint32_t c = h[top - j];
       if (cum + c >= need) {
-        scratch[NT / 64 + 1] = (uint32_t)(top - j);
-        scratch[NT / 64 + 2] = cum;
+        res[1] = (uint32_t)(top - j);
+        res[2] = cum;
+        res[3] = c;
         break;
       }
       cum += c;
     }
   }
   __syncthreads();
-  uint32_t d = scratch[NT / 64 + 1];
-  *above = scratch[NT / 64 + 2];
+  uint32_t d = res[1];
+  *above = res[2];
+  if (count) *count = res[3];
   if (total < need) { d = 0; *above = total; }
   __syncthreads();
   return d;
@@ -143,6 +157,82 @@ __device__ __forceinline__ uint32_t radix_kth(V&& visit, uint32_t need, uint32_t
   return (prefix << kShift2) | d3;
 }
 
+// Exact `need`-th largest key (1 <= need <= C) of ckey[0..C) in LDS, with
+// *take_eq = how many keys equal to it belong to the top `need`.  Digits of
+// up to 11 bits are taken over [kmin, kmax] of the candidates; when the bin
+// holding the answer has at most 64 keys they are ranked by one wave.
+// `hist` holds kBins1 words, `bucket` 64 words.
+template <int NT>
+__device__ __forceinline__ uint32_t select_kth(const uint32_t* ckey, uint32_t C, uint32_t need,
+                                               uint32_t* take_eq, uint32_t* hist, uint32_t* bucket,
+                                               uint32_t* scratch) {
+  constexpr int NW = NT / 64;
+  uint32_t* sx = scratch + 2 * NW;              // kmin, kmax, bucket fill, K*, take
+  const int lane = threadIdx.x & 63;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (uint32_t i = threadIdx.x; i < C; i += NT) {
+    const uint32_t x = ckey[i];
+    lo = min(lo, x);
+    hi = max(hi, x);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+  }
+  if (threadIdx.x == 0) { sx[0] = 0xffffffffu; sx[1] = 0u; }
+  __syncthreads();
+  if (lane == 0) { atomicMin(&sx[0], lo); atomicMax(&sx[1], hi); }
+  __syncthreads();
+  uint32_t base = sx[0];
+  const uint32_t top = sx[1];
+  int width = top == base ? 0 : 32 - __clz(top - base);   // keys in play: [base, base + 2^width)
+  while (width > 0) {
+    const int shift = width > 11 ? width - 11 : 0;
+    const int nb = 1 << (width - shift);
+    for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0;
+    if (threadIdx.x == 0) sx[2] = 0u;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < C; i += NT) {
+      const uint32_t x = ckey[i];
+      if (x >= base && ((uint64_t)(x - base) >> width) == 0) atomicAdd(&hist[(x - base) >> shift], 1u);
+    }
+    __syncthreads();
+    uint32_t above, in_bin;
+    const uint32_t d = find_digit<NT>(hist, nb, need, &above, scratch, &in_bin);
+    need -= above;
+    base += d << shift;
+    width = shift;
+    if (width > 0 && in_bin <= 64) {            // rank the bin's keys in one wave
+      for (uint32_t i = threadIdx.x; i < C; i += NT) {
+        const uint32_t x = ckey[i];
+        if (x >= base && ((uint64_t)(x - base) >> width) == 0) {
+          const uint32_t j = atomicAdd(&sx[2], 1u);
+          if (j < 64u) bucket[j] = x;
+        }
+      }
+      __syncthreads();
+      if ((uint32_t)threadIdx.x < in_bin) {
+        const uint32_t x = bucket[threadIdx.x];
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t j = 0; j < in_bin; ++j) {
+          const uint32_t y = bucket[j];
+          gt += y > x;
+          ge += y >= x;
+        }
+        if (gt < need && need <= ge) { sx[3] = x; sx[4] = need - gt; }
+      }
+      __syncthreads();
+      base = sx[3];
+      need = sx[4];
+      width = 0;
+      __syncthreads();
+    }
+  }
+  *take_eq = need;
+  return base;
+}
+
 // Write one row: `get(i)` returns (key, position) of the i-th of `count`
 // elements, in ascending position order.  Keys > kstar are taken, and the
 // first take_eq keys == kstar; the rest of the k slots get -1.
@@ -157,8 +247,18 @@ __device__ __forceinline__ void emit_ordered(G&& get, uint32_t count, uint32_t k
     gt += key > kstar;
     eq += key == kstar;
   }
-  const uint64_t pre = block_scan_excl64<NT>(((uint64_t)eq << 32) | gt, scratch);
-  uint32_t gb = (uint32_t)pre, eb = (uint32_t)(pre >> 32);
+  uint32_t gb, eb, gall, eall;
+  if (count < 65536u) {                         // both counts fit 16 bits: one 32-bit scan
+    uint32_t total;
+    const uint32_t pre = block_scan_excl<NT>((eq << 16) | gt, &total, scratch);
+    gb = pre & 0xffffu; eb = pre >> 16;
+    gall = total & 0xffffu; eall = total >> 16;
+  } else {
+    uint64_t total;
+    const uint64_t pre = block_scan_excl64<NT>(((uint64_t)eq << 32) | gt, &total, scratch);
+    gb = (uint32_t)pre; eb = (uint32_t)(pre >> 32);
+    gall = (uint32_t)total; eall = (uint32_t)(total >> 32);
+  }
   for (uint32_t i = i0; i < i1; ++i) {
     const uint2 kp = get(i);
     if (kp.x > kstar) {
@@ -170,11 +270,7 @@ __device__ __forceinline__ void emit_ordered(G&& get, uint32_t count, uint32_t k
       ++eb;
     }
   }
-  // every thread has the totals after the scan's last wave: recompute them
-  __syncthreads();
-  if (threadIdx.x == NT - 1) { scratch[0] = gb; scratch[1] = eb; }
-  __syncthreads();
-  const uint32_t written = min((uint32_t)k, scratch[0] + min(scratch[1], take_eq));
+  const uint32_t written = min((uint32_t)k, gall + min(eall, take_eq));
   for (uint32_t i = written + threadIdx.x; i < (uint32_t)k; i += NT) out[i] = -1;
   __syncthreads();
 }
@@ -199,28 +295,34 @@ __device__ __forceinline__ uint32_t sample_rank(int n, int ns, int k) {
   return (uint32_t)(j < ns ? j : ns);
 }
 
-// tau for one row: 0 (every key passes) when n <= all_below, else the
-// sample_rank-th largest sampled key rounded down to a multiple of 2^10.
-// Every thread of the block gets it.
 template <int NT>
-__device__ __forceinline__ uint32_t row_tau(const float* __restrict__ row, int n, int k, int all_below,
-                                            uint32_t* hist, uint32_t* scratch) {
-  if (n <= all_below) return 0u;
+constexpr int sample_per() { return (kMaxSample + NT - 1) / NT; }
+
+// Issue the loads of the row's sample into v[sample_per<NT>()]; returns the
+// sample size.
+template <int NT>
+__device__ __forceinline__ int sample_load(const float* __restrict__ row, int n, float* v) {
   const int S = sample_stride(n);
-  constexpr int kPer = (kMaxSample + NT - 1) / NT;
   int ns = (n + S - 1) / S;
   if (ns > 0 && sample_pos(ns - 1, S) >= n) --ns;
-  uint32_t keys[kPer];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
+  for (int e = 0; e < sample_per<NT>(); ++e) {
     const int j = threadIdx.x + e * NT;
-    keys[e] = j < ns ? order_key(row[sample_pos(j, S)]) : 0u;
+    v[e] = j < ns ? row[sample_pos(j, S)] : 0.f;
   }
+  return ns;
+}
+
+// tau from the loaded sample: the sample_rank-th largest sampled key rounded
+// down to a multiple of 2^10.  Every thread of the block gets it.
+template <int NT>
+__device__ __forceinline__ uint32_t sample_tau(const float* v, int ns, int n, int k, uint32_t* hist,
+                                               uint32_t* scratch) {
   uint32_t take;
   return radix_kth<NT, 2>([&](auto&& fn) {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if ((int)threadIdx.x + e * NT < ns) fn(keys[e]);
+    for (int e = 0; e < sample_per<NT>(); ++e)
+      if ((int)threadIdx.x + e * NT < ns) fn(order_key(v[e]));
   }, sample_rank(n, ns, k), &take, hist, scratch);
 }
 
