@@ -129,6 +129,25 @@ __device__ __forceinline__ TokenPos token_pos(const BatchArgs& b, int t) {
   return tp;
 }
 
+// token_pos for a whole wave (every lane active, same t): with fewer than 64
+// requests the lanes read query_start_loc and seq_lens in parallel and a ballot
+// finds the request, so the lookup costs one load latency, not a search.
+__device__ __forceinline__ TokenPos token_pos_wave(const BatchArgs& b, int t) {
+  if (b.num_reqs >= 64) return token_pos(b, t);
+  const int lane = threadIdx.x & 63;
+  const int q = lane <= b.num_reqs ? b.qsl[lane] : 0x7fffffff;
+  const int len = lane < b.num_reqs ? b.seq_lens[lane] : 0;
+  const int m = (int)__popcll(__ballot(lane < b.num_reqs && q <= t));
+  TokenPos tp;
+  tp.r = m > 0 ? m - 1 : 0;
+  const int q0 = __builtin_amdgcn_readlane(q, tp.r);
+  const int q1 = __builtin_amdgcn_readlane(q, tp.r + 1);
+  int n = __builtin_amdgcn_readlane(len, tp.r) - (q1 - q0) + (t - q0) + 1;
+  n = n < 0 ? 0 : n;
+  tp.n = n > b.max_seq_len ? b.max_seq_len : n;
+  return tp;
+}
+
 // Physical block of logical block `lb` of request r, or -1 if it lies outside
 // the block table or the pool.
 __device__ __forceinline__ int64_t phys_block(const BatchArgs& b, const CacheArgs& c, int r, int lb) {

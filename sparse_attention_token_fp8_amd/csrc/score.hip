@@ -153,11 +153,102 @@ __device__ __forceinline__ const uint8_t* block_base(const BatchArgs& b, const C
   return pb < 0 ? nullptr : c.data + pb * kBlockBytes;
 }
 
+// ------------------------------------------------------ LDS staging --
+// K blocks reach the MFMA operands through LDS: global loads are contiguous
+// (8 lanes per 128-byte code row, whole lines per instruction), while the
+// operand layout wants 16 rows x 64 bytes per load, which halves the lines
+// per request and costs about a quarter of the achievable HBM rate.
+// Same work split as above, but each K block is fetched once per work-group:
+// the work-group copies it with contiguous 16-byte loads into LDS, two slots
+// alternating, and every wave reads its MFMA operands from there.  The 16-byte
+// chunk j of code row r sits at chunk (j ^ (r & 7)) of that row, so the
+// MFMA-layout reads (16 rows, one chunk each, per lane group) hit distinct
+// banks.
+template <int NW>
+struct StageRegs {
+  static constexpr int kChunks = kBlockBytes / 16;                  // 528
+  static constexpr int kPerThread = (kChunks + NW * 64 - 1) / (NW * 64);
+  uint4 v[kPerThread];
+};
+
+template <int NW>
+__device__ __forceinline__ int stage_src(int ci) {
+  // LDS chunk ci <- global byte offset
+  if (ci < kCodeBytes / 16) {
+    const int r = ci >> 3, slot = ci & 7;
+    return r * kHeadDim + ((slot ^ (r & 7)) << 4);
+  }
+  return ci << 4;                                                    // scales, unswizzled
+}
+
+template <int NW>
+__device__ __forceinline__ void stage_load(StageRegs<NW>& st, const uint8_t* __restrict__ base) {
+#pragma unroll
+  for (int u = 0; u < StageRegs<NW>::kPerThread; ++u) {
+    const int ci = threadIdx.x + u * NW * 64;
+    if (ci < StageRegs<NW>::kChunks)
+      st.v[u] = base ? *reinterpret_cast<const uint4*>(base + stage_src<NW>(ci)) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void stage_store(const StageRegs<NW>& st, uint8_t* slot) {
+#pragma unroll
+  for (int u = 0; u < StageRegs<NW>::kPerThread; ++u) {
+    const int ci = threadIdx.x + u * NW * 64;
+    if (ci < StageRegs<NW>::kChunks) *reinterpret_cast<uint4*>(slot + (ci << 4)) = st.v[u];
+  }
+}
+
+__device__ __forceinline__ void lds_kblock(KBlock& kb, const uint8_t* slot, int lane) {
+  const int c = lane & 15, G = lane >> 4;
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) {
+    const int r = tl * 16 + c;
+    const uint8_t* row = slot + r * kHeadDim;
+    kb.b[tl] = pack8(*reinterpret_cast<const uint4*>(row + ((G ^ (r & 7)) << 4)),
+                     *reinterpret_cast<const uint4*>(row + (((4 + G) ^ (r & 7)) << 4)));
+  }
+  kb.ks = *reinterpret_cast<const float*>(slot + kCodeBytes + lane_pos(lane) * 4);
+}
+
+// One wave stages a whole block: 528 16-byte chunks, 9 per lane (in the last
+// round lanes 16-63 re-read the scales' 16 chunks, so every lane issues the
+// same loads).  A block absent from the table is read from a valid address
+// and zeroed when it is written to LDS: a select right after the load would
+// wait for it, and a branch around the loads would make the compiler wait for
+// every load in flight at the next use.
+struct WaveStage {
+  uint4 v[9];
+  uint32_t mask;   // all ones for a block in the table, else 0
+};
+
+__device__ __forceinline__ void wave_stage_load(WaveStage& st, const uint8_t* __restrict__ base,
+                                                bool valid, int lane) {
+#pragma unroll
+  for (int u = 0; u < 9; ++u) {
+    const int ci = u < 8 ? lane + 64 * u : 512 + (lane & 15);
+    st.v[u] = *reinterpret_cast<const uint4*>(base + stage_src<1>(ci));
+  }
+  st.mask = valid ? 0xffffffffu : 0u;
+}
+
+__device__ __forceinline__ void wave_stage_store(const WaveStage& st, uint8_t* slot, int lane) {
+#pragma unroll
+  for (int u = 0; u < 9; ++u) {
+    const int ci = lane + 64 * u;
+    const uint4 x = make_uint4(st.v[u].x & st.mask, st.v[u].y & st.mask, st.v[u].z & st.mask,
+                               st.v[u].w & st.mask);
+    if (u < 8 || lane < 16) *reinterpret_cast<uint4*>(slot + (ci << 4)) = x;
+  }
+}
+
 // ------------------------------------------------------------- decode --
 // One query token per work-group; the work-group covers `chunk_blocks`
 // consecutive 64-position blocks of its causal range and its four waves take
-// every fourth block.  A ring of NB block buffers keeps the loads of the next
-// NB-1 blocks in flight while the current one is scored.
+// every fourth block.  Each wave keeps the loads of its next NB-1 blocks in
+// flight in registers and passes the current block through its own LDS slot
+// into the MFMA layout.
 #ifndef IDX_DECODE_RING
 #define IDX_DECODE_RING 2
 #endif
@@ -174,40 +265,71 @@ __device__ __forceinline__ const uint8_t* block_base(const BatchArgs& b, const C
 #define IDX_PREFILL_WAVES 4
 #endif
 
+#ifndef IDX_DECODE_WAVES_PER_EU
+#define IDX_DECODE_WAVES_PER_EU 2
+#endif
+
 template <int NB>
-__global__ __launch_bounds__(256) void score_decode_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU)))
+void score_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int chunk_blocks) {
   const int t = blockIdx.y;
-  const TokenPos tp = token_pos(b, t);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  QFrag f[1];
+  load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);  // needs t only
+  const TokenPos tp = token_pos_wave(b, t);
   const int n = tp.n;
   const int lb0 = blockIdx.x * chunk_blocks;
   if (lb0 * kBlock >= n) return;
   const int nblk = min(chunk_blocks, (n - lb0 * kBlock + kBlock - 1) / kBlock);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lp = lane_pos(lane);
-  const int mine = nblk > wave ? (nblk - wave + 3) / 4 : 0;   // blocks of this wave
-
-  QFrag f[1];
-  load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
-  float* out = logits + (size_t)t * ld;
+  const int mine = nblk > wave ? (nblk - wave + 3) / 4 : 0;   // blocks of this wave (<= 16)
+  if (mine == 0) return;
   auto blk = [&](int j) { return lb0 + wave + 4 * j; };
+  float* out = logits + (size_t)t * ld;
+  if (cache.num_blocks == 0) {                  // no K at all: every score is 0
+    for (int j = 0; j < mine; ++j) {
+      const int s = blk(j) * kBlock + lp;
+      if (s < n) out[s] = 0.f;
+    }
+    return;
+  }
+  // lane j holds the physical block of this wave's j-th block, so no K load
+  // waits on a block-table load
+  const int pbl = lane < mine ? (int)phys_block(b, cache, tp.r, blk(lane)) : -1;
+  auto stage = [&](WaveStage& st, int j) {
+    const int pb = __builtin_amdgcn_readlane(pbl, j);
+    wave_stage_load(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes, pb >= 0, lane);
+  };
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[4][kBlockBytes];
+  uint8_t* slot = kbuf[wave];
 
-  KBlock ring[NB];
+  // Every iteration issues one block's loads (past the last block it re-reads
+  // that block, from L2), so the loop body has no branch around a load.
+  const int iters = (mine + NB - 1) / NB * NB;
+  WaveStage ring[NB];
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u)
-    if (u < mine) load_kblock(ring[u], block_base(b, cache, tp.r, blk(u)), lane);
-  for (int j0 = 0; j0 < mine; j0 += NB) {
+  for (int u = 0; u < NB - 1; ++u) stage(ring[u], min(u, mine - 1));
+  for (int j0 = 0; j0 < iters; j0 += NB) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int j = j0 + u;
-      if (j >= mine) break;
-      if (j + NB - 1 < mine)
-        load_kblock(ring[(u + NB - 1) % NB], block_base(b, cache, tp.r, blk(j + NB - 1)), lane);
+      stage(ring[(u + NB - 1) % NB], min(j + NB - 1, mine - 1));
+      __builtin_amdgcn_sched_barrier(0);        // nothing that needs block j moves above these loads
+      wave_stage_store(ring[u], slot, lane);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      KBlock kb;
+      lds_kblock(kb, slot, lane);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // reads done before the slot is rewritten
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       float v;
-      block_scores<1>(f, ring[u], &v);
+      block_scores<1>(f, kb, &v);
       const int s = blk(j) * kBlock + lp;
-      if (s < n) out[s] = v;
+      if (j < mine && s < n) out[s] = v;
     }
   }
 }
@@ -282,60 +404,6 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
 }
 
 // ------------------------------------------------- prefill, LDS-staged --
-// Same work split as above, but each K block is fetched once per work-group:
-// the work-group copies it with contiguous 16-byte loads into LDS, two slots
-// alternating, and every wave reads its MFMA operands from there.  The 16-byte
-// chunk j of code row r sits at chunk (j ^ (r & 7)) of that row, so the
-// MFMA-layout reads (16 rows, one chunk each, per lane group) hit distinct
-// banks.
-template <int NW>
-struct StageRegs {
-  static constexpr int kChunks = kBlockBytes / 16;                  // 528
-  static constexpr int kPerThread = (kChunks + NW * 64 - 1) / (NW * 64);
-  uint4 v[kPerThread];
-};
-
-template <int NW>
-__device__ __forceinline__ int stage_src(int ci) {
-  // LDS chunk ci <- global byte offset
-  if (ci < kCodeBytes / 16) {
-    const int r = ci >> 3, slot = ci & 7;
-    return r * kHeadDim + ((slot ^ (r & 7)) << 4);
-  }
-  return ci << 4;                                                    // scales, unswizzled
-}
-
-template <int NW>
-__device__ __forceinline__ void stage_load(StageRegs<NW>& st, const uint8_t* __restrict__ base) {
-#pragma unroll
-  for (int u = 0; u < StageRegs<NW>::kPerThread; ++u) {
-    const int ci = threadIdx.x + u * NW * 64;
-    if (ci < StageRegs<NW>::kChunks)
-      st.v[u] = base ? *reinterpret_cast<const uint4*>(base + stage_src<NW>(ci)) : make_uint4(0, 0, 0, 0);
-  }
-}
-
-template <int NW>
-__device__ __forceinline__ void stage_store(const StageRegs<NW>& st, uint8_t* slot) {
-#pragma unroll
-  for (int u = 0; u < StageRegs<NW>::kPerThread; ++u) {
-    const int ci = threadIdx.x + u * NW * 64;
-    if (ci < StageRegs<NW>::kChunks) *reinterpret_cast<uint4*>(slot + (ci << 4)) = st.v[u];
-  }
-}
-
-__device__ __forceinline__ void lds_kblock(KBlock& kb, const uint8_t* slot, int lane) {
-  const int c = lane & 15, G = lane >> 4;
-#pragma unroll
-  for (int tl = 0; tl < 4; ++tl) {
-    const int r = tl * 16 + c;
-    const uint8_t* row = slot + r * kHeadDim;
-    kb.b[tl] = pack8(*reinterpret_cast<const uint4*>(row + ((G ^ (r & 7)) << 4)),
-                     *reinterpret_cast<const uint4*>(row + (((4 + G) ^ (r & 7)) << 4)));
-  }
-  kb.ks = *reinterpret_cast<const float*>(slot + kCodeBytes + lane_pos(lane) * 4);
-}
-
 template <int TPW, int NW>
 __global__ __launch_bounds__(NW * 64) void score_prefill_lds_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
@@ -410,13 +478,13 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_lds_kernel(
 
 constexpr int kPrefillTPW = IDX_PREFILL_TPW;
 
-// Decode chunk: about three work-groups per CU over the whole batch, at least
-// 8 and at most 64 blocks per work-group.
+// Decode chunk: about two work-groups per CU over the whole batch (two fit
+// by registers), at least 8 and at most 64 blocks per work-group.
 int decode_chunk_blocks(const BatchArgs& b) {
   const int64_t blocks_per_row = (b.max_seq_len + kBlock - 1) / kBlock;
   const int64_t total = blocks_per_row * b.num_tokens;
 #ifndef IDX_DECODE_WG_PER_CU
-#define IDX_DECODE_WG_PER_CU 3
+#define IDX_DECODE_WG_PER_CU 2
 #endif
   const int64_t slots = 256 * IDX_DECODE_WG_PER_CU;
   int64_t cb = (total + slots - 1) / slots;

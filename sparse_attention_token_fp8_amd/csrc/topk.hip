@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
                                                                 int32_t* __restrict__ topk,
                                                                 int64_t ldo) {
   const int t = blockIdx.x;
-  const int n = token_pos(b, t).n;
+  const int n = token_pos_wave(b, t).n;
   int32_t* out = topk + (size_t)t * ldo;
   if (n <= k) {
     write_all<kRowThreads>(out, n, k);
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
                                                                int64_t ldo) {
   const int t = blockIdx.y;
   const int c = blockIdx.x;
-  const int n = token_pos(b, t).n;
+  const int n = token_pos_wave(b, t).n;
   if (n <= k) {
     if (c == 0) write_all<kThreads>(topk + (size_t)t * ldo, n, k);
     return;
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
     int32_t* __restrict__ topk, int64_t ldo) {
   constexpr int NT = kResolveThreads;
   const int t = blockIdx.x;
-  const int n = token_pos(b, t).n;
+  const int n = token_pos_wave(b, t).n;
   if (n <= k) return;                          // written by the filter
   __shared__ uint32_t ckey[kCandCap];
   __shared__ int32_t cpos[kCandCap];
