@@ -1,7 +1,7 @@
 // Top-k select over the causal scores of each query token (see
 // topk_device.hpp for the rule and the method).  Two launch shapes:
 //
-//   many rows     one 1024-thread work-group per row: tau from the row's
+//   many rows     one 512-thread work-group per row: tau from the row's
 //                 sample, candidates (key >= tau) compacted into LDS in
 //                 position order, exact select, ordered write-out.  No global
 //                 scratch and no atomics outside LDS.
@@ -20,8 +20,9 @@
 namespace idx {
 namespace {
 
-constexpr int kRowThreads = 1024;
-constexpr int kCandCap = 6144;       // LDS candidate capacity per row
+constexpr int kRowThreads = 512;
+constexpr int kRowCap = 5120;        // LDS candidate capacity of the row kernel
+constexpr int kCandCap = 6144;       // LDS candidate capacity of the resolve
 constexpr int kBatch = 8;            // positions per thread per batch in the row kernel
 constexpr int kChunk = 4096;         // positions per filter work-group
 constexpr int kPer = kChunk / kThreads;
@@ -32,15 +33,15 @@ __device__ __forceinline__ void write_all(int32_t* out, int n, int k) {
   for (int j = threadIdx.x; j < k; j += NT) out[j] = j < n ? j : -1;
 }
 
-// Exact select over the `C` candidates in LDS (k <= C <= kCandCap, ascending
+// Exact select over the `C` candidates in LDS (k <= C <= cap, ascending
 // positions), else over the whole row, then the ordered write-out.
-template <int NT>
+template <int NT, typename Pos>
 __device__ __forceinline__ void finish_row(const float* __restrict__ row, int n, int k, uint32_t C,
-                                           const uint32_t* ckey, const int32_t* cpos,
+                                           uint32_t cap, const uint32_t* ckey, const Pos* cpos,
                                            int32_t* __restrict__ out, uint32_t* hist,
                                            uint32_t* bucket, uint32_t* scratch) {
   uint32_t take;
-  if (C >= (uint32_t)k && C <= (uint32_t)kCandCap) {
+  if (C >= (uint32_t)k && C <= cap) {
     const uint32_t kstar = select_kth<NT>(ckey, C, (uint32_t)k, &take, hist, bucket, scratch);
     emit_ordered<NT>([&](uint32_t i) { return make_uint2(ckey[i], (uint32_t)cpos[i]); }, C, kstar,
                      take, k, out, scratch);
@@ -53,6 +54,10 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ row, int n,
   }
 }
 
+// One work-group per row.  Candidate positions are stored as Pos (16 bits
+// when every row fits in 65536 positions), which with 512 threads lets four
+// rows share a CU.
+template <typename Pos>
 __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __restrict__ logits,
                                                                 int64_t ld, BatchArgs b, int k,
                                                                 int32_t* __restrict__ topk,
@@ -64,15 +69,15 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
     write_all<kRowThreads>(out, n, k);
     return;
   }
-  __shared__ uint32_t ckey[kCandCap];
-  __shared__ int32_t cpos[kCandCap];
+  __shared__ uint32_t ckey[kRowCap];
+  __shared__ Pos cpos[kRowCap];
   __shared__ uint32_t hist[kBins1];
   __shared__ uint32_t table[kBatch * kRowThreads / 64 + 1];
   __shared__ uint32_t bucket[64];
   __shared__ uint32_t scratch[scratch_words<kRowThreads>()];
   const float* row = logits + (size_t)t * ld;
   constexpr int kStep = kRowThreads * kBatch;
-  const bool sampled = n > kCandCap;            // else every position is a candidate
+  const bool sampled = n > kRowCap;             // else every position is a candidate
   float sv[sample_per<kRowThreads>()];
   int ns = 0;
   if (sampled) ns = sample_load<kRowThreads>(row, n, sv);   // first: tau waits on these only
@@ -99,9 +104,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
         v[e] = s < n ? row[s] : 0.f;
       }
     }
-    C += compact_ordered<kRowThreads, kBatch>(key, pass, base, C, ckey, cpos, kCandCap, table);
+    C += compact_ordered<kRowThreads, kBatch>(key, pass, base, C, ckey, cpos, kRowCap, table);
   }
-  finish_row<kRowThreads>(row, n, k, C, ckey, cpos, out, hist, bucket, scratch);
+  finish_row<kRowThreads>(row, n, k, C, kRowCap, ckey, cpos, out, hist, bucket, scratch);
 }
 
 // ---------------------------------------------------------- long rows --
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
       cpos[i] = ws.cand_pos[a];
     }
     __syncthreads();
-    finish_row<NT>(row, n, k, C, ckey, cpos, out, hist, bucket, scratch);
+    finish_row<NT>(row, n, k, C, kCandCap, ckey, cpos, out, hist, bucket, scratch);
   } else if (C > (uint32_t)kCandCap) {          // too many for LDS: read the slots in place
     uint32_t take;
     const uint32_t kstar = radix_kth<NT, 3>([&](auto&& fn) {
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
       return make_uint2(ws.cand_key[a], (uint32_t)ws.cand_pos[a]);
     }, C, kstar, take, k, out, scratch);
   } else {
-    finish_row<NT>(row, n, k, C, ckey, cpos, out, hist, bucket, scratch);   // fewer than k: whole row
+    finish_row<NT>(row, n, k, C, kCandCap, ckey, cpos, out, hist, bucket, scratch);   // fewer than k: whole row
   }
 }
 
@@ -238,8 +243,12 @@ hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, cons
     hipLaunchKernelGGL(topk_resolve_kernel, dim3((unsigned)b.num_tokens), dim3(kResolveThreads), 0,
                        stream, logits, ld, b, k, ws, out, ldo);
   } else {
-    hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)b.num_tokens), dim3(kRowThreads), 0,
-                       stream, logits, ld, b, k, out, ldo);
+    if (b.max_seq_len <= 65536)
+      hipLaunchKernelGGL(topk_rows_kernel<uint16_t>, dim3((unsigned)b.num_tokens), dim3(kRowThreads),
+                         0, stream, logits, ld, b, k, out, ldo);
+    else
+      hipLaunchKernelGGL(topk_rows_kernel<int32_t>, dim3((unsigned)b.num_tokens), dim3(kRowThreads),
+                         0, stream, logits, ld, b, k, out, ldo);
   }
   return hipGetLastError();
 }

@@ -328,11 +328,12 @@ __device__ __forceinline__ uint32_t sample_tau(const float* v, int ns, int n, in
 
 // Ordered compaction of one batch: element (e, thread) sits at position
 // base + e*NT + threadIdx.x; those with pass[e] are appended to (ckey, cpos)
-// after `*count` entries, in ascending position order.  `table` holds
-// E*NT/64 words of LDS.  Returns the batch's number of passing elements.
-template <int NT, int E>
+// after `start` entries, in ascending position order (entries past `cap` are
+// counted, not stored).  `table` holds E*NT/64 + 1 words of LDS.  Returns the
+// batch's number of passing elements.
+template <int NT, int E, typename Pos>
 __device__ __forceinline__ uint32_t compact_ordered(const uint32_t* key, const bool* pass, int base,
-                                                    uint32_t start, uint32_t* ckey, int32_t* cpos,
+                                                    uint32_t start, uint32_t* ckey, Pos* cpos,
                                                     uint32_t cap, uint32_t* table) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -376,7 +377,7 @@ __device__ __forceinline__ uint32_t compact_ordered(const uint32_t* key, const b
     if (pass[e]) {
       const uint32_t slot = start + table[e * NW + wave] +
                             (uint32_t)__popcll(m[e] & ((1ull << lane) - 1ull));
-      if (slot < cap) { ckey[slot] = key[e]; cpos[slot] = base + e * NT + (int)threadIdx.x; }
+      if (slot < cap) { ckey[slot] = key[e]; cpos[slot] = (Pos)(base + e * NT + (int)threadIdx.x); }
     }
   }
   const uint32_t total = table[E * NW];
