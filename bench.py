@@ -188,8 +188,8 @@ def run_workload(m, torch, name, args):
         ach = a["flops"] / (ms_logits * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / FP8_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic("score_prefill_lds_kernel", name),
-                "kernel": "score_prefill_lds_kernel (idx_logits)", "ms_per_launch": round(ms_logits, 5),
+                "traffic": measured_traffic("score_prefill_kernel", name),
+                "kernel": "score_prefill_kernel (idx_logits)", "ms_per_launch": round(ms_logits, 5),
                 "flops_per_launch": a["flops"]}
     step_gbs = a["step_bytes"] / (ms_step * 1e-3) / 1e9
     res = dict(workload=name, tokens=wl.num_tokens, ms_per_step=ms_step,

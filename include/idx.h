@@ -79,6 +79,14 @@ typedef struct idx_kcache {
  * n_r = query_start_loc[r+1] - query_start_loc[r] are this step's new
  * tokens; query token t = query_start_loc[r] + i sits at position
  * p_t = seq_lens[r] - n_r + i and is scored against positions 0..p_t.
+ *
+ * num_decode_tokens (the metadata's decode count, decodes listed first) only
+ * chooses how scoring work is split, never the result: tokens
+ * 0..num_decode_tokens-1 are scored one token per work-group (the split for
+ * short queries over long contexts), the others in groups of consecutive
+ * tokens of one request (the split for prefill chunks), both kinds in one
+ * launch.  0 lets the library choose: the decode split when every request
+ * has at most one new token, else the prefill split for all.
  */
 typedef struct idx_batch {
   const int32_t* seq_lens;         /* device [num_reqs] */
@@ -89,6 +97,7 @@ typedef struct idx_batch {
   int32_t num_tokens;              /* host copy of query_start_loc[num_reqs] */
   int32_t max_seq_len;             /* host copy of max(seq_lens) */
   int32_t max_query_len;           /* host copy of max(n_r) */
+  int32_t num_decode_tokens;       /* 0..num_tokens, see above */
 } idx_batch_t;
 
 /*

@@ -39,7 +39,8 @@ class BatchC(ctypes.Structure):
     _fields_ = [("seq_lens", ctypes.c_void_p), ("query_start_loc", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int64),
                 ("num_reqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
-                ("max_seq_len", ctypes.c_int32), ("max_query_len", ctypes.c_int32)]
+                ("max_seq_len", ctypes.c_int32), ("max_query_len", ctypes.c_int32),
+                ("num_decode_tokens", ctypes.c_int32)]
 
 
 class LayerIOC(ctypes.Structure):
@@ -125,7 +126,7 @@ class KCache:
 class Batch:
     """Device batch metadata plus the host copies the library sizes grids with."""
 
-    def __init__(self, seq_lens, query_start_loc, block_table, device="cuda"):
+    def __init__(self, seq_lens, query_start_loc, block_table, device="cuda", num_decode_tokens=0):
         sl = np.asarray(seq_lens, dtype=np.int32)
         qsl = np.asarray(query_start_loc, dtype=np.int32)
         bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
@@ -137,9 +138,11 @@ class Batch:
         self.max_seq_len = int(sl.max()) if sl.size else 0
         self.max_query_len = int(np.diff(qsl).max()) if sl.size else 0
         self.block_table_stride = int(bt.shape[1])
+        self.num_decode_tokens = int(num_decode_tokens)
         self._c = BatchC(self.seq_lens.data_ptr(), self.query_start_loc.data_ptr(),
                          self.block_table.data_ptr(), self.block_table_stride, self.num_reqs,
-                         self.num_tokens, self.max_seq_len, self.max_query_len)
+                         self.num_tokens, self.max_seq_len, self.max_query_len,
+                         self.num_decode_tokens)
 
     def c(self):
         return ctypes.byref(self._c)

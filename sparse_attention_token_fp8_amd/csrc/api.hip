@@ -34,6 +34,7 @@ idx_status_t check_batch(const idx_batch_t* b) {
       b->block_table_stride < 1)
     return IDX_ERR_INVALID_ARG;
   if (b->max_query_len > b->num_tokens) return IDX_ERR_INVALID_ARG;
+  if (b->num_decode_tokens < 0 || b->num_decode_tokens > b->num_tokens) return IDX_ERR_INVALID_ARG;
   return IDX_OK;
 }
 
@@ -131,7 +132,8 @@ idx_status_t idx_logits(const uint8_t* q_fp8, const float* w, int32_t n_heads, i
   if (batch->num_tokens == 0) return IDX_OK;
   if (logits == nullptr || logits_stride < batch->max_seq_len) return IDX_ERR_INVALID_ARG;
   CacheArgs c{cache.data, cache.num_blocks};
-  return launched(launch_score(q_fp8, w, c, to_args(batch), logits, logits_stride, stream));
+  return launched(launch_score(q_fp8, w, c, to_args(batch), batch->num_decode_tokens, logits,
+                               logits_stride, stream));
 }
 
 size_t idx_topk_workspace_size(const idx_batch_t* batch, int32_t k) {
@@ -179,7 +181,7 @@ idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_head
   topk_workspace_layout(batch->num_tokens, batch->max_seq_len, fused_ld(batch), workspace, &ws);
   const BatchArgs b = to_args(batch);
   CacheArgs c{cache.data, cache.num_blocks};
-  hipError_t e = launch_score(q_fp8, w, c, b, ws.logits, ws.ld, stream);
+  hipError_t e = launch_score(q_fp8, w, c, b, batch->num_decode_tokens, ws.logits, ws.ld, stream);
   if (e == hipSuccess) e = launch_topk(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
   return launched(e);
 }

@@ -14,9 +14,12 @@ hipError_t launch_quant_q_fold(const uint16_t* q, const float* w_raw, int64_t nu
                                float softmax_scale, float head_norm, uint8_t* q8, float* w_out,
                                float* qs_out, hipStream_t stream);
 
-// Scores into `logits` (row stride ld).
+// Scores into `logits` (row stride ld).  Tokens below dec_tokens use the
+// decode work split (one token per work-group), the rest the prefill split; a
+// batch whose requests have at most one new token each is all decode.
 hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cache,
-                        const BatchArgs& b, float* logits, int64_t ld, hipStream_t stream);
+                        const BatchArgs& b, int64_t dec_tokens, float* logits, int64_t ld,
+                        hipStream_t stream);
 
 // Top-k rows from scores (row stride ld) into out (row stride ldo).
 hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, const TopkWorkspace& ws,

@@ -248,39 +248,33 @@ __device__ __forceinline__ void wave_stage_store(const WaveStage& st, uint8_t* s
 // consecutive 64-position blocks of its causal range and its four waves take
 // every fourth block.  Each wave keeps the loads of its next NB-1 blocks in
 // flight in registers and passes the current block through its own LDS slot
-// into the MFMA layout.
+// (`lds`: 4 * kBlockBytes) into the MFMA layout.
 #ifndef IDX_DECODE_RING
 #define IDX_DECODE_RING 2
-#endif
-#ifndef IDX_PREFILL_RING
-#define IDX_PREFILL_RING 2
 #endif
 #ifndef IDX_PREFILL_TPW
 #define IDX_PREFILL_TPW 2
 #endif
-#ifndef IDX_PREFILL_LDS
-#define IDX_PREFILL_LDS 1
-#endif
-#ifndef IDX_PREFILL_WAVES
-#define IDX_PREFILL_WAVES 4
-#endif
-
 #ifndef IDX_DECODE_WAVES_PER_EU
 #define IDX_DECODE_WAVES_PER_EU 2
 #endif
 
+constexpr int kScoreThreads = 256;              // four waves, both work splits
+constexpr int kPrefillTPW = IDX_PREFILL_TPW;    // query tokens per wave (prefill)
+constexpr int kPrefillTM = 4 * kPrefillTPW;     // query tokens per work-group (prefill)
+constexpr int kScoreLds = 4 * kBlockBytes;
+
 template <int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU)))
-void score_decode_kernel(
-    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    float* __restrict__ logits, int64_t ld, int chunk_blocks) {
-  const int t = blockIdx.y;
+__device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __restrict__ q8,
+                                            const float* __restrict__ w, const CacheArgs& cache,
+                                            const BatchArgs& b, float* __restrict__ logits,
+                                            int64_t ld, int chunk_blocks, uint8_t* lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   QFrag f[1];
   load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);  // needs t only
   const TokenPos tp = token_pos_wave(b, t);
   const int n = tp.n;
-  const int lb0 = blockIdx.x * chunk_blocks;
+  const int lb0 = bx * chunk_blocks;
   if (lb0 * kBlock >= n) return;
   const int nblk = min(chunk_blocks, (n - lb0 * kBlock + kBlock - 1) / kBlock);
   const int lp = lane_pos(lane);
@@ -302,8 +296,7 @@ void score_decode_kernel(
     const int pb = __builtin_amdgcn_readlane(pbl, j);
     wave_stage_load(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes, pb >= 0, lane);
   };
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[4][kBlockBytes];
-  uint8_t* slot = kbuf[wave];
+  uint8_t* slot = lds + wave * kBlockBytes;
 
   // Every iteration issues one block's loads (past the last block it re-reads
   // that block, from L2), so the loop body has no branch around a load.
@@ -335,87 +328,26 @@ void score_decode_kernel(
 }
 
 // ------------------------------------------------------------ prefill --
-// A work-group takes 4*TPW consecutive query tokens of one request (TPW per
-// wave) and `chunk_blocks` blocks of positions; all four waves walk the same
-// blocks, so each K block is fetched from HBM once per work-group and reused
-// from the caches by the other waves.
-template <int TPW, int NB>
-__global__ __launch_bounds__(256) void score_prefill_kernel(
-    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    float* __restrict__ logits, int64_t ld, int chunk_blocks, int groups_per_req) {
-  constexpr int TM = 4 * TPW;
-  const int r = blockIdx.y / groups_per_req;
-  const int g = blockIdx.y % groups_per_req;
+// A work-group takes kPrefillTM consecutive query tokens of one request
+// (kPrefillTPW per wave) and `chunk_blocks` blocks of positions.  Each K block
+// is fetched once per work-group: the work-group copies it with whole-line
+// loads into one of two LDS slots (`lds`: 2 * kBlockBytes) and every wave reads
+// its MFMA operands from there.  Tokens below `tok_lo` are left to the decode
+// work split of a mixed launch.
+__device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
+                                             const uint8_t* __restrict__ q8,
+                                             const float* __restrict__ w, const CacheArgs& cache,
+                                             const BatchArgs& b, float* __restrict__ logits,
+                                             int64_t ld, int chunk_blocks, int groups_per_req,
+                                             uint8_t* lds) {
+  constexpr int TPW = kPrefillTPW, NW = 4, TM = kPrefillTM;
+  const int r = gy / groups_per_req;
+  const int g = gy % groups_per_req;
   if (r >= b.num_reqs) return;
   const int q0 = b.qsl[r];
   const int nq = b.qsl[r + 1] - q0;
   const int tb = g * TM;
-  if (tb >= nq) return;
-  const int L = b.seq_lens[r];
-  auto count = [&](int i) {  // causal positions of the request's i-th new token
-    int n = L - nq + i + 1;
-    n = n < 0 ? 0 : n;
-    return n > b.max_seq_len ? b.max_seq_len : n;
-  };
-  const int n_max = count(min(tb + TM, nq) - 1);
-  const int lb0 = blockIdx.x * chunk_blocks;
-  if (lb0 * kBlock >= n_max) return;
-  const int nblk = min(chunk_blocks, (n_max - lb0 * kBlock + kBlock - 1) / kBlock);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lp = lane_pos(lane);
-
-  QFrag f[TPW];
-  int nt[TPW];
-  float* out[TPW];
-#pragma unroll
-  for (int j = 0; j < TPW; ++j) {
-    const int i = tb + wave * TPW + j;
-    const int t = q0 + i;
-    if (i < nq && t >= 0 && t < b.num_tokens) {
-      load_q(f[j], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
-      nt[j] = count(i);
-      out[j] = logits + (size_t)t * ld;
-    } else {
-      zero_q(f[j]);
-      nt[j] = 0;
-      out[j] = logits;
-    }
-  }
-
-  KBlock ring[NB];
-#pragma unroll
-  for (int u = 0; u < NB - 1; ++u)
-    if (u < nblk) load_kblock(ring[u], block_base(b, cache, r, lb0 + u), lane);
-  for (int j0 = 0; j0 < nblk; j0 += NB) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int j = j0 + u;
-      if (j >= nblk) break;
-      if (j + NB - 1 < nblk)
-        load_kblock(ring[(u + NB - 1) % NB], block_base(b, cache, r, lb0 + j + NB - 1), lane);
-      float v[TPW];
-      block_scores<TPW>(f, ring[u], v);
-      const int s = (lb0 + j) * kBlock + lp;
-#pragma unroll
-      for (int jj = 0; jj < TPW; ++jj)
-        if (s < nt[jj]) out[jj][s] = v[jj];
-    }
-  }
-}
-
-// ------------------------------------------------- prefill, LDS-staged --
-template <int TPW, int NW>
-__global__ __launch_bounds__(NW * 64) void score_prefill_lds_kernel(
-    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    float* __restrict__ logits, int64_t ld, int chunk_blocks, int groups_per_req) {
-  constexpr int TM = NW * TPW;
-  const int r = blockIdx.y / groups_per_req;
-  const int g = blockIdx.y % groups_per_req;
-  if (r >= b.num_reqs) return;
-  const int q0 = b.qsl[r];
-  const int nq = b.qsl[r + 1] - q0;
-  const int tb = g * TM;
-  if (tb >= nq) return;
+  if (tb >= nq || q0 + min(tb + TM, nq) <= tok_lo) return;
   const int L = b.seq_lens[r];
   auto count = [&](int i) {
     int n = L - nq + i + 1;
@@ -423,13 +355,13 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_lds_kernel(
     return n > b.max_seq_len ? b.max_seq_len : n;
   };
   const int n_max = count(min(tb + TM, nq) - 1);
-  const int lb0 = blockIdx.x * chunk_blocks;
+  const int lb0 = bx * chunk_blocks;
   if (lb0 * kBlock >= n_max) return;
   const int nblk = min(chunk_blocks, (n_max - lb0 * kBlock + kBlock - 1) / kBlock);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lp = lane_pos(lane);
-
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kBlockBytes];
+  uint8_t* kbuf0 = lds;
+  uint8_t* kbuf1 = lds + kBlockBytes;
 
   QFrag f[TPW];
   int nt[TPW];
@@ -438,7 +370,7 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_lds_kernel(
   for (int j = 0; j < TPW; ++j) {
     const int i = tb + wave * TPW + j;
     const int t = q0 + i;
-    if (i < nq && t >= 0 && t < b.num_tokens) {
+    if (i < nq && t >= tok_lo && t < b.num_tokens) {
       load_q(f[j], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
       nt[j] = count(i);
       out[j] = logits + (size_t)t * ld;
@@ -453,7 +385,7 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_lds_kernel(
   // issued while block j is scored and reach LDS one iteration later.
   StageRegs<NW> st[2];
   stage_load<NW>(st[0], block_base(b, cache, r, lb0));
-  stage_store<NW>(st[0], kbuf[0]);
+  stage_store<NW>(st[0], kbuf0);
   if (nblk > 1) stage_load<NW>(st[1], block_base(b, cache, r, lb0 + 1));
   if (nblk > 2) stage_load<NW>(st[0], block_base(b, cache, r, lb0 + 2));
   for (int j0 = 0; j0 < nblk; j0 += 2) {
@@ -462,10 +394,10 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_lds_kernel(
       const int j = j0 + u;
       if (j >= nblk) break;
       __syncthreads();                     // block j in slot j&1; slot (j+1)&1 free
-      if (j + 1 < nblk) stage_store<NW>(st[(u + 1) & 1], kbuf[(j + 1) & 1]);
+      if (j + 1 < nblk) stage_store<NW>(st[(u + 1) & 1], (j + 1) & 1 ? kbuf1 : kbuf0);
       if (j + 3 < nblk) stage_load<NW>(st[(u + 1) & 1], block_base(b, cache, r, lb0 + j + 3));
       KBlock kb;
-      lds_kblock(kb, kbuf[j & 1], lane);
+      lds_kblock(kb, j & 1 ? kbuf1 : kbuf0, lane);
       float v[TPW];
       block_scores<TPW>(f, kb, v);
       const int s = (lb0 + j) * kBlock + lp;
@@ -476,13 +408,46 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_lds_kernel(
   }
 }
 
-constexpr int kPrefillTPW = IDX_PREFILL_TPW;
+// ------------------------------------------------------------ kernels --
 
-// Decode chunk: about two work-groups per CU over the whole batch (two fit
+template <int NB>
+__global__ __launch_bounds__(kScoreThreads)
+__attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
+    float* __restrict__ logits, int64_t ld, int chunk_blocks) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
+  decode_body<NB>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks, lds);
+}
+
+__global__ __launch_bounds__(kScoreThreads) void score_prefill_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
+    float* __restrict__ logits, int64_t ld, int chunk_blocks, int groups_per_req) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBlockBytes];
+  prefill_body(blockIdx.x, blockIdx.y, 0, q8, w, cache, b, logits, ld, chunk_blocks, groups_per_req,
+               lds);
+}
+
+// Mixed batch in one launch: rows y < dec_tokens are tokens scored with the
+// decode split, the rest are prefill groups; the two kinds of work-group share
+// the machine (HBM-bound decode beside MFMA-bound prefill).
+template <int NB>
+__global__ __launch_bounds__(kScoreThreads) void score_mixed_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
+    float* __restrict__ logits, int64_t ld, int dec_tokens, int dec_chunk_blocks,
+    int pre_chunk_blocks, int groups_per_req) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
+  if ((int)blockIdx.y < dec_tokens)
+    decode_body<NB>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, dec_chunk_blocks, lds);
+  else
+    prefill_body(blockIdx.x, blockIdx.y - dec_tokens, dec_tokens, q8, w, cache, b, logits, ld,
+                 pre_chunk_blocks, groups_per_req, lds);
+}
+
+// Decode chunk: about two work-groups per CU over the decode tokens (two fit
 // by registers), at least 8 and at most 64 blocks per work-group.
-int decode_chunk_blocks(const BatchArgs& b) {
-  const int64_t blocks_per_row = (b.max_seq_len + kBlock - 1) / kBlock;
-  const int64_t total = blocks_per_row * b.num_tokens;
+int decode_chunk_blocks(int max_seq_len, int64_t tokens) {
+  const int64_t blocks_per_row = (max_seq_len + kBlock - 1) / kBlock;
+  const int64_t total = blocks_per_row * tokens;
 #ifndef IDX_DECODE_WG_PER_CU
 #define IDX_DECODE_WG_PER_CU 2
 #endif
@@ -494,8 +459,7 @@ int decode_chunk_blocks(const BatchArgs& b) {
 
 int prefill_chunk_blocks(const BatchArgs& b) {
   // aim for a few thousand work-groups; never more blocks than the longest row needs
-  const int tm = (IDX_PREFILL_LDS ? IDX_PREFILL_WAVES : 4) * kPrefillTPW;
-  const int gpr = (b.max_query_len + tm - 1) / tm;
+  const int gpr = (b.max_query_len + kPrefillTM - 1) / kPrefillTM;
   const int64_t groups = (int64_t)gpr * b.num_reqs;
 #ifndef IDX_PREFILL_MAX_CHUNK
 #define IDX_PREFILL_MAX_CHUNK 32
@@ -508,28 +472,30 @@ int prefill_chunk_blocks(const BatchArgs& b) {
 }  // namespace
 
 hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cache,
-                        const BatchArgs& b, float* logits, int64_t ld, hipStream_t stream) {
+                        const BatchArgs& b, int64_t dec_tokens, float* logits, int64_t ld,
+                        hipStream_t stream) {
   if (b.num_tokens == 0 || b.max_seq_len == 0) return hipSuccess;
-  if (b.max_query_len <= 1) {
-    const int cb = decode_chunk_blocks(b);
+  if (b.max_query_len <= 1) dec_tokens = b.num_tokens;
+  if (dec_tokens >= b.num_tokens) {
+    const int cb = decode_chunk_blocks(b.max_seq_len, b.num_tokens);
     const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
     const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
-    hipLaunchKernelGGL(score_decode_kernel<IDX_DECODE_RING>, grid, dim3(256), 0, stream, q8, w, cache, b, logits,
-                       ld, cb);
+    hipLaunchKernelGGL(score_decode_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0, stream,
+                       q8, w, cache, b, logits, ld, cb);
   } else {
-    const int cb = prefill_chunk_blocks(b);
-    const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
-    if (IDX_PREFILL_LDS) {
-      constexpr int tm = IDX_PREFILL_WAVES * kPrefillTPW;
-      const int gpr = (b.max_query_len + tm - 1) / tm;
-      const dim3 grid((unsigned)chunks, (unsigned)(gpr * b.num_reqs));
-      hipLaunchKernelGGL((score_prefill_lds_kernel<kPrefillTPW, IDX_PREFILL_WAVES>), grid,
-                         dim3(IDX_PREFILL_WAVES * 64), 0, stream, q8, w, cache, b, logits, ld, cb, gpr);
+    const int pcb = prefill_chunk_blocks(b);
+    const int pchunks = (b.max_seq_len + pcb * kBlock - 1) / (pcb * kBlock);
+    const int gpr = (b.max_query_len + kPrefillTM - 1) / kPrefillTM;
+    if (dec_tokens <= 0) {
+      const dim3 grid((unsigned)pchunks, (unsigned)(gpr * b.num_reqs));
+      hipLaunchKernelGGL(score_prefill_kernel, grid, dim3(kScoreThreads), 0, stream, q8, w, cache, b,
+                         logits, ld, pcb, gpr);
     } else {
-      const int gpr = (b.max_query_len + 4 * kPrefillTPW - 1) / (4 * kPrefillTPW);
-      const dim3 grid((unsigned)chunks, (unsigned)(gpr * b.num_reqs));
-      hipLaunchKernelGGL((score_prefill_kernel<kPrefillTPW, IDX_PREFILL_RING>), grid, dim3(256), 0,
-                         stream, q8, w, cache, b, logits, ld, cb, gpr);
+      const int dcb = decode_chunk_blocks(b.max_seq_len, dec_tokens);
+      const int dchunks = (b.max_seq_len + dcb * kBlock - 1) / (dcb * kBlock);
+      const dim3 grid((unsigned)std::max(dchunks, pchunks), (unsigned)(dec_tokens + gpr * b.num_reqs));
+      hipLaunchKernelGGL(score_mixed_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0, stream,
+                         q8, w, cache, b, logits, ld, (int)dec_tokens, dcb, pcb, gpr);
     }
   }
   return hipGetLastError();

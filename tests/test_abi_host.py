@@ -39,9 +39,11 @@ def test_every_declared_symbol_is_exported(m):
     assert set(names) <= set(m.binding.SIGNATURES), "binding misses a declared entry point"
 
 
-def _batch(m, num_reqs=1, num_tokens=1, max_seq_len=64, max_query_len=1, stride=1, null=False):
+def _batch(m, num_reqs=1, num_tokens=1, max_seq_len=64, max_query_len=1, stride=1, null=False,
+           num_decode_tokens=0):
     fake = 0 if null else 0x10000
-    return m.binding.BatchC(fake, fake, fake, stride, num_reqs, num_tokens, max_seq_len, max_query_len)
+    return m.binding.BatchC(fake, fake, fake, stride, num_reqs, num_tokens, max_seq_len, max_query_len,
+                            num_decode_tokens)
 
 
 FAKE = ctypes.c_void_p(0x10000)
@@ -78,6 +80,9 @@ def test_scoring_rejects(m):
     assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(_batch(m, max_seq_len=65)), FAKE, 65, S) == -1
     assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(_batch(m, num_tokens=70000)), FAKE, 64, S) == -2
     assert L.idx_logits(ctypes.c_void_p(0x10008), FAKE, 64, 128, _cache(m), B(ok), FAKE, 64, S) == -1
+    for nd in (-1, 2):                                          # decode split outside 0..num_tokens
+        assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(_batch(m, num_decode_tokens=nd)),
+                            FAKE, 64, S) == -1
     assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(_batch(m, num_tokens=0, max_query_len=0)),
                         None, 64, S) == 0
 
