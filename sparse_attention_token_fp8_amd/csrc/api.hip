@@ -76,6 +76,40 @@ int64_t fused_ld(const idx_batch_t* b) {
 
 idx_status_t launched(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH; }
 
+size_t fused_workspace(const idx_batch_t* b, void* base, TopkWorkspace* ws) {
+  return topk_workspace_layout(b->num_tokens, b->max_seq_len, fused_ld(b), base, ws);
+}
+
+idx_status_t check_k_rows(const uint16_t* k_bf16, int64_t k_row_stride, const int64_t* slot_mapping,
+                          const idx_kcache_t& cache, int64_t num_tokens) {
+  if (num_tokens == 0) return IDX_OK;
+  if (k_bf16 == nullptr || slot_mapping == nullptr || cache.data == nullptr)
+    return IDX_ERR_INVALID_ARG;
+  if (k_row_stride < kHeadDim || (k_row_stride % 4) != 0 || !aligned(k_bf16, 8))
+    return IDX_ERR_INVALID_ARG;
+  return IDX_OK;
+}
+
+// Scores + top-k of one batch into `topk`; with kq set, this step's new K rows
+// are quantised into the cache first.  Arguments are already checked.
+hipError_t score_topk(const uint8_t* q_fp8, const float* w, const idx_kcache_t& cache,
+                      const idx_batch_t* batch, int32_t k, int32_t* topk, int64_t topk_stride,
+                      void* workspace, const uint16_t* kq, int64_t kq_stride,
+                      const int64_t* slots, hipStream_t stream) {
+  TopkWorkspace ws;
+  fused_workspace(batch, workspace, &ws);
+  const BatchArgs b = to_args(batch);
+  const CacheArgs c{cache.data, cache.num_blocks};
+  hipError_t e = hipSuccess;
+  if (kq != nullptr)
+    e = launch_quant_write_k(kq, batch->num_tokens, kq_stride, slots, cache.data,
+                             cache.num_blocks * kBlock, stream);
+  if (e == hipSuccess)
+    e = launch_score(q_fp8, w, c, b, batch->num_decode_tokens, ws.logits, ws.ld, stream);
+  if (e == hipSuccess) e = launch_topk(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,8 +195,8 @@ idx_status_t idx_topk(const float* logits, int64_t logits_stride, const idx_batc
 
 size_t idx_score_topk_workspace_size(const idx_batch_t* batch, int32_t k) {
   if (batch == nullptr || batch->num_tokens <= 0 || k < 1) return 0;
-  return topk_workspace_layout(batch->num_tokens, batch->max_seq_len, fused_ld(batch), nullptr,
-                               nullptr);
+  if (check_batch(batch) != IDX_OK) return 0;
+  return fused_workspace(batch, nullptr, nullptr);
 }
 
 idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
@@ -177,13 +211,8 @@ idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_head
   const size_t need = idx_score_topk_workspace_size(batch, k);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
     return IDX_ERR_WORKSPACE;
-  TopkWorkspace ws;
-  topk_workspace_layout(batch->num_tokens, batch->max_seq_len, fused_ld(batch), workspace, &ws);
-  const BatchArgs b = to_args(batch);
-  CacheArgs c{cache.data, cache.num_blocks};
-  hipError_t e = launch_score(q_fp8, w, c, b, batch->num_decode_tokens, ws.logits, ws.ld, stream);
-  if (e == hipSuccess) e = launch_topk(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
-  return launched(e);
+  return launched(score_topk(q_fp8, w, cache, batch, k, topk, topk_stride, workspace, nullptr, 0,
+                             nullptr, stream));
 }
 
 idx_status_t idx_indexcache_layer(const idx_layer_io_t* layer, int32_t is_full, int32_t write_k,
@@ -193,24 +222,24 @@ idx_status_t idx_indexcache_layer(const idx_layer_io_t* layer, int32_t is_full, 
   if (layer == nullptr) return IDX_ERR_INVALID_ARG;
   idx_status_t s = check_batch(batch);
   if (s != IDX_OK) return s;
-  if (is_full) {
-    s = check_scoring(layer->q_fp8, layer->w, kHeads, kHeadDim, layer->cache, batch);
-    if (s != IDX_OK) return s;
-    s = check_k(k, topk_stride, topk, batch->num_tokens);
-    if (s != IDX_OK) return s;
-    if (batch->num_tokens > 0 &&
-        (workspace == nullptr || workspace_bytes < idx_score_topk_workspace_size(batch, k)))
-      return IDX_ERR_WORKSPACE;
+  if (!is_full) {
+    if (!write_k) return IDX_OK;
+    return idx_quant_write_k(layer->k_bf16, batch->num_tokens, kHeadDim, layer->k_row_stride,
+                             slot_mapping, layer->cache, stream);
   }
-  if (is_full || write_k) {
-    s = idx_quant_write_k(layer->k_bf16, batch->num_tokens, kHeadDim, layer->k_row_stride,
-                          slot_mapping, layer->cache, stream);
-    if (s != IDX_OK) return s;
-  }
-  if (is_full)
-    return idx_score_topk(layer->q_fp8, layer->w, kHeads, kHeadDim, layer->cache, batch, k, topk,
-                          topk_stride, workspace, workspace_bytes, stream);
-  return IDX_OK;
+  s = check_scoring(layer->q_fp8, layer->w, kHeads, kHeadDim, layer->cache, batch);
+  if (s != IDX_OK) return s;
+  s = check_k(k, topk_stride, topk, batch->num_tokens);
+  if (s != IDX_OK) return s;
+  s = check_k_rows(layer->k_bf16, layer->k_row_stride, slot_mapping, layer->cache,
+                   batch->num_tokens);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens == 0) return IDX_OK;
+  if (workspace == nullptr || workspace_bytes < idx_score_topk_workspace_size(batch, k) ||
+      !aligned(workspace, 256))
+    return IDX_ERR_WORKSPACE;
+  return launched(score_topk(layer->q_fp8, layer->w, layer->cache, batch, k, topk, topk_stride,
+                             workspace, layer->k_bf16, layer->k_row_stride, slot_mapping, stream));
 }
 
 idx_status_t idx_indexcache_stack(const idx_layer_io_t* layers, int32_t num_layers,

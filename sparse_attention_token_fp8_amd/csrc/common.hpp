@@ -44,17 +44,19 @@ struct CacheArgs {
   int64_t num_blocks;
 };
 
-// Top-k workspace (device, caller-owned).  The fused entry point keeps the
-// scores in `logits`; the long-row launch shape keeps each (row, 4096-position
-// chunk) candidate slot in `cand_key` / `cand_pos` with its count in `counts`.
+// Top-k workspace (device, caller-owned).  The fused entry points keep the
+// scores in `logits`.  Long rows keep their candidates in `nslots` slots of
+// `slot_cap` entries per row (`cand_key` / `cand_pos`, in position order
+// across the slots; one slot per 4096-position chunk) with each slot's count
+// in `counts`.
 struct TopkWorkspace {
   float* logits;       // [T][ld] (fused path only)
-  uint32_t* cand_key;  // [T][nchunks][4096]
-  int32_t* cand_pos;   // [T][nchunks][4096]
-  uint32_t* counts;    // [T][nchunks]
+  uint32_t* cand_key;  // [T][nslots][slot_cap]
+  int32_t* cand_pos;   // [T][nslots][slot_cap]
+  uint32_t* counts;    // [T][nslots]
   int64_t ld;
-  int32_t nchunks;
-  int32_t pad;
+  int32_t nslots;
+  int32_t slot_cap;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -64,22 +66,25 @@ int topk_nchunks(int max_seq_len);
 int topk_chunk();
 int topk_max_seq_len();
 
+constexpr int kMaxSlots = 1024;                 // slots per row the resolve can index
+
 // Layout of the workspace for T rows of up to max_seq_len positions; returns
-// the total bytes.  When base is non-null also fills `ws`.  logits_ld is 0 for
-// idx_topk (scores come from the caller).
+// the total bytes.  When base is non-null also fills `ws`.  logits_ld is 0
+// for idx_topk (scores come from the caller).
 inline size_t topk_workspace_layout(int64_t T, int max_seq_len, int64_t logits_ld, void* base,
                                     TopkWorkspace* ws) {
   const bool lr = topk_uses_long_rows(T, max_seq_len);
-  const int64_t nch = lr ? topk_nchunks(max_seq_len) : 0;
+  const int64_t nslots = lr ? topk_nchunks(max_seq_len) : 0;
+  const int64_t cap = lr ? topk_chunk() : 0;
   size_t off = 0;
   const size_t o_logits = off;
   off = align_up(off + sizeof(float) * (size_t)logits_ld * (size_t)T, 256);
   const size_t o_ckey = off;
-  off = align_up(off + sizeof(uint32_t) * (size_t)topk_chunk() * (size_t)nch * (size_t)T, 256);
+  off = align_up(off + sizeof(uint32_t) * (size_t)cap * (size_t)nslots * (size_t)T, 256);
   const size_t o_cpos = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)topk_chunk() * (size_t)nch * (size_t)T, 256);
+  off = align_up(off + sizeof(int32_t) * (size_t)cap * (size_t)nslots * (size_t)T, 256);
   const size_t o_counts = off;
-  off = align_up(off + sizeof(uint32_t) * (size_t)nch * (size_t)T, 256);
+  off = align_up(off + sizeof(uint32_t) * (size_t)nslots * (size_t)T, 256);
   if (off == 0) off = 256;
   if (base && ws) {
     char* b = static_cast<char*>(base);
@@ -88,8 +93,8 @@ inline size_t topk_workspace_layout(int64_t T, int max_seq_len, int64_t logits_l
     ws->cand_pos = reinterpret_cast<int32_t*>(b + o_cpos);
     ws->counts = reinterpret_cast<uint32_t*>(b + o_counts);
     ws->ld = logits_ld;
-    ws->nchunks = (int32_t)nch;
-    ws->pad = 0;
+    ws->nslots = (int32_t)nslots;
+    ws->slot_cap = (int32_t)cap;
   }
   return off;
 }

@@ -21,6 +21,11 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
                         const BatchArgs& b, int64_t dec_tokens, float* logits, int64_t ld,
                         hipStream_t stream);
 
+// Finish long rows from the candidate slots of `ws`.
+hipError_t launch_topk_resolve(const float* logits, int64_t ld, const BatchArgs& b,
+                               const TopkWorkspace& ws, int k, int32_t* out, int64_t ldo,
+                               hipStream_t stream);
+
 // Top-k rows from scores (row stride ld) into out (row stride ldo).
 hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, const TopkWorkspace& ws,
                        int k, int32_t* out, int64_t ldo, hipStream_t stream);

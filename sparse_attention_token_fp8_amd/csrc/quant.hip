@@ -9,79 +9,17 @@
 // with ue8m0 scales and folds q_scale * softmax_scale * n_head^-0.5 into the
 // weights.
 //
-// Everything below works on the bf16 bit patterns with integer arithmetic:
-// a row scale is a power of two, so x / scale is an exponent shift, and the
-// round-to-nearest-even of the E4M3 mantissa is a shift with a sticky test.
-// No floating-point instruction touches the data, so the result cannot
-// depend on the denormal mode.
+// The quantiser itself (integer-only, see quant_device.hpp) is shared with the
+// top-k planning kernel.
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "quant_device.hpp"
 
 namespace idx {
 namespace {
 
 constexpr int kRowsPerBlock = 8;  // 32 lanes per 128-wide row, 256 threads
-
-// Scale exponent e of a row: the smallest e with max(amax, 1e-4) <= 448 * 2^e.
-// `amag` is the bf16 magnitude bit pattern (sign cleared) of the row's amax.
-__device__ __forceinline__ int ue8m0_exponent(uint32_t amag) {
-  const float a = __uint_as_float(amag << 16);
-  if (!(a >= 1e-4f)) return -22;                 // floor: 1e-4 <= 448 * 2^-22
-  const int E = (int)(amag >> 7);                // biased exponent (normal here)
-  const int m = (int)(amag & 0x7F);
-  // a = (1 + m/128) 2^(E-127) and 448 = 1.75 * 2^8
-  return (E - 127) - 8 + (m > 96 ? 1 : 0);
-}
-
-// E4M3 code of bf16 value x scaled by 2^-e: nearest, ties to even, sign kept,
-// saturating at 448 (never reached when e comes from the row's amax).
-__device__ __forceinline__ uint32_t encode_e4m3(uint32_t x, int e) {
-  const uint32_t sign = (x >> 15) & 1u;
-  const uint32_t mag = x & 0x7FFFu;
-  if (mag == 0) return sign << 7;
-  const int E = (int)(mag >> 7);
-  uint32_t M;
-  int P;                                          // |x| = M * 2^P
-  if (E == 0) { M = mag & 0x7Fu; P = -133; }      // bf16 subnormal
-  else { M = 0x80u | (mag & 0x7Fu); P = E - 134; }
-  if (E == 0xFF) return (sign << 7) | 0x7Eu;      // inf / nan: saturate (not produced by callers)
-  P -= e;
-  const int msb = 31 - __clz(M);
-  const int j = msb + P;                          // floor(log2 |y|)
-  const int qexp = j < -6 ? -9 : j - 3;           // E4M3 spacing in that binade
-  const int sh = qexp - P;
-  uint32_t N;
-  if (sh <= 0) {
-    N = M << (-sh);
-  } else if (sh >= 10) {
-    N = 0;                                        // below half a quantum (M < 2^9)
-  } else {
-    const uint32_t q = M >> sh;
-    const uint32_t rem = M & ((1u << sh) - 1u);
-    const uint32_t half = 1u << (sh - 1);
-    N = q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
-  }
-  uint32_t code = (j >= -6) ? (uint32_t)((j + 6) * 8) + N : N;
-  code = code > 0x7Eu ? 0x7Eu : code;
-  return (sign << 7) | code;
-}
-
-// One 128-wide row per 32 lanes: each lane owns 4 consecutive values.
-// Returns this lane's 4 codes packed little-endian and the row exponent.
-__device__ __forceinline__ uint32_t quant_row_lane(uint2 v, int* e_out) {
-  const uint32_t x0 = v.x & 0xFFFFu, x1 = v.x >> 16, x2 = v.y & 0xFFFFu, x3 = v.y >> 16;
-  uint32_t am = max(max(x0 & 0x7FFFu, x1 & 0x7FFFu), max(x2 & 0x7FFFu, x3 & 0x7FFFu));
-  // NaN patterns compare above every finite magnitude; inputs are finite.
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off, 32));
-  const int e = ue8m0_exponent(am);
-  *e_out = e;
-  return encode_e4m3(x0, e) | (encode_e4m3(x1, e) << 8) | (encode_e4m3(x2, e) << 16) |
-         (encode_e4m3(x3, e) << 24);
-}
-
-__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
 __global__ __launch_bounds__(256) void quant_write_k_kernel(const uint16_t* __restrict__ k,
                                                             int64_t num_rows, int64_t stride,
@@ -91,15 +29,7 @@ __global__ __launch_bounds__(256) void quant_write_k_kernel(const uint16_t* __re
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 5);
   const int lane = threadIdx.x & 31;
   if (row >= num_rows) return;                     // whole 32-lane group leaves together
-  const int64_t slot = slots[row];
-  if (slot < 0 || slot >= num_slots) return;
-  const uint2 v = *reinterpret_cast<const uint2*>(k + row * stride + lane * 4);
-  int e;
-  const uint32_t codes = quant_row_lane(v, &e);
-  const int64_t blk = slot / kBlock, off = slot % kBlock;
-  uint8_t* base = cache + blk * kBlockBytes;
-  *reinterpret_cast<uint32_t*>(base + off * kHeadDim + lane * 4) = codes;
-  if (lane == 0) *reinterpret_cast<float*>(base + kCodeBytes + off * 4) = pow2f(e);
+  quant_write_row(k + row * stride, slots[row], cache, num_slots, lane);
 }
 
 __global__ __launch_bounds__(256) void quant_q_fold_kernel(const uint16_t* __restrict__ q,

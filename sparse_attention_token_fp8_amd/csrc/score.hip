@@ -245,10 +245,10 @@ __device__ __forceinline__ void wave_stage_store(const WaveStage& st, uint8_t* s
 
 // ------------------------------------------------------------- decode --
 // One query token per work-group; the work-group covers `chunk_blocks`
-// consecutive 64-position blocks of its causal range and its four waves take
-// every fourth block.  Each wave keeps the loads of its next NB-1 blocks in
-// flight in registers and passes the current block through its own LDS slot
-// (`lds`: 4 * kBlockBytes) into the MFMA layout.
+// consecutive 64-position blocks of its causal range, split into four
+// consecutive runs, one per wave.  Each wave keeps the loads of its next NB-1
+// blocks in flight in registers and passes the current block through its own
+// LDS slot (`lds`: 4 * kBlockBytes) into the MFMA layout.
 #ifndef IDX_DECODE_RING
 #define IDX_DECODE_RING 2
 #endif
@@ -277,16 +277,18 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
   const int lb0 = bx * chunk_blocks;
   if (lb0 * kBlock >= n) return;
   const int nblk = min(chunk_blocks, (n - lb0 * kBlock + kBlock - 1) / kBlock);
-  const int lp = lane_pos(lane);
-  const int mine = nblk > wave ? (nblk - wave + 3) / 4 : 0;   // blocks of this wave (<= 16)
+  const int per = (nblk + 3) / 4;
+  const int mine = max(0, min(per, nblk - wave * per));        // blocks of this wave (<= 16)
   if (mine == 0) return;
-  auto blk = [&](int j) { return lb0 + wave + 4 * j; };
+  const int lp = lane_pos(lane);
+  auto blk = [&](int j) { return lb0 + wave * per + j; };
   float* out = logits + (size_t)t * ld;
+  auto emit = [&](int j, float v) {
+    const int s = blk(j) * kBlock + lp;
+    if (j < mine && s < n) out[s] = v;
+  };
   if (cache.num_blocks == 0) {                  // no K at all: every score is 0
-    for (int j = 0; j < mine; ++j) {
-      const int s = blk(j) * kBlock + lp;
-      if (s < n) out[s] = 0.f;
-    }
+    for (int j = 0; j < mine; ++j) emit(j, 0.f);
     return;
   }
   // lane j holds the physical block of this wave's j-th block, so no K load
@@ -321,8 +323,7 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       float v;
       block_scores<1>(f, kb, &v);
-      const int s = blk(j) * kBlock + lp;
-      if (j < mine && s < n) out[s] = v;
+      emit(j, v);
     }
   }
 }

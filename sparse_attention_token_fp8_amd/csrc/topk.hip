@@ -26,7 +26,7 @@ constexpr int kCandCap = 6144;       // LDS candidate capacity of the resolve
 constexpr int kBatch = 8;            // positions per thread per batch in the row kernel
 constexpr int kChunk = 4096;         // positions per filter work-group
 constexpr int kPer = kChunk / kThreads;
-constexpr int kMaxChunks = 1024;     // rows up to 4M positions
+constexpr int kMaxChunks = 1024;     // rows up to 4M positions (one filter slot per chunk)
 
 template <int NT>
 __device__ __forceinline__ void write_all(int32_t* out, int n, int k) {
@@ -124,7 +124,10 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     return;
   }
   const int s0 = c * kChunk;
-  if (s0 >= n) return;
+  if (s0 >= n) {                                // past the row: an empty slot
+    if (threadIdx.x == 0) ws.counts[(size_t)t * ws.nslots + c] = 0u;
+    return;
+  }
   __shared__ uint32_t hist[kBins1];
   __shared__ uint32_t table[kPer * kThreads / 64 + 1];
   __shared__ uint32_t scratch[scratch_words<kThreads>()];
@@ -147,10 +150,10 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     key[e] = order_key(v[e]);
     pass[e] = s0 + e * kThreads + (int)threadIdx.x < n && key[e] >= tau;
   }
-  const size_t slot = ((size_t)t * ws.nchunks + c) * kChunk;
+  const size_t slot = ((size_t)t * ws.nslots + c) * ws.slot_cap;
   const uint32_t cnt = compact_ordered<kThreads, kPer>(key, pass, s0, 0, ws.cand_key + slot,
                                                        ws.cand_pos + slot, kChunk, table);
-  if (threadIdx.x == 0) ws.counts[(size_t)t * ws.nchunks + c] = cnt;
+  if (threadIdx.x == 0) ws.counts[(size_t)t * ws.nslots + c] = cnt;
 }
 
 #ifndef IDX_RESOLVE_THREADS
@@ -158,43 +161,49 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
 #endif
 constexpr int kResolveThreads = IDX_RESOLVE_THREADS;
 
+// One work-group per long row: gathers the row's candidate slots in order and
+// finishes the row.  Works for either slot layout of the workspace.
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
     const float* __restrict__ logits, int64_t ld, BatchArgs b, int k, TopkWorkspace ws,
     int32_t* __restrict__ topk, int64_t ldo) {
   constexpr int NT = kResolveThreads;
   const int t = blockIdx.x;
   const int n = token_pos_wave(b, t).n;
-  if (n <= k) return;                          // written by the filter
+  int32_t* out = topk + (size_t)t * ldo;
+  if (n <= k) {
+    write_all<NT>(out, n, k);
+    return;
+  }
   __shared__ uint32_t ckey[kCandCap];
   __shared__ int32_t cpos[kCandCap];
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t pre[kMaxChunks + 1];
+  __shared__ uint32_t pre[kMaxSlots + 1];
   __shared__ uint32_t bucket[64];
   __shared__ uint32_t scratch[scratch_words<NT>()];
-  const int nch = min((n + kChunk - 1) / kChunk, kMaxChunks);
-  const uint32_t* cnts = ws.counts + (size_t)t * ws.nchunks;
-  {
-    const int per = (nch + NT - 1) / NT;
-    const int c0 = min(nch, per * (int)threadIdx.x), c1 = min(nch, c0 + per);
+  const int nsl = min(ws.nslots, kMaxSlots);
+  const uint32_t* cnts = ws.counts + (size_t)t * ws.nslots;
+  const uint32_t cap = (uint32_t)ws.slot_cap;
+  {                                             // every slot count is written; clamp anyway
+    const int per = (nsl + NT - 1) / NT;
+    const int c0 = min(nsl, per * (int)threadIdx.x), c1 = min(nsl, c0 + per);
     uint32_t s = 0;
-    for (int c = c0; c < c1; ++c) s += cnts[c];
+    for (int c = c0; c < c1; ++c) s += min(cnts[c], cap);
     uint32_t total;
     uint32_t run = block_scan_excl<NT>(s, &total, scratch);
-    for (int c = c0; c < c1; ++c) { pre[c] = run; run += cnts[c]; }
-    if (threadIdx.x == 0) pre[nch] = total;
+    for (int c = c0; c < c1; ++c) { pre[c] = run; run += min(cnts[c], cap); }
+    if (threadIdx.x == 0) pre[nsl] = total;
   }
   __syncthreads();
-  const uint32_t C = pre[nch];
+  const uint32_t C = pre[nsl];
   const float* row = logits + (size_t)t * ld;
-  int32_t* out = topk + (size_t)t * ldo;
-  const size_t base = (size_t)t * ws.nchunks * kChunk;
+  const size_t base = (size_t)t * ws.nslots * ws.slot_cap;
   auto at = [&](uint32_t i) {                   // workspace index of candidate i (position order)
-    int lo = 0, hi = nch - 1;
+    int lo = 0, hi = nsl - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (pre[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    return base + (size_t)lo * kChunk + (i - pre[lo]);
+    return base + (size_t)lo * ws.slot_cap + (i - pre[lo]);
   };
   if (C >= (uint32_t)k && C <= (uint32_t)kCandCap) {
     for (uint32_t i = threadIdx.x; i < C; i += NT) {
@@ -207,9 +216,9 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
   } else if (C > (uint32_t)kCandCap) {          // too many for LDS: read the slots in place
     uint32_t take;
     const uint32_t kstar = radix_kth<NT, 3>([&](auto&& fn) {
-      for (int c = 0; c < nch; ++c) {
-        const size_t sb = base + (size_t)c * kChunk;
-        for (uint32_t i = threadIdx.x; i < cnts[c]; i += NT) fn(ws.cand_key[sb + i]);
+      for (int c = 0; c < nsl; ++c) {
+        const size_t sb = base + (size_t)c * ws.slot_cap;
+        for (uint32_t i = threadIdx.x; i < pre[c + 1] - pre[c]; i += NT) fn(ws.cand_key[sb + i]);
       }
     }, (uint32_t)k, &take, hist, scratch);
     emit_ordered<NT>([&](uint32_t i) {
@@ -231,6 +240,15 @@ int topk_chunk() { return kChunk; }
 
 int topk_max_seq_len() { return kChunk * kMaxChunks; }
 
+hipError_t launch_topk_resolve(const float* logits, int64_t ld, const BatchArgs& b,
+                               const TopkWorkspace& ws, int k, int32_t* out, int64_t ldo,
+                               hipStream_t stream) {
+  if (b.num_tokens == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_resolve_kernel, dim3((unsigned)b.num_tokens), dim3(kResolveThreads), 0,
+                     stream, logits, ld, b, k, ws, out, ldo);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, const TopkWorkspace& ws,
                        int k, int32_t* out, int64_t ldo, hipStream_t stream) {
   if (b.num_tokens == 0) return hipSuccess;
@@ -240,8 +258,7 @@ hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, cons
                        out, ldo);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_resolve_kernel, dim3((unsigned)b.num_tokens), dim3(kResolveThreads), 0,
-                       stream, logits, ld, b, k, ws, out, ldo);
+    return launch_topk_resolve(logits, ld, b, ws, k, out, ldo, stream);
   } else {
     if (b.max_seq_len <= 65536)
       hipLaunchKernelGGL(topk_rows_kernel<uint16_t>, dim3((unsigned)b.num_tokens), dim3(kRowThreads),

@@ -260,6 +260,53 @@ def test_score_topk_vs_oracle(env):
             check_topk_band(got[t], sc, wl.k, f"token {t}")
 
 
+def test_topk_threshold_fallbacks(env):
+    """Long rows take as candidates the scores at or above a threshold placed
+    from a fixed sample of the row (positions j*S + ((37j + 11) mod S), S the
+    power of two that keeps at most 2048 of them).  White-box cases for the
+    paths that do not depend on the threshold being well placed:
+      * rows of at most 4k positions take every score as a candidate, which for
+        n > 6144 exceeds the LDS list and is selected from the global slots;
+      * one request whose sampled positions are made hot (K rows x4) puts the
+        threshold above all but about a hundred positions, so fewer than k
+        pass and the row is selected from the full score row.
+    The fused result must equal the unfused idx_logits + idx_topk and the
+    oracle."""
+    import synth.gen as sg
+    m, torch = env
+
+    class HotSampled(sg.Workload):
+        def request_k(self, layer, r):
+            kb = super().request_k(layer, r)
+            if r != 1:
+                return kb
+            n = int(self.seq_lens[r])
+            S = 16
+            while (n + S - 1) // S > 2048:
+                S *= 2
+            j = np.arange((n + S - 1) // S)
+            pos = j * S + ((37 * j + 11) & (S - 1))
+            pos = pos[pos < n]
+            x = (kb.astype(np.uint32) << 16).view(np.float32).copy()
+            x[pos] *= np.float32(4.0)
+            return f32_to_bf16_bits(x)
+
+    base = random_batch(4006, [7000, 40000, 8100, 12000], 1, k=2048)
+    wl = HotSampled(base.name, base.seed, base.seq_lens, base.new_tokens, base.block_table,
+                    base.num_blocks, base.k)
+    say("threshold fallbacks", wl.seq_lens.tolist())
+    dev = device_layer(m, torch, wl, 0, with_new=True)
+    orc = oracle_layer(wl, 0)
+    batch = device_batch(m, wl)
+    lg = m.idx_logits(dev["q8"], dev["w"], dev["cache"], batch)
+    a = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+    b = m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], batch, wl.k).cpu().numpy()
+    assert np.array_equal(a, b)
+    want = oracle.logits.logits(orc["q8"], orc["w"], orc["cache"], oracle_batch(wl))
+    for t, sc in want.items():
+        check_topk_band(b[t], sc, wl.k, f"token {t}")
+
+
 def test_topk_to_physical(env):
     m, torch = env
     wl = random_batch(5001, [100, 700, 64], [2, 1, 3], k=32, pool_factor=2.0)
