@@ -1,9 +1,9 @@
 """Throughput of the DSA lightning-indexer path on one MI355X.
 
-A step is the whole hot path for one batch: quantise + scatter this step's
-new K rows (idx_quant_write_k), then score every causal position and select
-the top-k into the persistent buffer (idx_score_topk).  Inputs are resident
-in HBM before timing starts.  The headline workload is the 128K decode batch
+A step is the whole hot path for one batch: one F layer of the IndexCache
+stack (idx_indexcache_layer), which quantises + scatters this step's new K
+rows, scores every causal position and selects the top-k into the persistent
+buffer.  Inputs are resident in HBM before timing starts.  The headline workload is the 128K decode batch
 (8 requests x 131072 positions, k = 2048); the 32K chunked prefill (24576
 cached + 8192 new tokens) is reported alongside in the same JSON line.
 
@@ -166,10 +166,10 @@ def run_workload(m, torch, name, args):
     ws = torch.empty(m.idx_score_topk_workspace_size(B, k), dtype=torch.uint8, device="cuda")
     logits = torch.empty((wl.num_tokens, wl.max_seq_len), dtype=torch.float32, device="cuda")
 
-    def step(i):
+    def step(i):                                       # one F layer: a1 + a4
         c = d["caches"][i % reps]
-        m.idx_quant_write_k(d["k_new"], d["slots"], c)
-        m.idx_score_topk(d["q8"], d["w"], c, B, k, topk=topk, workspace=ws)
+        m.idx_indexcache_layer(d["k_new"], c, d["q8"], d["w"], True, True, d["slots"], B, k, topk,
+                               workspace=ws)
 
     def score_only(i):
         m.idx_logits(d["q8"], d["w"], d["caches"][i % reps], B, logits=logits)

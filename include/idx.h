@@ -201,6 +201,14 @@ idx_status_t idx_layer_schedule(int32_t use_index_cache, const char* pattern, in
  * If is_full: idx_score_topk into topk.  An S layer leaves topk untouched, so
  * its consumer reads the rows of the most recent F layer.
  * layer->q_fp8 and layer->w may be NULL on S layers.
+ * On an F layer whose batch is scored one token per work-group (every
+ * request has one new token, or num_decode_tokens == num_tokens with at most
+ * 4 new tokens per request) the new rows are written by the scoring kernel
+ * itself, which scores each new row from registers.  The cache bytes and the
+ * top-k rows are those of the separate calls whenever every new token's slot
+ * is the block-table slot of its position (as the serving metadata has it);
+ * a row whose slot differs is still written, but its position is then scored
+ * from the cache's previous contents.
  */
 typedef struct idx_layer_io {
   const uint16_t* k_bf16;   /* new K rows [num_tokens, k_row_stride] bf16 bits */

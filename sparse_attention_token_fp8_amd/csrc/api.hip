@@ -91,7 +91,8 @@ idx_status_t check_k_rows(const uint16_t* k_bf16, int64_t k_row_stride, const in
 }
 
 // Scores + top-k of one batch into `topk`; with kq set, this step's new K rows
-// are quantised into the cache first.  Arguments are already checked.
+// are quantised into the cache first (by the decode scoring kernel itself
+// when it scores the whole batch).  Arguments are already checked.
 hipError_t score_topk(const uint8_t* q_fp8, const float* w, const idx_kcache_t& cache,
                       const idx_batch_t* batch, int32_t k, int32_t* topk, int64_t topk_stride,
                       void* workspace, const uint16_t* kq, int64_t kq_stride,
@@ -101,11 +102,16 @@ hipError_t score_topk(const uint8_t* q_fp8, const float* w, const idx_kcache_t& 
   const BatchArgs b = to_args(batch);
   const CacheArgs c{cache.data, cache.num_blocks};
   hipError_t e = hipSuccess;
-  if (kq != nullptr)
-    e = launch_quant_write_k(kq, batch->num_tokens, kq_stride, slots, cache.data,
-                             cache.num_blocks * kBlock, stream);
-  if (e == hipSuccess)
-    e = launch_score(q_fp8, w, c, b, batch->num_decode_tokens, ws.logits, ws.ld, stream);
+  if (kq != nullptr && score_writes_k(b, batch->num_decode_tokens)) {
+    e = launch_score_write_k(q_fp8, w, c, b, kq, kq_stride, slots, cache.data, ws.logits, ws.ld,
+                             stream);
+  } else {
+    if (kq != nullptr)
+      e = launch_quant_write_k(kq, batch->num_tokens, kq_stride, slots, cache.data,
+                               cache.num_blocks * kBlock, stream);
+    if (e == hipSuccess)
+      e = launch_score(q_fp8, w, c, b, batch->num_decode_tokens, ws.logits, ws.ld, stream);
+  }
   if (e == hipSuccess) e = launch_topk(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
   return e;
 }

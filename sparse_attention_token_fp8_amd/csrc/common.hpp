@@ -119,16 +119,20 @@ __device__ __forceinline__ int find_request(const int32_t* __restrict__ qsl, int
 }
 
 struct TokenPos {
-  int r;  // request
-  int n;  // number of causal positions (p_t + 1), clamped to [0, max_seq_len]
+  int r;    // request
+  int n;    // number of causal positions (p_t + 1), clamped to [0, max_seq_len]
+  int q0;   // the request's first query token
+  int nq;   // the request's number of new tokens
+  int len;  // the request's sequence length
 };
 
 __device__ __forceinline__ TokenPos token_pos(const BatchArgs& b, int t) {
   TokenPos tp;
   tp.r = find_request(b.qsl, b.num_reqs, t);
-  const int q0 = b.qsl[tp.r];
-  const int nr = b.qsl[tp.r + 1] - q0;
-  int n = b.seq_lens[tp.r] - nr + (t - q0) + 1;
+  tp.q0 = b.qsl[tp.r];
+  tp.nq = b.qsl[tp.r + 1] - tp.q0;
+  tp.len = b.seq_lens[tp.r];
+  int n = tp.len - tp.nq + (t - tp.q0) + 1;
   n = n < 0 ? 0 : n;
   tp.n = n > b.max_seq_len ? b.max_seq_len : n;
   return tp;
@@ -145,9 +149,10 @@ __device__ __forceinline__ TokenPos token_pos_wave(const BatchArgs& b, int t) {
   const int m = (int)__popcll(__ballot(lane < b.num_reqs && q <= t));
   TokenPos tp;
   tp.r = m > 0 ? m - 1 : 0;
-  const int q0 = __builtin_amdgcn_readlane(q, tp.r);
-  const int q1 = __builtin_amdgcn_readlane(q, tp.r + 1);
-  int n = __builtin_amdgcn_readlane(len, tp.r) - (q1 - q0) + (t - q0) + 1;
+  tp.q0 = __builtin_amdgcn_readlane(q, tp.r);
+  tp.nq = __builtin_amdgcn_readlane(q, tp.r + 1) - tp.q0;
+  tp.len = __builtin_amdgcn_readlane(len, tp.r);
+  int n = tp.len - tp.nq + (t - tp.q0) + 1;
   n = n < 0 ? 0 : n;
   tp.n = n > b.max_seq_len ? b.max_seq_len : n;
   return tp;

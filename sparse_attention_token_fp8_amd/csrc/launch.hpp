@@ -21,6 +21,19 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
                         const BatchArgs& b, int64_t dec_tokens, float* logits, int64_t ld,
                         hipStream_t stream);
 
+// Whether launch_score_write_k can score this batch: every token scored with
+// the decode split and at most a few new tokens per request.
+bool score_writes_k(const BatchArgs& b, int64_t dec_tokens);
+
+// Decode scoring that also quantises this step's new K rows (row t of k to
+// slots[t]) into the cache, as launch_quant_write_k would before scoring.
+// Rows whose slot is not the block-table slot of their position are written
+// but not patched into the scores.
+hipError_t launch_score_write_k(const uint8_t* q8, const float* w, const CacheArgs& cache,
+                                const BatchArgs& b, const uint16_t* k, int64_t k_stride,
+                                const int64_t* slots, uint8_t* cache_w, float* logits, int64_t ld,
+                                hipStream_t stream);
+
 // Finish long rows from the candidate slots of `ws`.
 hipError_t launch_topk_resolve(const float* logits, int64_t ld, const BatchArgs& b,
                                const TopkWorkspace& ws, int k, int32_t* out, int64_t ldo,

@@ -25,6 +25,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "quant_device.hpp"
 
 namespace idx {
 namespace {
@@ -264,11 +265,27 @@ constexpr int kPrefillTPW = IDX_PREFILL_TPW;    // query tokens per wave (prefil
 constexpr int kPrefillTM = 4 * kPrefillTPW;     // query tokens per work-group (prefill)
 constexpr int kScoreLds = 4 * kBlockBytes;
 
-template <int NB>
+// This step's new K rows, for scoring kernels that write them into the cache
+// themselves (decode batches of an F layer): row i of `k` belongs to query
+// token i and goes to slots[i].
+struct NewRows {
+  const uint16_t* k;
+  int64_t stride;
+  const int64_t* slots;
+  uint8_t* cache;      // the scored cache, writable
+  int64_t num_slots;
+};
+
+// Requests with at most this many new tokens get their new rows written by
+// the decode scoring kernel (a wave quantises the rows its blocks hold).
+constexpr int kMaxFusedRows = 4;
+
+template <int NB, bool FK>
 __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __restrict__ q8,
                                             const float* __restrict__ w, const CacheArgs& cache,
                                             const BatchArgs& b, float* __restrict__ logits,
-                                            int64_t ld, int chunk_blocks, uint8_t* lds) {
+                                            int64_t ld, int chunk_blocks, uint8_t* lds,
+                                            const NewRows& nk) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   QFrag f[1];
   load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);  // needs t only
@@ -306,6 +323,46 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
   WaveStage ring[NB];
 #pragma unroll
   for (int u = 0; u < NB - 1; ++u) stage(ring[u], min(u, mine - 1));
+
+  // New rows of this token's request that fall in this wave's blocks and in
+  // its causal range (positions len-nq .. p_t): quantised here, patched into
+  // the staged block below, and the token's own row written to the cache.  A
+  // row is patched only where its slot is the block-table slot of its
+  // position; elsewhere the cache's contents are scored.
+  uint32_t fcode[kMaxFusedRows];
+  uint32_t fscale[kMaxFusedRows];
+  int fpos0 = 0, nfix = 0;
+  if (FK) {
+    const int newlo = tp.len - tp.nq;
+    const int lo = max(newlo, blk(0) * kBlock);
+    const int hi = min(n - 1, (blk(mine - 1) + 1) * kBlock - 1);
+    nfix = min(kMaxFusedRows, max(0, hi - lo + 1));
+    fpos0 = lo;
+#pragma unroll
+    for (int i = 0; i < kMaxFusedRows; ++i) {
+      fcode[i] = 0u;
+      fscale[i] = 0u;
+      if (i < nfix) {
+        const int P = lo + i;
+        const int row = tp.q0 + (P - newlo);
+        const uint2 v = *reinterpret_cast<const uint2*>(nk.k + (int64_t)row * nk.stride + (lane & 31) * 4);
+        const int64_t want = nk.slots[row];
+        int e;
+        const uint32_t code = quant_row_lane(v, &e);
+        const uint32_t sc = __float_as_uint(pow2f(e));
+        const int pb = __builtin_amdgcn_readlane(pbl, P / kBlock - blk(0));
+        const bool patch = pb >= 0 && want == (int64_t)pb * kBlock + P % kBlock;
+        fcode[i] = code;
+        fscale[i] = patch ? sc : 0xFFFFFFFFu;   // all ones: leave the row as the cache has it
+        if (row == t && want >= 0 && want < nk.num_slots) {   // the token's own row: to the cache
+          uint8_t* cb = nk.cache + (want / kBlock) * kBlockBytes;
+          if (lane < 32) *reinterpret_cast<uint32_t*>(cb + (want % kBlock) * kHeadDim + lane * 4) = code;
+          if (lane == 0) *reinterpret_cast<uint32_t*>(cb + kCodeBytes + (want % kBlock) * 4) = sc;
+        }
+      }
+    }
+  }
+
   for (int j0 = 0; j0 < iters; j0 += NB) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
@@ -313,6 +370,19 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
       stage(ring[(u + NB - 1) % NB], min(j + NB - 1, mine - 1));
       __builtin_amdgcn_sched_barrier(0);        // nothing that needs block j moves above these loads
       wave_stage_store(ring[u], slot, lane);
+      if (FK) {
+#pragma unroll
+        for (int i = 0; i < kMaxFusedRows; ++i) {
+          const int P = fpos0 + i;
+          if (i < nfix && fscale[i] != 0xFFFFFFFFu && P / kBlock == blk(j)) {
+            const int rr = P % kBlock;
+            if (lane < 32)
+              *reinterpret_cast<uint32_t*>(slot + rr * kHeadDim + (((lane >> 2) ^ (rr & 7)) << 4) +
+                                           (lane & 3) * 4) = fcode[i];
+            if (lane == 0) *reinterpret_cast<uint32_t*>(slot + kCodeBytes + rr * 4) = fscale[i];
+          }
+        }
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -417,7 +487,18 @@ __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int chunk_blocks) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
-  decode_body<NB>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks, lds);
+  decode_body<NB, false>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks, lds,
+                         NewRows{});
+}
+
+// Decode scoring of an F layer that also writes this step's new K rows.
+template <int NB>
+__global__ __launch_bounds__(kScoreThreads)
+__attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_write_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
+    float* __restrict__ logits, int64_t ld, int chunk_blocks, NewRows nk) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
+  decode_body<NB, true>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks, lds, nk);
 }
 
 __global__ __launch_bounds__(kScoreThreads) void score_prefill_kernel(
@@ -438,7 +519,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_mixed_kernel(
     int pre_chunk_blocks, int groups_per_req) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
   if ((int)blockIdx.y < dec_tokens)
-    decode_body<NB>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, dec_chunk_blocks, lds);
+    decode_body<NB, false>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, dec_chunk_blocks,
+                           lds, NewRows{});
   else
     prefill_body(blockIdx.x, blockIdx.y - dec_tokens, dec_tokens, q8, w, cache, b, logits, ld,
                  pre_chunk_blocks, groups_per_req, lds);
@@ -471,6 +553,26 @@ int prefill_chunk_blocks(const BatchArgs& b) {
 }
 
 }  // namespace
+
+bool score_writes_k(const BatchArgs& b, int64_t dec_tokens) {
+  return b.max_query_len <= kMaxFusedRows && (b.max_query_len <= 1 || dec_tokens >= b.num_tokens);
+}
+
+hipError_t launch_score_write_k(const uint8_t* q8, const float* w, const CacheArgs& cache,
+                                const BatchArgs& b, const uint16_t* k, int64_t k_stride,
+                                const int64_t* slots, uint8_t* cache_w, float* logits, int64_t ld,
+                                hipStream_t stream) {
+  if (b.num_tokens == 0) return hipSuccess;
+  if (b.max_seq_len == 0) return launch_quant_write_k(k, b.num_tokens, k_stride, slots, cache_w,
+                                                      cache.num_blocks * kBlock, stream);
+  const int cb = decode_chunk_blocks(b.max_seq_len, b.num_tokens);
+  const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
+  const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
+  const NewRows nk{k, k_stride, slots, cache_w, cache.num_blocks * kBlock};
+  hipLaunchKernelGGL(score_decode_write_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0,
+                     stream, q8, w, cache, b, logits, ld, cb, nk);
+  return hipGetLastError();
+}
 
 hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cache,
                         const BatchArgs& b, int64_t dec_tokens, float* logits, int64_t ld,

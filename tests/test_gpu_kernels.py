@@ -307,6 +307,35 @@ def test_topk_threshold_fallbacks(env):
         check_topk_band(b[t], sc, wl.k, f"token {t}")
 
 
+def test_layer_k_write_inside_scoring(env):
+    """An F layer of a decode batch writes its new K rows from inside the decode
+    scoring kernel.  The cache bytes and the top-k rows must equal the separate
+    idx_quant_write_k + idx_logits + idx_topk on a copy of the cache: a plain
+    decode batch with one padding token (slot -1, not written, its position
+    scored from the cache), and requests with three new tokens each, scored
+    with the decode split (rows written inside scoring) and without it."""
+    m, torch = env
+    cases = [(random_batch(7001, [3000, 9000, 20000, 700, 1500], 1, k=512), [0], [3]),
+             (random_batch(7002, [2500, 9000, 4000], 3, k=256), [9, 0], [])]
+    for wl, splits, pad in cases:
+        for nd in splits:
+            say("layer K write", wl.seq_lens.tolist(), wl.new_tokens.tolist(), "decode tokens", nd)
+            dev = device_layer(m, torch, wl, 0)
+            slots = dev["slots_new"].clone()
+            for p in pad:
+                slots[p] = -1
+            batch = m.Batch(wl.seq_lens, wl.query_start_loc, wl.block_table, num_decode_tokens=nd)
+            ref_cache = m.KCache(wl.num_blocks, tensor=dev["cache"].tensor.clone())
+            m.idx_quant_write_k(dev["k_new"], slots, ref_cache)
+            lg = m.idx_logits(dev["q8"], dev["w"], ref_cache, batch)
+            want = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+            topk = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
+            m.idx_indexcache_layer(dev["k_new"], dev["cache"], dev["q8"], dev["w"], True, True, slots,
+                                   batch, wl.k, topk)
+            assert np.array_equal(dev["cache"].tensor.cpu().numpy(), ref_cache.tensor.cpu().numpy())
+            assert np.array_equal(topk.cpu().numpy(), want)
+
+
 def test_topk_to_physical(env):
     m, torch = env
     wl = random_batch(5001, [100, 700, 64], [2, 1, 3], k=32, pool_factor=2.0)
