@@ -104,13 +104,13 @@ hipError_t score_topk(const uint8_t* q_fp8, const float* w, const idx_kcache_t& 
   hipError_t e = hipSuccess;
   if (kq != nullptr && score_writes_k(b, batch->num_decode_tokens)) {
     e = launch_score_write_k(q_fp8, w, c, b, kq, kq_stride, slots, cache.data, ws.logits, ws.ld,
-                             stream);
+                             ws.samp, stream);
   } else {
     if (kq != nullptr)
       e = launch_quant_write_k(kq, batch->num_tokens, kq_stride, slots, cache.data,
                                cache.num_blocks * kBlock, stream);
     if (e == hipSuccess)
-      e = launch_score(q_fp8, w, c, b, batch->num_decode_tokens, ws.logits, ws.ld, stream);
+      e = launch_score(q_fp8, w, c, b, batch->num_decode_tokens, ws.logits, ws.ld, ws.samp, stream);
   }
   if (e == hipSuccess) e = launch_topk(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
   return e;
@@ -173,7 +173,7 @@ idx_status_t idx_logits(const uint8_t* q_fp8, const float* w, int32_t n_heads, i
   if (logits == nullptr || logits_stride < batch->max_seq_len) return IDX_ERR_INVALID_ARG;
   CacheArgs c{cache.data, cache.num_blocks};
   return launched(launch_score(q_fp8, w, c, to_args(batch), batch->num_decode_tokens, logits,
-                               logits_stride, stream));
+                               logits_stride, nullptr, stream));
 }
 
 size_t idx_topk_workspace_size(const idx_batch_t* batch, int32_t k) {

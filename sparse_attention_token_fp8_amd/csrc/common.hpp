@@ -44,13 +44,28 @@ struct CacheArgs {
   int64_t num_blocks;
 };
 
+// Sample of a row used to place the top-k threshold: positions
+// j*S + ((37*j + 11) & (S-1)), S a power of two chosen so that at most
+// kMaxSample positions are drawn.
+constexpr int kMaxSample = 2048;
+
+__host__ __device__ inline int sample_stride(int n) {
+  int S = 16;
+  while ((n + S - 1) / S > kMaxSample) S <<= 1;
+  return S;
+}
+
+__host__ __device__ inline int sample_pos(int j, int S) { return j * S + ((37 * j + 11) & (S - 1)); }
+
 // Top-k workspace (device, caller-owned).  The fused entry points keep the
-// scores in `logits`.  Long rows keep their candidates in `nslots` slots of
-// `slot_cap` entries per row (`cand_key` / `cand_pos`, in position order
-// across the slots; one slot per 4096-position chunk) with each slot's count
-// in `counts`.
+// scores in `logits` and, for long rows, each row's sampled scores in `samp`
+// (entry j = the score at sample_pos(j, S)), written by the scoring kernels.
+// Long rows keep their candidates in `nslots` slots of `slot_cap` entries per
+// row (`cand_key` / `cand_pos`, in position order across the slots; one slot
+// per 4096-position chunk) with each slot's count in `counts`.
 struct TopkWorkspace {
   float* logits;       // [T][ld] (fused path only)
+  float* samp;         // [T][kMaxSample] (fused path, long rows only)
   uint32_t* cand_key;  // [T][nslots][slot_cap]
   int32_t* cand_pos;   // [T][nslots][slot_cap]
   uint32_t* counts;    // [T][nslots]
@@ -85,10 +100,14 @@ inline size_t topk_workspace_layout(int64_t T, int max_seq_len, int64_t logits_l
   off = align_up(off + sizeof(int32_t) * (size_t)cap * (size_t)nslots * (size_t)T, 256);
   const size_t o_counts = off;
   off = align_up(off + sizeof(uint32_t) * (size_t)nslots * (size_t)T, 256);
+  const bool samp = lr && logits_ld > 0;
+  const size_t o_samp = off;
+  off = align_up(off + (samp ? sizeof(float) * (size_t)kMaxSample * (size_t)T : 0), 256);
   if (off == 0) off = 256;
   if (base && ws) {
     char* b = static_cast<char*>(base);
     ws->logits = logits_ld ? reinterpret_cast<float*>(b + o_logits) : nullptr;
+    ws->samp = samp ? reinterpret_cast<float*>(b + o_samp) : nullptr;
     ws->cand_key = reinterpret_cast<uint32_t*>(b + o_ckey);
     ws->cand_pos = reinterpret_cast<int32_t*>(b + o_cpos);
     ws->counts = reinterpret_cast<uint32_t*>(b + o_counts);

@@ -14,12 +14,13 @@ hipError_t launch_quant_q_fold(const uint16_t* q, const float* w_raw, int64_t nu
                                float softmax_scale, float head_norm, uint8_t* q8, float* w_out,
                                float* qs_out, hipStream_t stream);
 
-// Scores into `logits` (row stride ld).  Tokens below dec_tokens use the
+// Scores into `logits` (row stride ld), and each row's sampled scores into
+// samp[t][...] when samp is not null.  Tokens below dec_tokens use the
 // decode work split (one token per work-group), the rest the prefill split; a
 // batch whose requests have at most one new token each is all decode.
 hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cache,
                         const BatchArgs& b, int64_t dec_tokens, float* logits, int64_t ld,
-                        hipStream_t stream);
+                        float* samp, hipStream_t stream);
 
 // Whether launch_score_write_k can score this batch: every token scored with
 // the decode split and at most a few new tokens per request.
@@ -32,7 +33,7 @@ bool score_writes_k(const BatchArgs& b, int64_t dec_tokens);
 hipError_t launch_score_write_k(const uint8_t* q8, const float* w, const CacheArgs& cache,
                                 const BatchArgs& b, const uint16_t* k, int64_t k_stride,
                                 const int64_t* slots, uint8_t* cache_w, float* logits, int64_t ld,
-                                hipStream_t stream);
+                                float* samp, hipStream_t stream);
 
 // Finish long rows from the candidate slots of `ws`.
 hipError_t launch_topk_resolve(const float* logits, int64_t ld, const BatchArgs& b,

@@ -285,7 +285,7 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
                                             const float* __restrict__ w, const CacheArgs& cache,
                                             const BatchArgs& b, float* __restrict__ logits,
                                             int64_t ld, int chunk_blocks, uint8_t* lds,
-                                            const NewRows& nk) {
+                                            const NewRows& nk, float* __restrict__ samp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   QFrag f[1];
   load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);  // needs t only
@@ -300,9 +300,17 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
   const int lp = lane_pos(lane);
   auto blk = [&](int j) { return lb0 + wave * per + j; };
   float* out = logits + (size_t)t * ld;
+  // the row's sampled scores also go to their compact copy (see sample_pos)
+  float* srow = samp ? samp + (size_t)t * kMaxSample : nullptr;
+  const int sS = sample_stride(n), sSh = 31 - __clz(sS);
   auto emit = [&](int j, float v) {
     const int s = blk(j) * kBlock + lp;
-    if (j < mine && s < n) out[s] = v;
+    const bool in = j < mine && s < n;
+    if (in) out[s] = v;
+    if (srow != nullptr) {
+      const int sj = s >> sSh;
+      if (in && (s & (sS - 1)) == ((37 * sj + 11) & (sS - 1))) srow[sj] = v;
+    }
   };
   if (cache.num_blocks == 0) {                  // no K at all: every score is 0
     for (int j = 0; j < mine; ++j) emit(j, 0.f);
@@ -410,7 +418,7 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
                                              const float* __restrict__ w, const CacheArgs& cache,
                                              const BatchArgs& b, float* __restrict__ logits,
                                              int64_t ld, int chunk_blocks, int groups_per_req,
-                                             uint8_t* lds) {
+                                             uint8_t* lds, float* __restrict__ samp) {
   constexpr int TPW = kPrefillTPW, NW = 4, TM = kPrefillTM;
   const int r = gy / groups_per_req;
   const int g = gy % groups_per_req;
@@ -437,6 +445,8 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
   QFrag f[TPW];
   int nt[TPW];
   float* out[TPW];
+  float* srow[TPW];                             // compact sample copies (or null)
+  int sS[TPW], sSh[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
     const int i = tb + wave * TPW + j;
@@ -445,11 +455,15 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
       load_q(f[j], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
       nt[j] = count(i);
       out[j] = logits + (size_t)t * ld;
+      srow[j] = samp ? samp + (size_t)t * kMaxSample : nullptr;
     } else {
       zero_q(f[j]);
       nt[j] = 0;
       out[j] = logits;
+      srow[j] = nullptr;
     }
+    sS[j] = sample_stride(nt[j]);
+    sSh[j] = 31 - __clz(sS[j]);
   }
 
   // Staging registers for blocks j+1 and j+2 alternate: block j+2's loads are
@@ -473,8 +487,13 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
       block_scores<TPW>(f, kb, v);
       const int s = (lb0 + j) * kBlock + lp;
 #pragma unroll
-      for (int jj = 0; jj < TPW; ++jj)
+      for (int jj = 0; jj < TPW; ++jj) {
         if (s < nt[jj]) out[jj][s] = v[jj];
+        if (srow[jj] != nullptr) {
+          const int sj = s >> sSh[jj];
+          if (s < nt[jj] && (s & (sS[jj] - 1)) == ((37 * sj + 11) & (sS[jj] - 1))) srow[jj][sj] = v[jj];
+        }
+      }
     }
   }
 }
@@ -485,10 +504,10 @@ template <int NB>
 __global__ __launch_bounds__(kScoreThreads)
 __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    float* __restrict__ logits, int64_t ld, int chunk_blocks) {
+    float* __restrict__ logits, int64_t ld, int chunk_blocks, float* samp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
   decode_body<NB, false>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks, lds,
-                         NewRows{});
+                         NewRows{}, samp);
 }
 
 // Decode scoring of an F layer that also writes this step's new K rows.
@@ -496,17 +515,18 @@ template <int NB>
 __global__ __launch_bounds__(kScoreThreads)
 __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_write_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    float* __restrict__ logits, int64_t ld, int chunk_blocks, NewRows nk) {
+    float* __restrict__ logits, int64_t ld, int chunk_blocks, NewRows nk, float* samp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
-  decode_body<NB, true>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks, lds, nk);
+  decode_body<NB, true>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks, lds, nk,
+                        samp);
 }
 
 __global__ __launch_bounds__(kScoreThreads) void score_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    float* __restrict__ logits, int64_t ld, int chunk_blocks, int groups_per_req) {
+    float* __restrict__ logits, int64_t ld, int chunk_blocks, int groups_per_req, float* samp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBlockBytes];
   prefill_body(blockIdx.x, blockIdx.y, 0, q8, w, cache, b, logits, ld, chunk_blocks, groups_per_req,
-               lds);
+               lds, samp);
 }
 
 // Mixed batch in one launch: rows y < dec_tokens are tokens scored with the
@@ -516,14 +536,14 @@ template <int NB>
 __global__ __launch_bounds__(kScoreThreads) void score_mixed_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int dec_tokens, int dec_chunk_blocks,
-    int pre_chunk_blocks, int groups_per_req) {
+    int pre_chunk_blocks, int groups_per_req, float* samp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
   if ((int)blockIdx.y < dec_tokens)
     decode_body<NB, false>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, dec_chunk_blocks,
-                           lds, NewRows{});
+                           lds, NewRows{}, samp);
   else
     prefill_body(blockIdx.x, blockIdx.y - dec_tokens, dec_tokens, q8, w, cache, b, logits, ld,
-                 pre_chunk_blocks, groups_per_req, lds);
+                 pre_chunk_blocks, groups_per_req, lds, samp);
 }
 
 // Decode chunk: about two work-groups per CU over the decode tokens (two fit
@@ -561,7 +581,7 @@ bool score_writes_k(const BatchArgs& b, int64_t dec_tokens) {
 hipError_t launch_score_write_k(const uint8_t* q8, const float* w, const CacheArgs& cache,
                                 const BatchArgs& b, const uint16_t* k, int64_t k_stride,
                                 const int64_t* slots, uint8_t* cache_w, float* logits, int64_t ld,
-                                hipStream_t stream) {
+                                float* samp, hipStream_t stream) {
   if (b.num_tokens == 0) return hipSuccess;
   if (b.max_seq_len == 0) return launch_quant_write_k(k, b.num_tokens, k_stride, slots, cache_w,
                                                       cache.num_blocks * kBlock, stream);
@@ -570,13 +590,13 @@ hipError_t launch_score_write_k(const uint8_t* q8, const float* w, const CacheAr
   const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
   const NewRows nk{k, k_stride, slots, cache_w, cache.num_blocks * kBlock};
   hipLaunchKernelGGL(score_decode_write_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0,
-                     stream, q8, w, cache, b, logits, ld, cb, nk);
+                     stream, q8, w, cache, b, logits, ld, cb, nk, samp);
   return hipGetLastError();
 }
 
 hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cache,
                         const BatchArgs& b, int64_t dec_tokens, float* logits, int64_t ld,
-                        hipStream_t stream) {
+                        float* samp, hipStream_t stream) {
   if (b.num_tokens == 0 || b.max_seq_len == 0) return hipSuccess;
   if (b.max_query_len <= 1) dec_tokens = b.num_tokens;
   if (dec_tokens >= b.num_tokens) {
@@ -584,7 +604,7 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
     const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
     const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
     hipLaunchKernelGGL(score_decode_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0, stream,
-                       q8, w, cache, b, logits, ld, cb);
+                       q8, w, cache, b, logits, ld, cb, samp);
   } else {
     const int pcb = prefill_chunk_blocks(b);
     const int pchunks = (b.max_seq_len + pcb * kBlock - 1) / (pcb * kBlock);
@@ -592,13 +612,13 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
     if (dec_tokens <= 0) {
       const dim3 grid((unsigned)pchunks, (unsigned)(gpr * b.num_reqs));
       hipLaunchKernelGGL(score_prefill_kernel, grid, dim3(kScoreThreads), 0, stream, q8, w, cache, b,
-                         logits, ld, pcb, gpr);
+                         logits, ld, pcb, gpr, samp);
     } else {
       const int dcb = decode_chunk_blocks(b.max_seq_len, dec_tokens);
       const int dchunks = (b.max_seq_len + dcb * kBlock - 1) / (dcb * kBlock);
       const dim3 grid((unsigned)std::max(dchunks, pchunks), (unsigned)(dec_tokens + gpr * b.num_reqs));
       hipLaunchKernelGGL(score_mixed_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0, stream,
-                         q8, w, cache, b, logits, ld, (int)dec_tokens, dcb, pcb, gpr);
+                         q8, w, cache, b, logits, ld, (int)dec_tokens, dcb, pcb, gpr, samp);
     }
   }
   return hipGetLastError();

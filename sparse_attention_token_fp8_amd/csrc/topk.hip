@@ -135,7 +135,9 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
   const bool sampled = n > 4 * k;               // else every position is a candidate
   float sv[sample_per<kThreads>()];
   int ns = 0;
-  if (sampled) ns = sample_load<kThreads>(row, n, sv);      // first: tau waits on these only
+  if (sampled)                                  // first: tau waits on these only
+    ns = ws.samp ? sample_load_compact<kThreads>(ws.samp + (size_t)t * kMaxSample, n, sv)
+                 : sample_load<kThreads>(row, n, sv);
   float v[kPer];                                // the chunk's loads fly while tau is placed
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {

@@ -275,18 +275,6 @@ __device__ __forceinline__ void emit_ordered(G&& get, uint32_t count, uint32_t k
   __syncthreads();
 }
 
-// Sample of a row used to place tau: positions j*S + ((37*j + 11) & (S-1)),
-// S a power of two chosen so that at most kMaxSample positions are drawn.
-constexpr int kMaxSample = 2048;
-
-__device__ __forceinline__ int sample_stride(int n) {
-  int S = 16;
-  while ((n + S - 1) / S > kMaxSample) S <<= 1;
-  return S;
-}
-
-__device__ __forceinline__ int sample_pos(int j, int S) { return j * S + ((37 * j + 11) & (S - 1)); }
-
 // Rank (1-based) of the sample key used as tau: about 1.5k of the n keys are
 // expected at or above it, plus a margin of 16 sample steps (the count stays
 // several standard deviations above k for samples of a few hundred keys).
@@ -309,6 +297,21 @@ __device__ __forceinline__ int sample_load(const float* __restrict__ row, int n,
   for (int e = 0; e < sample_per<NT>(); ++e) {
     const int j = threadIdx.x + e * NT;
     v[e] = j < ns ? row[sample_pos(j, S)] : 0.f;
+  }
+  return ns;
+}
+
+// The same sample read from a compact copy (entry j = the score at
+// sample_pos(j, S)) that the scoring kernel wrote.
+template <int NT>
+__device__ __forceinline__ int sample_load_compact(const float* __restrict__ samp, int n, float* v) {
+  const int S = sample_stride(n);
+  int ns = (n + S - 1) / S;
+  if (ns > 0 && sample_pos(ns - 1, S) >= n) --ns;
+#pragma unroll
+  for (int e = 0; e < sample_per<NT>(); ++e) {
+    const int j = threadIdx.x + e * NT;
+    v[e] = j < ns ? samp[j] : 0.f;
   }
   return ns;
 }
