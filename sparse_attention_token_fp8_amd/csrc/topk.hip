@@ -182,6 +182,8 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
   __shared__ uint32_t pre[kMaxSlots + 1];
   __shared__ uint32_t bucket[64];
   __shared__ uint32_t scratch[scratch_words<NT>()];
+  __shared__ uint32_t krange[2];
+  if (threadIdx.x == 0) { krange[0] = 0xffffffffu; krange[1] = 0u; }   // before the scan's barriers
   const int nsl = min(ws.nslots, kMaxSlots);
   const uint32_t* cnts = ws.counts + (size_t)t * ws.nslots;
   const uint32_t cap = (uint32_t)ws.slot_cap;
@@ -208,13 +210,27 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
     return base + (size_t)lo * ws.slot_cap + (i - pre[lo]);
   };
   if (C >= (uint32_t)k && C <= (uint32_t)kCandCap) {
+    uint32_t lo = 0xffffffffu, hi = 0u;         // the keys' range, taken on the way into LDS
     for (uint32_t i = threadIdx.x; i < C; i += NT) {
       const size_t a = at(i);
-      ckey[i] = ws.cand_key[a];
+      const uint32_t key = ws.cand_key[a];
+      ckey[i] = key;
       cpos[i] = ws.cand_pos[a];
+      lo = min(lo, key);
+      hi = max(hi, key);
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+    }
+    if ((threadIdx.x & 63) == 0) { atomicMin(&krange[0], lo); atomicMax(&krange[1], hi); }
     __syncthreads();
-    finish_row<NT>(row, n, k, C, kCandCap, ckey, cpos, out, hist, bucket, scratch);
+    uint32_t take;
+    const uint32_t kstar = select_kth_range<NT>(ckey, C, (uint32_t)k, krange[0], krange[1], &take,
+                                                hist, bucket, scratch);
+    emit_ordered<NT>([&](uint32_t i) { return make_uint2(ckey[i], (uint32_t)cpos[i]); }, C, kstar,
+                     take, k, out, scratch);
   } else if (C > (uint32_t)kCandCap) {          // too many for LDS: read the slots in place
     uint32_t take;
     const uint32_t kstar = radix_kth<NT, 3>([&](auto&& fn) {

@@ -161,13 +161,70 @@ __device__ __forceinline__ uint32_t radix_kth(V&& visit, uint32_t need, uint32_t
 // *take_eq = how many keys equal to it belong to the top `need`.  Digits of
 // up to 11 bits are taken over [kmin, kmax] of the candidates; when the bin
 // holding the answer has at most 64 keys they are ranked by one wave.
-// `hist` holds kBins1 words, `bucket` 64 words.
+// `hist` holds kBins1 words, `bucket` 64 words.  select_kth_range takes the
+// range from the caller (every key must lie in [kmin, kmax]).
+template <int NT>
+__device__ __forceinline__ uint32_t select_kth_range(const uint32_t* ckey, uint32_t C, uint32_t need,
+                                                     uint32_t kmin, uint32_t kmax,
+                                                     uint32_t* take_eq, uint32_t* hist,
+                                                     uint32_t* bucket, uint32_t* scratch) {
+  constexpr int NW = NT / 64;
+  uint32_t* sx = scratch + 2 * NW;              // bucket fill, K*, take
+  uint32_t base = kmin;
+  int width = kmax == kmin ? 0 : 32 - __clz(kmax - kmin);   // keys in play: [base, base + 2^width)
+  while (width > 0) {
+    const int shift = width > 11 ? width - 11 : 0;
+    const int nb = 1 << (width - shift);
+    for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0;
+    if (threadIdx.x == 0) sx[0] = 0u;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < C; i += NT) {
+      const uint32_t x = ckey[i];
+      if (x >= base && ((uint64_t)(x - base) >> width) == 0) atomicAdd(&hist[(x - base) >> shift], 1u);
+    }
+    __syncthreads();
+    uint32_t above, in_bin;
+    const uint32_t d = find_digit<NT>(hist, nb, need, &above, scratch, &in_bin);
+    need -= above;
+    base += d << shift;
+    width = shift;
+    if (width > 0 && in_bin <= 64) {            // rank the bin's keys in one wave
+      for (uint32_t i = threadIdx.x; i < C; i += NT) {
+        const uint32_t x = ckey[i];
+        if (x >= base && ((uint64_t)(x - base) >> width) == 0) {
+          const uint32_t j = atomicAdd(&sx[0], 1u);
+          if (j < 64u) bucket[j] = x;
+        }
+      }
+      __syncthreads();
+      if ((uint32_t)threadIdx.x < in_bin) {
+        const uint32_t x = bucket[threadIdx.x];
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t j = 0; j < in_bin; ++j) {
+          const uint32_t y = bucket[j];
+          gt += y > x;
+          ge += y >= x;
+        }
+        if (gt < need && need <= ge) { sx[1] = x; sx[2] = need - gt; }
+      }
+      __syncthreads();
+      base = sx[1];
+      need = sx[2];
+      width = 0;
+      __syncthreads();
+    }
+  }
+  *take_eq = need;
+  return base;
+}
+
+// The same, with the range taken from the keys first.
 template <int NT>
 __device__ __forceinline__ uint32_t select_kth(const uint32_t* ckey, uint32_t C, uint32_t need,
                                                uint32_t* take_eq, uint32_t* hist, uint32_t* bucket,
                                                uint32_t* scratch) {
   constexpr int NW = NT / 64;
-  uint32_t* sx = scratch + 2 * NW;              // kmin, kmax, bucket fill, K*, take
+  uint32_t* sx = scratch + 2 * NW + 4;          // kmin, kmax
   const int lane = threadIdx.x & 63;
   uint32_t lo = 0xffffffffu, hi = 0u;
   for (uint32_t i = threadIdx.x; i < C; i += NT) {
@@ -184,53 +241,7 @@ __device__ __forceinline__ uint32_t select_kth(const uint32_t* ckey, uint32_t C,
   __syncthreads();
   if (lane == 0) { atomicMin(&sx[0], lo); atomicMax(&sx[1], hi); }
   __syncthreads();
-  uint32_t base = sx[0];
-  const uint32_t top = sx[1];
-  int width = top == base ? 0 : 32 - __clz(top - base);   // keys in play: [base, base + 2^width)
-  while (width > 0) {
-    const int shift = width > 11 ? width - 11 : 0;
-    const int nb = 1 << (width - shift);
-    for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0;
-    if (threadIdx.x == 0) sx[2] = 0u;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < C; i += NT) {
-      const uint32_t x = ckey[i];
-      if (x >= base && ((uint64_t)(x - base) >> width) == 0) atomicAdd(&hist[(x - base) >> shift], 1u);
-    }
-    __syncthreads();
-    uint32_t above, in_bin;
-    const uint32_t d = find_digit<NT>(hist, nb, need, &above, scratch, &in_bin);
-    need -= above;
-    base += d << shift;
-    width = shift;
-    if (width > 0 && in_bin <= 64) {            // rank the bin's keys in one wave
-      for (uint32_t i = threadIdx.x; i < C; i += NT) {
-        const uint32_t x = ckey[i];
-        if (x >= base && ((uint64_t)(x - base) >> width) == 0) {
-          const uint32_t j = atomicAdd(&sx[2], 1u);
-          if (j < 64u) bucket[j] = x;
-        }
-      }
-      __syncthreads();
-      if ((uint32_t)threadIdx.x < in_bin) {
-        const uint32_t x = bucket[threadIdx.x];
-        uint32_t gt = 0, ge = 0;
-        for (uint32_t j = 0; j < in_bin; ++j) {
-          const uint32_t y = bucket[j];
-          gt += y > x;
-          ge += y >= x;
-        }
-        if (gt < need && need <= ge) { sx[3] = x; sx[4] = need - gt; }
-      }
-      __syncthreads();
-      base = sx[3];
-      need = sx[4];
-      width = 0;
-      __syncthreads();
-    }
-  }
-  *take_eq = need;
-  return base;
+  return select_kth_range<NT>(ckey, C, need, sx[0], sx[1], take_eq, hist, bucket, scratch);
 }
 
 // Write one row: `get(i)` returns (key, position) of the i-th of `count`
