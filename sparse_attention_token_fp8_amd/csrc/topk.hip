@@ -162,6 +162,8 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
 #define IDX_RESOLVE_THREADS 1024
 #endif
 constexpr int kResolveThreads = IDX_RESOLVE_THREADS;
+constexpr int kSpecSlots = 64;      // rows of up to 64 filter slots preload their candidates
+constexpr int kSpecPer = 8;         // entries each resolve thread preloads
 
 // One work-group per long row: gathers the row's candidate slots in order and
 // finishes the row.  Works for either slot layout of the workspace.
@@ -187,6 +189,26 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
   const int nsl = min(ws.nslots, kMaxSlots);
   const uint32_t* cnts = ws.counts + (size_t)t * ws.nslots;
   const uint32_t cap = (uint32_t)ws.slot_cap;
+  const size_t base = (size_t)t * ws.nslots * ws.slot_cap;
+  // With at most kSpecSlots slots, each slot's first entries are loaded before
+  // the counts are known (NT / nsl threads per slot, kSpecPer entries each),
+  // so the count and candidate round trips overlap.
+  const bool spec = nsl <= kSpecSlots && nsl > 0;
+  const int tps = spec ? NT / nsl : 1;
+  const int my_slot = spec ? min((int)threadIdx.x / tps, nsl - 1) : 0;
+  const int my_lane = spec ? (int)threadIdx.x - my_slot * tps : 0;
+  const bool my_ok = spec && (int)threadIdx.x < tps * nsl;
+  uint32_t sk[kSpecPer];
+  int32_t sp[kSpecPer];
+  if (spec) {
+    const size_t sb = base + (size_t)my_slot * ws.slot_cap;
+#pragma unroll
+    for (int u = 0; u < kSpecPer; ++u) {
+      const uint32_t j = min((uint32_t)(my_lane + tps * u), cap - 1u);
+      sk[u] = ws.cand_key[sb + j];
+      sp[u] = ws.cand_pos[sb + j];
+    }
+  }
   {                                             // every slot count is written; clamp anyway
     const int per = (nsl + NT - 1) / NT;
     const int c0 = min(nsl, per * (int)threadIdx.x), c1 = min(nsl, c0 + per);
@@ -200,7 +222,6 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
   __syncthreads();
   const uint32_t C = pre[nsl];
   const float* row = logits + (size_t)t * ld;
-  const size_t base = (size_t)t * ws.nslots * ws.slot_cap;
   auto at = [&](uint32_t i) {                   // workspace index of candidate i (position order)
     int lo = 0, hi = nsl - 1;
     while (lo < hi) {
@@ -211,13 +232,30 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
   };
   if (C >= (uint32_t)k && C <= (uint32_t)kCandCap) {
     uint32_t lo = 0xffffffffu, hi = 0u;         // the keys' range, taken on the way into LDS
-    for (uint32_t i = threadIdx.x; i < C; i += NT) {
-      const size_t a = at(i);
-      const uint32_t key = ws.cand_key[a];
+    auto put = [&](uint32_t i, uint32_t key, int32_t pos) {
       ckey[i] = key;
-      cpos[i] = ws.cand_pos[a];
+      cpos[i] = pos;
       lo = min(lo, key);
       hi = max(hi, key);
+    };
+    if (spec) {
+      const uint32_t cnt = pre[my_slot + 1] - pre[my_slot], at0 = pre[my_slot];
+      if (my_ok) {
+#pragma unroll
+        for (int u = 0; u < kSpecPer; ++u) {
+          const uint32_t j = (uint32_t)(my_lane + tps * u);
+          if (j < cnt) put(at0 + j, sk[u], sp[u]);
+        }
+        // entries beyond the preloaded ones (rare): read them now
+        const size_t sb = base + (size_t)my_slot * ws.slot_cap;
+        for (uint32_t j = (uint32_t)(my_lane + tps * kSpecPer); j < cnt; j += (uint32_t)tps)
+          put(at0 + j, ws.cand_key[sb + j], ws.cand_pos[sb + j]);
+      }
+    } else {
+      for (uint32_t i = threadIdx.x; i < C; i += NT) {
+        const size_t a = at(i);
+        put(i, ws.cand_key[a], ws.cand_pos[a]);
+      }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
