@@ -280,18 +280,26 @@ struct NewRows {
 // the decode scoring kernel (a wave quantises the rows its blocks hold).
 constexpr int kMaxFusedRows = 4;
 
+// `ident`: token t is request t (every request has exactly one new token),
+// which the host knows; the block-table slice of a full chunk is then read
+// at once, in parallel with the request metadata.
 template <int NB, bool FK>
 __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __restrict__ q8,
                                             const float* __restrict__ w, const CacheArgs& cache,
                                             const BatchArgs& b, float* __restrict__ logits,
-                                            int64_t ld, int chunk_blocks, uint8_t* lds,
+                                            int64_t ld, int chunk_blocks, bool ident, uint8_t* lds,
                                             const NewRows& nk, float* __restrict__ samp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  QFrag f[1];
-  load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);  // needs t only
-  const TokenPos tp = token_pos_wave(b, t);
-  const int n = tp.n;
   const int lb0 = bx * chunk_blocks;
+  const int per_full = chunk_blocks / 4;        // chunk_blocks is a multiple of 4
+  const int lb_full = lb0 + wave * per_full + lane;
+  int bt_full = -1;                             // raw id; checked only once it is needed
+  if (ident && lane < per_full)
+    bt_full = b.bt[(int64_t)t * b.bt_stride + min(lb_full, (int)b.bt_stride - 1)];
+  const TokenPos tp = token_pos_wave(b, t);
+  QFrag f[1];
+  load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);  // first used by the MFMAs
+  const int n = tp.n;
   if (lb0 * kBlock >= n) return;
   const int nblk = min(chunk_blocks, (n - lb0 * kBlock + kBlock - 1) / kBlock);
   const int per = (nblk + 3) / 4;
@@ -318,7 +326,12 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
   }
   // lane j holds the physical block of this wave's j-th block, so no K load
   // waits on a block-table load
-  const int pbl = lane < mine ? (int)phys_block(b, cache, tp.r, blk(lane)) : -1;
+  int pbl;
+  if (ident && nblk == chunk_blocks)
+    pbl = (lane < per_full && lb_full < b.bt_stride && bt_full >= 0 && bt_full < cache.num_blocks)
+              ? bt_full : -1;
+  else
+    pbl = lane < mine ? (int)phys_block(b, cache, tp.r, blk(lane)) : -1;
   auto stage = [&](WaveStage& st, int j) {
     const int pb = __builtin_amdgcn_readlane(pbl, j);
     wave_stage_load(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes, pb >= 0, lane);
@@ -504,10 +517,10 @@ template <int NB>
 __global__ __launch_bounds__(kScoreThreads)
 __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    float* __restrict__ logits, int64_t ld, int chunk_blocks, float* samp) {
+    float* __restrict__ logits, int64_t ld, int chunk_blocks, int ident, float* samp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
-  decode_body<NB, false>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks, lds,
-                         NewRows{}, samp);
+  decode_body<NB, false>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks,
+                         ident != 0, lds, NewRows{}, samp);
 }
 
 // Decode scoring of an F layer that also writes this step's new K rows.
@@ -515,10 +528,10 @@ template <int NB>
 __global__ __launch_bounds__(kScoreThreads)
 __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_write_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    float* __restrict__ logits, int64_t ld, int chunk_blocks, NewRows nk, float* samp) {
+    float* __restrict__ logits, int64_t ld, int chunk_blocks, int ident, NewRows nk, float* samp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
-  decode_body<NB, true>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks, lds, nk,
-                        samp);
+  decode_body<NB, true>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks,
+                        ident != 0, lds, nk, samp);
 }
 
 __global__ __launch_bounds__(kScoreThreads) void score_prefill_kernel(
@@ -540,7 +553,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_mixed_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
   if ((int)blockIdx.y < dec_tokens)
     decode_body<NB, false>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, dec_chunk_blocks,
-                           lds, NewRows{}, samp);
+                           false, lds, NewRows{}, samp);
   else
     prefill_body(blockIdx.x, blockIdx.y - dec_tokens, dec_tokens, q8, w, cache, b, logits, ld,
                  pre_chunk_blocks, groups_per_req, lds, samp);
@@ -589,8 +602,9 @@ hipError_t launch_score_write_k(const uint8_t* q8, const float* w, const CacheAr
   const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
   const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
   const NewRows nk{k, k_stride, slots, cache_w, cache.num_blocks * kBlock};
+  const int ident = b.num_reqs == b.num_tokens && b.max_query_len <= 1;
   hipLaunchKernelGGL(score_decode_write_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0,
-                     stream, q8, w, cache, b, logits, ld, cb, nk, samp);
+                     stream, q8, w, cache, b, logits, ld, cb, ident, nk, samp);
   return hipGetLastError();
 }
 
@@ -604,7 +618,8 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
     const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
     const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
     hipLaunchKernelGGL(score_decode_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0, stream,
-                       q8, w, cache, b, logits, ld, cb, samp);
+                       q8, w, cache, b, logits, ld, cb,
+                       (int)(b.num_reqs == b.num_tokens && b.max_query_len <= 1), samp);
   } else {
     const int pcb = prefill_chunk_blocks(b);
     const int pchunks = (b.max_seq_len + pcb * kBlock - 1) / (pcb * kBlock);
