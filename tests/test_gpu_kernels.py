@@ -214,6 +214,18 @@ def test_topk_exact_random(env):
     _topk_case(m, torch, lengths, 2048, lambda t, n: rng.standard_normal(n).astype(np.float32))
 
 
+def test_topk_small_k_and_tiny_rows(env):
+    """k = 1 and small odd k, rows of one position and rows just around k, in
+    both launch shapes (many short rows; few rows longer than 8192)."""
+    m, torch = env
+    rng = np.random.default_rng(3004)
+    for k in (1, 3, 7):
+        _topk_case(m, torch, [1, 2, 3, k, k + 1, 64, 1000], k,
+                   lambda t, n: rng.standard_normal(n).astype(np.float32))
+        _topk_case(m, torch, [1, k, 9000, 20000], k,
+                   lambda t, n: rng.standard_normal(n).astype(np.float32))
+
+
 def test_topk_exact_with_ties(env):
     m, torch = env
     rng = np.random.default_rng(3002)
