@@ -18,7 +18,10 @@
  *     never allocates, frees or synchronises; scratch memory is passed in as
  *     a caller-owned workspace whose size the *_workspace_size calls report.
  *   - Every call validates its arguments on the host first.  A non-zero
- *     status means nothing was enqueued.  Otherwise the kernels are enqueued
+ *     status means nothing was enqueued.  Device arrays must be aligned to
+ *     their element size (int32 / fp32 to 4 bytes, int64 to 8, bf16 rows to
+ *     8), q_fp8 and the cache to 16, workspaces to 256; a misaligned pointer
+ *     is IDX_ERR_INVALID_ARG (IDX_ERR_WORKSPACE for a workspace).  Otherwise the kernels are enqueued
  *     on `stream` and the call returns at once; a failure inside a kernel
  *     surfaces at the caller's next synchronisation as a HIP error.
  *   - Kernels bound every memory access by the host-side sizes they are given

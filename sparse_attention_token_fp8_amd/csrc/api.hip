@@ -30,6 +30,8 @@ idx_status_t check_batch(const idx_batch_t* b) {
   if (b->num_tokens > kMaxTokens || b->max_seq_len > topk_max_seq_len()) return IDX_ERR_UNSUPPORTED;
   if (b->seq_lens == nullptr || b->query_start_loc == nullptr || b->block_table == nullptr)
     return IDX_ERR_INVALID_ARG;
+  if (!aligned(b->seq_lens, 4) || !aligned(b->query_start_loc, 4) || !aligned(b->block_table, 4))
+    return IDX_ERR_INVALID_ARG;
   if (b->block_table_stride < (int64_t)(b->max_seq_len + kBlock - 1) / kBlock ||
       b->block_table_stride < 1)
     return IDX_ERR_INVALID_ARG;
@@ -67,6 +69,7 @@ idx_status_t check_k(int32_t k, int64_t topk_stride, const int32_t* topk, int32_
   if (k < 1 || k > kMaxK) return IDX_ERR_UNSUPPORTED;
   if (topk_stride < k) return IDX_ERR_INVALID_ARG;
   if (num_tokens > 0 && topk == nullptr) return IDX_ERR_INVALID_ARG;
+  if (!aligned(topk, 4)) return IDX_ERR_INVALID_ARG;
   return IDX_OK;
 }
 
@@ -85,7 +88,8 @@ idx_status_t check_k_rows(const uint16_t* k_bf16, int64_t k_row_stride, const in
   if (num_tokens == 0) return IDX_OK;
   if (k_bf16 == nullptr || slot_mapping == nullptr || cache.data == nullptr)
     return IDX_ERR_INVALID_ARG;
-  if (k_row_stride < kHeadDim || (k_row_stride % 4) != 0 || !aligned(k_bf16, 8))
+  if (k_row_stride < kHeadDim || (k_row_stride % 4) != 0 || !aligned(k_bf16, 8) ||
+      !aligned(slot_mapping, 8))
     return IDX_ERR_INVALID_ARG;
   return IDX_OK;
 }
@@ -143,7 +147,8 @@ idx_status_t idx_quant_write_k(const uint16_t* k_bf16, int64_t num_tokens, int32
   if (num_tokens == 0) return IDX_OK;
   if (k_bf16 == nullptr || slot_mapping == nullptr || cache.data == nullptr)
     return IDX_ERR_INVALID_ARG;
-  if (k_row_stride < head_dim || (k_row_stride % 4) != 0 || !aligned(k_bf16, 8))
+  if (k_row_stride < head_dim || (k_row_stride % 4) != 0 || !aligned(k_bf16, 8) ||
+      !aligned(slot_mapping, 8))
     return IDX_ERR_INVALID_ARG;
   return launched(launch_quant_write_k(k_bf16, num_tokens, k_row_stride, slot_mapping, cache.data,
                                        cache.num_blocks * kBlock, stream));
@@ -158,7 +163,9 @@ idx_status_t idx_quant_q_fold_w(const uint16_t* q_bf16, const float* w_raw, int6
   if (num_tokens == 0) return IDX_OK;
   if (q_bf16 == nullptr || w_raw == nullptr || q_fp8 == nullptr || w_folded == nullptr)
     return IDX_ERR_INVALID_ARG;
-  if (!aligned(q_bf16, 8) || !aligned(q_fp8, 4)) return IDX_ERR_INVALID_ARG;
+  if (!aligned(q_bf16, 8) || !aligned(q_fp8, 4) || !aligned(w_raw, 4) || !aligned(w_folded, 4) ||
+      !aligned(q_scale_out, 4))
+    return IDX_ERR_INVALID_ARG;
   const float head_norm = (float)(1.0 / __builtin_sqrt((double)n_heads));
   return launched(launch_quant_q_fold(q_bf16, w_raw, num_tokens * n_heads, softmax_scale,
                                       head_norm, q_fp8, w_folded, q_scale_out, stream));
@@ -170,7 +177,8 @@ idx_status_t idx_logits(const uint8_t* q_fp8, const float* w, int32_t n_heads, i
   idx_status_t s = check_scoring(q_fp8, w, n_heads, head_dim, cache, batch);
   if (s != IDX_OK) return s;
   if (batch->num_tokens == 0) return IDX_OK;
-  if (logits == nullptr || logits_stride < batch->max_seq_len) return IDX_ERR_INVALID_ARG;
+  if (logits == nullptr || logits_stride < batch->max_seq_len || !aligned(logits, 4))
+    return IDX_ERR_INVALID_ARG;
   CacheArgs c{cache.data, cache.num_blocks};
   return launched(launch_score(q_fp8, w, c, to_args(batch), batch->num_decode_tokens, logits,
                                logits_stride, nullptr, stream));
@@ -189,7 +197,8 @@ idx_status_t idx_topk(const float* logits, int64_t logits_stride, const idx_batc
   s = check_k(k, topk_stride, topk, batch->num_tokens);
   if (s != IDX_OK) return s;
   if (batch->num_tokens == 0) return IDX_OK;
-  if (logits == nullptr || logits_stride < batch->max_seq_len) return IDX_ERR_INVALID_ARG;
+  if (logits == nullptr || logits_stride < batch->max_seq_len || !aligned(logits, 4))
+    return IDX_ERR_INVALID_ARG;
   const size_t need = idx_topk_workspace_size(batch, k);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
     return IDX_ERR_WORKSPACE;
@@ -268,7 +277,8 @@ idx_status_t idx_indexcache_stack(const idx_layer_io_t* layers, int32_t num_laye
     }
     if ((is_full[l] || write_k_on_s) && batch->num_tokens > 0 &&
         (L.k_bf16 == nullptr || L.k_row_stride < kHeadDim || (L.k_row_stride % 4) != 0 ||
-         !aligned(L.k_bf16, 8) || slot_mapping == nullptr || L.cache.data == nullptr))
+         !aligned(L.k_bf16, 8) || slot_mapping == nullptr || !aligned(slot_mapping, 8) ||
+         L.cache.data == nullptr))
       return IDX_ERR_INVALID_ARG;
   }
   s = check_k(k, topk_stride, topk, batch->num_tokens);
@@ -301,6 +311,8 @@ idx_status_t idx_topk_to_physical(const int32_t* logical, int64_t logical_stride
   if (logical_stride < k || physical_stride < k) return IDX_ERR_INVALID_ARG;
   if (batch->num_tokens == 0) return IDX_OK;
   if (logical == nullptr || physical == nullptr) return IDX_ERR_INVALID_ARG;
+  if (!aligned(logical, 4) || !aligned(physical, 4) || !aligned(valid_counts, 4))
+    return IDX_ERR_INVALID_ARG;
   return launched(launch_topk_to_physical(logical, logical_stride, to_args(batch), block_size,
                                           num_blocks, k, stride_rows, physical, physical_stride,
                                           valid_counts, stream));

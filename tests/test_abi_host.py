@@ -64,6 +64,7 @@ def test_quant_write_k_rejects(m):
     assert L.idx_quant_write_k(FAKE, 1, 128, 64, FAKE, _cache(m), S) == -1          # stride < 128
     assert L.idx_quant_write_k(ctypes.c_void_p(0x10002), 1, 128, 128, FAKE, _cache(m), S) == -1
     assert L.idx_quant_write_k(FAKE, 1, 128, 128, FAKE, _cache(m, data=0x10004), S) == -1
+    assert L.idx_quant_write_k(FAKE, 1, 128, 128, ctypes.c_void_p(0x10004), _cache(m), S) == -1  # slots
     assert L.idx_quant_write_k(FAKE, 0, 128, 128, FAKE, _cache(m), S) == 0           # no-op
 
 
@@ -80,6 +81,10 @@ def test_scoring_rejects(m):
     assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(_batch(m, max_seq_len=65)), FAKE, 65, S) == -1
     assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(_batch(m, num_tokens=70000)), FAKE, 64, S) == -2
     assert L.idx_logits(ctypes.c_void_p(0x10008), FAKE, 64, 128, _cache(m), B(ok), FAKE, 64, S) == -1
+    odd = ctypes.c_void_p(0x10002)
+    assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(ok), odd, 64, S) == -1     # logits
+    bad = m.binding.BatchC(0x10002, 0x10000, 0x10000, 1, 1, 1, 64, 1, 0)             # seq_lens
+    assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(bad), FAKE, 64, S) == -1
     for nd in (-1, 2):                                          # decode split outside 0..num_tokens
         assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(_batch(m, num_decode_tokens=nd)),
                             FAKE, 64, S) == -1
@@ -96,6 +101,7 @@ def test_topk_rejects(m):
     assert L.idx_topk(FAKE, 64, B(ok), 0, FAKE, 16, FAKE, need, S) == -2
     assert L.idx_topk(FAKE, 64, B(ok), 4096, FAKE, 4096, FAKE, 1 << 30, S) == -2
     assert L.idx_topk(FAKE, 64, B(ok), 16, FAKE, 8, FAKE, need, S) == -1             # stride < k
+    assert L.idx_topk(FAKE, 64, B(ok), 16, ctypes.c_void_p(0x10002), 16, FAKE, need, S) == -1  # topk
     assert L.idx_topk(FAKE, 64, B(ok), 16, FAKE, 16, FAKE, need - 1, S) == -3
     assert L.idx_topk(FAKE, 64, B(ok), 16, FAKE, 16, None, need, S) == -3
     assert L.idx_topk(FAKE, 64, B(ok), 16, FAKE, 16, ctypes.c_void_p(0x10010), need, S) == -3
