@@ -62,7 +62,7 @@ __host__ __device__ inline int sample_pos(int j, int S) { return j * S + ((37 * 
 // (entry j = the score at sample_pos(j, S)), written by the scoring kernels.
 // Long rows keep their candidates in `nslots` slots of `slot_cap` entries per
 // row (`cand_key` / `cand_pos`, in position order across the slots; one slot
-// per 4096-position chunk) with each slot's count in `counts`.
+// per chunk of topk_chunk() positions) with each slot's count in `counts`.
 struct TopkWorkspace {
   float* logits;       // [T][ld] (fused path only)
   float* samp;         // [T][kMaxSample] (fused path, long rows only)
@@ -77,11 +77,12 @@ struct TopkWorkspace {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool topk_uses_long_rows(int64_t T, int max_seq_len);
-int topk_nchunks(int max_seq_len);
-int topk_chunk();
+// Filter chunk (positions per slot); shorter when the sample copy exists.
+int topk_chunk(bool sample_copy);
+int topk_nchunks(int max_seq_len, bool sample_copy);
 int topk_max_seq_len();
 
-constexpr int kMaxSlots = 1024;                 // slots per row the resolve can index
+constexpr int kMaxSlots = 2048;                 // slots per row the resolve can index
 
 // Layout of the workspace for T rows of up to max_seq_len positions; returns
 // the total bytes.  When base is non-null also fills `ws`.  logits_ld is 0
@@ -89,8 +90,9 @@ constexpr int kMaxSlots = 1024;                 // slots per row the resolve can
 inline size_t topk_workspace_layout(int64_t T, int max_seq_len, int64_t logits_ld, void* base,
                                     TopkWorkspace* ws) {
   const bool lr = topk_uses_long_rows(T, max_seq_len);
-  const int64_t nslots = lr ? topk_nchunks(max_seq_len) : 0;
-  const int64_t cap = lr ? topk_chunk() : 0;
+  const bool samp = lr && logits_ld > 0;
+  const int64_t nslots = lr ? topk_nchunks(max_seq_len, samp) : 0;
+  const int64_t cap = lr ? topk_chunk(samp) : 0;
   size_t off = 0;
   const size_t o_logits = off;
   off = align_up(off + sizeof(float) * (size_t)logits_ld * (size_t)T, 256);
@@ -100,7 +102,6 @@ inline size_t topk_workspace_layout(int64_t T, int max_seq_len, int64_t logits_l
   off = align_up(off + sizeof(int32_t) * (size_t)cap * (size_t)nslots * (size_t)T, 256);
   const size_t o_counts = off;
   off = align_up(off + sizeof(uint32_t) * (size_t)nslots * (size_t)T, 256);
-  const bool samp = lr && logits_ld > 0;
   const size_t o_samp = off;
   off = align_up(off + (samp ? sizeof(float) * (size_t)kMaxSample * (size_t)T : 0), 256);
   if (off == 0) off = 256;

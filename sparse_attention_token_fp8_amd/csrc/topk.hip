@@ -24,9 +24,14 @@ constexpr int kRowThreads = 512;
 constexpr int kRowCap = 5120;        // LDS candidate capacity of the row kernel
 constexpr int kCandCap = 6144;       // LDS candidate capacity of the resolve
 constexpr int kBatch = 8;            // positions per thread per batch in the row kernel
-constexpr int kChunk = 4096;         // positions per filter work-group
-constexpr int kPer = kChunk / kThreads;
-constexpr int kMaxChunks = 1024;     // rows up to 4M positions (one filter slot per chunk)
+// Positions per filter work-group.  With the scoring kernel's compact sample
+// copy each work-group's tau costs one contiguous 8 KiB read, so smaller chunks
+// (more work-groups per CU to hide the latency chains) pay; without it every
+// work-group gathers the sample from the row, and larger chunks do better.
+constexpr int kChunkSampled = 2048;
+constexpr int kChunkPlain = 4096;
+constexpr int kMaxLongRow = 1 << 22;                 // rows up to 4M positions
+static_assert(kMaxLongRow / kChunkSampled <= kMaxSlots, "one slot per chunk");
 
 template <int NT>
 __device__ __forceinline__ void write_all(int32_t* out, int n, int k) {
@@ -111,11 +116,13 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
 
 // ---------------------------------------------------------- long rows --
 
+template <int kChunk>
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __restrict__ logits,
                                                                int64_t ld, BatchArgs b, int k,
                                                                TopkWorkspace ws,
                                                                int32_t* __restrict__ topk,
                                                                int64_t ldo) {
+  constexpr int kPer = kChunk / kThreads;
   const int t = blockIdx.y;
   const int c = blockIdx.x;
   const int n = token_pos_wave(b, t).n;
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
 #define IDX_RESOLVE_THREADS 1024
 #endif
 constexpr int kResolveThreads = IDX_RESOLVE_THREADS;
-constexpr int kSpecSlots = 64;      // rows of up to 64 filter slots preload their candidates
+constexpr int kSpecSlots = 128;     // rows of up to 128 filter slots preload their candidates
 constexpr int kSpecPer = 8;         // entries each resolve thread preloads
 
 // One work-group per long row: gathers the row's candidate slots in order and
@@ -290,11 +297,14 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
 
 bool topk_uses_long_rows(int64_t T, int max_seq_len) { return T < 256 && max_seq_len > 8192; }
 
-int topk_nchunks(int max_seq_len) { return (max_seq_len + kChunk - 1) / kChunk; }
+int topk_chunk(bool sample_copy) { return sample_copy ? kChunkSampled : kChunkPlain; }
 
-int topk_chunk() { return kChunk; }
+int topk_nchunks(int max_seq_len, bool sample_copy) {
+  const int c = topk_chunk(sample_copy);
+  return (max_seq_len + c - 1) / c;
+}
 
-int topk_max_seq_len() { return kChunk * kMaxChunks; }
+int topk_max_seq_len() { return kMaxLongRow; }
 
 hipError_t launch_topk_resolve(const float* logits, int64_t ld, const BatchArgs& b,
                                const TopkWorkspace& ws, int k, int32_t* out, int64_t ldo,
@@ -309,9 +319,16 @@ hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, cons
                        int k, int32_t* out, int64_t ldo, hipStream_t stream) {
   if (b.num_tokens == 0) return hipSuccess;
   if (topk_uses_long_rows(b.num_tokens, b.max_seq_len)) {
-    const dim3 grid((unsigned)std::max(1, topk_nchunks(b.max_seq_len)), (unsigned)b.num_tokens);
-    hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kThreads), 0, stream, logits, ld, b, k, ws,
-                       out, ldo);
+    // the workspace layout fixed the chunking: one slot of slot_cap entries per chunk
+    const dim3 grid((unsigned)std::max(1, ws.nslots), (unsigned)b.num_tokens);
+    if (ws.slot_cap == kChunkSampled)
+      hipLaunchKernelGGL(topk_filter_kernel<kChunkSampled>, grid, dim3(kThreads), 0, stream, logits,
+                         ld, b, k, ws, out, ldo);
+    else if (ws.slot_cap == kChunkPlain)
+      hipLaunchKernelGGL(topk_filter_kernel<kChunkPlain>, grid, dim3(kThreads), 0, stream, logits,
+                         ld, b, k, ws, out, ldo);
+    else
+      return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_topk_resolve(logits, ld, b, ws, k, out, ldo, stream);

@@ -249,8 +249,12 @@ def test_topk_candidate_overflow_path(env):
 
 
 def test_score_topk_fused_equals_unfused(env):
+    """The fused path filters long rows in 2048-position chunks (it has the
+    sample copy), the unfused one in 4096-position chunks: rows end on either
+    side of both chunk edges."""
     m, torch = env
     for wl in (random_batch(4001, [100, 3000, 5000, 20000], 1, k=512),
+               random_batch(4005, [2047, 2049, 4095, 4097, 6143, 12289], 1, k=512),
                random_batch(4002, [3000, 900], [300, 50], k=256)):
         dev = device_layer(m, torch, wl, 0, with_new=True)
         batch = device_batch(m, wl)
