@@ -5,7 +5,7 @@
 //                 sample, candidates (key >= tau) compacted into LDS in
 //                 position order, exact select, ordered write-out.  No global
 //                 scratch and no atomics outside LDS.
-//   few long rows filter: work-groups of 4096 positions compact their
+//   few long rows filter: work-groups of 2048 or 4096 positions compact their
 //                 candidates, in order, into a private slot of the workspace
 //                 (no atomics, nothing to clear); resolve: one work-group per
 //                 row gathers the slots in order and finishes as above.
