@@ -1,4 +1,5 @@
-"""GPU parity at the size limits of the top-k and for empty batches.
+"""GPU parity at the size limits of the top-k, for empty batches, and for
+rows whose scores are all equal.
 
 Long rows are filtered in chunks (2048 positions on the fused path, which has
 the scoring kernel's sample copy; 4096 for idx_topk alone), one candidate slot
@@ -81,3 +82,29 @@ def test_empty_batch(env):
     lg = torch.empty((0, 9), dtype=torch.float32, device="cuda")
     assert m.idx_topk(lg, batch, 16).shape == (0, 16)
     torch.cuda.synchronize()
+
+
+def test_score_topk_all_scores_equal(env):
+    """Head weights all zero (and, separately, q all zero) make every score
+    exactly +0: each row then selects its lowest k positions, on the few-long-
+    rows shape (every position a candidate, more than the LDS list holds) and
+    on the many-rows shape, fused and unfused alike."""
+    m, torch = env
+    for wl in (random_batch(3103, [100, 3000, 20000, 70000], 1, k=2048),
+               random_batch(3104, [5000, 300], [200, 60], k=256)):
+        dev = device_layer(m, torch, wl, 0, with_new=True)
+        batch = device_batch(m, wl)
+        for what, q8, w in (("w = 0", dev["q8"], torch.zeros_like(dev["w"])),
+                            ("q = 0", torch.zeros_like(dev["q8"]), dev["w"])):
+            lg = m.idx_logits(q8, w, dev["cache"], batch)
+            a = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+            b = m.idx_score_topk(q8, w, dev["cache"], batch, wl.k).cpu().numpy()
+            lg = lg.cpu().numpy()
+            ob = oracle_batch(wl)
+            for t in range(wl.num_tokens):
+                n = ob.token_position(t) + 1
+                assert np.all(lg[t, :n].view(np.uint32) == 0), f"{what} token {t}: scores not +0"
+                want = np.full(wl.k, -1, np.int32)
+                want[:min(n, wl.k)] = np.arange(min(n, wl.k))
+                assert np.array_equal(a[t], want), f"{what} token {t} (unfused)"
+                assert np.array_equal(b[t], want), f"{what} token {t} (fused)"
