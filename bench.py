@@ -10,7 +10,7 @@ cached + 8192 new tokens) is reported alongside in the same JSON line.
 Decode steps rotate through several copies of the K cache so the 256 MB
 Infinity Cache cannot serve the K bytes across iterations.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-next-rows]
     python bench.py --copy-calibration     # plain 1 GiB copies, for the counter scale
 
 `roofline.traffic` is the dominant kernel's HBM bytes per launch as the
@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--secondary", default="prefill-24k+8k", help="'' to skip")
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-next-rows", action="store_true",
+                   help="skip the q-fold / physical-conversion / mixed-batch / graph measurements")
     p.add_argument("--cpu-sample", type=int, default=8, help="query tokens the oracle scores")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed oracle work")
     p.add_argument("--copy-calibration", action="store_true",
@@ -204,6 +206,137 @@ def run_workload(m, torch, name, args):
     return res, wl
 
 
+def _layers(m, torch, wl):
+    """Per-layer device state for a multi-layer workload (context K, q_fp8 / w, new K rows)."""
+    layers = []
+    reqs = [r for r in range(wl.num_reqs) if wl.seq_lens[r] > wl.new_tokens[r]]
+    for l in range(wl.num_layers):
+        cache = m.KCache(wl.num_blocks, fill=0)
+        for r in reqs:
+            kb, slots = wl.ctx_rows(l, [r])
+            m.idx_quant_write_k(torch.from_numpy(kb.view(np.int16)).cuda(),
+                                torch.from_numpy(slots).cuda(), cache)
+        q8, w, _ = m.idx_quant_q_fold_w(torch.from_numpy(wl.q_bits(l).view(np.int16)).cuda(),
+                                        torch.from_numpy(wl.w_raw(l)).cuda())
+        nb, ns = wl.new_rows(l)
+        layers.append((torch.from_numpy(nb.view(np.int16)).cuda(), cache, q8, w))
+    return layers, torch.from_numpy(ns).cuda()
+
+
+def run_next_rows(m, torch, steps=20, warmup=3):
+    """The steps next to the path, each timed live with HIP events:
+    NEXT-1 q quantisation + weight fold and NEXT-2 logical -> physical top-k on
+    the 32K prefill chunk's shapes (HBM-bound, inputs rotated over three copies
+    so the Infinity Cache cannot serve them); NEXT-3 a mixed decode + prefill
+    batch in one launch against the two launches it replaces, and a 16-layer
+    FSSS x4 stack of small decode layers replayed from a HIP graph against
+    eager launches."""
+    from synth import CONFIGS, make_workload, random_batch
+    out = {}
+    wl = make_workload(CONFIGS["prefill-24k+8k"])
+    T, H, D, k = wl.num_tokens, 64, 128, wl.k
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20251)
+
+    # NEXT-1
+    qs = [torch.randn((T, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3)]
+    wr = [torch.randn((T, H), generator=g, device="cuda") for _ in range(3)]
+    q8 = [torch.empty((T, H, D), dtype=torch.uint8, device="cuda") for _ in range(3)]
+    wf = [torch.empty((T, H), dtype=torch.float32, device="cuda") for _ in range(3)]
+    sc = [torch.empty((T, H), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ms = time_loop(torch, lambda i: m.idx_quant_q_fold_w(qs[i % 3], wr[i % 3], q_fp8=q8[i % 3],
+                                                         w_folded=wf[i % 3], q_scale=sc[i % 3]),
+                   steps, warmup)
+    nbytes = T * H * (2 * D + 4) + T * H * (D + 4 + 4)
+    out["next1_quant_q_fold"] = _hbm_row("quant_q_fold_kernel", nbytes, ms, f"{T} tokens x {H} heads")
+    del qs, wr, q8, wf, sc
+
+    # NEXT-2
+    batch = m.Batch(wl.seq_lens, wl.query_start_loc, wl.block_table)
+    hi = torch.from_numpy((wl.token_pos() + 1).astype(np.float32)).cuda()[:, None]
+    lg = [torch.sort((torch.rand((T, k), generator=g, device="cuda") * hi).to(torch.int32), dim=1)[0]
+          for _ in range(3)]
+    ph = [torch.empty((T, k), dtype=torch.int32, device="cuda") for _ in range(3)]
+    vc = [torch.empty((T,), dtype=torch.int32, device="cuda") for _ in range(3)]
+    ms = time_loop(torch, lambda i: m.idx_topk_to_physical(lg[i % 3], batch, wl.num_blocks,
+                                                           physical=ph[i % 3], valid_counts=vc[i % 3]),
+                   steps, warmup)
+    nbytes = 2 * T * k * 4 + T * 4
+    out["next2_topk_to_physical"] = _hbm_row("to_physical_kernel", nbytes, ms, f"{T} rows x k {k}")
+    del lg, ph, vc
+
+    # NEXT-3: one mixed launch (64 decode tokens, then a 2048-token prefill chunk)
+    rng = np.random.default_rng(20252)
+    dec = rng.integers(16384, 32769, 64).tolist()
+    mw = random_batch(20252, dec + [16384 + 2048], [1] * 64 + [2048], k=2048)
+    d = setup(m, torch, mw, 1)
+    cache = d["caches"][0]
+    mixed = m.Batch(mw.seq_lens, mw.query_start_loc, mw.block_table, num_decode_tokens=64)
+    bd = m.Batch(mw.seq_lens[:64], mw.query_start_loc[:65], mw.block_table[:64])
+    bp = m.Batch(mw.seq_lens[64:], mw.query_start_loc[64:] - 64, mw.block_table[64:])
+    lm = torch.empty((mw.num_tokens, mw.max_seq_len), dtype=torch.float32, device="cuda")
+    ld = torch.empty((64, bd.max_seq_len), dtype=torch.float32, device="cuda")
+    lp = torch.empty((2048, bp.max_seq_len), dtype=torch.float32, device="cuda")
+    q8d, wd, q8p, wp = d["q8"][:64], d["w"][:64], d["q8"][64:], d["w"][64:]
+    ms1 = time_loop(torch, lambda i: m.idx_logits(d["q8"], d["w"], cache, mixed, logits=lm), steps, warmup)
+
+    def two(i):
+        m.idx_logits(q8d, wd, cache, bd, logits=ld)
+        m.idx_logits(q8p, wp, cache, bp, logits=lp)
+
+    ms2 = time_loop(torch, two, steps, warmup)
+    a = algorithmic(mw)
+    pos = mw.token_pos() + 1
+    dec_bytes = int(np.sum(pos[:64])) * 136 + 64 * (H * D + H * 4)
+    pre_flops = 2 * H * D * int(np.sum(pos[64:]))
+    bound_ms = max(dec_bytes / (HBM_PEAK_GBS * 1e9), pre_flops / (FP8_PEAK_TFLOPS * 1e12)) * 1e3
+    out["next3_mixed_batch"] = {
+        "kernel": "score_mixed_kernel (idx_logits, num_decode_tokens = 64)",
+        "batch": "64 decode tokens over 16K-32K contexts + one 2048-token prefill chunk over 16K",
+        "ms_one_launch": round(ms1, 5), "ms_two_launches": round(ms2, 5),
+        "decode_bytes": dec_bytes, "prefill_flops": pre_flops, "positions": a["positions"],
+        "bound": "max(hbm, mfma)", "bound_ms": round(bound_ms, 5), "frac": round(bound_ms / ms1, 4)}
+    del d, cache, lm, ld, lp
+    torch.cuda.empty_cache()
+
+    # NEXT-3: the F/S stack from a HIP graph
+    sw = random_batch(20253, [4096] * 8, 1, k=512, num_layers=16, pattern="FSSS" * 4)
+    layers, slots = _layers(m, torch, sw)
+    sb = m.Batch(sw.seq_lens, sw.query_start_loc, sw.block_table)
+    full = m.idx_layer_schedule(True, sw.pattern, 1, 2, sw.num_layers)
+    topk = torch.empty((sw.num_tokens, sw.k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(m.idx_score_topk_workspace_size(sb, sw.k), dtype=torch.uint8, device="cuda")
+
+    def stack(i):
+        m.idx_indexcache_stack(layers, full, True, slots, sb, sw.k, topk, workspace=ws)
+
+    ms_eager = time_loop(torch, stack, steps, warmup)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        stack(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack(0)
+    ms_graph = time_loop(torch, lambda i: graph.replay(), steps, warmup)
+    out["next3_stack_graph"] = {
+        "stack": "16 layers FSSS x4, 8 decode requests x 4096 positions, k 512",
+        "ms_eager": round(ms_eager, 5), "ms_graph_replay": round(ms_graph, 5),
+        "speedup": round(ms_eager / ms_graph, 3)}
+    del graph, layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def _hbm_row(kernel, nbytes, ms, shape):
+    ach = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": kernel, "shape": shape, "bound": "hbm", "bytes_per_launch": nbytes,
+            "ms_per_launch": round(ms, 5), "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(wl, sample, min_seconds=10.0):
     """The oracle, as it stands, on `sample` query tokens of the workload, repeated
     until at least `min_seconds` of work has been timed."""
@@ -272,6 +405,11 @@ def main():
         out["secondary"] = {k: sec[k] for k in ("workload", "value", "ms_per_step", "roofline",
                                                  "step_mfma_frac", "config")}
         out["secondary"]["value"] = round(sec["value"], 1)
+    if not args.no_next_rows:
+        try:
+            out["next_rows"] = run_next_rows(m, torch)
+        except Exception as e:                         # reported, never fatal to the bench line
+            out["next_rows"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample, args.cpu_seconds)
     print(json.dumps(out), flush=True)

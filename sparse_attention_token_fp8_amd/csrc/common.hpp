@@ -158,20 +158,38 @@ __device__ __forceinline__ TokenPos token_pos(const BatchArgs& b, int t) {
   return tp;
 }
 
-// token_pos for a whole wave (every lane active, same t): with fewer than 64
-// requests the lanes read query_start_loc and seq_lens in parallel and a ballot
-// finds the request, so the lookup costs one load latency, not a search.
+// token_pos for a whole wave (every lane active, same t): with fewer than 256
+// requests the lanes read query_start_loc and seq_lens in one round (request
+// 64u + lane in slot u) and ballots find the request, so the lookup costs one
+// load latency, not a search.
 __device__ __forceinline__ TokenPos token_pos_wave(const BatchArgs& b, int t) {
-  if (b.num_reqs >= 64) return token_pos(b, t);
+  constexpr int U = 4;
+  if (b.num_reqs >= 64 * U) return token_pos(b, t);
   const int lane = threadIdx.x & 63;
-  const int q = lane <= b.num_reqs ? b.qsl[lane] : 0x7fffffff;
-  const int len = lane < b.num_reqs ? b.seq_lens[lane] : 0;
-  const int m = (int)__popcll(__ballot(lane < b.num_reqs && q <= t));
+  int q[U], len[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = 64 * u + lane;
+    q[u] = r <= b.num_reqs ? b.qsl[r] : 0x7fffffff;
+    len[u] = r < b.num_reqs ? b.seq_lens[r] : 0;
+  }
+  int m = 0;                                    // requests starting at or before t
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    m += (int)__popcll(__ballot(64 * u + lane < b.num_reqs && q[u] <= t));
   TokenPos tp;
   tp.r = m > 0 ? m - 1 : 0;
-  tp.q0 = __builtin_amdgcn_readlane(q, tp.r);
-  tp.nq = __builtin_amdgcn_readlane(q, tp.r + 1) - tp.q0;
-  tp.len = __builtin_amdgcn_readlane(len, tp.r);
+  // the value of request r (uniform) from its slot; values, not the arrays,
+  // are passed so that q[] and len[] stay in registers
+  auto pick = [](int v0, int v1, int v2, int v3, int r) {
+    const int u = r >> 6;
+    const int x = u == 0 ? v0 : u == 1 ? v1 : u == 2 ? v2 : v3;
+    return __builtin_amdgcn_readlane(x, r & 63);
+  };
+  static_assert(U == 4, "pick takes four slots");
+  tp.q0 = pick(q[0], q[1], q[2], q[3], tp.r);
+  tp.nq = pick(q[0], q[1], q[2], q[3], tp.r + 1) - tp.q0;
+  tp.len = pick(len[0], len[1], len[2], len[3], tp.r);
   int n = tp.len - tp.nq + (t - tp.q0) + 1;
   n = n < 0 ? 0 : n;
   tp.n = n > b.max_seq_len ? b.max_seq_len : n;

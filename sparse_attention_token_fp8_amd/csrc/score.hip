@@ -296,7 +296,16 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
   int bt_full = -1;                             // raw id; checked only once it is needed
   if (ident && lane < per_full)
     bt_full = b.bt[(int64_t)t * b.bt_stride + min(lb_full, (int)b.bt_stride - 1)];
-  const TokenPos tp = token_pos_wave(b, t);
+  TokenPos tp;
+  if (ident) {                                  // one new token per request: token t is request t
+    tp.r = t;
+    tp.q0 = t;
+    tp.nq = 1;
+    tp.len = b.seq_lens[t];
+    tp.n = min(max(tp.len, 0), b.max_seq_len);
+  } else {
+    tp = token_pos_wave(b, t);
+  }
   QFrag f[1];
   load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);  // first used by the MFMAs
   const int n = tp.n;
@@ -420,6 +429,84 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
 }
 
 // ------------------------------------------------------------ prefill --
+// Prefill groups are numbered across the batch: request r holds
+// ceil(m_r / kPrefillTM) groups, m_r = its tokens at or above tok_lo (the
+// first of them starting its first group), so ceil(P / kPrefillTM) + num_reqs
+// groups cover any batch with P such tokens, and requests without prefill
+// tokens (the decodes of a mixed batch) take no work-groups.  Every wave finds
+// its group's request with a scan of the per-request group counts, 256
+// requests per round of loads.
+struct PrefillGroup {
+  int r;    // request
+  int q0;   // its first token (batch index), qsl[r]
+  int nq;   // its tokens, qsl[r+1] - qsl[r]
+  int len;  // its positions, seq_lens[r]
+  int t0;   // first token of the group (batch index)
+  int nt;   // tokens in the group, 1..kPrefillTM
+};
+
+__device__ __forceinline__ bool prefill_group(const BatchArgs& b, int G, int tok_lo, int gpr,
+                                              PrefillGroup* pg) {
+  constexpr int TM = kPrefillTM, U = 4;
+  if (gpr > 0) {                                // per-request numbering: gpr groups per request
+    const int r = G / gpr, g = G % gpr;
+    if (r >= b.num_reqs) return false;
+    pg->r = r;
+    pg->q0 = b.qsl[r];
+    pg->nq = b.qsl[r + 1] - pg->q0;
+    pg->len = b.seq_lens[r];
+    pg->t0 = pg->q0 + g * TM;
+    pg->nt = min(TM, pg->nq - g * TM);
+    return pg->nt > 0 && pg->t0 + pg->nt > tok_lo;
+  }
+  const int lane = threadIdx.x & 63;
+  int base = 0;                                 // groups of the requests already passed
+  for (int r0 = 0; r0 < b.num_reqs; r0 += 64 * U) {
+    int lo[U], hi[U], len[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {               // every load of the round first
+      const int r = r0 + 64 * u + lane;
+      lo[u] = r < b.num_reqs ? b.qsl[r] : 0;
+      hi[u] = r < b.num_reqs ? b.qsl[r + 1] : 0;
+      len[u] = r < b.num_reqs ? b.seq_lens[r] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int l = max(lo[u], tok_lo);
+      const int cnt = hi[u] > l ? (hi[u] - l + TM - 1) / TM : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const int total = __shfl(incl, 63, 64);
+      if (G < base + total) {
+        const uint64_t past = __ballot(G < base + incl);
+        const int L = __ffsll((unsigned long long)past) - 1;
+        const int excl = __builtin_amdgcn_readlane(incl - cnt, L);
+        const int lL = __builtin_amdgcn_readlane(l, L);
+        const int hL = __builtin_amdgcn_readlane(hi[u], L);
+        pg->r = r0 + 64 * u + L;
+        pg->q0 = __builtin_amdgcn_readlane(lo[u], L);
+        pg->nq = hL - pg->q0;
+        pg->len = __builtin_amdgcn_readlane(len[u], L);
+        pg->t0 = lL + (G - base - excl) * TM;
+        pg->nt = min(TM, hL - pg->t0);
+        return true;
+      }
+      base += total;
+    }
+  }
+  return false;
+}
+
+// Groups the prefill split launches for P tokens at or above tok_lo (at most
+// one partial group per request that holds such tokens).
+inline int64_t prefill_groups_bound(int64_t P, int num_reqs) {
+  return (P + kPrefillTM - 1) / kPrefillTM + std::min<int64_t>(num_reqs, P);
+}
+
 // A work-group takes kPrefillTM consecutive query tokens of one request
 // (kPrefillTPW per wave) and `chunk_blocks` blocks of positions.  Each K block
 // is fetched once per work-group: the work-group copies it with whole-line
@@ -430,23 +517,22 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
                                              const uint8_t* __restrict__ q8,
                                              const float* __restrict__ w, const CacheArgs& cache,
                                              const BatchArgs& b, float* __restrict__ logits,
-                                             int64_t ld, int chunk_blocks, int groups_per_req,
+                                             int64_t ld, int chunk_blocks, int gpr,
                                              uint8_t* lds, float* __restrict__ samp) {
   constexpr int TPW = kPrefillTPW, NW = 4, TM = kPrefillTM;
-  const int r = gy / groups_per_req;
-  const int g = gy % groups_per_req;
-  if (r >= b.num_reqs) return;
-  const int q0 = b.qsl[r];
-  const int nq = b.qsl[r + 1] - q0;
-  const int tb = g * TM;
-  if (tb >= nq || q0 + min(tb + TM, nq) <= tok_lo) return;
-  const int L = b.seq_lens[r];
+  PrefillGroup pg;
+  if (!prefill_group(b, gy, tok_lo, gpr, &pg)) return;
+  const int r = pg.r;
+  const int q0 = pg.q0;
+  const int nq = pg.nq;
+  const int tb = pg.t0 - q0;                    // the group's tokens: tb .. tb + pg.nt - 1 of r
+  const int L = pg.len;
   auto count = [&](int i) {
     int n = L - nq + i + 1;
     n = n < 0 ? 0 : n;
     return n > b.max_seq_len ? b.max_seq_len : n;
   };
-  const int n_max = count(min(tb + TM, nq) - 1);
+  const int n_max = count(tb + pg.nt - 1);
   const int lb0 = bx * chunk_blocks;
   if (lb0 * kBlock >= n_max) return;
   const int nblk = min(chunk_blocks, (n_max - lb0 * kBlock + kBlock - 1) / kBlock);
@@ -464,7 +550,7 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
   for (int j = 0; j < TPW; ++j) {
     const int i = tb + wave * TPW + j;
     const int t = q0 + i;
-    if (i < nq && t >= tok_lo && t < b.num_tokens) {
+    if (i < tb + pg.nt && t >= tok_lo && t < b.num_tokens) {
       load_q(f[j], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
       nt[j] = count(i);
       out[j] = logits + (size_t)t * ld;
@@ -512,6 +598,17 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
 }
 
 // ------------------------------------------------------------ kernels --
+// Work-groups reach the XCDs round-robin in dispatch order (blockIdx.x
+// fastest).  Each one takes its (chunk, row) from that order with the row
+// fastest, so the chunks of one row -- whose costs differ: causal rows end
+// early, a request's later chunks can be empty -- are spread over every XCD
+// instead of chunk c always landing on XCD c mod 8.
+__device__ __forceinline__ void xcd_spread(int* chunk, int* row) {
+  const int L = blockIdx.y * gridDim.x + blockIdx.x;
+  *row = L % gridDim.y;
+  *chunk = L / gridDim.y;
+}
+
 
 template <int NB>
 __global__ __launch_bounds__(kScoreThreads)
@@ -519,7 +616,9 @@ __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int chunk_blocks, int ident, float* samp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
-  decode_body<NB, false>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks,
+  int cx, ry;
+  xcd_spread(&cx, &ry);
+  decode_body<NB, false>(cx, ry, q8, w, cache, b, logits, ld, chunk_blocks,
                          ident != 0, lds, NewRows{}, samp);
 }
 
@@ -530,16 +629,19 @@ __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int chunk_blocks, int ident, NewRows nk, float* samp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
-  decode_body<NB, true>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, chunk_blocks,
+  int cx, ry;
+  xcd_spread(&cx, &ry);
+  decode_body<NB, true>(cx, ry, q8, w, cache, b, logits, ld, chunk_blocks,
                         ident != 0, lds, nk, samp);
 }
 
 __global__ __launch_bounds__(kScoreThreads) void score_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    float* __restrict__ logits, int64_t ld, int chunk_blocks, int groups_per_req, float* samp) {
+    float* __restrict__ logits, int64_t ld, int chunk_blocks, int gpr, float* samp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBlockBytes];
-  prefill_body(blockIdx.x, blockIdx.y, 0, q8, w, cache, b, logits, ld, chunk_blocks, groups_per_req,
-               lds, samp);
+  int cx, ry;
+  xcd_spread(&cx, &ry);
+  prefill_body(cx, ry, 0, q8, w, cache, b, logits, ld, chunk_blocks, gpr, lds, samp);
 }
 
 // Mixed batch in one launch: rows y < dec_tokens are tokens scored with the
@@ -549,14 +651,16 @@ template <int NB>
 __global__ __launch_bounds__(kScoreThreads) void score_mixed_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int dec_tokens, int dec_chunk_blocks,
-    int pre_chunk_blocks, int groups_per_req, float* samp) {
+    int pre_chunk_blocks, int gpr, float* samp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
-  if ((int)blockIdx.y < dec_tokens)
-    decode_body<NB, false>(blockIdx.x, blockIdx.y, q8, w, cache, b, logits, ld, dec_chunk_blocks,
+  int cx, ry;
+  xcd_spread(&cx, &ry);
+  if (ry < dec_tokens)
+    decode_body<NB, false>(cx, ry, q8, w, cache, b, logits, ld, dec_chunk_blocks,
                            false, lds, NewRows{}, samp);
   else
-    prefill_body(blockIdx.x, blockIdx.y - dec_tokens, dec_tokens, q8, w, cache, b, logits, ld,
-                 pre_chunk_blocks, groups_per_req, lds, samp);
+    prefill_body(cx, ry - dec_tokens, dec_tokens, q8, w, cache, b, logits, ld,
+                 pre_chunk_blocks, gpr, lds, samp);
 }
 
 // Decode chunk: about two work-groups per CU over the decode tokens (two fit
@@ -573,10 +677,8 @@ int decode_chunk_blocks(int max_seq_len, int64_t tokens) {
   return (int)std::min<int64_t>(64, std::max<int64_t>(8, cb));
 }
 
-int prefill_chunk_blocks(const BatchArgs& b) {
+int prefill_chunk_blocks(const BatchArgs& b, int64_t groups) {
   // aim for a few thousand work-groups; never more blocks than the longest row needs
-  const int gpr = (b.max_query_len + kPrefillTM - 1) / kPrefillTM;
-  const int64_t groups = (int64_t)gpr * b.num_reqs;
 #ifndef IDX_PREFILL_MAX_CHUNK
 #define IDX_PREFILL_MAX_CHUNK 32
 #endif
@@ -621,17 +723,25 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
                        q8, w, cache, b, logits, ld, cb,
                        (int)(b.num_reqs == b.num_tokens && b.max_query_len <= 1), samp);
   } else {
-    const int pcb = prefill_chunk_blocks(b);
+    if (dec_tokens < 0) dec_tokens = 0;
+    // groups numbered per request (gpr each) when that wastes little, else
+    // numbered across the batch (a scan finds each group's request)
+    const int64_t per_req = (int64_t)((b.max_query_len + kPrefillTM - 1) / kPrefillTM);
+    const int64_t flat = prefill_groups_bound(b.num_tokens - dec_tokens, b.num_reqs);
+    const bool arith = per_req * b.num_reqs <= flat + flat / 4;
+    const int gpr = arith ? (int)per_req : 0;
+    const int64_t groups = arith ? per_req * b.num_reqs : flat;
+    if (dec_tokens + groups > 65535) return hipErrorInvalidConfiguration;   // grid y-extent
+    const int pcb = prefill_chunk_blocks(b, groups);
     const int pchunks = (b.max_seq_len + pcb * kBlock - 1) / (pcb * kBlock);
-    const int gpr = (b.max_query_len + kPrefillTM - 1) / kPrefillTM;
-    if (dec_tokens <= 0) {
-      const dim3 grid((unsigned)pchunks, (unsigned)(gpr * b.num_reqs));
+    if (dec_tokens == 0) {
+      const dim3 grid((unsigned)pchunks, (unsigned)groups);
       hipLaunchKernelGGL(score_prefill_kernel, grid, dim3(kScoreThreads), 0, stream, q8, w, cache, b,
                          logits, ld, pcb, gpr, samp);
     } else {
       const int dcb = decode_chunk_blocks(b.max_seq_len, dec_tokens);
       const int dchunks = (b.max_seq_len + dcb * kBlock - 1) / (dcb * kBlock);
-      const dim3 grid((unsigned)std::max(dchunks, pchunks), (unsigned)(dec_tokens + gpr * b.num_reqs));
+      const dim3 grid((unsigned)std::max(dchunks, pchunks), (unsigned)(dec_tokens + groups));
       hipLaunchKernelGGL(score_mixed_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0, stream,
                          q8, w, cache, b, logits, ld, (int)dec_tokens, dcb, pcb, gpr, samp);
     }
