@@ -15,6 +15,11 @@
 namespace idx {
 namespace {
 
+// One work-group per token; each thread converts 8 consecutive entries (two
+// 16-byte loads and stores when the row is 16-byte aligned), so the block-table
+// reads of a row are all in flight together.
+constexpr int kPhysPer = 8;
+
 __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restrict__ logical,
                                                           int64_t ldl, BatchArgs b, CacheArgs c,
                                                           int block_size, int k,
@@ -22,18 +27,43 @@ __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ phys, int64_t ldp,
                                                           int32_t* __restrict__ valid) {
   const int t = blockIdx.x;
-  const TokenPos tp = token_pos(b, t);
+  const TokenPos tp = token_pos_wave(b, t);
   __shared__ uint32_t scratch[8];
+  const int32_t* in = logical + (size_t)t * ldl;
+  int32_t* out = phys + (size_t)t * ldp;
+  const bool vec = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
   uint32_t cnt = 0;
-  for (int j = threadIdx.x; j < k; j += kThreads) {
-    const int pos = logical[(size_t)t * ldl + j];
-    int32_t o = -1;
-    if (pos >= 0 && pos < tp.n) {
-      const int64_t blk = phys_block(b, c, tp.r, pos / block_size);
-      if (blk >= 0) o = (int32_t)(blk * stride_rows + pos % block_size);
+  for (int j0 = 0; j0 < k; j0 += kThreads * kPhysPer) {
+    const int jb = j0 + (int)threadIdx.x * kPhysPer;
+    const bool full = vec && jb + kPhysPer <= k;
+    int pos[kPhysPer];
+    if (full) {
+      const int4 a = *reinterpret_cast<const int4*>(in + jb);
+      const int4 d = *reinterpret_cast<const int4*>(in + jb + 4);
+      pos[0] = a.x; pos[1] = a.y; pos[2] = a.z; pos[3] = a.w;
+      pos[4] = d.x; pos[5] = d.y; pos[6] = d.z; pos[7] = d.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPhysPer; ++e) pos[e] = jb + e < k ? in[jb + e] : -1;
     }
-    phys[(size_t)t * ldp + j] = o;
-    cnt += o >= 0;
+    int32_t o[kPhysPer];
+#pragma unroll
+    for (int e = 0; e < kPhysPer; ++e) {
+      o[e] = -1;
+      if (pos[e] >= 0 && pos[e] < tp.n) {
+        const int64_t blk = phys_block(b, c, tp.r, pos[e] / block_size);
+        if (blk >= 0) o[e] = (int32_t)(blk * stride_rows + pos[e] % block_size);
+      }
+      cnt += (jb + e < k && o[e] >= 0) ? 1u : 0u;
+    }
+    if (full) {
+      *reinterpret_cast<int4*>(out + jb) = make_int4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<int4*>(out + jb + 4) = make_int4(o[4], o[5], o[6], o[7]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPhysPer; ++e)
+        if (jb + e < k) out[jb + e] = o[e];
+    }
   }
   uint32_t total;
   (void)block_scan_excl<kThreads>(cnt, &total, scratch);

@@ -2,11 +2,13 @@
 // the quantise-and-scatter kernels and the top-k planning kernel, so every
 // path writes the same bytes.
 //
-// Everything works on the bf16 bit patterns with integer arithmetic: a row
+// encode_e4m3 works on the bf16 bit patterns with integer arithmetic: a row
 // scale is a power of two, so x / scale is an exponent shift, and the
-// round-to-nearest-even of the E4M3 mantissa is a shift with a sticky test.
-// No floating-point instruction touches the data, so the result cannot
-// depend on the denormal mode.
+// round-to-nearest-even of the E4M3 mantissa is a shift with a sticky test, so
+// the result cannot depend on the denormal mode.  The K writes use it.  The
+// q-side kernel, which quantises 64 rows per token, uses the hardware
+// conversion instead (quant_row_lane8_cvt); the two give the same bytes on
+// every finite bf16 value at every row scale (checked exhaustively).
 #pragma once
 
 #include "common.hpp"
@@ -71,7 +73,55 @@ __device__ __forceinline__ uint32_t quant_row_lane(uint2 v, int* e_out) {
          (encode_e4m3(x3, e) << 24);
 }
 
+// The same row quantiser with 16 lanes per 128-wide row, 8 consecutive values
+// per lane (one 16-byte load).  Returns this lane's 8 codes, little-endian.
+__device__ __forceinline__ uint2 quant_row_lane8(uint4 v, int* e_out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off, 16));
+  const int e = ue8m0_exponent(am);
+  *e_out = e;
+  uint2 c;
+  c.x = encode_e4m3(w[0] & 0xFFFFu, e) | (encode_e4m3(w[0] >> 16, e) << 8) |
+        (encode_e4m3(w[1] & 0xFFFFu, e) << 16) | (encode_e4m3(w[1] >> 16, e) << 24);
+  c.y = encode_e4m3(w[2] & 0xFFFFu, e) | (encode_e4m3(w[2] >> 16, e) << 8) |
+        (encode_e4m3(w[3] & 0xFFFFu, e) << 16) | (encode_e4m3(w[3] >> 16, e) << 24);
+  return c;
+}
+
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// quant_row_lane8 with the matrix cores' own conversion: x * 2^-e is exact in
+// fp32 (a power-of-two scaling of a bf16 value; the results a flush of fp32
+// denormals could touch lie far below half an E4M3 quantum and give a signed
+// zero either way), and v_cvt_pk_fp8_f32 rounds it to the nearest E4M3 code,
+// ties to even, as encode_e4m3 does.  |x * 2^-e| <= 448, so nothing saturates.
+__device__ __forceinline__ uint2 quant_row_lane8_cvt(uint4 v, int* e_out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off, 16));
+  const int e = ue8m0_exponent(am);
+  *e_out = e;
+  const float s = pow2f(-e);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16) * s;
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) * s;
+  }
+  uint2 c;
+  c.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  c.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], (int)c.x, true);
+  c.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  c.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], (int)c.y, true);
+  return c;
+}
 
 // Quantise one K row (32 lanes, row pointer `k`) and store it at `slot` of
 // the paged cache; slots outside 0..num_slots-1 are skipped.

@@ -101,13 +101,39 @@ def test_quant_q_fold_bitexact(env):
     x[4, 9] *= 1e5
     qb = f32_to_bf16_bits(x)
     w_raw = rng.standard_normal((37, 64)).astype(np.float32)
-    q8, w, qs = m.idx_quant_q_fold_w(torch.from_numpy(qb.view(np.int16)).cuda(),
-                                     torch.from_numpy(w_raw).cuda())
     oq8, oqs = oquant.quantize_q(qb)
     ow = oquant.fold_weights(w_raw, oqs)
-    assert np.array_equal(q8.cpu().numpy(), oq8)
-    assert np.array_equal(qs.cpu().numpy(), oqs)
-    assert np.array_equal(w.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+    flat = torch.from_numpy(qb.view(np.int16).reshape(-1)).cuda()
+    # q 16-byte aligned (16 lanes per row) and only 8-byte aligned (32 lanes per row)
+    padded = torch.empty(flat.numel() + 4, dtype=torch.int16, device="cuda")
+    padded[4:] = flat
+    for what, q in (("aligned", flat.view(37, 64, 128)), ("8-byte", padded[4:].view(37, 64, 128))):
+        assert (q.data_ptr() % 16 == 0) == (what == "aligned")
+        q8, w, qs = m.idx_quant_q_fold_w(q, torch.from_numpy(w_raw).cuda())
+        assert np.array_equal(q8.cpu().numpy(), oq8), what
+        assert np.array_equal(qs.cpu().numpy(), oqs), what
+        assert np.array_equal(w.cpu().numpy().view(np.uint32), ow.view(np.uint32)), what
+
+
+def test_quant_q_fold_all_finite_bf16_patterns(env):
+    """Every finite bf16 pattern as q, in rows of similar magnitude (sorted) and
+    of mixed magnitude (shuffled), bit-exact against the oracle's quantiser."""
+    m, torch = env
+    bits = all_finite_bf16_bits()
+    pad = (-bits.size) % (64 * 128)
+    bits = np.concatenate([bits, np.zeros(pad, np.uint16)])
+    rng = np.random.default_rng(1005)
+    for arrangement in ("sorted", "shuffled"):
+        b = bits if arrangement == "sorted" else rng.permutation(bits)
+        qb = b.reshape(-1, 64, 128)
+        w_raw = rng.standard_normal(qb.shape[:2]).astype(np.float32)
+        q8, w, qs = m.idx_quant_q_fold_w(torch.from_numpy(qb.view(np.int16)).cuda(),
+                                         torch.from_numpy(w_raw).cuda())
+        oq8, oqs = oquant.quantize_q(qb)
+        got = q8.cpu().numpy()
+        bad = np.argwhere(got != oq8)
+        assert bad.size == 0, f"{arrangement}: {bad.shape[0]} codes differ, first {bad[:3].tolist()}"
+        assert np.array_equal(qs.cpu().numpy(), oqs), arrangement
 
 
 # --------------------------------------------------------------- scores --
