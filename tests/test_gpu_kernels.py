@@ -187,19 +187,25 @@ def test_decode_and_prefill_kernels_agree_bitwise(env):
     assert np.array_equal(a[0].cpu().numpy().view(np.uint32), b[2].cpu().numpy().view(np.uint32))
 
 
-def test_mixed_batch_split_is_result_neutral(env):
+@pytest.mark.parametrize("lengths,new,splits", [
+    # decodes then two prefill chunks: prefill groups numbered across the batch
+    ([5000, 3000, 9000, 1200, 2500], [1, 1, 1, 300, 40], (0, 3, 5, None)),
+    # two equal chunks: groups numbered per request, the split cuts the first
+    ([4000, 3500], [300, 300], (0, 5, 300, 301, None)),
+])
+def test_mixed_batch_split_is_result_neutral(env, lengths, new, splits):
     """Decode requests first, then prefill chunks, scored in one launch with the
     decode work split for the first num_decode_tokens tokens: any split (none,
     the decodes, one that cuts a prefill request, all tokens) gives bit-identical
     scores, within tolerance of the oracle, and identical top-k rows."""
     m, torch = env
-    wl = random_batch(2004, [5000, 3000, 9000, 1200, 2500], [1, 1, 1, 300, 40], k=128)
+    wl = random_batch(2004 + len(lengths), lengths, new, k=128)
     say("mixed batch", wl.seq_lens.tolist(), wl.new_tokens.tolist())
     dev = device_layer(m, torch, wl, 0, with_new=True)
     orc = oracle_layer(wl, 0)
     want = oracle.logits.logits(orc["q8"], orc["w"], orc["cache"], oracle_batch(wl))
     ref = ref_topk = None
-    for nd in (0, 3, 5, wl.num_tokens):
+    for nd in [wl.num_tokens if x is None else x for x in splits]:
         say("  num_decode_tokens", nd)
         batch = m.Batch(wl.seq_lens, wl.query_start_loc, wl.block_table, num_decode_tokens=nd)
         lg = torch.full((wl.num_tokens, wl.max_seq_len), float("nan"), device="cuda")
