@@ -75,7 +75,7 @@ SIGNATURES = {
 def _load(path=LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
-                          "`python -m sparse_attention_token_fp8_amd.build` (there is no fallback)")
+                          "`python sparse_attention_token_fp8_amd/build.py` (there is no fallback)")
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

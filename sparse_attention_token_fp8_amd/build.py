@@ -1,6 +1,9 @@
 """Build libidx.so for gfx950 in-tree with hipcc (no GPU needed).
 
-    python -m sparse_attention_token_fp8_amd.build
+    python sparse_attention_token_fp8_amd/build.py
+
+This file imports nothing from the package (whose import needs the built
+library), so it is run or loaded by its file path.
 """
 
 import concurrent.futures as cf

@@ -18,8 +18,8 @@ LIB = os.path.join(ROOT, "sparse_attention_token_fp8_amd", "libidx.so")
 @pytest.fixture(scope="module")
 def m():
     if not os.path.exists(LIB):
-        from sparse_attention_token_fp8_amd import build
-        build.build()
+        import __graft_entry__
+        __graft_entry__._builder().build()
     import sparse_attention_token_fp8_amd as pkg
     return pkg
 
