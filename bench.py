@@ -37,8 +37,7 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 PROFILES = os.path.join(ROOT, "profiles")
 SCORE_SOURCES = ("sparse_attention_token_fp8_amd/csrc/score.hip",
-                 "sparse_attention_token_fp8_amd/csrc/common.hpp",
-                 "sparse_attention_token_fp8_amd/build.py")
+                 "sparse_attention_token_fp8_amd/csrc/common.hpp")
 
 
 def log(*a):
@@ -63,12 +62,24 @@ def parse():
     return p.parse_args()
 
 
+def score_build_flags():
+    """The hipcc flags the scoring kernels are compiled with (read from build.py by path)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_idx_build_flags", os.path.join(ROOT, "sparse_attention_token_fp8_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return [os.path.basename(f) if f.startswith("-I") else f
+            for f in mod.COMMON + mod.EXTRA.get("score.hip", [])]
+
+
 def sources_digest():
-    """Digest of the scoring kernels' sources and build flags."""
+    """Digest of the scoring kernels' sources and their compile flags."""
     h = hashlib.sha256()
     for f in SCORE_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(score_build_flags()).encode())
     return h.hexdigest()[:16]
 
 
