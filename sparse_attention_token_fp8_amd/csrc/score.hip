@@ -148,12 +148,6 @@ __device__ __forceinline__ void block_scores(const QFrag* f, const KBlock& kb, f
     out[j] = reduce_block(part[j][0], part[j][1], part[j][2], part[j][3]) * kb.ks;
 }
 
-__device__ __forceinline__ const uint8_t* block_base(const BatchArgs& b, const CacheArgs& c, int r,
-                                                     int lb) {
-  const int64_t pb = phys_block(b, c, r, lb);
-  return pb < 0 ? nullptr : c.data + pb * kBlockBytes;
-}
-
 // ------------------------------------------------------ LDS staging --
 // K blocks reach the MFMA operands through LDS: global loads are contiguous
 // (8 lanes per 128-byte code row, whole lines per instruction), while the
@@ -170,6 +164,7 @@ struct StageRegs {
   static constexpr int kChunks = kBlockBytes / 16;                  // 528
   static constexpr int kPerThread = (kChunks + NW * 64 - 1) / (NW * 64);
   uint4 v[kPerThread];
+  uint32_t mask;   // all ones for a block in the table, else 0 (stored as zeros)
 };
 
 template <int NW>
@@ -182,14 +177,24 @@ __device__ __forceinline__ int stage_src(int ci) {
   return ci << 4;                                                    // scales, unswizzled
 }
 
+// Every thread issues the same number of loads from a valid block address (in
+// the last round the threads past the block's 528 chunks re-read one of its
+// scale chunks), so no load sits behind a branch: a branch around a load makes
+// the compiler wait for every load in flight at the next use, which would
+// drain the prefetch.  A block absent from the table is read from block 0 and
+// stored as zeros.
 template <int NW>
-__device__ __forceinline__ void stage_load(StageRegs<NW>& st, const uint8_t* __restrict__ base) {
+__device__ __forceinline__ void stage_load(StageRegs<NW>& st, const uint8_t* __restrict__ base,
+                                           bool valid) {
+  constexpr int kC = StageRegs<NW>::kChunks;
 #pragma unroll
   for (int u = 0; u < StageRegs<NW>::kPerThread; ++u) {
-    const int ci = threadIdx.x + u * NW * 64;
-    if (ci < StageRegs<NW>::kChunks)
-      st.v[u] = base ? *reinterpret_cast<const uint4*>(base + stage_src<NW>(ci)) : make_uint4(0, 0, 0, 0);
+    int ci = threadIdx.x + u * NW * 64;
+    if (u == StageRegs<NW>::kPerThread - 1 && (kC % (NW * 64)) != 0)
+      ci = ci < kC ? ci : kC - 16 + (threadIdx.x & 15);
+    st.v[u] = *reinterpret_cast<const uint4*>(base + stage_src<NW>(ci));
   }
+  st.mask = valid ? 0xffffffffu : 0u;
 }
 
 template <int NW>
@@ -197,7 +202,9 @@ __device__ __forceinline__ void stage_store(const StageRegs<NW>& st, uint8_t* sl
 #pragma unroll
   for (int u = 0; u < StageRegs<NW>::kPerThread; ++u) {
     const int ci = threadIdx.x + u * NW * 64;
-    if (ci < StageRegs<NW>::kChunks) *reinterpret_cast<uint4*>(slot + (ci << 4)) = st.v[u];
+    const uint4 x = make_uint4(st.v[u].x & st.mask, st.v[u].y & st.mask, st.v[u].z & st.mask,
+                               st.v[u].w & st.mask);
+    if (ci < StageRegs<NW>::kChunks) *reinterpret_cast<uint4*>(slot + (ci << 4)) = x;
   }
 }
 
@@ -540,6 +547,9 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
   const int lp = lane_pos(lane);
   uint8_t* kbuf0 = lds;
   uint8_t* kbuf1 = lds + kBlockBytes;
+  // lane j holds the physical block of the chunk's j-th block (chunk_blocks <=
+  // 64), read before the q loads so the first K loads wait on it alone
+  const int pbl = lane < nblk ? (int)phys_block(b, cache, r, lb0 + lane) : -1;
 
   QFrag f[TPW];
   int nt[TPW];
@@ -565,21 +575,44 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
     sSh[j] = 31 - __clz(sS[j]);
   }
 
+  if (cache.num_blocks == 0) {                  // no K at all: every score is 0
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj)
+      for (int j = 0; j < nblk; ++j) {
+        const int s = (lb0 + j) * kBlock + lp;
+        if (s < nt[jj]) out[jj][s] = 0.f;
+        if (srow[jj] != nullptr) {
+          const int sj = s >> sSh[jj];
+          if (s < nt[jj] && (s & (sS[jj] - 1)) == ((37 * sj + 11) & (sS[jj] - 1))) srow[jj][sj] = 0.f;
+        }
+      }
+    return;
+  }
+  // block min(j, nblk-1) (past the last block it is re-read, from L2, so the
+  // loop body issues its loads unconditionally)
+  auto stage = [&](StageRegs<NW>& st, int j) {
+    const int pb = __builtin_amdgcn_readlane(pbl, min(j, nblk - 1));
+    stage_load<NW>(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes, pb >= 0);
+  };
+
   // Staging registers for blocks j+1 and j+2 alternate: block j+2's loads are
   // issued while block j is scored and reach LDS one iteration later.
   StageRegs<NW> st[2];
-  stage_load<NW>(st[0], block_base(b, cache, r, lb0));
+  stage(st[0], 0);
+  stage(st[1], 1);
   stage_store<NW>(st[0], kbuf0);
-  if (nblk > 1) stage_load<NW>(st[1], block_base(b, cache, r, lb0 + 1));
-  if (nblk > 2) stage_load<NW>(st[0], block_base(b, cache, r, lb0 + 2));
-  for (int j0 = 0; j0 < nblk; j0 += 2) {
+  stage(st[0], 2);
+  // Whole turns of the two-slot ring (an odd block count ends with one turn
+  // that only stages), so the loop body has no exit between its loads.
+  const int iters = (nblk + 1) & ~1;
+  for (int j0 = 0; j0 < iters; j0 += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int j = j0 + u;
-      if (j >= nblk) break;
       __syncthreads();                     // block j in slot j&1; slot (j+1)&1 free
-      if (j + 1 < nblk) stage_store<NW>(st[(u + 1) & 1], (j + 1) & 1 ? kbuf1 : kbuf0);
-      if (j + 3 < nblk) stage_load<NW>(st[(u + 1) & 1], block_base(b, cache, r, lb0 + j + 3));
+      stage_store<NW>(st[(u + 1) & 1], (j + 1) & 1 ? kbuf1 : kbuf0);   // unused past the end
+      stage(st[(u + 1) & 1], j + 3);
+      if (j >= nblk) continue;
       KBlock kb;
       lds_kblock(kb, j & 1 ? kbuf1 : kbuf0, lane);
       float v[TPW];
@@ -682,6 +715,7 @@ int prefill_chunk_blocks(const BatchArgs& b, int64_t groups) {
 #ifndef IDX_PREFILL_MAX_CHUNK
 #define IDX_PREFILL_MAX_CHUNK 32
 #endif
+  static_assert(IDX_PREFILL_MAX_CHUNK <= 64, "a wave holds the chunk's block ids, one per lane");
   int cb = IDX_PREFILL_MAX_CHUNK;
   while (cb > 4 && groups * ((b.max_seq_len + cb * kBlock - 1) / (cb * kBlock)) < 2048) cb >>= 1;
   return cb;
