@@ -713,7 +713,7 @@ int decode_chunk_blocks(int max_seq_len, int64_t tokens) {
 int prefill_chunk_blocks(const BatchArgs& b, int64_t groups) {
   // aim for a few thousand work-groups; never more blocks than the longest row needs
 #ifndef IDX_PREFILL_MAX_CHUNK
-#define IDX_PREFILL_MAX_CHUNK 32
+#define IDX_PREFILL_MAX_CHUNK 64
 #endif
   static_assert(IDX_PREFILL_MAX_CHUNK <= 64, "a wave holds the chunk's block ids, one per lane");
   int cb = IDX_PREFILL_MAX_CHUNK;
