@@ -12,9 +12,16 @@
 //    in register i.  Both operands use the same byte->k assignment (lane group
 //    G = lane/16 holds k in [16G, 16G+16) and [64+16G, 64+16G+16)), so the
 //    contraction covers all 128 dims whatever the hardware's k order is.
-//  * The ReLU and head weighting run in registers on the MFMA output; each lane
-//    sums its 16 heads of a tile.  Two accumulator sets alternate so the next
-//    tile's MFMAs run while the previous tile's epilogue executes.
+//  * The ReLU is split: w * max(d, 0) = (w/2) |d| + (w/2) d.  The first half
+//    is one fma per MFMA output (the absolute value is a free source
+//    modifier); each lane sums its 16 heads of a tile.  The second half, summed
+//    over the heads, is linear in k: sum_h (w_h/2) q8[h] . k8 = u . k8 with
+//    u = sum_h (w_h/2) q8[h] (fp32, once per token).  u is held as four E4M3
+//    pieces, u ~= sum_j 2^(c-4j) p_j (each piece codes the previous residual,
+//    so four of them carry about 16 significant bits), and one more MFMA per
+//    tile contracts them with the same K operand for all of a wave's tokens.
+//    Two accumulator sets alternate so the next tile's MFMAs run while the
+//    previous tile's epilogue executes.
 //  * The four per-tile partials (each split over the four lane groups) are
 //    reduced and transposed at once with v_permlane32_swap / v_permlane16_swap:
 //    afterwards lane `lane` holds the full 64-head sum of one position,
@@ -30,11 +37,22 @@
 namespace idx {
 namespace {
 
-// One token's q as four A operands (16 heads each) plus this lane's 16 weights
-// w[16*hg + 4*(lane/16) + i] in w[4*hg + i].
+// One token's q as four A operands (16 heads each) plus this lane's 16 halved
+// weights w[16*hg + 4*(lane/16) + i] / 2 in w[4*hg + i], and the halved weights
+// of the heads whose q rows it holds, w[16*hg + lane%16] / 2 in wc[hg].
 struct QFrag {
   v8i a[4];
   float w[16];
+  float wc[4];
+};
+
+// The linear half's MFMA operand for up to four tokens of a wave: row 4j+t
+// (lane%16) holds piece j of token t over this lane group's k range, and
+// sc[t] = 2^(c_t - 4*(lane/16)) scales the output row this lane receives for
+// token t (piece lane/16 of it).
+struct LinFrag {
+  v8i a;
+  float sc[4];
 };
 
 // One 64-position block: the four tiles' B operands and the scale of the
@@ -69,8 +87,9 @@ __device__ __forceinline__ void load_q(QFrag& f, const uint8_t* __restrict__ qt,
     f.a[hg] = pack8(*reinterpret_cast<const uint4*>(row + 16 * G),
                     *reinterpret_cast<const uint4*>(row + 64 + 16 * G));
     const float4 wv = *reinterpret_cast<const float4*>(wt + hg * 16 + 4 * G);
-    f.w[hg * 4 + 0] = wv.x; f.w[hg * 4 + 1] = wv.y;
-    f.w[hg * 4 + 2] = wv.z; f.w[hg * 4 + 3] = wv.w;
+    f.w[hg * 4 + 0] = 0.5f * wv.x; f.w[hg * 4 + 1] = 0.5f * wv.y;
+    f.w[hg * 4 + 2] = 0.5f * wv.z; f.w[hg * 4 + 3] = 0.5f * wv.w;
+    f.wc[hg] = 0.5f * wt[hg * 16 + c];
   }
 }
 
@@ -78,9 +97,107 @@ __device__ __forceinline__ void zero_q(QFrag& f) {
 #pragma unroll
   for (int hg = 0; hg < 4; ++hg) {
     f.a[hg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    f.wc[hg] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.w[hg * 4 + i] = 0.f;
   }
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Builds the linear half's pieces for NT tokens (f[0..NT-1]); `scratch` is 4 KB
+// of LDS owned by this wave.  Per token: each lane sums its four heads' halved
+// weights times q over its lane group's 32 k values; the 16 lanes of a group
+// (16 different heads each) are summed, quads by DPP and the four quads through
+// LDS, so that each lane ends with u at two k values.  The exponent c is the
+// smallest with max|u| <= 448 * 2^c (clamped to [-100, 100]); piece j codes the
+// residual times 2^-(c-4j) to the nearest E4M3 value and the residual loses it.
+// Every step runs in a fixed order, so a token's pieces do not depend on the
+// other tokens of the wave or on which kernel builds them.
+template <int NT>
+__device__ __forceinline__ void make_lin(LinFrag& lf, const QFrag* f, uint8_t* scratch, int lane) {
+  const int c = lane & 15, G = lane >> 4;
+  float* part = reinterpret_cast<float*>(scratch);           // [G][quad][32] fp32: 2 KB
+  uint8_t* pcs = scratch + 2048;                             // [t][j][G][32] codes: 2 KB
+  int ct[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float p[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) p[k] = 0.f;
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+      for (int dw = 0; dw < 8; ++dw) {
+        const int x = f[t].a[hg][dw];
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+        p[4 * dw + 0] = fmaf(f[t].wc[hg], lo[0], p[4 * dw + 0]);
+        p[4 * dw + 1] = fmaf(f[t].wc[hg], lo[1], p[4 * dw + 1]);
+        p[4 * dw + 2] = fmaf(f[t].wc[hg], hi[0], p[4 * dw + 2]);
+        p[4 * dw + 3] = fmaf(f[t].wc[hg], hi[1], p[4 * dw + 3]);
+      }
+    // quad sums (lane ^ 1, then lane ^ 2): additions commute exactly, so the
+    // four lanes of a quad hold the same bits
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      p[k] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(p[k]), 0xB1, 0xF, 0xF, false));
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      p[k] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(p[k]), 0x4E, 0xF, 0xF, false));
+    if ((c & 3) == 0) {                                       // one lane per quad stores its sums
+      float4* dst = reinterpret_cast<float4*>(part + (G * 4 + (c >> 2)) * 32);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dst[q] = make_float4(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
+    }
+    wave_sync_lds();
+    float u0, u1;
+    {
+      const float2 a0 = *reinterpret_cast<const float2*>(part + (G * 4 + 0) * 32 + 2 * c);
+      const float2 a1 = *reinterpret_cast<const float2*>(part + (G * 4 + 1) * 32 + 2 * c);
+      const float2 a2 = *reinterpret_cast<const float2*>(part + (G * 4 + 2) * 32 + 2 * c);
+      const float2 a3 = *reinterpret_cast<const float2*>(part + (G * 4 + 3) * 32 + 2 * c);
+      u0 = ((a0.x + a1.x) + a2.x) + a3.x;
+      u1 = ((a0.y + a1.y) + a2.y) + a3.y;
+    }
+    wave_sync_lds();                                          // part is reused by the next token
+    uint32_t mb = max(__float_as_uint(fabsf(u0)), __float_as_uint(fabsf(u1)));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off));
+    int c0 = (int)((mb >> 23) & 0xFF) - 127 - 8 + ((mb & 0x7FFFFF) > 0x600000 ? 1 : 0);
+    c0 = min(100, max(-100, c0));
+    float r0 = u0, r1 = u1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cj = c0 - 4 * j;
+      const float down = __uint_as_float((uint32_t)(127 - cj) << 23);
+      const float up = __uint_as_float((uint32_t)(127 + cj) << 23);
+      const int code = __builtin_amdgcn_cvt_pk_fp8_f32(r0 * down, r1 * down, 0, false);
+      const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+      r0 = fmaf(-back[0], up, r0);
+      r1 = fmaf(-back[1], up, r1);
+      *reinterpret_cast<uint16_t*>(pcs + ((t * 4 + j) * 4 + G) * 32 + 2 * c) = (uint16_t)code;
+    }
+    ct[t] = c0;
+  }
+  wave_sync_lds();
+  {
+    const int t = c & 3, j = c >> 2;
+    if (t < NT) {
+      const uint8_t* src = pcs + ((t * 4 + j) * 4 + G) * 32;
+      lf.a = pack8(*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 16));
+    } else {
+      lf.a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  wave_sync_lds();                                            // reads done before the region is reused
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    lf.sc[t] = t < NT ? __uint_as_float((uint32_t)(127 + ct[t < NT ? t : 0] - 4 * G) << 23) : 0.f;
 }
 
 __device__ __forceinline__ void load_kblock(KBlock& kb, const uint8_t* __restrict__ base, int lane) {
@@ -108,13 +225,20 @@ __device__ __forceinline__ void tile_mfma(TileAcc& acc, const QFrag& f, const v8
   }
 }
 
-// This lane's 16 heads of one tile: sum of w * max(d, 0) in a fixed order.
+__device__ __forceinline__ v4f lin_mfma(const LinFrag& lf, const v8i& b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lf.a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// This lane's 16 heads of one tile: sum of (w/2) |d| in a fixed order.  Its
+// share of the linear half (the piece output row it holds for the token, times
+// LinFrag::sc) is added right after, by the caller.
 __device__ __forceinline__ float tile_epilogue(const QFrag& f, const TileAcc& acc) {
   float part = 0.f;
 #pragma unroll
   for (int hg = 0; hg < 4; ++hg)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part = fmaf(f.w[hg * 4 + i], fmaxf(acc.d[hg][i], 0.f), part);
+    for (int i = 0; i < 4; ++i) part = fmaf(f.w[hg * 4 + i], fabsf(acc.d[hg][i]), part);
   return part;
 }
 
@@ -131,21 +255,70 @@ __device__ __forceinline__ float reduce_block(float p0, float p1, float p2, floa
 
 // Scores of one block for NT tokens: out[j] is token j's score at position
 // lane_pos(lane).  Work items (token, tile) are issued token-fastest and
-// pipelined two deep.
-template <int NT>
-__device__ __forceinline__ void block_scores(const QFrag* f, const KBlock& kb, float* out) {
+// pipelined two deep.  `bop(tl)` gives tile tl's B operand; it is asked for
+// one tile ahead, so when it reads LDS the read is covered by a tile of MFMAs
+// and only two tiles' operands are live.
+template <int NT, typename BOp>
+__device__ __forceinline__ void block_scores_with(const QFrag* f, const LinFrag& lf, BOp&& bop, float ks,
+                                                  float* out) {
   constexpr int NI = 4 * NT;
   float part[NT][4];
   TileAcc acc[2];
-  tile_mfma(acc[0], f[0], kb.b[0]);
+  v8i b[2];
+  b[0] = bop(0);
+  b[1] = bop(1);
+  if constexpr (NT == 1) {
+    v4f lin[2];
+    lin[0] = lin_mfma(lf, b[0]);
+    tile_mfma(acc[0], f[0], b[0]);
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    if (i + 1 < NI) tile_mfma(acc[(i + 1) & 1], f[(i + 1) % NT], kb.b[(i + 1) / NT]);
-    part[i % NT][i / NT] = tile_epilogue(f[i % NT], acc[i & 1]);
+    for (int i = 0; i < NI; ++i) {
+      if (i + 1 < NI) {
+        const int tn = i + 1;
+        if (tn >= 1 && tn + 1 < 4) b[(tn + 1) & 1] = bop(tn + 1);
+        lin[tn & 1] = lin_mfma(lf, b[tn & 1]);
+        tile_mfma(acc[(i + 1) & 1], f[0], b[tn & 1]);
+      }
+      part[0][i] = fmaf(lin[i & 1][0], lf.sc[0], tile_epilogue(f[0], acc[i & 1]));
+    }
+  } else {
+    // the linear MFMA of a tile goes with its last token's MFMAs; its terms are
+    // added once that token's epilogue is done (same operation order per token)
+    v4f lin;
+    tile_mfma(acc[0], f[0], b[0]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (i + 1 < NI) {
+        const int tn = (i + 1) / NT;
+        if ((i + 1) % NT == 0 && tn >= 1 && tn + 1 < 4) b[(tn + 1) & 1] = bop(tn + 1);
+        if ((i + 1) % NT == NT - 1) lin = lin_mfma(lf, b[tn & 1]);
+        tile_mfma(acc[(i + 1) & 1], f[(i + 1) % NT], b[tn & 1]);
+      }
+      const int t = i % NT, tl = i / NT;
+      part[t][tl] = tile_epilogue(f[t], acc[i & 1]);
+      if (t == NT - 1) {
+#pragma unroll
+        for (int u = 0; u < NT; ++u) part[u][tl] = fmaf(lin[u], lf.sc[u], part[u][tl]);
+      }
+    }
   }
 #pragma unroll
   for (int j = 0; j < NT; ++j)
-    out[j] = reduce_block(part[j][0], part[j][1], part[j][2], part[j][3]) * kb.ks;
+    out[j] = reduce_block(part[j][0], part[j][1], part[j][2], part[j][3]) * ks;
+}
+
+template <int NT>
+__device__ __forceinline__ void block_scores(const QFrag* f, const LinFrag& lf, const KBlock& kb, float* out) {
+  block_scores_with<NT>(f, lf, [&](int tl) { return kb.b[tl]; }, kb.ks, out);
+}
+
+// Tile tl's B operand straight from a staged block in LDS.
+__device__ __forceinline__ v8i lds_tile(const uint8_t* slot, int tl, int lane) {
+  const int c = lane & 15, G = lane >> 4;
+  const int r = tl * 16 + c;
+  const uint8_t* row = slot + r * kHeadDim;
+  return pack8(*reinterpret_cast<const uint4*>(row + ((G ^ (r & 7)) << 4)),
+               *reinterpret_cast<const uint4*>(row + (((4 + G) ^ (r & 7)) << 4)));
 }
 
 // ------------------------------------------------------ LDS staging --
@@ -209,14 +382,8 @@ __device__ __forceinline__ void stage_store(const StageRegs<NW>& st, uint8_t* sl
 }
 
 __device__ __forceinline__ void lds_kblock(KBlock& kb, const uint8_t* slot, int lane) {
-  const int c = lane & 15, G = lane >> 4;
 #pragma unroll
-  for (int tl = 0; tl < 4; ++tl) {
-    const int r = tl * 16 + c;
-    const uint8_t* row = slot + r * kHeadDim;
-    kb.b[tl] = pack8(*reinterpret_cast<const uint4*>(row + ((G ^ (r & 7)) << 4)),
-                     *reinterpret_cast<const uint4*>(row + (((4 + G) ^ (r & 7)) << 4)));
-  }
+  for (int tl = 0; tl < 4; ++tl) kb.b[tl] = lds_tile(slot, tl, lane);
   kb.ks = *reinterpret_cast<const float*>(slot + kCodeBytes + lane_pos(lane) * 4);
 }
 
@@ -270,7 +437,10 @@ __device__ __forceinline__ void wave_stage_store(const WaveStage& st, uint8_t* s
 constexpr int kScoreThreads = 256;              // four waves, both work splits
 constexpr int kPrefillTPW = IDX_PREFILL_TPW;    // query tokens per wave (prefill)
 constexpr int kPrefillTM = 4 * kPrefillTPW;     // query tokens per work-group (prefill)
+constexpr int kLinScratch = 4096;                // LDS per wave for make_lin
+constexpr int kPrefillLds = 2 * kBlockBytes + 4 * kLinScratch;
 constexpr int kScoreLds = 4 * kBlockBytes;
+static_assert(kScoreLds >= kPrefillLds && kBlockBytes >= kLinScratch, "LDS layout");
 
 // This step's new K rows, for scoring kernels that write them into the cache
 // themselves (decode batches of an F layer): row i of `k` belongs to query
@@ -296,7 +466,8 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
                                             const BatchArgs& b, float* __restrict__ logits,
                                             int64_t ld, int chunk_blocks, bool ident, uint8_t* lds,
                                             const NewRows& nk, float* __restrict__ samp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
   const int lb0 = bx * chunk_blocks;
   const int per_full = chunk_blocks / 4;        // chunk_blocks is a multiple of 4
   const int lb_full = lb0 + wave * per_full + lane;
@@ -360,6 +531,10 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
   WaveStage ring[NB];
 #pragma unroll
   for (int u = 0; u < NB - 1; ++u) stage(ring[u], min(u, mine - 1));
+  // the linear half's pieces, built in the wave's slot while the first loads
+  // are in flight
+  LinFrag lf;
+  make_lin<1>(lf, f, slot, lane);
 
   // New rows of this token's request that fall in this wave's blocks and in
   // its causal range (positions len-nq .. p_t): quantised here, patched into
@@ -429,7 +604,7 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       float v;
-      block_scores<1>(f, kb, &v);
+      block_scores<1>(f, lf, kb, &v);
       emit(j, v);
     }
   }
@@ -543,7 +718,8 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
   const int lb0 = bx * chunk_blocks;
   if (lb0 * kBlock >= n_max) return;
   const int nblk = min(chunk_blocks, (n_max - lb0 * kBlock + kBlock - 1) / kBlock);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
   const int lp = lane_pos(lane);
   uint8_t* kbuf0 = lds;
   uint8_t* kbuf1 = lds + kBlockBytes;
@@ -551,10 +727,11 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
   // 64), read before the q loads so the first K loads wait on it alone
   const int pbl = lane < nblk ? (int)phys_block(b, cache, r, lb0 + lane) : -1;
 
+  // Per token only wave-uniform integers are kept (the row pointers are formed
+  // where they are used), so they live in scalar registers.
   QFrag f[TPW];
   int nt[TPW];
-  float* out[TPW];
-  float* srow[TPW];                             // compact sample copies (or null)
+  int tk[TPW];                                  // batch index of the token (0 when absent)
   int sS[TPW], sSh[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
@@ -563,27 +740,27 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
     if (i < tb + pg.nt && t >= tok_lo && t < b.num_tokens) {
       load_q(f[j], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
       nt[j] = count(i);
-      out[j] = logits + (size_t)t * ld;
-      srow[j] = samp ? samp + (size_t)t * kMaxSample : nullptr;
+      tk[j] = t;
     } else {
       zero_q(f[j]);
       nt[j] = 0;
-      out[j] = logits;
-      srow[j] = nullptr;
+      tk[j] = 0;
     }
     sS[j] = sample_stride(nt[j]);
     sSh[j] = 31 - __clz(sS[j]);
   }
+  auto out = [&](int j) { return logits + (size_t)tk[j] * ld; };
+  auto srow = [&](int j) { return samp + (size_t)tk[j] * kMaxSample; };   // compact sample copy
 
   if (cache.num_blocks == 0) {                  // no K at all: every score is 0
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj)
       for (int j = 0; j < nblk; ++j) {
         const int s = (lb0 + j) * kBlock + lp;
-        if (s < nt[jj]) out[jj][s] = 0.f;
-        if (srow[jj] != nullptr) {
+        if (s < nt[jj]) out(jj)[s] = 0.f;
+        if (samp != nullptr) {
           const int sj = s >> sSh[jj];
-          if (s < nt[jj] && (s & (sS[jj] - 1)) == ((37 * sj + 11) & (sS[jj] - 1))) srow[jj][sj] = 0.f;
+          if (s < nt[jj] && (s & (sS[jj] - 1)) == ((37 * sj + 11) & (sS[jj] - 1))) srow(jj)[sj] = 0.f;
         }
       }
     return;
@@ -597,33 +774,32 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
 
   // Staging registers for blocks j+1 and j+2 alternate: block j+2's loads are
   // issued while block j is scored and reach LDS one iteration later.
-  StageRegs<NW> st[2];
-  stage(st[0], 0);
-  stage(st[1], 1);
-  stage_store<NW>(st[0], kbuf0);
-  stage(st[0], 2);
-  // Whole turns of the two-slot ring (an odd block count ends with one turn
-  // that only stages), so the loop body has no exit between its loads.
+  StageRegs<NW> st;
+  stage(st, 0);
+  LinFrag lf;
+  make_lin<TPW>(lf, f, lds + 2 * kBlockBytes + wave * kLinScratch, lane);
+  stage_store<NW>(st, kbuf0);
+  stage(st, 1);
   const int iters = (nblk + 1) & ~1;
   for (int j0 = 0; j0 < iters; j0 += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int j = j0 + u;
       __syncthreads();                     // block j in slot j&1; slot (j+1)&1 free
-      stage_store<NW>(st[(u + 1) & 1], (j + 1) & 1 ? kbuf1 : kbuf0);   // unused past the end
-      stage(st[(u + 1) & 1], j + 3);
+      stage_store<NW>(st, (j + 1) & 1 ? kbuf1 : kbuf0);   // unused past the end
+      stage(st, j + 2);
       if (j >= nblk) continue;
-      KBlock kb;
-      lds_kblock(kb, j & 1 ? kbuf1 : kbuf0, lane);
+      const uint8_t* kslot = j & 1 ? kbuf1 : kbuf0;
+      const float ks = *reinterpret_cast<const float*>(kslot + kCodeBytes + lp * 4);
       float v[TPW];
-      block_scores<TPW>(f, kb, v);
+      block_scores_with<TPW>(f, lf, [&](int tl) { return lds_tile(kslot, tl, lane); }, ks, v);
       const int s = (lb0 + j) * kBlock + lp;
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj) {
-        if (s < nt[jj]) out[jj][s] = v[jj];
-        if (srow[jj] != nullptr) {
+        if (s < nt[jj]) out(jj)[s] = v[jj];
+        if (samp != nullptr) {
           const int sj = s >> sSh[jj];
-          if (s < nt[jj] && (s & (sS[jj] - 1)) == ((37 * sj + 11) & (sS[jj] - 1))) srow[jj][sj] = v[jj];
+          if (s < nt[jj] && (s & (sS[jj] - 1)) == ((37 * sj + 11) & (sS[jj] - 1))) srow(jj)[sj] = v[jj];
         }
       }
     }
@@ -668,10 +844,12 @@ __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_
                         ident != 0, lds, nk, samp);
 }
 
-__global__ __launch_bounds__(kScoreThreads) void score_prefill_kernel(
+// two work-groups per CU: the register budget is 256 VGPRs
+__global__ __launch_bounds__(kScoreThreads)
+__attribute__((amdgpu_waves_per_eu(2))) void score_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int chunk_blocks, int gpr, float* samp) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBlockBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kPrefillLds];
   int cx, ry;
   xcd_spread(&cx, &ry);
   prefill_body(cx, ry, 0, q8, w, cache, b, logits, ld, chunk_blocks, gpr, lds, samp);
@@ -681,7 +859,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_prefill_kernel(
 // decode split, the rest are prefill groups; the two kinds of work-group share
 // the machine (HBM-bound decode beside MFMA-bound prefill).
 template <int NB>
-__global__ __launch_bounds__(kScoreThreads) void score_mixed_kernel(
+__global__ __launch_bounds__(kScoreThreads)
+__attribute__((amdgpu_waves_per_eu(2))) void score_mixed_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int dec_tokens, int dec_chunk_blocks,
     int pre_chunk_blocks, int gpr, float* samp) {
