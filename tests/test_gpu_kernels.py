@@ -187,6 +187,57 @@ def test_decode_and_prefill_kernels_agree_bitwise(env):
     assert np.array_equal(a[0].cpu().numpy().view(np.uint32), b[2].cpu().numpy().view(np.uint32))
 
 
+def _adversarial_q_w(rng, T):
+    """q codes and folded weights chosen to stress the scores' linear half.
+
+    The scoring kernels split w*max(d, 0) into (w/2)|d| + (w/2)d and contract
+    the second half as u . k with u = sum_h (w_h/2) q_h held in four E4M3
+    pieces; these rows give u a wide dynamic range, saturated codes, exact
+    cancellation and weights over several decades.
+    """
+    H, D = 64, 128
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    q8 = rng.choice(finite, size=(T, H, D)).astype(np.uint8)
+    # four decades of weights, up to ~10x the folded weights of N(0,1) data (larger ones make
+    # the plain fp32 head sum itself miss the tolerance where the terms cancel)
+    w = (rng.choice([-1.0, 1.0], size=(T, H)) * 10.0 ** rng.uniform(-7, -3, size=(T, H))).astype(np.float32)
+    q8[0] = 0x7E                                  # every code +448: u is w-weighted sum of 448s
+    q8[1, :, :] = 0x01                            # smallest subnormal everywhere ...
+    q8[1, :, 0] = 0x7E                            # ... but one dimension at +448: u spans ~2^18
+    w[2, 1::2] = -w[2, 0::2]                      # pairs of heads with opposite weights ...
+    q8[2, 1::2] = q8[2, 0::2]                     # ... and equal q rows: every score is 0 (u = 0)
+    q8[3] = np.where(rng.random((H, D)) < 0.5, 0x80, q8[3])   # half the codes -0
+    w[4] = 0.0                                    # all weights zero
+    w[5] = np.float32(1e-30)                      # tiny weights (u far below the clamp range)
+    return q8, w
+
+
+def test_logits_linear_half_adversarial(env):
+    """Scores from adversarial q / w stay within tolerance of the oracle, and the
+    decode and prefill kernels give the same bits for them."""
+    m, torch = env
+    L, T = 3000, 12
+    wl = random_batch(2005, [L], T, k=64)          # one request, T new tokens (prefill kernel)
+    dev = device_layer(m, torch, wl, 0, with_new=True)
+    orc = oracle_layer(wl, 0)
+    assert np.array_equal(dev["cache"].tensor.cpu().numpy(), orc["cache"])
+    rng = np.random.default_rng(2005)
+    q8, w = _adversarial_q_w(rng, T)
+    batch = device_batch(m, wl)
+    got = m.idx_logits(torch.from_numpy(q8).cuda(), torch.from_numpy(w).cuda(), dev["cache"], batch)
+    got = got.cpu().numpy()
+    want = oracle.logits.logits(q8, w, orc["cache"], oracle_batch(wl))
+    for t, row in want.items():
+        check_logits_row(got[t, :row.shape[0]], row, f"adversarial token {t}")
+    assert np.all(got[4, :L - T + 5].view(np.uint32) == 0)   # +0 exactly
+    # the last token again as a one-token decode batch (decode kernel): same bits
+    wl1 = random_batch(2005, [L], 1, k=64)
+    d1 = device_layer(m, torch, wl1, 0, with_new=True)
+    one = m.idx_logits(torch.from_numpy(q8[T - 1:]).cuda(), torch.from_numpy(w[T - 1:]).cuda(),
+                       d1["cache"], device_batch(m, wl1)).cpu().numpy()
+    assert np.array_equal(one[0, :L].view(np.uint32), got[T - 1, :L].view(np.uint32))
+
+
 @pytest.mark.parametrize("lengths,new,splits", [
     # decodes then two prefill chunks: prefill groups numbered across the batch
     ([5000, 3000, 9000, 1200, 2500], [1, 1, 1, 300, 40], (0, 3, 5, None)),
