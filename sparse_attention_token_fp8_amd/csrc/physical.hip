@@ -17,8 +17,24 @@ namespace {
 
 // One work-group per token; each thread converts 8 consecutive entries (two
 // 16-byte loads and stores when the row is 16-byte aligned), so the block-table
-// reads of a row are all in flight together.
+// reads of a row are all in flight together.  The row's first entries are
+// loaded before the token's request is looked up, so the two round trips
+// overlap; the valid count is summed with ballots (no block scan).  (Two or
+// four tokens per work-group measured slower.)
 constexpr int kPhysPer = 8;
+
+__device__ __forceinline__ void phys_load(int* pos, const int32_t* __restrict__ in, int jb, int k,
+                                          bool vec) {
+  if (vec && jb + kPhysPer <= k) {
+    const int4 a = *reinterpret_cast<const int4*>(in + jb);
+    const int4 d = *reinterpret_cast<const int4*>(in + jb + 4);
+    pos[0] = a.x; pos[1] = a.y; pos[2] = a.z; pos[3] = a.w;
+    pos[4] = d.x; pos[5] = d.y; pos[6] = d.z; pos[7] = d.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPhysPer; ++e) pos[e] = jb + e < k ? in[jb + e] : -1;
+  }
+}
 
 __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restrict__ logical,
                                                           int64_t ldl, BatchArgs b, CacheArgs c,
@@ -26,26 +42,17 @@ __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restr
                                                           int64_t stride_rows,
                                                           int32_t* __restrict__ phys, int64_t ldp,
                                                           int32_t* __restrict__ valid) {
+  constexpr int kStep = kThreads * kPhysPer;
   const int t = blockIdx.x;
-  const TokenPos tp = token_pos_wave(b, t);
-  __shared__ uint32_t scratch[8];
   const int32_t* in = logical + (size_t)t * ldl;
   int32_t* out = phys + (size_t)t * ldp;
   const bool vec = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
-  uint32_t cnt = 0;
-  for (int j0 = 0; j0 < k; j0 += kThreads * kPhysPer) {
+  int pos[kPhysPer];
+  phys_load(pos, in, (int)threadIdx.x * kPhysPer, k, vec);
+  const TokenPos tp = token_pos_wave(b, t);
+  uint32_t cnt = 0;                             // valid entries of this wave (uniform)
+  for (int j0 = 0; j0 < k; j0 += kStep) {
     const int jb = j0 + (int)threadIdx.x * kPhysPer;
-    const bool full = vec && jb + kPhysPer <= k;
-    int pos[kPhysPer];
-    if (full) {
-      const int4 a = *reinterpret_cast<const int4*>(in + jb);
-      const int4 d = *reinterpret_cast<const int4*>(in + jb + 4);
-      pos[0] = a.x; pos[1] = a.y; pos[2] = a.z; pos[3] = a.w;
-      pos[4] = d.x; pos[5] = d.y; pos[6] = d.z; pos[7] = d.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < kPhysPer; ++e) pos[e] = jb + e < k ? in[jb + e] : -1;
-    }
     int32_t o[kPhysPer];
 #pragma unroll
     for (int e = 0; e < kPhysPer; ++e) {
@@ -54,9 +61,9 @@ __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restr
         const int64_t blk = phys_block(b, c, tp.r, pos[e] / block_size);
         if (blk >= 0) o[e] = (int32_t)(blk * stride_rows + pos[e] % block_size);
       }
-      cnt += (jb + e < k && o[e] >= 0) ? 1u : 0u;
+      cnt += (uint32_t)__popcll(__ballot(jb + e < k && o[e] >= 0));
     }
-    if (full) {
+    if (vec && jb + kPhysPer <= k) {
       *reinterpret_cast<int4*>(out + jb) = make_int4(o[0], o[1], o[2], o[3]);
       *reinterpret_cast<int4*>(out + jb + 4) = make_int4(o[4], o[5], o[6], o[7]);
     } else {
@@ -64,10 +71,19 @@ __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restr
       for (int e = 0; e < kPhysPer; ++e)
         if (jb + e < k) out[jb + e] = o[e];
     }
+    if (j0 + kStep < k) phys_load(pos, in, jb + kStep, k, vec);
   }
-  uint32_t total;
-  (void)block_scan_excl<kThreads>(cnt, &total, scratch);
-  if (valid && threadIdx.x == 0) valid[t] = (int32_t)total;
+  if (valid != nullptr) {
+    __shared__ uint32_t part[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t total = 0;
+#pragma unroll
+      for (int i = 0; i < kThreads / 64; ++i) total += part[i];
+      valid[t] = (int32_t)total;
+    }
+  }
 }
 
 }  // namespace
