@@ -86,15 +86,20 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
   float sv[sample_per<kRowThreads>()];
   int ns = 0;
   if (sampled) ns = sample_load<kRowThreads>(row, n, sv);   // first: tau waits on these only
-  float v[kBatch];
+  // Two batches in flight: while one is compacted the next two are loading.
+  // Loads past the row re-read its last position (the pass test drops them),
+  // so no load sits behind a branch and the compiler waits only for the batch
+  // it needs.
+  auto load_batch = [&](float* v, int base) {
 #pragma unroll
-  for (int e = 0; e < kBatch; ++e) {
-    const int s = e * kRowThreads + threadIdx.x;
-    v[e] = s < n ? row[s] : 0.f;
-  }
+    for (int e = 0; e < kBatch; ++e) v[e] = row[min(base + e * kRowThreads + (int)threadIdx.x, n - 1)];
+  };
+  float va[kBatch], vb[kBatch];
+  load_batch(va, 0);
+  load_batch(vb, kStep);
   const uint32_t tau = sampled ? sample_tau<kRowThreads>(sv, ns, n, k, hist, scratch) : 0u;
   uint32_t C = 0;
-  for (int base = 0; base < n; base += kStep) {
+  auto batch = [&](float* v, int base) {
     uint32_t key[kBatch];
     bool pass[kBatch];
 #pragma unroll
@@ -102,14 +107,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
       key[e] = order_key(v[e]);
       pass[e] = base + e * kRowThreads + (int)threadIdx.x < n && key[e] >= tau;
     }
-    if (base + kStep < n) {                     // next batch in flight during the compaction
-#pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        const int s = base + kStep + e * kRowThreads + threadIdx.x;
-        v[e] = s < n ? row[s] : 0.f;
-      }
-    }
+    load_batch(v, base + 2 * kStep);            // two batches ahead
     C += compact_ordered<kRowThreads, kBatch>(key, pass, base, C, ckey, cpos, kRowCap, table);
+  };
+  for (int base = 0; base < n; base += 2 * kStep) {
+    batch(va, base);
+    if (base + kStep < n) batch(vb, base + kStep);
   }
   finish_row<kRowThreads>(row, n, k, C, kRowCap, ckey, cpos, out, hist, bucket, scratch);
 }
