@@ -117,15 +117,16 @@ __device__ __forceinline__ void wave_sync_lds() {
 // smallest with max|u| <= 448 * 2^c (clamped to [-100, 100]); piece j codes the
 // residual times 2^-(c-4j) to the nearest E4M3 value and the residual loses it.
 // Every step runs in a fixed order, so a token's pieces do not depend on the
-// other tokens of the wave or on which kernel builds them.
+// other tokens of the wave or on which kernel builds them.  The tokens go
+// through each step together, so their LDS round trips overlap.
 template <int NT>
 __device__ __forceinline__ void make_lin(LinFrag& lf, const QFrag* f, uint8_t* scratch, int lane) {
+  static_assert(NT <= 2, "4 KB of scratch holds two tokens' partial sums");
   const int c = lane & 15, G = lane >> 4;
-  float* part = reinterpret_cast<float*>(scratch);           // [G][quad][32] fp32: 2 KB
-  uint8_t* pcs = scratch + 2048;                             // [t][j][G][32] codes: 2 KB
-  int ct[NT];
+  float u0[NT], u1[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
+    float* part = reinterpret_cast<float*>(scratch) + t * 512;   // [G][quad][32] fp32: 2 KB
     float p[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) p[k] = 0.f;
@@ -154,23 +155,35 @@ __device__ __forceinline__ void make_lin(LinFrag& lf, const QFrag* f, uint8_t* s
 #pragma unroll
       for (int q = 0; q < 8; ++q) dst[q] = make_float4(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
     }
-    wave_sync_lds();
-    float u0, u1;
-    {
-      const float2 a0 = *reinterpret_cast<const float2*>(part + (G * 4 + 0) * 32 + 2 * c);
-      const float2 a1 = *reinterpret_cast<const float2*>(part + (G * 4 + 1) * 32 + 2 * c);
-      const float2 a2 = *reinterpret_cast<const float2*>(part + (G * 4 + 2) * 32 + 2 * c);
-      const float2 a3 = *reinterpret_cast<const float2*>(part + (G * 4 + 3) * 32 + 2 * c);
-      u0 = ((a0.x + a1.x) + a2.x) + a3.x;
-      u1 = ((a0.y + a1.y) + a2.y) + a3.y;
-    }
-    wave_sync_lds();                                          // part is reused by the next token
-    uint32_t mb = max(__float_as_uint(fabsf(u0)), __float_as_uint(fabsf(u1)));
+  }
+  wave_sync_lds();
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off));
-    int c0 = (int)((mb >> 23) & 0xFF) - 127 - 8 + ((mb & 0x7FFFFF) > 0x600000 ? 1 : 0);
+  for (int t = 0; t < NT; ++t) {
+    const float* part = reinterpret_cast<const float*>(scratch) + t * 512;
+    const float2 a0 = *reinterpret_cast<const float2*>(part + (G * 4 + 0) * 32 + 2 * c);
+    const float2 a1 = *reinterpret_cast<const float2*>(part + (G * 4 + 1) * 32 + 2 * c);
+    const float2 a2 = *reinterpret_cast<const float2*>(part + (G * 4 + 2) * 32 + 2 * c);
+    const float2 a3 = *reinterpret_cast<const float2*>(part + (G * 4 + 3) * 32 + 2 * c);
+    u0[t] = ((a0.x + a1.x) + a2.x) + a3.x;
+    u1[t] = ((a0.y + a1.y) + a2.y) + a3.y;
+  }
+  wave_sync_lds();                                            // the partial sums' space takes the codes
+  uint8_t* pcs = scratch;                                     // [t][j][G][32] codes
+  int ct[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    // max |u| over the 128 k values: rotations within each row of 16 lanes,
+    // then the four rows (max is exact in any order)
+    int mb = (int)max(__float_as_uint(fabsf(u0[t])), __float_as_uint(fabsf(u1[t])));
+    mb = max((uint32_t)mb, (uint32_t)__builtin_amdgcn_update_dpp(0, mb, 0x128, 0xF, 0xF, false));
+    mb = max((uint32_t)mb, (uint32_t)__builtin_amdgcn_update_dpp(0, mb, 0x124, 0xF, 0xF, false));
+    mb = max((uint32_t)mb, (uint32_t)__builtin_amdgcn_update_dpp(0, mb, 0x122, 0xF, 0xF, false));
+    mb = max((uint32_t)mb, (uint32_t)__builtin_amdgcn_update_dpp(0, mb, 0x121, 0xF, 0xF, false));
+    const uint32_t m = max(max((uint32_t)__builtin_amdgcn_readlane(mb, 0), (uint32_t)__builtin_amdgcn_readlane(mb, 16)),
+                           max((uint32_t)__builtin_amdgcn_readlane(mb, 32), (uint32_t)__builtin_amdgcn_readlane(mb, 48)));
+    int c0 = (int)((m >> 23) & 0xFF) - 127 - 8 + ((m & 0x7FFFFF) > 0x600000 ? 1 : 0);
     c0 = min(100, max(-100, c0));
-    float r0 = u0, r1 = u1;
+    float r0 = u0[t], r1 = u1[t];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cj = c0 - 4 * j;
