@@ -57,6 +57,8 @@ def parse():
                    help="skip the q-fold / physical-conversion / mixed-batch / graph measurements")
     p.add_argument("--cpu-sample", type=int, default=8, help="query tokens the oracle scores")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed oracle work")
+    p.add_argument("--stack", action="store_true",
+                   help="also time the 16-layer IndexCache stack at full size (FSSS x4 and all F)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain 1 GiB device copies (counter calibration)")
     return p.parse_args()
@@ -232,6 +234,45 @@ def _layers(m, torch, wl):
         nb, ns = wl.new_rows(l)
         layers.append((torch.from_numpy(nb.view(np.int16)).cuda(), cache, q8, w))
     return layers, torch.from_numpy(ns).cuda()
+
+
+def run_stack(m, torch, steps=20, warmup=3):
+    """stack-16L-32x64k: the 16-layer stack (idx_indexcache_stack) with the FSSS x4
+    schedule and with every layer F.  Layer 0's context K is written once and copied
+    into 16 distinct caches, so every F layer reads its own 277 MB."""
+    import concurrent.futures as cf
+    from synth import CONFIGS, make_workload
+    t0 = time.time()
+    wl = make_workload(CONFIGS["stack-16L-32x64k"])
+    batch = m.Batch(wl.seq_lens, wl.query_start_loc, wl.block_table)
+    cache = m.KCache(wl.num_blocks, fill=0)
+    nw = max(1, min(16, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(nw) as ex:
+        for kb, slots in ex.map(lambda r: wl.ctx_rows(0, [r]), range(wl.num_reqs)):
+            m.idx_quant_write_k(torch.from_numpy(kb.view(np.int16)).cuda(),
+                                torch.from_numpy(slots).cuda(), cache)
+    layers = []
+    for l in range(wl.num_layers):
+        c = cache if l == 0 else m.KCache(wl.num_blocks, tensor=cache.tensor.clone())
+        q8, w, _ = m.idx_quant_q_fold_w(torch.from_numpy(wl.q_bits(l).view(np.int16)).cuda(),
+                                        torch.from_numpy(wl.w_raw(l)).cuda())
+        nb, ns = wl.new_rows(l)
+        layers.append((torch.from_numpy(nb.view(np.int16)).cuda(), c, q8, w))
+    slots = torch.from_numpy(ns).cuda()
+    topk = torch.empty((wl.num_tokens, wl.k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(m.idx_score_topk_workspace_size(batch, wl.k), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"setup {wl.name}: {time.time() - t0:.1f}s, {wl.num_layers} caches")
+    fsss = m.idx_layer_schedule(True, wl.pattern, 1, 2, wl.num_layers)
+    res = {}
+    for name, full in (("fsss", fsss), ("all_f", [True] * wl.num_layers)):
+        res[name] = time_loop(torch, lambda i: m.idx_indexcache_stack(
+            layers, full, True, slots, batch, wl.k, topk, workspace=ws), steps, warmup)
+    log(f"{wl.name}: FSSS x4 {res['fsss'] * 1e3:.1f} us, all F {res['all_f'] * 1e3:.1f} us per stack")
+    return {"workload": wl.name, "layers": wl.num_layers, "f_layers": [i for i, f in enumerate(fsss) if f],
+            "ms_fsss": round(res["fsss"], 5), "ms_all_f": round(res["all_f"], 5),
+            "speedup": round(res["all_f"] / res["fsss"], 3),
+            "query_tokens_per_s": round(wl.num_tokens / (res["fsss"] * 1e-3), 1)}
 
 
 def run_next_rows(m, torch, steps=20, warmup=3):
@@ -421,6 +462,8 @@ def main():
             out["next_rows"] = run_next_rows(m, torch)
         except Exception as e:                         # reported, never fatal to the bench line
             out["next_rows"] = {"error": f"{type(e).__name__}: {e}"}
+    if args.stack:
+        out["stack"] = run_stack(m, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample, args.cpu_seconds)
     print(json.dumps(out), flush=True)
