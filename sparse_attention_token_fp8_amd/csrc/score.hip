@@ -443,6 +443,9 @@ __device__ __forceinline__ void wave_stage_store(const WaveStage& st, uint8_t* s
 #ifndef IDX_PREFILL_TPW
 #define IDX_PREFILL_TPW 2
 #endif
+#ifndef IDX_PREFILL_MAX_CHUNK
+#define IDX_PREFILL_MAX_CHUNK 64
+#endif
 #ifndef IDX_DECODE_WAVES_PER_EU
 #define IDX_DECODE_WAVES_PER_EU 2
 #endif
@@ -450,6 +453,7 @@ __device__ __forceinline__ void wave_stage_store(const WaveStage& st, uint8_t* s
 constexpr int kScoreThreads = 256;              // four waves, both work splits
 constexpr int kPrefillTPW = IDX_PREFILL_TPW;    // query tokens per wave (prefill)
 constexpr int kPrefillTM = 4 * kPrefillTPW;     // query tokens per work-group (prefill)
+constexpr int kPrefillWin = (IDX_PREFILL_MAX_CHUNK + 63) / 64;   // block-id registers per lane (prefill)
 constexpr int kLinScratch = 4096;                // LDS per wave for make_lin
 constexpr int kPrefillLds = 2 * kBlockBytes + 4 * kLinScratch;
 constexpr int kScoreLds = 4 * kBlockBytes;
@@ -736,9 +740,12 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
   const int lp = lane_pos(lane);
   uint8_t* kbuf0 = lds;
   uint8_t* kbuf1 = lds + kBlockBytes;
-  // lane j holds the physical block of the chunk's j-th block (chunk_blocks <=
-  // 64), read before the q loads so the first K loads wait on it alone
-  const int pbl = lane < nblk ? (int)phys_block(b, cache, r, lb0 + lane) : -1;
+  // pbl[w] of lane i holds the physical block of the chunk's (64w + i)-th
+  // block, read before the q loads so the first K loads wait on them alone
+  int pbl[kPrefillWin];
+#pragma unroll
+  for (int w = 0; w < kPrefillWin; ++w)
+    pbl[w] = 64 * w + lane < nblk ? (int)phys_block(b, cache, r, lb0 + 64 * w + lane) : -1;
 
   // Per token only wave-uniform integers are kept (the row pointers are formed
   // where they are used), so they live in scalar registers.
@@ -781,7 +788,11 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
   // block min(j, nblk-1) (past the last block it is re-read, from L2, so the
   // loop body issues its loads unconditionally)
   auto stage = [&](StageRegs<NW>& st, int j) {
-    const int pb = __builtin_amdgcn_readlane(pbl, min(j, nblk - 1));
+    const int jc = min(j, nblk - 1);
+    int v = pbl[0];
+#pragma unroll
+    for (int w = 1; w < kPrefillWin; ++w) v = (jc >> 6) == w ? pbl[w] : v;   // wave-uniform choice
+    const int pb = __builtin_amdgcn_readlane(v, jc & 63);
     stage_load<NW>(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes, pb >= 0);
   };
 
@@ -904,10 +915,6 @@ int decode_chunk_blocks(int max_seq_len, int64_t tokens) {
 
 int prefill_chunk_blocks(const BatchArgs& b, int64_t groups) {
   // aim for a few thousand work-groups; never more blocks than the longest row needs
-#ifndef IDX_PREFILL_MAX_CHUNK
-#define IDX_PREFILL_MAX_CHUNK 64
-#endif
-  static_assert(IDX_PREFILL_MAX_CHUNK <= 64, "a wave holds the chunk's block ids, one per lane");
   int cb = IDX_PREFILL_MAX_CHUNK;
   while (cb > 4 && groups * ((b.max_seq_len + cb * kBlock - 1) / (cb * kBlock)) < 2048) cb >>= 1;
   return cb;
