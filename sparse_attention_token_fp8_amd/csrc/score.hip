@@ -454,6 +454,7 @@ constexpr int kScoreThreads = 256;              // four waves, both work splits
 constexpr int kPrefillTPW = IDX_PREFILL_TPW;    // query tokens per wave (prefill)
 constexpr int kPrefillTM = 4 * kPrefillTPW;     // query tokens per work-group (prefill)
 constexpr int kPrefillWin = (IDX_PREFILL_MAX_CHUNK + 63) / 64;   // block-id registers per lane (prefill)
+static_assert(IDX_PREFILL_MAX_CHUNK >= 4 && IDX_PREFILL_MAX_CHUNK <= 256, "prefill chunk of 4..256 blocks");
 constexpr int kLinScratch = 4096;                // LDS per wave for make_lin
 constexpr int kPrefillLds = 2 * kBlockBytes + 4 * kLinScratch;
 constexpr int kScoreLds = 4 * kBlockBytes;
