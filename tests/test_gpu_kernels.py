@@ -238,6 +238,31 @@ def test_logits_linear_half_adversarial(env):
     assert np.array_equal(one[0, :L].view(np.uint32), got[T - 1, :L].view(np.uint32))
 
 
+@pytest.mark.parametrize("new", [1, 37])
+def test_logits_absent_blocks(env, new):
+    """Block-table entries of -1 or outside the pool: the call completes, and the
+    scores of positions in the other blocks equal the oracle's (positions in an
+    absent block have unspecified values)."""
+    m, torch = env
+    wl = random_batch(2006, [4000, 2500], new, k=64)
+    dev = device_layer(m, torch, wl, 0, with_new=True)
+    orc = oracle_layer(wl, 0)
+    bt = wl.block_table.copy()
+    absent = {(0, 3): -1, (0, 40): wl.num_blocks, (1, 0): -7, (1, 20): wl.num_blocks + 100}
+    for (r, lb), v in absent.items():
+        bt[r, lb] = v
+    batch = m.Batch(wl.seq_lens, wl.query_start_loc, bt)
+    got = m.idx_logits(dev["q8"], dev["w"], dev["cache"], batch).cpu().numpy()
+    want = oracle.logits.logits(orc["q8"], orc["w"], orc["cache"], oracle_batch(wl))
+    for t, row in want.items():
+        r = int(np.searchsorted(wl.query_start_loc, t, side="right") - 1)
+        keep = np.ones(row.shape[0], bool)
+        for (rr, lb), _ in absent.items():
+            if rr == r:
+                keep[lb * 64:(lb + 1) * 64] = False
+        check_logits_row(got[t, :row.shape[0]][keep], row[keep], f"absent blocks, token {t}")
+
+
 @pytest.mark.parametrize("lengths,new,splits", [
     # decodes then two prefill chunks: prefill groups numbered across the batch
     ([5000, 3000, 9000, 1200, 2500], [1, 1, 1, 300, 40], (0, 3, 5, None)),
