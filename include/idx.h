@@ -146,7 +146,12 @@ idx_status_t idx_quant_q_fold_w(const uint16_t* q_bf16, const float* w_raw, int6
  *   q_fp8   device uint8 [num_tokens, 64, 128], 16-byte aligned
  *   w       device fp32 [num_tokens, 64] (q_scale etc. already folded in)
  *   logits  device fp32, logits_stride >= max_seq_len
- * Sums are fp32 (fp8 x fp8 products accumulated by the matrix cores).
+ * Sums are fp32 (fp8 x fp8 products accumulated by the matrix cores).  The
+ * kernels evaluate w * max(d, 0) as (w/2) |d| + (w/2) d, the second half
+ * through sum_h (w_h/2) q8[t,h,:] held in four fp8 pieces (about 16
+ * significant bits), so scores carry rounding of order 1e-6 relative to the
+ * sum of |terms|.  A token's scores are the same bits whichever kernel, batch
+ * composition or entry point computes them.
  */
 idx_status_t idx_logits(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
                         idx_kcache_t cache, const idx_batch_t* batch,
