@@ -22,6 +22,7 @@ sources are byte-identical to the ones that summary was taken on (else null).
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -75,12 +76,20 @@ def score_build_flags():
             for f in mod.COMMON + mod.EXTRA.get("score.hip", [])]
 
 
+def _code_only(text):
+    """Source text without comments and with runs of blank space collapsed, so an
+    edit of comments alone keeps the digest."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def sources_digest():
-    """Digest of the scoring kernels' sources and their compile flags."""
+    """Digest of the scoring kernels' code (comments aside) and their compile flags."""
     h = hashlib.sha256()
     for f in SCORE_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     h.update(" ".join(score_build_flags()).encode())
     return h.hexdigest()[:16]
 

@@ -797,8 +797,8 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
     stage_load<NW>(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes, pb >= 0);
   };
 
-  // Staging registers for blocks j+1 and j+2 alternate: block j+2's loads are
-  // issued while block j is scored and reach LDS one iteration later.
+  // One set of staging registers: in iteration j it stores block j+1 into LDS
+  // and takes block j+2's loads, which are in flight while block j is scored.
   StageRegs<NW> st;
   stage(st, 0);
   LinFrag lf;
