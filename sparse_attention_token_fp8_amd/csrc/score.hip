@@ -213,23 +213,6 @@ __device__ __forceinline__ void make_lin(LinFrag& lf, const QFrag* f, uint8_t* s
     lf.sc[t] = t < NT ? __uint_as_float((uint32_t)(127 + ct[t < NT ? t : 0] - 4 * G) << 23) : 0.f;
 }
 
-__device__ __forceinline__ void load_kblock(KBlock& kb, const uint8_t* __restrict__ base, int lane) {
-  const int c = lane & 15, G = lane >> 4;
-  if (base == nullptr) {
-#pragma unroll
-    for (int tl = 0; tl < 4; ++tl) kb.b[tl] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    kb.ks = 0.f;
-    return;
-  }
-#pragma unroll
-  for (int tl = 0; tl < 4; ++tl) {
-    const uint8_t* row = base + (tl * 16 + c) * kHeadDim;
-    kb.b[tl] = pack8(*reinterpret_cast<const uint4*>(row + 16 * G),
-                     *reinterpret_cast<const uint4*>(row + 64 + 16 * G));
-  }
-  kb.ks = *reinterpret_cast<const float*>(base + kCodeBytes + lane_pos(lane) * 4);
-}
-
 __device__ __forceinline__ void tile_mfma(TileAcc& acc, const QFrag& f, const v8i& b) {
 #pragma unroll
   for (int hg = 0; hg < 4; ++hg) {
@@ -719,7 +702,7 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
                                              const BatchArgs& b, float* __restrict__ logits,
                                              int64_t ld, int chunk_blocks, int gpr,
                                              uint8_t* lds, float* __restrict__ samp) {
-  constexpr int TPW = kPrefillTPW, NW = 4, TM = kPrefillTM;
+  constexpr int TPW = kPrefillTPW, NW = 4;
   PrefillGroup pg;
   if (!prefill_group(b, gy, tok_lo, gpr, &pg)) return;
   const int r = pg.r;
