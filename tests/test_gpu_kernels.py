@@ -170,6 +170,24 @@ def test_logits_prefill_ragged(env):
     _run_logits(m, torch, wl, "prefill")
 
 
+def test_logits_decode_many_ragged(env):
+    """40 one-token requests of very different lengths (1 to 6000 positions)
+    against the oracle, and the same bits as each request scored on its own."""
+    m, torch = env
+    lengths = np.random.default_rng(2007).integers(1, 6000, 40).tolist()
+    lengths[3] = 1
+    lengths[17] = 64
+    lengths[29] = 65
+    wl = random_batch(2007, lengths, 1, k=64)
+    say("logits decode many ragged", wl.seq_lens.tolist())
+    dev, _, _, got, _ = _run_logits(m, torch, wl, "decode many ragged")
+    for r in (0, 3, 17, 29, 39):                      # one request per call
+        one = m.Batch(wl.seq_lens[r:r + 1], [0, 1], wl.block_table[r:r + 1])
+        g1 = m.idx_logits(dev["q8"][r:r + 1], dev["w"][r:r + 1], dev["cache"], one).cpu().numpy()
+        L = int(wl.seq_lens[r])
+        assert np.array_equal(g1[0, :L].view(np.uint32), got[r, :L].view(np.uint32)), r
+
+
 def test_decode_and_prefill_kernels_agree_bitwise(env):
     m, torch = env
     L = 2000
@@ -439,8 +457,11 @@ def test_layer_k_write_inside_scoring(env):
     scored from the cache), and requests with three new tokens each, scored
     with the decode split (rows written inside scoring) and without it."""
     m, torch = env
+    many_lengths = np.random.default_rng(7003).integers(1, 6000, 40).tolist()
     cases = [(random_batch(7001, [3000, 9000, 20000, 700, 1500], 1, k=512), [0], [3]),
-             (random_batch(7002, [2500, 9000, 4000], 3, k=256), [9, 0], [])]
+             (random_batch(7002, [2500, 9000, 4000], 3, k=256), [9, 0], []),
+             # 40 requests of one new token, 1 to 6000 positions
+             (random_batch(7003, many_lengths, 1, k=256), [0], [5])]
     for wl, splits, pad in cases:
         for nd in splits:
             say("layer K write", wl.seq_lens.tolist(), wl.new_tokens.tolist(), "decode tokens", nd)
