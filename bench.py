@@ -179,6 +179,24 @@ def time_loop(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps   # ms
 
 
+def step_quantiles(torch, fn, steps, warmup):
+    """p10 / median / p90 of single steps, each bracketed by its own events on the
+    current stream (a separate loop from the mean, which uses one event pair)."""
+    for i in range(warmup):
+        fn(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.sort(np.array([a.elapsed_time(b) for a, b in ev]))
+    q = lambda f: round(float(t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))]), 5)
+    return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "steps": steps}
+
+
 def run_workload(m, torch, name, args):
     from synth import CONFIGS, make_workload
     wl = make_workload(CONFIGS[name])
@@ -200,6 +218,7 @@ def run_workload(m, torch, name, args):
 
     ms_step = time_loop(torch, step, args.steps, args.warmup)
     ms_logits = time_loop(torch, score_only, args.steps, args.warmup)
+    quant = step_quantiles(torch, step, max(args.steps, 50), args.warmup)
     a = algorithmic(wl)
     if decode:
         ach = a["logits_bytes"] / (ms_logits * 1e-3) / 1e9
@@ -216,7 +235,7 @@ def run_workload(m, torch, name, args):
                 "kernel": "score_prefill_kernel (idx_logits)", "ms_per_launch": round(ms_logits, 5),
                 "flops_per_launch": a["flops"]}
     step_gbs = a["step_bytes"] / (ms_step * 1e-3) / 1e9
-    res = dict(workload=name, tokens=wl.num_tokens, ms_per_step=ms_step,
+    res = dict(workload=name, tokens=wl.num_tokens, ms_per_step=ms_step, step_ms_quantiles=quant,
                value=wl.num_tokens / (ms_step * 1e-3), roofline=roof,
                step_hbm_frac=round(step_gbs / HBM_PEAK_GBS, 4),
                step_mfma_frac=round(a["flops"] / (ms_step * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
@@ -471,11 +490,12 @@ def main():
            "ms_per_step": round(main_res["ms_per_step"], 5), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
            "config": main_res["config"], "roofline": main_res["roofline"],
+           "step_ms_quantiles": main_res["step_ms_quantiles"],
            "step_hbm_frac": main_res["step_hbm_frac"]}
     if args.secondary:
         sec, _ = run_workload(m, torch, args.secondary, args)
         out["secondary"] = {k: sec[k] for k in ("workload", "value", "ms_per_step", "roofline",
-                                                 "step_mfma_frac", "config")}
+                                                 "step_mfma_frac", "step_ms_quantiles", "config")}
         out["secondary"]["value"] = round(sec["value"], 1)
     if not args.no_next_rows:
         try:
