@@ -76,7 +76,12 @@ __global__ __launch_bounds__(256) void quant_q_fold16_kernel(const uint16_t* __r
   for (int p = 0; p < kFoldPass; ++p) {
     const int64_t row = row0 + 16 * p;
     const bool ok = row < num_rows;             // uniform over the 16 lanes of the row
-    v[p] = ok ? *reinterpret_cast<const uint4*>(q + row * kHeadDim + lane * 8) : make_uint4(0, 0, 0, 0);
+    // q is read once and q8 written once per call: non-temporal (67% -> 75%
+    // of the HBM peak on 8192 tokens x 64 heads)
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    u4v x = {0u, 0u, 0u, 0u};
+    if (ok) x = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(q + row * kHeadDim + lane * 8));
+    v[p] = make_uint4(x[0], x[1], x[2], x[3]);
     wr[p] = ok && lane == 0 ? w_raw[row] : 0.f;
   }
 #pragma unroll
@@ -85,7 +90,11 @@ __global__ __launch_bounds__(256) void quant_q_fold16_kernel(const uint16_t* __r
     int e;
     const uint2 codes = quant_row_lane8_cvt(v[p], &e);
     if (row >= num_rows) continue;
-    *reinterpret_cast<uint2*>(q8 + row * kHeadDim + lane * 8) = codes;
+    {
+      typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+      u2v c2 = {codes.x, codes.y};
+      __builtin_nontemporal_store(c2, reinterpret_cast<u2v*>(q8 + row * kHeadDim + lane * 8));
+    }
     if (lane == 0) {
       const float qs = pow2f(e);
       float wf = __fmul_rn(wr[p], qs);
