@@ -19,17 +19,19 @@ namespace {
 // 16-byte loads and stores when the row is 16-byte aligned), so the block-table
 // reads of a row are all in flight together.  The row's first entries are
 // loaded before the token's request is looked up, so the two round trips
-// overlap; the valid count is summed with ballots (no block scan).  (Two or
-// four tokens per work-group measured slower.)
+// overlap; the valid count is summed with ballots (no block scan).  Rows are
+// read and written once, with non-temporal loads and stores.  (Two or four
+// tokens per work-group measured slower.)
 constexpr int kPhysPer = 8;
 
 __device__ __forceinline__ void phys_load(int* pos, const int32_t* __restrict__ in, int jb, int k,
                                           bool vec) {
   if (vec && jb + kPhysPer <= k) {
-    const int4 a = *reinterpret_cast<const int4*>(in + jb);
-    const int4 d = *reinterpret_cast<const int4*>(in + jb + 4);
-    pos[0] = a.x; pos[1] = a.y; pos[2] = a.z; pos[3] = a.w;
-    pos[4] = d.x; pos[5] = d.y; pos[6] = d.z; pos[7] = d.w;
+    typedef int i4v __attribute__((ext_vector_type(4)));
+    const i4v a = __builtin_nontemporal_load(reinterpret_cast<const i4v*>(in + jb));
+    const i4v d = __builtin_nontemporal_load(reinterpret_cast<const i4v*>(in + jb + 4));
+    pos[0] = a[0]; pos[1] = a[1]; pos[2] = a[2]; pos[3] = a[3];
+    pos[4] = d[0]; pos[5] = d[1]; pos[6] = d[2]; pos[7] = d[3];
   } else {
 #pragma unroll
     for (int e = 0; e < kPhysPer; ++e) pos[e] = jb + e < k ? in[jb + e] : -1;
@@ -64,8 +66,10 @@ __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restr
       cnt += (uint32_t)__popcll(__ballot(jb + e < k && o[e] >= 0));
     }
     if (vec && jb + kPhysPer <= k) {
-      *reinterpret_cast<int4*>(out + jb) = make_int4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<int4*>(out + jb + 4) = make_int4(o[4], o[5], o[6], o[7]);
+      typedef int i4o __attribute__((ext_vector_type(4)));
+      const i4o o0 = {o[0], o[1], o[2], o[3]}, o1 = {o[4], o[5], o[6], o[7]};
+      __builtin_nontemporal_store(o0, reinterpret_cast<i4o*>(out + jb));
+      __builtin_nontemporal_store(o1, reinterpret_cast<i4o*>(out + jb + 4));
     } else {
 #pragma unroll
       for (int e = 0; e < kPhysPer; ++e)
