@@ -889,24 +889,30 @@ __attribute__((amdgpu_waves_per_eu(2))) void score_mixed_kernel(
                  pre_chunk_blocks, gpr, lds, samp);
 }
 
+#ifndef IDX_DECODE_WG_PER_CU
+#define IDX_DECODE_WG_PER_CU 2
+#endif
+constexpr int64_t kDecodeSlots = 256 * IDX_DECODE_WG_PER_CU;   // resident decode work-groups
+
 // Decode chunk: about two work-groups per CU over the decode tokens (two fit
 // by registers), at least 8 and at most 64 blocks per work-group.
 int decode_chunk_blocks(int max_seq_len, int64_t tokens) {
   const int64_t blocks_per_row = (max_seq_len + kBlock - 1) / kBlock;
   const int64_t total = blocks_per_row * tokens;
-#ifndef IDX_DECODE_WG_PER_CU
-#define IDX_DECODE_WG_PER_CU 2
-#endif
-  const int64_t slots = 256 * IDX_DECODE_WG_PER_CU;
-  int64_t cb = (total + slots - 1) / slots;
+  int64_t cb = (total + kDecodeSlots - 1) / kDecodeSlots;
   cb = (cb + 3) / 4 * 4;
   return (int)std::min<int64_t>(64, std::max<int64_t>(8, cb));
 }
 
-int prefill_chunk_blocks(const BatchArgs& b, int64_t groups) {
-  // aim for a few thousand work-groups; never more blocks than the longest row needs
+// Prefill chunk: halved from the maximum until the grid holds `target`
+// prefill work-groups, down to 4 blocks.  The target is 1024 (two per
+// work-group slot): smaller chunks add more per-work-group set-up than they
+// balance.  When a mixed launch's decode work-groups alone fill every slot,
+// the target is 2048, so that short prefill work-groups fill in around them.
+int prefill_chunk_blocks(const BatchArgs& b, int64_t groups, bool fill_around) {
+  const int64_t target = fill_around ? 2048 : 1024;
   int cb = IDX_PREFILL_MAX_CHUNK;
-  while (cb > 4 && groups * ((b.max_seq_len + cb * kBlock - 1) / (cb * kBlock)) < 2048) cb >>= 1;
+  while (cb > 4 && groups * ((b.max_seq_len + cb * kBlock - 1) / (cb * kBlock)) < target) cb >>= 1;
   return cb;
 }
 
@@ -955,15 +961,15 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
     const int gpr = arith ? (int)per_req : 0;
     const int64_t groups = arith ? per_req * b.num_reqs : flat;
     if (dec_tokens + groups > 65535) return hipErrorInvalidConfiguration;   // grid y-extent
-    const int pcb = prefill_chunk_blocks(b, groups);
+    const int dcb = decode_chunk_blocks(b.max_seq_len, dec_tokens);
+    const int dchunks = (b.max_seq_len + dcb * kBlock - 1) / (dcb * kBlock);
+    const int pcb = prefill_chunk_blocks(b, groups, dec_tokens * dchunks >= kDecodeSlots);
     const int pchunks = (b.max_seq_len + pcb * kBlock - 1) / (pcb * kBlock);
     if (dec_tokens == 0) {
       const dim3 grid((unsigned)pchunks, (unsigned)groups);
       hipLaunchKernelGGL(score_prefill_kernel, grid, dim3(kScoreThreads), 0, stream, q8, w, cache, b,
                          logits, ld, pcb, gpr, samp);
     } else {
-      const int dcb = decode_chunk_blocks(b.max_seq_len, dec_tokens);
-      const int dchunks = (b.max_seq_len + dcb * kBlock - 1) / (dcb * kBlock);
       const dim3 grid((unsigned)std::max(dchunks, pchunks), (unsigned)(dec_tokens + groups));
       hipLaunchKernelGGL(score_mixed_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0, stream,
                          q8, w, cache, b, logits, ld, (int)dec_tokens, dcb, pcb, gpr, samp);
