@@ -281,11 +281,19 @@ def test_logits_absent_blocks(env, new):
         check_logits_row(got[t, :row.shape[0]][keep], row[keep], f"absent blocks, token {t}")
 
 
+# 64 decode rows of 8.5K-9K positions: their decode work-groups (8 chunks each)
+# fill every resident slot, so the mixed launch cuts its prefill part into
+# finer chunks than a launch without them
+_LONG_DECODES = [int(x) for x in np.random.default_rng(5).integers(8500, 9001, 64)]
+
+
 @pytest.mark.parametrize("lengths,new,splits", [
     # decodes then two prefill chunks: prefill groups numbered across the batch
     ([5000, 3000, 9000, 1200, 2500], [1, 1, 1, 300, 40], (0, 3, 5, None)),
     # two equal chunks: groups numbered per request, the split cuts the first
     ([4000, 3500], [300, 300], (0, 5, 300, 301, None)),
+    # many long decodes and one prefill chunk: both prefill chunkings
+    (_LONG_DECODES + [2000], [1] * 64 + [200], (0, 64, None)),
 ])
 def test_mixed_batch_split_is_result_neutral(env, lengths, new, splits):
     """Decode requests first, then prefill chunks, scored in one launch with the
