@@ -464,8 +464,10 @@ constexpr int kMaxFusedRows = 4;
 
 // `ident`: token t is request t (every request has exactly one new token),
 // which the host knows; the block-table slice of a full chunk is then read
-// at once, in parallel with the request metadata.
-template <int NB, bool FK>
+// at once, in parallel with the request metadata.  With SPEC (the decode
+// rows of a mixed batch, decodes first) request t's slice is read alongside
+// the token lookup and kept if the lookup finds request t.
+template <int NB, bool FK, bool SPEC = false>
 __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __restrict__ q8,
                                             const float* __restrict__ w, const CacheArgs& cache,
                                             const BatchArgs& b, float* __restrict__ logits,
@@ -477,7 +479,8 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
   const int per_full = chunk_blocks / 4;        // chunk_blocks is a multiple of 4
   const int lb_full = lb0 + wave * per_full + lane;
   int bt_full = -1;                             // raw id; checked only once it is needed
-  if (ident && lane < per_full)
+  const bool spec = SPEC && !ident && t < b.num_reqs;
+  if ((ident || spec) && lane < per_full)
     bt_full = b.bt[(int64_t)t * b.bt_stride + min(lb_full, (int)b.bt_stride - 1)];
   TokenPos tp;
   if (ident) {                                  // one new token per request: token t is request t
@@ -519,7 +522,7 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
   // lane j holds the physical block of this wave's j-th block, so no K load
   // waits on a block-table load
   int pbl;
-  if (ident && nblk == chunk_blocks)
+  if ((ident || (spec && tp.r == t)) && nblk == chunk_blocks)
     pbl = (lane < per_full && lb_full < b.bt_stride && bt_full >= 0 && bt_full < cache.num_blocks)
               ? bt_full : -1;
   else
@@ -882,8 +885,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void score_mixed_kernel(
   int cx, ry;
   xcd_spread(&cx, &ry);
   if (ry < dec_tokens)
-    decode_body<NB, false>(cx, ry, q8, w, cache, b, logits, ld, dec_chunk_blocks,
-                           false, lds, NewRows{}, samp);
+    decode_body<NB, false, true>(cx, ry, q8, w, cache, b, logits, ld, dec_chunk_blocks,
+                                 false, lds, NewRows{}, samp);
   else
     prefill_body(cx, ry - dec_tokens, dec_tokens, q8, w, cache, b, logits, ld,
                  pre_chunk_blocks, gpr, lds, samp);
