@@ -38,9 +38,15 @@ __device__ __forceinline__ void phys_load(int* pos, const int32_t* __restrict__ 
   }
 }
 
+// POW2: block_size is 1 << bs_shift, so an entry's block and offset are a
+// shift and a mask instead of a division.  Every slot of the pool fits in 32
+// bits (num_blocks * stride_rows <= INT32_MAX, checked on the host), so the
+// per-entry arithmetic is 32-bit; only the request's block-table row is
+// addressed in 64 bits, once.
+template <bool POW2>
 __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restrict__ logical,
                                                           int64_t ldl, BatchArgs b, CacheArgs c,
-                                                          int block_size, int k,
+                                                          int block_size, int bs_shift, int k,
                                                           int64_t stride_rows,
                                                           int32_t* __restrict__ phys, int64_t ldp,
                                                           int32_t* __restrict__ valid) {
@@ -52,6 +58,10 @@ __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restr
   int pos[kPhysPer];
   phys_load(pos, in, (int)threadIdx.x * kPhysPer, k, vec);
   const TokenPos tp = token_pos_wave(b, t);
+  const int32_t* __restrict__ btr = b.bt + (int64_t)tp.r * b.bt_stride;
+  const int bt_n = (int)min(b.bt_stride, (int64_t)INT32_MAX);
+  const int nb = (int)min(c.num_blocks, (int64_t)INT32_MAX);
+  const uint32_t srow = (uint32_t)min(stride_rows, (int64_t)INT32_MAX);   // used only when nb > 0
   uint32_t cnt = 0;                             // valid entries of this wave (uniform)
   for (int j0 = 0; j0 < k; j0 += kStep) {
     const int jb = j0 + (int)threadIdx.x * kPhysPer;
@@ -59,9 +69,14 @@ __global__ __launch_bounds__(256) void to_physical_kernel(const int32_t* __restr
 #pragma unroll
     for (int e = 0; e < kPhysPer; ++e) {
       o[e] = -1;
-      if (pos[e] >= 0 && pos[e] < tp.n) {
-        const int64_t blk = phys_block(b, c, tp.r, pos[e] / block_size);
-        if (blk >= 0) o[e] = (int32_t)(blk * stride_rows + pos[e] % block_size);
+      const int p = pos[e];
+      if (p >= 0 && p < tp.n) {
+        const int lb = POW2 ? p >> bs_shift : p / block_size;
+        const int off = POW2 ? p & (block_size - 1) : p - lb * block_size;
+        if (lb < bt_n) {
+          const int blk = btr[lb];
+          if (blk >= 0 && blk < nb) o[e] = (int32_t)((uint32_t)blk * srow + (uint32_t)off);
+        }
       }
       cnt += (uint32_t)__popcll(__ballot(jb + e < k && o[e] >= 0));
     }
@@ -98,8 +113,13 @@ hipError_t launch_topk_to_physical(const int32_t* logical, int64_t ldl, const Ba
                                    hipStream_t stream) {
   if (b.num_tokens == 0) return hipSuccess;
   CacheArgs c{nullptr, num_blocks};
-  hipLaunchKernelGGL(to_physical_kernel, dim3((unsigned)b.num_tokens), dim3(256), 0, stream,
-                     logical, ldl, b, c, block_size, k, stride_rows, physical, ldp, valid);
+  if ((block_size & (block_size - 1)) == 0)
+    hipLaunchKernelGGL(to_physical_kernel<true>, dim3((unsigned)b.num_tokens), dim3(256), 0, stream,
+                       logical, ldl, b, c, block_size, __builtin_ctz((unsigned)block_size), k,
+                       stride_rows, physical, ldp, valid);
+  else
+    hipLaunchKernelGGL(to_physical_kernel<false>, dim3((unsigned)b.num_tokens), dim3(256), 0, stream,
+                       logical, ldl, b, c, block_size, 0, k, stride_rows, physical, ldp, valid);
   return hipGetLastError();
 }
 

@@ -507,3 +507,35 @@ def test_topk_to_physical(env):
     want, wv = oracle.physical.to_physical(lg, wl.token_req(), wl.block_table, 64)
     assert np.array_equal(phys.cpu().numpy(), want)
     assert np.array_equal(valid.cpu().numpy(), wv)
+
+
+
+@pytest.mark.parametrize("block_size,stride", [(48, 0), (32, 100), (64, 96)])
+def test_topk_to_physical_block_shapes(env, block_size, stride):
+    """Block sizes other than the cache's 64 (a power of two or not) and block
+    strides wider than the block give the oracle's slots and counts."""
+    m, torch = env
+    rng = np.random.default_rng(5100 + block_size)
+    wl = random_batch(5003, [100, 700, 64, 1500], [2, 1, 3, 40], k=64)
+    say("to_physical block_size", block_size, "stride", stride)
+    width = -(-wl.max_seq_len // block_size)
+    per_req = [-(-int(n) // block_size) for n in wl.seq_lens]
+    pool = 2 * sum(per_req)
+    ids = rng.permutation(pool)
+    bt = np.full((len(per_req), width), -1, np.int32)
+    o = 0
+    for r, nb in enumerate(per_req):
+        bt[r, :nb] = ids[o:o + nb]
+        o += nb
+    pos = wl.token_pos()
+    logical = np.full((wl.num_tokens, 64), -1, np.int32)
+    for t in range(wl.num_tokens):
+        n = int(pos[t]) + 1
+        c = np.sort(rng.choice(n, min(n, 50), replace=False))
+        logical[t, :c.size] = c
+    batch = m.Batch(wl.seq_lens, wl.query_start_loc, bt)
+    phys, valid = m.idx_topk_to_physical(torch.from_numpy(logical).cuda(), batch, pool,
+                                         block_size=block_size, block_stride_rows=stride)
+    want, wv = oracle.physical.to_physical(logical, wl.token_req(), bt, block_size, stride or None)
+    assert np.array_equal(phys.cpu().numpy(), want)
+    assert np.array_equal(valid.cpu().numpy(), wv)
