@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
   __shared__ uint32_t ckey[kRowCap];
   __shared__ Pos cpos[kRowCap];
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t table[kBatch * kRowThreads / 64 + 1];
+  __shared__ uint32_t table[2][kBatch * kRowThreads / 64];   // alternate batches alternate tables
   __shared__ uint32_t bucket[64];
   __shared__ uint32_t scratch[scratch_words<kRowThreads>()];
   const float* row = logits + (size_t)t * ld;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
   load_batch(vb, kStep);
   const uint32_t tau = sampled ? sample_tau<kRowThreads>(sv, ns, n, k, hist, scratch) : 0u;
   uint32_t C = 0;
-  auto batch = [&](float* v, int base) {
+  auto batch = [&](float* v, int base, uint32_t* tab) {
     uint32_t key[kBatch];
     bool pass[kBatch];
 #pragma unroll
@@ -108,12 +108,13 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
       pass[e] = base + e * kRowThreads + (int)threadIdx.x < n && key[e] >= tau;
     }
     load_batch(v, base + 2 * kStep);            // two batches ahead
-    C += compact_ordered<kRowThreads, kBatch>(key, pass, base, C, ckey, cpos, kRowCap, table);
+    C += compact_ordered<kRowThreads, kBatch>(key, pass, base, C, ckey, cpos, kRowCap, tab);
   };
   for (int base = 0; base < n; base += 2 * kStep) {
-    batch(va, base);
-    if (base + kStep < n) batch(vb, base + kStep);
+    batch(va, base, table[0]);
+    if (base + kStep < n) batch(vb, base + kStep, table[1]);
   }
+  __syncthreads();                              // the compacted candidates, before the select reads them
   finish_row<kRowThreads>(row, n, k, C, kRowCap, ckey, cpos, out, hist, bucket, scratch);
 }
 
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     return;
   }
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t table[kPer * kThreads / 64 + 1];
+  __shared__ uint32_t table[kPer * kThreads / 64];
   __shared__ uint32_t scratch[scratch_words<kThreads>()];
   const float* row = logits + (size_t)t * ld;
   const bool sampled = n > 4 * k;               // else every position is a candidate

@@ -343,14 +343,19 @@ __device__ __forceinline__ uint32_t sample_tau(const float* v, int ns, int n, in
 // Ordered compaction of one batch: element (e, thread) sits at position
 // base + e*NT + threadIdx.x; those with pass[e] are appended to (ckey, cpos)
 // after `start` entries, in ascending position order (entries past `cap` are
-// counted, not stored).  `table` holds E*NT/64 + 1 words of LDS.  Returns the
-// batch's number of passing elements.
+// counted, not stored).  `table` holds E*NT/64 <= 64 words of LDS.  There is
+// one barrier: every wave scans the per-(e, wave) counts itself.  So two
+// consecutive calls must not share a table (callers alternate two), and a
+// caller synchronises before it reads what was compacted into LDS.  Returns
+// the batch's number of passing elements.
 template <int NT, int E, typename Pos>
 __device__ __forceinline__ uint32_t compact_ordered(const uint32_t* key, const bool* pass, int base,
                                                     uint32_t start, uint32_t* ckey, Pos* cpos,
                                                     uint32_t cap, uint32_t* table) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(E * NW <= 64, "one count per lane");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   uint64_t m[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -358,44 +363,25 @@ __device__ __forceinline__ uint32_t compact_ordered(const uint32_t* key, const b
     if (lane == 0) table[e * NW + wave] = (uint32_t)__popcll(m[e]);
   }
   __syncthreads();
-  // exclusive prefix over the E*NW counts, in (e, wave) order, by wave 0
-  if (wave == 0) {
-    constexpr int PER = (E * NW + 63) / 64;
-    uint32_t v[PER];
-    uint32_t s = 0;
+  // exclusive prefix over the E*NW counts in (e, wave) order, lane i holding count i
+  const uint32_t c = lane < E * NW ? table[lane] : 0u;
+  uint32_t incl = c;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int idx = lane * PER + q;
-      v[q] = idx < E * NW ? table[idx] : 0u;
-      s += v[q];
-    }
-    uint32_t incl = s;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    uint32_t run = incl - s;
-    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int idx = lane * PER + q;
-      if (idx < E * NW) table[idx] = run;
-      run += v[q];
-    }
-    if (lane == 0) table[E * NW] = total;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
+    if (lane >= off) incl += y;
   }
-  __syncthreads();
+  const uint32_t excl = incl - c;
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
+    const uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)excl, e * NW + wave);
     if (pass[e]) {
-      const uint32_t slot = start + table[e * NW + wave] +
-                            (uint32_t)__popcll(m[e] & ((1ull << lane) - 1ull));
+      const uint32_t slot = start + at + (uint32_t)__popcll(m[e] & below);
       if (slot < cap) { ckey[slot] = key[e]; cpos[slot] = (Pos)(base + e * NT + (int)threadIdx.x); }
     }
   }
-  const uint32_t total = table[E * NW];
-  __syncthreads();
   return total;
 }
 
