@@ -220,7 +220,22 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
       sp[u] = ws.cand_pos[sb + j];
     }
   }
-  {                                             // every slot count is written; clamp anyway
+  // slot offsets (every slot count is written; clamp anyway): one wave scans
+  // up to 64 slots, the block scans more
+  if (nsl <= 64) {
+    if (threadIdx.x < 64) {
+      const int c = threadIdx.x;
+      const uint32_t v = c < nsl ? min(cnts[c], cap) : 0u;
+      uint32_t incl = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (c >= off) incl += y;
+      }
+      if (c < nsl) pre[c] = incl - v;
+      if (c == 63) pre[nsl] = incl;
+    }
+  } else {
     const int per = (nsl + NT - 1) / NT;
     const int c0 = min(nsl, per * (int)threadIdx.x), c1 = min(nsl, c0 + per);
     uint32_t s = 0;

@@ -23,7 +23,9 @@ namespace idx {
 
 constexpr int kThreads = 256;
 
-template <int NT>
+// LEAD: synchronise before writing `scratch`, for callers whose threads may
+// still be reading it from an earlier scan.
+template <int NT, bool LEAD = true>
 __device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* total, uint32_t* scratch) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -33,7 +35,7 @@ __device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* total,
     const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
     if (lane >= off) incl += y;
   }
-  __syncthreads();
+  if (LEAD) __syncthreads();
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -94,7 +96,9 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32
   uint32_t* res = scratch + NT / 64;
   if (threadIdx.x == 0) { res[1] = 0u; res[2] = 0u; res[3] = 0u; }
   uint32_t total;
-  const uint32_t before = block_scan_excl<NT>(sum, &total, scratch);
+  // Every caller has synchronised after filling `h` (so after any earlier
+  // reads of `scratch`): the scan needs no leading barrier.
+  const uint32_t before = block_scan_excl<NT, false>(sum, &total, scratch);
   if ((int)threadIdx.x < active && before < need && before + sum >= need) {
     uint32_t cum = before;
     for (int j = 0; j < per; ++j) {
