@@ -510,14 +510,15 @@ def test_topk_to_physical(env):
 
 
 
-@pytest.mark.parametrize("block_size,stride", [(48, 0), (32, 100), (64, 96)])
-def test_topk_to_physical_block_shapes(env, block_size, stride):
+@pytest.mark.parametrize("block_size,stride,k", [(48, 0, 64), (32, 100, 64), (64, 96, 64), (64, 0, 30)])
+def test_topk_to_physical_block_shapes(env, block_size, stride, k):
     """Block sizes other than the cache's 64 (a power of two or not) and block
-    strides wider than the block give the oracle's slots and counts."""
+    strides wider than the block give the oracle's slots and counts; k = 30
+    makes rows of 120 bytes, so every other row takes the unaligned path."""
     m, torch = env
     rng = np.random.default_rng(5100 + block_size)
-    wl = random_batch(5003, [100, 700, 64, 1500], [2, 1, 3, 40], k=64)
-    say("to_physical block_size", block_size, "stride", stride)
+    wl = random_batch(5003, [100, 700, 64, 1500], [2, 1, 3, 40], k=k)
+    say("to_physical block_size", block_size, "stride", stride, "k", k)
     width = -(-wl.max_seq_len // block_size)
     per_req = [-(-int(n) // block_size) for n in wl.seq_lens]
     pool = 2 * sum(per_req)
@@ -528,10 +529,10 @@ def test_topk_to_physical_block_shapes(env, block_size, stride):
         bt[r, :nb] = ids[o:o + nb]
         o += nb
     pos = wl.token_pos()
-    logical = np.full((wl.num_tokens, 64), -1, np.int32)
+    logical = np.full((wl.num_tokens, k), -1, np.int32)
     for t in range(wl.num_tokens):
         n = int(pos[t]) + 1
-        c = np.sort(rng.choice(n, min(n, 50), replace=False))
+        c = np.sort(rng.choice(n, min(n, k - 10), replace=False))
         logical[t, :c.size] = c
     batch = m.Batch(wl.seq_lens, wl.query_start_loc, bt)
     phys, valid = m.idx_topk_to_physical(torch.from_numpy(logical).cuda(), batch, pool,
