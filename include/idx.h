@@ -127,7 +127,7 @@ idx_status_t idx_quant_write_k(const uint16_t* k_bf16, int64_t num_tokens, int32
  * use_ue8m0=True), then weights * q_scale * softmax_scale * n_head^-0.5).
  *   q_bf16        device bf16 bits [num_tokens, n_heads, head_dim], contiguous
  *   w_raw         device fp32 [num_tokens, n_heads]
- *   q_fp8         device out uint8 [num_tokens, n_heads, head_dim]
+ *   q_fp8         device out uint8 [num_tokens, n_heads, head_dim], 16-byte aligned
  *   w_folded      device out fp32 [num_tokens, n_heads]:
  *                 ((w_raw * q_scale) * softmax_scale) * n_heads^-0.5, fp32
  *   q_scale_out   device out fp32 [num_tokens, n_heads], or NULL

@@ -23,7 +23,9 @@ idx_status_t check_cache(const idx_kcache_t& c) {
   return IDX_OK;
 }
 
-idx_status_t check_batch(const idx_batch_t* b) {
+// block_size: positions per block-table entry (the cache's 64 for every
+// scoring call; the caller's for the physical conversion).
+idx_status_t check_batch(const idx_batch_t* b, int64_t block_size = kBlock) {
   if (b == nullptr) return IDX_ERR_INVALID_ARG;
   if (b->num_reqs < 1 || b->num_tokens < 0 || b->max_seq_len < 0 || b->max_query_len < 0)
     return IDX_ERR_INVALID_ARG;
@@ -32,7 +34,8 @@ idx_status_t check_batch(const idx_batch_t* b) {
     return IDX_ERR_INVALID_ARG;
   if (!aligned(b->seq_lens, 4) || !aligned(b->query_start_loc, 4) || !aligned(b->block_table, 4))
     return IDX_ERR_INVALID_ARG;
-  if (b->block_table_stride < (int64_t)(b->max_seq_len + kBlock - 1) / kBlock ||
+  if (block_size < 1 ||
+      b->block_table_stride < ((int64_t)b->max_seq_len + block_size - 1) / block_size ||
       b->block_table_stride < 1)
     return IDX_ERR_INVALID_ARG;
   if (b->max_query_len > b->num_tokens) return IDX_ERR_INVALID_ARG;
@@ -163,7 +166,7 @@ idx_status_t idx_quant_q_fold_w(const uint16_t* q_bf16, const float* w_raw, int6
   if (num_tokens == 0) return IDX_OK;
   if (q_bf16 == nullptr || w_raw == nullptr || q_fp8 == nullptr || w_folded == nullptr)
     return IDX_ERR_INVALID_ARG;
-  if (!aligned(q_bf16, 8) || !aligned(q_fp8, 4) || !aligned(w_raw, 4) || !aligned(w_folded, 4) ||
+  if (!aligned(q_bf16, 8) || !aligned(q_fp8, 16) || !aligned(w_raw, 4) || !aligned(w_folded, 4) ||
       !aligned(q_scale_out, 4))
     return IDX_ERR_INVALID_ARG;
   const float head_norm = (float)(1.0 / __builtin_sqrt((double)n_heads));
@@ -300,14 +303,14 @@ idx_status_t idx_topk_to_physical(const int32_t* logical, int64_t logical_stride
                                   int32_t k, int64_t block_stride_rows, int32_t* physical,
                                   int64_t physical_stride, int32_t* valid_counts,
                                   hipStream_t stream) {
-  idx_status_t s = check_batch(batch);
+  if (block_size < 1) return IDX_ERR_INVALID_ARG;
+  idx_status_t s = check_batch(batch, block_size);
   if (s != IDX_OK) return s;
   if (k < 1 || k > kMaxK) return IDX_ERR_UNSUPPORTED;
-  if (block_size < 1 || num_blocks < 0 || block_stride_rows < 0) return IDX_ERR_INVALID_ARG;
+  if (num_blocks < 0 || block_stride_rows < 0) return IDX_ERR_INVALID_ARG;
   const int64_t stride_rows = block_stride_rows ? block_stride_rows : block_size;
   if (stride_rows < block_size) return IDX_ERR_INVALID_ARG;
   if (num_blocks * stride_rows > (int64_t)INT32_MAX) return IDX_ERR_UNSUPPORTED;
-  if (batch->block_table_stride * block_size < batch->max_seq_len) return IDX_ERR_INVALID_ARG;
   if (logical_stride < k || physical_stride < k) return IDX_ERR_INVALID_ARG;
   if (batch->num_tokens == 0) return IDX_OK;
   if (logical == nullptr || physical == nullptr) return IDX_ERR_INVALID_ARG;

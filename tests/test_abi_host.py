@@ -153,3 +153,31 @@ def test_physical_rejects(m):
     assert L.idx_topk_to_physical(FAKE, 8, B(ok), 0, 10, 8, 0, FAKE, 8, None, S) == -1
     assert L.idx_topk_to_physical(FAKE, 8, B(ok), 64, 10, 8, 32, FAKE, 8, None, S) == -1  # stride < bs
     assert L.idx_topk_to_physical(FAKE, 8, B(ok), 64, 1 << 30, 8, 64, FAKE, 8, None, S) == -2
+
+
+def test_quant_q_fold_requires_16_byte_q_fp8(m):
+    L = m.lib()
+    # q_fp8 only 4-byte aligned: rejected before any launch (the 16-lane kernel stores 8 bytes)
+    assert L.idx_quant_q_fold_w(FAKE, FAKE, 1, 64, 128, 0.088, ctypes.c_void_p(0x10004), FAKE,
+                                None, S) == -1
+    assert L.idx_quant_q_fold_w(FAKE, FAKE, 1, 64, 128, 0.088, ctypes.c_void_p(0x10008), FAKE,
+                                None, S) == -1
+
+
+def test_physical_checks_table_width_against_its_block_size(m):
+    L = m.lib()
+    B = ctypes.byref
+    # 1024 positions in blocks of 128 need 8 table entries: accepted up to the pointer checks
+    # (a null physical pointer then gives -1 only after the batch passed)
+    wide = _batch(m, max_seq_len=1024, stride=8)
+    assert L.idx_topk_to_physical(FAKE, 8, B(wide), 128, 10, 8, 0, None, 8, None, S) == -1
+    assert L.idx_topk_to_physical(FAKE, 8, B(_batch(m, max_seq_len=1024, stride=8, num_tokens=0,
+                                                    max_query_len=0)),
+                                  128, 10, 8, 0, FAKE, 8, None, S) == 0
+    # seven entries are too few for 1024 positions in blocks of 128
+    narrow = _batch(m, max_seq_len=1024, stride=7, num_tokens=0, max_query_len=0)
+    assert L.idx_topk_to_physical(FAKE, 8, B(narrow), 128, 10, 8, 0, FAKE, 8, None, S) == -1
+    # the scoring calls still need one entry per 64 positions
+    assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(_batch(m, max_seq_len=1024, stride=8,
+                                                                 num_tokens=0, max_query_len=0)),
+                        FAKE, 1024, S) == -1
