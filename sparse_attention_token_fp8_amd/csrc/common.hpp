@@ -196,6 +196,18 @@ __device__ __forceinline__ TokenPos token_pos_wave(const BatchArgs& b, int t) {
   return tp;
 }
 
+// A buffer resource over the `bytes` bytes at `base` (gfx9 raw buffer, data
+// format 32).  A load from an offset at or past `bytes` returns zeros and
+// moves no data: the hardware's range check, which the staging loops use for
+// blocks that are absent or past the end, so that every load stays
+// unconditional without fetching anything.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Buffer-load cache policy: non-temporal (streamed past the caches).
+constexpr int kLoadStream = 2;
+
 // Physical block of logical block `lb` of request r, or -1 if it lies outside
 // the block table or the pool.
 __device__ __forceinline__ int64_t phys_block(const BatchArgs& b, const CacheArgs& c, int r, int lb) {

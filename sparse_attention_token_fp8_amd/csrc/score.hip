@@ -336,6 +336,9 @@ struct StageRegs {
   uint32_t mask;   // all ones for a block in the table, else 0 (stored as zeros)
 };
 
+// Offset past every block: a buffer load from it returns zeros and moves no data.
+constexpr int kPastBlock = 0x10000;
+
 template <int NW>
 __device__ __forceinline__ int stage_src(int ci) {
   // LDS chunk ci <- global byte offset
@@ -351,7 +354,9 @@ __device__ __forceinline__ int stage_src(int ci) {
 // scale chunks), so no load sits behind a branch: a branch around a load makes
 // the compiler wait for every load in flight at the next use, which would
 // drain the prefetch.  A block absent from the table is read from block 0 and
-// stored as zeros.
+// stored as zeros.  (Plain loads here: the range-checked buffer loads that the
+// decode staging uses made prefill scoring ~3% slower, 1619-1647 against
+// 1666-1701 us on 8192 tokens over 32K, alternated on one box.)
 template <int NW>
 __device__ __forceinline__ void stage_load(StageRegs<NW>& st, const uint8_t* __restrict__ base,
                                            bool valid) {
@@ -384,37 +389,31 @@ __device__ __forceinline__ void lds_kblock(KBlock& kb, const uint8_t* slot, int 
 }
 
 // One wave stages a whole block: 528 16-byte chunks, 9 per lane (in the last
-// round lanes 16-63 re-read the scales' 16 chunks, so every lane issues the
-// same loads).  A block absent from the table is read from a valid address
-// and zeroed when it is written to LDS: a select right after the load would
-// wait for it, and a branch around the loads would make the compiler wait for
-// every load in flight at the next use.
+// round lanes 16-63 load from past the block, which fetches nothing), so every
+// lane issues the same loads.  A block absent from the table or past the
+// wave's run is loaded with `bytes` = 0: zeros, and no data moved.
 struct WaveStage {
   uint4 v[9];
-  uint32_t mask;   // all ones for a block in the table, else 0
 };
 
 // The K stream of a decode batch is read once, so its loads are non-temporal
 // (streamed past the caches): 59% -> 64.5% of the HBM peak on 8 x 128K rows.
 __device__ __forceinline__ void wave_stage_load(WaveStage& st, const uint8_t* __restrict__ base,
-                                                bool valid, int lane) {
-  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+                                                int bytes, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = byte_rsrc(base, bytes);
 #pragma unroll
   for (int u = 0; u < 9; ++u) {
-    const int ci = u < 8 ? lane + 64 * u : 512 + (lane & 15);
-    const u4v x = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(base + stage_src<1>(ci)));
+    const int off = u < 8 ? stage_src<1>(lane + 64 * u) : (lane < 16 ? (512 + lane) << 4 : kPastBlock);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kLoadStream);
     st.v[u] = make_uint4(x[0], x[1], x[2], x[3]);
   }
-  st.mask = valid ? 0xffffffffu : 0u;
 }
 
 __device__ __forceinline__ void wave_stage_store(const WaveStage& st, uint8_t* slot, int lane) {
 #pragma unroll
   for (int u = 0; u < 9; ++u) {
     const int ci = lane + 64 * u;
-    const uint4 x = make_uint4(st.v[u].x & st.mask, st.v[u].y & st.mask, st.v[u].z & st.mask,
-                               st.v[u].w & st.mask);
-    if (u < 8 || lane < 16) *reinterpret_cast<uint4*>(slot + (ci << 4)) = x;
+    if (u < 8 || lane < 16) *reinterpret_cast<uint4*>(slot + (ci << 4)) = st.v[u];
   }
 }
 
@@ -527,18 +526,20 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
               ? bt_full : -1;
   else
     pbl = lane < mine ? (int)phys_block(b, cache, tp.r, blk(lane)) : -1;
+  // block j of the run (j <= mine + NB - 2 < 64); past the run it loads nothing
   auto stage = [&](WaveStage& st, int j) {
     const int pb = __builtin_amdgcn_readlane(pbl, j);
-    wave_stage_load(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes, pb >= 0, lane);
+    wave_stage_load(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes,
+                    (j < mine && pb >= 0) ? kBlockBytes : 0, lane);
   };
   uint8_t* slot = lds + wave * kBlockBytes;
 
-  // Every iteration issues one block's loads (past the last block it re-reads
-  // that block, from L2), so the loop body has no branch around a load.
+  // Every iteration issues one block's loads (past the last block they fetch
+  // nothing), so the loop body has no branch around a load.
   const int iters = (mine + NB - 1) / NB * NB;
   WaveStage ring[NB];
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u) stage(ring[u], min(u, mine - 1));
+  for (int u = 0; u < NB - 1; ++u) stage(ring[u], u);
   // the linear half's pieces, built in the wave's slot while the first loads
   // are in flight
   LinFrag lf;
@@ -587,7 +588,7 @@ __device__ __forceinline__ void decode_body(int bx, int t, const uint8_t* __rest
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int j = j0 + u;
-      stage(ring[(u + NB - 1) % NB], min(j + NB - 1, mine - 1));
+      stage(ring[(u + NB - 1) % NB], j + NB - 1);
       __builtin_amdgcn_sched_barrier(0);        // nothing that needs block j moves above these loads
       wave_stage_store(ring[u], slot, lane);
       if (FK) {
