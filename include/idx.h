@@ -188,6 +188,28 @@ idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_head
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * idx_score_topk with its workspace taken from a device array that the
+ * library holds, IDX_NOALLOC_SCRATCH_BYTES per device, from the first call
+ * on a device until the process ends.  The call itself allocates nothing.
+ * It uses the current device's array, so `stream` must belong to the current
+ * device.  Results equal idx_score_topk's on the same inputs.
+ * Returns IDX_ERR_WORKSPACE when idx_score_topk_workspace_size(batch, k)
+ * exceeds IDX_NOALLOC_SCRATCH_BYTES (nothing is launched), and
+ * IDX_ERR_LAUNCH if the array's device address cannot be looked up.  Every
+ * call on a device shares that device's array, and nothing in it needs to
+ * start at zero: calls that overlap on one device (other streams, other
+ * threads) race and must be ordered by the caller.
+ */
+#define IDX_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+idx_status_t idx_score_topk_noalloc(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                    int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
+                                    int32_t k, int32_t* topk, int64_t topk_stride,
+                                    hipStream_t stream);
+
+/*
  * IndexCache schedule ([blog] skip_topk snippet; [pr] deepseek_v2.py snippet
  * and Risks & impact).  Host-only.  is_full[l] = 1 for an F layer (runs the
  * indexer, refreshes the top-k buffer), 0 for an S layer (reuses it).

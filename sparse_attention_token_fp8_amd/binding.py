@@ -62,6 +62,8 @@ SIGNATURES = {
     "idx_score_topk_workspace_size": (_sz, [_PBatch, _i32]),
     "idx_score_topk": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _i32, _vp, _i64,
                                       _vp, _sz, _vp]),
+    "idx_score_topk_noalloc": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _i32, _vp,
+                                              _i64, _vp]),
     "idx_layer_schedule": (ctypes.c_int, [_i32, ctypes.c_char_p, _i32, _i32, _i32, _vp]),
     "idx_indexcache_layer": (ctypes.c_int, [ctypes.POINTER(LayerIOC), _i32, _i32, _vp, _PBatch,
                                             _i32, _vp, _i64, _vp, _sz, _vp]),
@@ -230,6 +232,17 @@ def idx_score_topk(q_fp8, w, cache, batch, k, topk=None, workspace=None, stream=
            _lib.idx_score_topk(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(), k,
                                _ptr(topk), int(topk.stride(0)), _ptr(ws), ws.numel(),
                                _stream(stream)))
+    return topk
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def idx_score_topk_noalloc(q_fp8, w, cache, batch, k, topk, stream=None):
+    """idx_score_topk with the library's own per-device scratch (no workspace argument)."""
+    _check("idx_score_topk_noalloc",
+           _lib.idx_score_topk_noalloc(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(),
+                                       k, _ptr(topk), int(topk.stride(0)), _stream(stream)))
     return topk
 
 

@@ -4,6 +4,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -125,6 +127,37 @@ hipError_t score_topk(const uint8_t* q_fp8, const float* w, const idx_kcache_t& 
 
 }  // namespace
 
+// Workspace of idx_score_topk_noalloc, for callers that cannot allocate: one
+// copy of this array per device, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol); it passes the device address looked up once per
+// device by noalloc_scratch().
+static __device__ __align__(256) uint8_t scratch[IDX_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's copy of `scratch`, looked up on the first call per device
+// (with that device current); nullptr if the lookup fails.
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* idx_status_str(idx_status_t s) {
@@ -230,6 +263,23 @@ idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_head
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
     return IDX_ERR_WORKSPACE;
   return launched(score_topk(q_fp8, w, cache, batch, k, topk, topk_stride, workspace, nullptr, 0,
+                             nullptr, stream));
+}
+
+idx_status_t idx_score_topk_noalloc(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                    int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
+                                    int32_t k, int32_t* topk, int64_t topk_stride,
+                                    hipStream_t stream) {
+  idx_status_t s = check_scoring(q_fp8, w, n_heads, head_dim, cache, batch);
+  if (s != IDX_OK) return s;
+  s = check_k(k, topk_stride, topk, batch->num_tokens);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens == 0) return IDX_OK;
+  if (idx_score_topk_workspace_size(batch, k) > (size_t)IDX_NOALLOC_SCRATCH_BYTES)
+    return IDX_ERR_WORKSPACE;
+  void* ws = noalloc_scratch();
+  if (ws == nullptr) return IDX_ERR_LAUNCH;
+  return launched(score_topk(q_fp8, w, cache, batch, k, topk, topk_stride, ws, nullptr, 0,
                              nullptr, stream));
 }
 
