@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 PROFILES = os.path.join(ROOT, "profiles")
 SCORE_SOURCES = ("sparse_attention_token_fp8_amd/csrc/score.hip",
+                 "sparse_attention_token_fp8_amd/csrc/score_device.hpp",
                  "sparse_attention_token_fp8_amd/csrc/common.hpp")
 
 

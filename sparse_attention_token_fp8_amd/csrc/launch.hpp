@@ -22,6 +22,10 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
                         const BatchArgs& b, int64_t dec_tokens, float* logits, int64_t ld,
                         float* samp, hipStream_t stream);
 
+// Blocks per decode work-group for `tokens` rows of up to max_seq_len
+// positions (a multiple of 4, 8..64).
+int decode_chunk_blocks(int max_seq_len, int64_t tokens);
+
 // Whether launch_score_write_k can score this batch: every token scored with
 // the decode split and at most a few new tokens per request.
 bool score_writes_k(const BatchArgs& b, int64_t dec_tokens);
