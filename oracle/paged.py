@@ -50,6 +50,21 @@ def write_token(cache, slot, codes, scale):
     flat[b, base:base + 4] = sb
 
 
+def write_tokens(cache, slots, codes, scales):
+    """write_token for many tokens at once: row i of ``codes`` and ``scales[i]``
+    go to ``slots[i]`` (slots distinct, all >= 0).  The same byte placement as
+    the per-token form, written with one fancy-indexed assignment per field."""
+    block_size = cache.shape[1]
+    slots = np.asarray(slots, dtype=np.int64)
+    if slots.size == 0:
+        return
+    b, off = slots // block_size, slots % block_size
+    flat = _flat(cache)
+    flat[b[:, None], off[:, None] * HEAD_DIM + np.arange(HEAD_DIM)[None, :]] = codes
+    sb = np.asarray(scales, dtype="<f4").reshape(-1).view(np.uint8).reshape(-1, 4)
+    flat[b[:, None], block_size * HEAD_DIM + off[:, None] * 4 + np.arange(4)[None, :]] = sb
+
+
 def read_tokens(cache, block_table_row, positions):
     """Codes [n,128] (uint8) and scales [n] (float64) of logical positions of one request.
 

@@ -78,10 +78,8 @@ def quant_write_k(cache, k_bits, slot_mapping):
     if slots.shape[0] != k_bits.shape[0]:
         raise ValueError("one slot per K row")
     codes, scale = quantize_rows(k_bits)
-    for i, s in enumerate(slots):
-        if s < 0:
-            continue
-        paged.write_token(cache, s, codes[i], scale[i])
+    keep = slots >= 0
+    paged.write_tokens(cache, slots[keep], codes[keep], scale[keep])
     return cache
 
 

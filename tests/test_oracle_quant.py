@@ -156,3 +156,20 @@ def test_quantize_q_per_head(shape):
     assert q8.shape == shape and qs.shape == shape[:2]
     # each (token, head) row has its own scale: the scaled-up head gets a larger one
     assert qs[1, 7] > 8 * np.median(qs)
+
+
+def test_write_tokens_equals_token_by_token():
+    """The many-token scatter places every byte exactly as write_token does,
+    and leaves every other byte alone."""
+    rng = np.random.default_rng(5)
+    nb, bs = 9, 64
+    a = paged.new_cache(nb, bs, fill=0xEE)
+    b = paged.new_cache(nb, bs, fill=0xEE)
+    slots = rng.permutation(nb * bs)[:200]
+    codes = rng.integers(0, 256, (200, 128), dtype=np.uint8)
+    scales = np.ldexp(1.0, rng.integers(-20, 10, 200)).astype(np.float32)
+    for s_, c, sc in zip(slots, codes, scales):
+        paged.write_token(a, s_, c, sc)
+    paged.write_tokens(b, slots, codes, scales)
+    assert np.array_equal(a, b)
+    assert np.count_nonzero(a != 0xEE) <= 200 * 132
