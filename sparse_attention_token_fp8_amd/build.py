@@ -32,8 +32,10 @@ COMMON = [
 
 # Per-source extras.  The scoring kernels: ReLU on MFMA results needs no NaN
 # canonicalisation, and MFMA results stay in VGPRs (no AGPR round trip).
+SCORE_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA = {
-    "score.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "score.hip": SCORE_FLAGS,
+    "fused.hip": SCORE_FLAGS,
 }
 
 

@@ -106,6 +106,20 @@ hipError_t score_topk(const uint8_t* q_fp8, const float* w, const idx_kcache_t& 
                       const idx_batch_t* batch, int32_t k, int32_t* topk, int64_t topk_stride,
                       void* workspace, const uint16_t* kq, int64_t kq_stride,
                       const int64_t* slots, hipStream_t stream) {
+  if (keep_path(to_args(batch), batch->num_decode_tokens)) {
+    const BatchArgs b = to_args(batch);
+    const CacheArgs c{cache.data, cache.num_blocks};
+    KeepSlots ks;
+    keep_workspace_layout(b, workspace, &ks);
+    const bool fk = kq != nullptr && score_writes_k(b, batch->num_decode_tokens);
+    if (kq != nullptr && !fk) {
+      const hipError_t e = launch_quant_write_k(kq, batch->num_tokens, kq_stride, slots, cache.data,
+                                                cache.num_blocks * kBlock, stream);
+      if (e != hipSuccess) return e;
+    }
+    return launch_score_topk_keep(q_fp8, w, c, b, fk ? kq : nullptr, kq_stride, slots, cache.data,
+                                  k, ks, topk, topk_stride, stream);
+  }
   TopkWorkspace ws;
   fused_workspace(batch, workspace, &ws);
   const BatchArgs b = to_args(batch);
@@ -247,6 +261,8 @@ idx_status_t idx_topk(const float* logits, int64_t logits_stride, const idx_batc
 size_t idx_score_topk_workspace_size(const idx_batch_t* batch, int32_t k) {
   if (batch == nullptr || batch->num_tokens <= 0 || k < 1) return 0;
   if (check_batch(batch) != IDX_OK) return 0;
+  if (keep_path(to_args(batch), batch->num_decode_tokens))
+    return keep_workspace_layout(to_args(batch), nullptr, nullptr);
   return fused_workspace(batch, nullptr, nullptr);
 }
 

@@ -74,6 +74,21 @@ struct TopkWorkspace {
   int32_t slot_cap;
 };
 
+// Workspace of the fused score + top-k for decode-split batches over long
+// rows: each (row, chunk) slot holds up to `cap` candidates (key, position) in
+// position order, their count, the chunk's threshold and its largest key.  cap
+// is the chunk's positions (chunk_blocks * 64), so a row's slots can also hold
+// all its keys as one flat array when the row has to be rescored.
+struct KeepSlots {
+  uint2* cand;         // [T][nslots][cap] (key, position)
+  uint32_t* counts;    // [T][nslots]
+  uint32_t* taus;      // [T][nslots]
+  uint32_t* maxes;     // [T][nslots]: the chunk's largest key
+  int32_t nslots;
+  int32_t cap;
+  int32_t chunk_blocks;
+};
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool topk_uses_long_rows(int64_t T, int max_seq_len);
@@ -120,6 +135,40 @@ inline size_t topk_workspace_layout(int64_t T, int max_seq_len, int64_t logits_l
 }
 
 // ---------------------------------------------------------------- device --
+
+// ------------------------------------------------------ wave primitives --
+// Scans and reductions over the 64 lanes of a wave with DPP moves (row shifts
+// within rows of 16 lanes, then row broadcasts): a few cycles per step, where
+// a lane shuffle is a round trip through the LDS.  Every lane must be active.
+// `id` is the operation's identity; lanes with no source lane receive it.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v, uint32_t id, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
+}
+
+// Inclusive prefix sum over the lanes (lane i: v_0 + ... + v_i).
+__device__ __forceinline__ uint32_t wave_sum_incl(uint32_t v) {
+  return wave_scan_incl(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// The sum / max / min over the wave, in every lane (a wave-uniform value).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_sum_incl(v), 63);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane(
+      (int)wave_scan_incl(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; }), 63);
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane(
+      (int)wave_scan_incl(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; }), 63);
+}
 
 // Monotone map float -> uint32 (larger float, larger key); -0 maps to +0.
 __device__ __forceinline__ uint32_t order_key(float f) {

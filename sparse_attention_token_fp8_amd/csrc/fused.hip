@@ -1,0 +1,463 @@
+// Fused score + top-k for batches scored one token per work-group (decode
+// batches over long contexts): the scores never reach HBM.
+//
+// IndexCache blog post, SparseAttnIndexer.forward_cuda and the op body: one op
+// takes q_fp8, the paged K cache and the folded weights and leaves the top-k
+// positions in topk_indices_buffer; no score tensor crosses its boundary.
+//
+// Method.  A row of n causal positions is scored by work-groups that each own
+// a chunk of positions (the decode work split of score_device.hpp).
+//  1. Each work-group keeps its chunk's scores in LDS.  It places a threshold
+//     tau_c with at least m_c keys of the chunk at or above it, where m_c is
+//     the chunk's expected share of the row's top k plus a wide margin
+//     (chunk_keep), and compacts the keys >= tau_c, in position order, into the
+//     chunk's slot of the workspace, with tau_c and the count beside them.
+//     (A chunk with at most m_c positions keeps them all, tau_c = 0.)
+//  2. One work-group per row gathers the slots.  Let T = max_c tau_c.  Every
+//     key of the row at or above T is a candidate (a chunk drops only keys
+//     below its tau_c <= T).  So if at least k candidates are >= T, the k-th
+//     largest key of the row is the k-th largest candidate, every key above it
+//     and every key equal to it is a candidate, and the exact select over the
+//     candidates (ties to the lower position) is the exact top-k of the row.
+//  3. Otherwise (some chunk held far more than its share of the row's top k)
+//     the row is scored again, whole, and selected from all its keys.  So the
+//     result never depends on the thresholds; they only decide how much work
+//     the exact select does.
+//
+// The rescoring uses the same per-block operation sequence as the scoring
+// kernels, so every key equals the one idx_logits would produce, and the rows
+// equal those of idx_logits + idx_topk bit for bit.
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "score_device.hpp"
+#include "topk_device.hpp"
+
+#include <algorithm>
+
+namespace idx {
+namespace {
+
+constexpr int kMaxChunkPos = 64 * kBlock;       // decode chunks are at most 64 blocks
+constexpr int kKeepPer = kMaxChunkPos / kScoreThreads;   // 16 positions per thread
+
+// Keys a chunk of `nvalid` of a row's n positions keeps at least: its expected
+// share e of the row's top k plus 6 sqrt(e) + 8.  The number of top-k keys in
+// a chunk is hypergeometric with variance below e, so with scores that do not
+// depend on the position a chunk holds more than that with probability below
+// 1e-10 (for 8 rows x 131072 positions, k = 2048: 7e-11 per chunk, about
+// 3e-8 per call); and where it does happen the row is rescored (step 3).
+__device__ __forceinline__ uint32_t chunk_keep(int k, int nvalid, int n) {
+  const float e = (float)k * (float)nvalid / (float)n;
+  return (uint32_t)ceilf(e + 6.f * sqrtf(e)) + 8u;
+}
+
+// Threshold histograms: the top 12 bits of the order key (sign, exponent and
+// three mantissa bits, so bins are an eighth of an octave wide; counted by the
+// scoring loop), then the next 10 bits of the keys in the bin that holds the
+// m-th largest.
+constexpr int kTauBins = 4096;
+constexpr int kTauShift = kKeepHistShift;
+constexpr int kTau2Bins = 1024;
+constexpr int kTau2Shift = 10;
+
+// In the histogram h[0..64*PER) of one work-group, the bin holding the
+// need-th largest entry (1 <= need <= total), found by one wave on its own:
+// lane i sums bins [(63-i)*PER, (64-i)*PER) (lanes in descending key order),
+// one scan finds the lane whose bins reach `need`, a second scan over that
+// lane's bins the bin.  *above = entries in higher bins.
+template <int PER>
+__device__ __forceinline__ uint32_t wave_find_bin(const uint32_t* h, uint32_t need, uint32_t* above,
+                                                  int lane) {
+  static_assert(PER % 4 == 0 && PER <= 64, "bins per lane");
+  constexpr int NB = 64 * PER, Q = PER / 4;
+  const uint32_t* hb = h + NB - PER * (lane + 1);
+  // Lanes' ranges are PER words apart, so at the same offset they would all hit
+  // one bank group: lane l reads its 16-byte chunks starting at chunk l % Q.
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hb + 4 * ((i + lane) % Q));
+    sum += v.x + v.y + v.z + v.w;
+  }
+  const uint32_t incl = wave_sum_incl(sum);
+  const int L = __ffsll((unsigned long long)__ballot(incl >= need)) - 1;
+  const uint32_t before = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), L);
+  const uint32_t* hl = h + NB - PER * (L + 1);
+  const uint32_t c = lane < PER ? hl[PER - 1 - lane] : 0u;   // lane j: the lane's j-th highest bin
+  const uint32_t inc2 = wave_sum_incl(c);
+  const int j = __ffsll((unsigned long long)__ballot(lane < PER && before + inc2 >= need)) - 1;
+  *above = before + (uint32_t)__builtin_amdgcn_readlane((int)(inc2 - c), j);
+  return (uint32_t)(NB - PER * (L + 1) + (PER - 1 - j));
+}
+
+// Step 1, after the work-group's scores are in `kept` (position order), their
+// level-1 histogram in `hist` and their largest key in table[0], every wave
+// past the scoring loop; hist2 is zero.  tau is the lower edge of the level-2
+// bin holding the m-th largest key (so at least m keys are >= tau, and at most
+// the bin's other keys besides them); every wave finds it on its own from the
+// shared histograms.  `table` holds 65 words.
+__device__ __forceinline__ void chunk_filter(const float* kept, int t, int cx, int chunk_blocks,
+                                             int n, int k, const KeepSlots& ks, uint32_t* hist,
+                                             uint32_t* hist2, uint32_t* table) {
+  constexpr int NT = kScoreThreads, E = kKeepPer;
+  const int lane = threadIdx.x & 63;
+  const int base = cx * chunk_blocks * kBlock;
+  const int nvalid = min(n - base, chunk_blocks * kBlock);
+  const uint32_t m = chunk_keep(k, nvalid, n);
+  const bool cut = (uint32_t)nvalid > m;          // else the chunk keeps every key
+  uint32_t key[E];
+  bool pass[E];
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = kept[e * NT + threadIdx.x];   // all reads first (in bounds)
+  const uint32_t kmax = table[0];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    pass[e] = e * NT + (int)threadIdx.x < nvalid;
+    key[e] = pass[e] ? order_key(v[e]) : 0u;
+  }
+  uint32_t tau = 0u;
+  if (cut) {                                      // uniform over the work-group
+    uint32_t above;
+    const uint32_t d1 = wave_find_bin<kTauBins / 64>(hist, m, &above, lane);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (pass[e] && (key[e] >> kTauShift) == d1)
+        atomicAdd(&hist2[(key[e] >> kTau2Shift) & (kTau2Bins - 1)], 1u);
+    __syncthreads();
+    uint32_t above2;
+    const uint32_t d2 = wave_find_bin<kTau2Bins / 64>(hist2, m - above, &above2, lane);
+    tau = (d1 << kTauShift) | (d2 << kTau2Shift);
+#pragma unroll
+    for (int e = 0; e < E; ++e) pass[e] = pass[e] && key[e] >= tau;
+  }
+  const size_t slot = (size_t)t * ks.nslots + cx;
+  uint2* dst = ks.cand + slot * ks.cap;
+  const uint32_t cap = (uint32_t)ks.cap;
+  const uint32_t cnt = compact_ordered_to<NT, E>(key, pass, base, 0u, table + 1,
+                                                 [&](uint32_t i, uint32_t kk, int pos) {
+                                                   if (i < cap) dst[i] = make_uint2(kk, (uint32_t)pos);
+                                                 });
+  if (threadIdx.x == 0) {
+    ks.counts[slot] = cnt;
+    ks.taus[slot] = tau;
+    ks.maxes[slot] = kmax;
+  }
+}
+
+// Decode scoring that keeps each chunk's candidates (step 1).  With FK it also
+// writes this step's new K rows, as score_decode_write_kernel does.
+template <int NB, bool FK>
+__global__ __launch_bounds__(kScoreThreads)
+__attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_keep_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
+    int chunk_blocks, int ident, NewRows nk, int k, KeepSlots ks) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
+  __shared__ float kept[kMaxChunkPos];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kTauBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist2[kTau2Bins];
+  __shared__ uint32_t table[1 + kKeepPer * kScoreThreads / 64];
+  // the scoring loop counts into hist and maximises into table[0]
+  for (int i = threadIdx.x; i < kTauBins / 4; i += kScoreThreads)
+    reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = threadIdx.x; i < kTau2Bins / 4; i += kScoreThreads)
+    reinterpret_cast<uint4*>(hist2)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) table[0] = 0u;
+  __syncthreads();
+  int cx, ry;
+  xcd_spread(&cx, &ry);
+  const int n = decode_body<NB, FK, false, true>(cx, ry, q8, w, cache, b, nullptr, 0, chunk_blocks,
+                                                 ident != 0, lds, nk, nullptr, kept, hist, table);
+  if (n <= k) return;                           // nothing here, or a row the resolve takes whole
+  __syncthreads();                              // every wave's scores are in `kept`
+  chunk_filter(kept, ry, cx, chunk_blocks, n, k, ks, hist, hist2, table);
+}
+
+// ------------------------------------------------------------- resolve --
+
+constexpr int kResThreads = 1024;
+constexpr int kResCap = 8192;                   // candidates a row can hold in LDS
+constexpr int kRescoreWaves = 8;
+constexpr int kSpecSlots = 128;                 // rows of up to 128 slots preload candidates
+constexpr int kSpecPer = 8;                     // entries each thread preloads
+
+struct ResolveLds {
+  uint32_t ckey[kResCap];
+  int32_t cpos[kResCap];
+  uint32_t hist[kBins1];
+  uint32_t pre[kMaxSlots + 1];
+  uint32_t bucket[64];
+  uint32_t scratch[scratch_words<kResThreads>()];
+  uint32_t misc[4];                             // T, largest key, candidates >= T
+};
+struct RescoreLds {
+  uint8_t stage[kRescoreWaves][kBlockBytes];
+  uint8_t lin[kRescoreWaves][kLinScratch];
+};
+constexpr size_t kResolveSmem = sizeof(ResolveLds) > sizeof(RescoreLds) ? sizeof(ResolveLds)
+                                                                         : sizeof(RescoreLds);
+
+// Step 3: keys of all n positions of token t's row into keys[0..n), by
+// kRescoreWaves waves of the work-group (the others idle), with the scoring
+// kernels' per-block operations.
+__device__ __forceinline__ void rescore_row(const uint8_t* __restrict__ q8,
+                                            const float* __restrict__ w, const CacheArgs& cache,
+                                            const BatchArgs& b, int t, int r, int n,
+                                            uint32_t* __restrict__ keys, RescoreLds* sm) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  if (wave >= kRescoreWaves) return;
+  QFrag f[1];
+  load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
+  LinFrag lf;
+  make_lin<1>(lf, f, sm->lin[wave], lane);
+  uint8_t* slot = sm->stage[wave];
+  const int lp = lane_pos(lane);
+  const int nb = (n + kBlock - 1) / kBlock;
+  for (int lb = wave; lb < nb; lb += kRescoreWaves) {
+    const int64_t pb = phys_block(b, cache, r, lb);
+    WaveStage st;
+    wave_stage_load(st, cache.data + (pb >= 0 ? pb : 0) * kBlockBytes, pb >= 0 ? kBlockBytes : 0,
+                    lane);
+    wave_stage_store(st, slot, lane);
+    wave_sync_lds();
+    KBlock kb;
+    lds_kblock(kb, slot, lane);
+    wave_sync_lds();                            // reads done before the slot is rewritten
+    float v;
+    block_scores<1>(f, lf, kb, &v);
+    const int s = lb * kBlock + lp;
+    if (s < n) keys[s] = order_key(v);
+  }
+}
+
+// Steps 2 and 3 for one row per work-group.  The row's length, the slot
+// counts, thresholds and maxima and (for rows of up to kSpecSlots slots) the
+// first entries of every slot are loaded at once, so the gather costs one
+// round trip to memory.
+__global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
+    int ident, int k, KeepSlots ks, int32_t* __restrict__ topk, int64_t ldo) {
+  constexpr int NT = kResThreads;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kResolveSmem];
+  ResolveLds* sm = reinterpret_cast<ResolveLds*>(smem);
+  const int t = blockIdx.x;
+  const uint32_t cap = (uint32_t)ks.cap;
+  const size_t rbase = (size_t)t * ks.nslots;   // the row's first slot
+  // Preload, before the row's length is known: thread i takes slot i / tps of
+  // the kSpecSlots (or fewer) first slots; entries past a slot's count are
+  // read but never used.
+  const int nsp = min(ks.nslots, kSpecSlots);
+  const int tps = NT / nsp;
+  const int my_slot = min((int)threadIdx.x / tps, nsp - 1);
+  const int my_lane = (int)threadIdx.x - my_slot * tps;
+  const bool my_ok = (int)threadIdx.x < tps * nsp;
+  uint2 sc[kSpecPer];
+  {
+    const size_t sb = (rbase + my_slot) * cap;
+#pragma unroll
+    for (int u = 0; u < kSpecPer; ++u) sc[u] = ks.cand[sb + min((uint32_t)(my_lane + tps * u), cap - 1u)];
+  }
+  // slot summaries of the first 64 slots, one per lane of wave 0
+  const int c0 = threadIdx.x;
+  uint32_t v0 = 0u, tv0 = 0u, mx0 = 0u;
+  if (c0 < 64 && c0 < ks.nslots) {
+    v0 = ks.counts[rbase + c0];
+    tv0 = ks.taus[rbase + c0];
+    mx0 = ks.maxes[rbase + c0];
+  }
+  int r, n;
+  if (ident) {                                  // one new token per request: token t is request t
+    r = t;
+    n = min(max(b.seq_lens[t], 0), b.max_seq_len);
+  } else {
+    const TokenPos tp = token_pos_wave(b, t);
+    r = tp.r;
+    n = tp.n;
+  }
+  int32_t* out = topk + (size_t)t * ldo;
+  if (n <= k) {
+    for (int j = threadIdx.x; j < k; j += NT) out[j] = j < n ? j : -1;
+    return;
+  }
+  const int nsl = min((n + ks.cap - 1) / ks.cap, ks.nslots);
+  for (int i = threadIdx.x; i < kBins1; i += NT) sm->hist[i] = 0u;   // for the select's first pass
+  // slot offsets, T = the largest threshold, the largest key
+  if (nsl <= 64) {
+    if (threadIdx.x < 64) {
+      const int c = threadIdx.x;
+      const uint32_t v = c < nsl ? min(v0, cap) : 0u;
+      const uint32_t incl = wave_sum_incl(v);
+      const uint32_t tv = wave_max(c < nsl ? tv0 : 0u), mx = wave_max(c < nsl ? mx0 : 0u);
+      if (c < nsl) sm->pre[c] = incl - v;
+      if (c == 63) { sm->pre[nsl] = incl; sm->misc[0] = tv; sm->misc[1] = mx; }
+    }
+  } else {
+    if (threadIdx.x == 0) { sm->misc[0] = 0u; sm->misc[1] = 0u; }
+    const int per = (nsl + NT - 1) / NT;
+    const int a0 = min(nsl, per * (int)threadIdx.x), a1 = min(nsl, a0 + per);
+    uint32_t sum = 0, tv = 0, mx = 0;
+    for (int c = a0; c < a1; ++c) {
+      sum += min(ks.counts[rbase + c], cap);
+      tv = max(tv, ks.taus[rbase + c]);
+      mx = max(mx, ks.maxes[rbase + c]);
+    }
+    uint32_t total;
+    uint32_t run = block_scan_excl<NT>(sum, &total, sm->scratch);   // orders misc's reset first
+    for (int c = a0; c < a1; ++c) { sm->pre[c] = run; run += min(ks.counts[rbase + c], cap); }
+    if (threadIdx.x == 0) sm->pre[nsl] = total;
+    atomicMax(&sm->misc[0], tv);
+    atomicMax(&sm->misc[1], mx);
+  }
+  __syncthreads();
+  const uint32_t C = sm->pre[nsl];
+  const uint32_t T = sm->misc[0];
+  const uint32_t kmax = sm->misc[1];
+  auto at = [&](uint32_t i) {                   // workspace index of candidate i (position order)
+    int lo = 0, hi = nsl - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm->pre[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return (rbase + lo) * cap + (i - sm->pre[lo]);
+  };
+  bool decided = false;                         // step 2 settled the row
+  if (C <= (uint32_t)kResCap) {
+    if (nsl <= nsp) {                           // every slot of the row was preloaded
+      const uint32_t cnt = sm->pre[my_slot + 1] - sm->pre[my_slot], at0 = sm->pre[my_slot];
+      if (my_ok && my_slot < nsl) {
+#pragma unroll
+        for (int u = 0; u < kSpecPer; ++u) {
+          const uint32_t j = (uint32_t)(my_lane + tps * u);
+          if (j < cnt) { sm->ckey[at0 + j] = sc[u].x; sm->cpos[at0 + j] = (int32_t)sc[u].y; }
+        }
+        const size_t sb = (rbase + my_slot) * cap;   // entries beyond the preloaded ones
+        for (uint32_t j = (uint32_t)(my_lane + tps * kSpecPer); j < cnt; j += (uint32_t)tps) {
+          const uint2 e = ks.cand[sb + j];
+          sm->ckey[at0 + j] = e.x;
+          sm->cpos[at0 + j] = (int32_t)e.y;
+        }
+      }
+    } else {
+      for (uint32_t i = threadIdx.x; i < C; i += NT) {
+        const size_t a = at(i);
+        const uint2 e = ks.cand[a];
+        sm->ckey[i] = e.x;
+        sm->cpos[i] = (int32_t)e.y;
+      }
+    }
+    __syncthreads();
+    uint32_t take, in_range;
+    const uint32_t kstar = select_kth_range<NT, false>(sm->ckey, C, (uint32_t)k, T, kmax, &take,
+                                                       sm->hist, sm->bucket, sm->scratch, &in_range);
+    if (in_range >= (uint32_t)k) {              // at least k candidates at or above T
+      emit_ordered<NT>([&](uint32_t i) { return make_uint2(sm->ckey[i], (uint32_t)sm->cpos[i]); },
+                       C, kstar, take, k, out, sm->scratch);
+      decided = true;
+    }
+  } else {                                      // too many for LDS: select in place
+    uint32_t above = 0u;
+    for (uint32_t i = threadIdx.x; i < C; i += NT) above += ks.cand[at(i)].x >= T;
+    above = wave_sum(above);
+    if (threadIdx.x == 0) sm->misc[2] = 0u;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) atomicAdd(&sm->misc[2], above);
+    __syncthreads();
+    if (sm->misc[2] >= (uint32_t)k) {
+      uint32_t take;
+      const uint32_t kstar = radix_kth<NT, 3>([&](auto&& fn) {
+        for (uint32_t i = threadIdx.x; i < C; i += NT) {
+          const uint32_t key = ks.cand[at(i)].x;
+          if (key >= T) fn(key);
+        }
+      }, (uint32_t)k, &take, sm->hist, sm->scratch);
+      emit_ordered<NT>([&](uint32_t i) {
+        const size_t a = at(i);
+        return ks.cand[a];
+      }, C, kstar, take, k, out, sm->scratch);
+      decided = true;
+    }
+  }
+  if (decided) return;
+  // Step 3: the row's own slots (nslots * cap entries of 8 bytes, n <=
+  // nslots * cap) take its rescored keys as one flat array of n words.
+  __syncthreads();                              // the candidates' LDS is reused
+  uint32_t* keys = reinterpret_cast<uint32_t*>(ks.cand + rbase * cap);
+  rescore_row(q8, w, cache, b, t, r, n, keys, reinterpret_cast<RescoreLds*>(smem));
+  __syncthreads();                              // every key written before any is read
+  uint32_t take;
+  const uint32_t kstar = radix_kth<NT, 3>([&](auto&& fn) {
+    for (int i = threadIdx.x; i < n; i += NT) fn(keys[i]);
+  }, (uint32_t)k, &take, sm->hist, sm->scratch);
+  emit_ordered<NT>([&](uint32_t i) { return make_uint2(keys[i], i); }, (uint32_t)n, kstar, take, k,
+                   out, sm->scratch);
+}
+
+}  // namespace
+
+bool keep_path(const BatchArgs& b, int64_t dec_tokens) {
+  const bool decode_split = b.max_query_len <= 1 || dec_tokens >= b.num_tokens;
+  if (!decode_split || !topk_uses_long_rows(b.num_tokens, b.max_seq_len)) return false;
+  const int cb = decode_chunk_blocks(b.max_seq_len, b.num_tokens);
+  const int64_t nslots = (b.max_seq_len + (int64_t)cb * kBlock - 1) / ((int64_t)cb * kBlock);
+  return nslots <= kMaxSlots;
+}
+
+size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks) {
+  const int cb = decode_chunk_blocks(b.max_seq_len, b.num_tokens);
+  const int64_t cap = (int64_t)cb * kBlock;
+  const int64_t nslots = std::max<int64_t>(1, (b.max_seq_len + cap - 1) / cap);
+  const size_t T = (size_t)b.num_tokens;
+  size_t off = 0;
+  const size_t o_cand = off;
+  off = align_up(off + sizeof(uint2) * T * nslots * cap, 256);
+  const size_t o_cnt = off;
+  off = align_up(off + sizeof(uint32_t) * T * nslots, 256);
+  const size_t o_tau = off;
+  off = align_up(off + sizeof(uint32_t) * T * nslots, 256);
+  const size_t o_max = off;
+  off = align_up(off + sizeof(uint32_t) * T * nslots, 256);
+  if (base && ks) {
+    char* p = static_cast<char*>(base);
+    ks->cand = reinterpret_cast<uint2*>(p + o_cand);
+    ks->counts = reinterpret_cast<uint32_t*>(p + o_cnt);
+    ks->taus = reinterpret_cast<uint32_t*>(p + o_tau);
+    ks->maxes = reinterpret_cast<uint32_t*>(p + o_max);
+    ks->nslots = (int32_t)nslots;
+    ks->cap = (int32_t)cap;
+    ks->chunk_blocks = cb;
+  }
+  return off;
+}
+
+hipError_t launch_score_topk_keep(const uint8_t* q8, const float* w, const CacheArgs& cache,
+                                  const BatchArgs& b, const uint16_t* kq, int64_t kq_stride,
+                                  const int64_t* slots, uint8_t* cache_w, int k,
+                                  const KeepSlots& ks, int32_t* out, int64_t ldo,
+                                  hipStream_t stream) {
+  if (b.num_tokens == 0) return hipSuccess;
+  const int ident = b.num_reqs == b.num_tokens && b.max_query_len <= 1;
+  if (b.max_seq_len > 0) {
+    const dim3 grid((unsigned)ks.nslots, (unsigned)b.num_tokens);
+    if (kq != nullptr) {
+      const NewRows nk{kq, kq_stride, slots, cache_w, cache.num_blocks * kBlock};
+      hipLaunchKernelGGL((score_keep_kernel<IDX_DECODE_RING, true>), grid, dim3(kScoreThreads), 0,
+                         stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+    } else {
+      hipLaunchKernelGGL((score_keep_kernel<IDX_DECODE_RING, false>), grid, dim3(kScoreThreads), 0,
+                         stream, q8, w, cache, b, ks.chunk_blocks, ident, NewRows{}, k, ks);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (kq != nullptr) {
+    const hipError_t e = launch_quant_write_k(kq, b.num_tokens, kq_stride, slots, cache_w,
+                                              cache.num_blocks * kBlock, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(topk_keep_resolve_kernel, dim3((unsigned)b.num_tokens), dim3(kResThreads), 0,
+                     stream, q8, w, cache, b, ident, k, ks, out, ldo);
+  return hipGetLastError();
+}
+
+}  // namespace idx

@@ -39,6 +39,22 @@ hipError_t launch_score_write_k(const uint8_t* q8, const float* w, const CacheAr
                                 const int64_t* slots, uint8_t* cache_w, float* logits, int64_t ld,
                                 float* samp, hipStream_t stream);
 
+// Whether idx_score_topk takes the fused path for this batch: every token
+// scored with the decode split, rows long enough for the long-row top-k.
+bool keep_path(const BatchArgs& b, int64_t dec_tokens);
+
+// Workspace of the fused path; returns its bytes and, with a base, fills `ks`.
+size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks);
+
+// Fused score + top-k (scores kept on chip, candidates compacted per chunk,
+// one exact select per row).  With kq, this step's new K rows are written to
+// the cache by the scoring kernel (score_writes_k must hold).
+hipError_t launch_score_topk_keep(const uint8_t* q8, const float* w, const CacheArgs& cache,
+                                  const BatchArgs& b, const uint16_t* kq, int64_t kq_stride,
+                                  const int64_t* slots, uint8_t* cache_w, int k,
+                                  const KeepSlots& ks, int32_t* out, int64_t ldo,
+                                  hipStream_t stream);
+
 // Finish long rows from the candidate slots of `ws`.
 hipError_t launch_topk_resolve(const float* logits, int64_t ld, const BatchArgs& b,
                                const TopkWorkspace& ws, int k, int32_t* out, int64_t ldo,

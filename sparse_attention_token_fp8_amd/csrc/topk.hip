@@ -226,12 +226,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
     if (threadIdx.x < 64) {
       const int c = threadIdx.x;
       const uint32_t v = c < nsl ? min(cnts[c], cap) : 0u;
-      uint32_t incl = v;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
-        if (c >= off) incl += y;
-      }
+      const uint32_t incl = wave_sum_incl(v);
       if (c < nsl) pre[c] = incl - v;
       if (c == 63) pre[nsl] = incl;
     }
@@ -283,11 +278,8 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
         put(i, ws.cand_key[a], ws.cand_pos[a]);
       }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
-      hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
-    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
     if ((threadIdx.x & 63) == 0) { atomicMin(&krange[0], lo); atomicMax(&krange[1], hi); }
     __syncthreads();
     uint32_t take;

@@ -29,12 +29,7 @@ template <int NT, bool LEAD = true>
 __device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* total, uint32_t* scratch) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
-    if (lane >= off) incl += y;
-  }
+  const uint32_t incl = wave_sum_incl(v);
   if (LEAD) __syncthreads();
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
@@ -79,46 +74,64 @@ __device__ __forceinline__ uint64_t block_scan_excl64(uint64_t v, uint64_t* tota
 template <int NT>
 constexpr int scratch_words() { return 2 * (NT / 64) + 8; }
 
-// In an LDS histogram h[0..nb) find the digit d, searching from the top, with
-// #(digit > d) < need <= #(digit >= d).  Returns d to every thread and sets
-// *above = #(digit > d) and *count = h[d].  If the histogram holds fewer than
-// `need` entries the result is digit 0 with *above = total.
+// In an LDS histogram h[0..nb), nb a power of two <= 2048, the digit d,
+// searched from the top, with #(digit > d) < need <= #(digit >= d): found by
+// one wave on its own (every wave of a block gets the same answer, with no
+// barrier).  Lane l sums the bins [nb - per(l+1), nb - per*l), per =
+// max(nb/64, 1) (lanes in descending key order; reads rotated by lane so that
+// few lanes of a pass hit one bank), one scan finds the lane whose bins reach
+// `need`, a second scan that lane's bins.  Sets *above = #(digit > d), *count = h[d] and
+// *total; with fewer than `need` entries the result is digit 0, *above = total.
+__device__ __forceinline__ uint32_t wave_digit(const uint32_t* h, int nb, uint32_t need,
+                                               uint32_t* above, uint32_t* count, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int per = nb >= 64 ? nb / 64 : 1;
+  const int active = nb >= 64 ? 64 : nb;
+  uint32_t sum = 0u;
+  if (lane < active) {
+    const uint32_t* hb = h + nb - per * (lane + 1);
+#pragma unroll
+    for (int i = 0; i < kBins1 / 64; ++i)
+      if (i < per) sum += hb[(i + lane) & (per - 1)];
+  }
+  const uint32_t incl = wave_sum_incl(sum);
+  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  *total = tot;
+  if (tot < need) {
+    *above = tot;
+    *count = 0u;
+    return 0u;
+  }
+  const int L = __ffsll((unsigned long long)__ballot(incl >= need)) - 1;
+  const uint32_t before = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), L);
+  const uint32_t* hl = h + nb - per * (L + 1);
+  const uint32_t c = lane < per ? hl[per - 1 - lane] : 0u;   // lane j: the lane's j-th highest bin
+  const uint32_t inc2 = wave_sum_incl(c);
+  const int j = __ffsll((unsigned long long)__ballot(lane < per && before + inc2 >= need)) - 1;
+  *above = before + (uint32_t)__builtin_amdgcn_readlane((int)(inc2 - c), j);
+  *count = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
+  return (uint32_t)(nb - per * (L + 1) + (per - 1 - j));
+}
+
+// wave_digit for a block of NT threads, every thread getting the answer: up
+// to four waves each search on their own; larger blocks let wave 0 search and
+// pass the result through `scratch` (four words) and one barrier.  Callers
+// synchronise before they reuse `h`.
 template <int NT>
-__device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32_t need,
-                                               uint32_t* above, uint32_t* scratch,
-                                               uint32_t* count = nullptr) {
-  const int per = nb / NT > 0 ? nb / NT : 1;
-  const int active = nb / per;
-  const int top = nb - 1 - per * (int)threadIdx.x;
-  uint32_t sum = 0;
-  if ((int)threadIdx.x < active)
-    for (int j = 0; j < per; ++j) sum += h[top - j];
-  uint32_t* res = scratch + NT / 64;
-  if (threadIdx.x == 0) { res[1] = 0u; res[2] = 0u; res[3] = 0u; }
-  uint32_t total;
-  // Every caller has synchronised after filling `h` (so after any earlier
-  // reads of `scratch`): the scan needs no leading barrier.
-  const uint32_t before = block_scan_excl<NT, false>(sum, &total, scratch);
-  if ((int)threadIdx.x < active && before < need && before + sum >= need) {
-    uint32_t cum = before;
-    for (int j = 0; j < per; ++j) {
-      const uint32_t c = h[top - j];
-      if (cum + c >= need) {
-        res[1] = (uint32_t)(top - j);
-        res[2] = cum;
-        res[3] = c;
-        break;
-      }
-      cum += c;
-    }
+__device__ __forceinline__ uint32_t block_digit(const uint32_t* h, int nb, uint32_t need,
+                                                uint32_t* above, uint32_t* count, uint32_t* total,
+                                                uint32_t* scratch) {
+  if (NT <= 256) return wave_digit(h, nb, need, above, count, total);
+  if (threadIdx.x < 64) {
+    uint32_t a, c, t;
+    const uint32_t d = wave_digit(h, nb, need, &a, &c, &t);
+    if (threadIdx.x == 0) { scratch[0] = d; scratch[1] = a; scratch[2] = c; scratch[3] = t; }
   }
   __syncthreads();
-  uint32_t d = res[1];
-  *above = res[2];
-  if (count) *count = res[3];
-  if (total < need) { d = 0; *above = total; }
-  __syncthreads();
-  return d;
+  *above = scratch[1];
+  *count = scratch[2];
+  *total = scratch[3];
+  return scratch[0];
 }
 
 // The `need`-th largest key (need >= 1) of the set visited by `visit(fn)`,
@@ -130,35 +143,55 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32
 template <int NT, int LEVELS, typename V>
 __device__ __forceinline__ uint32_t radix_kth(V&& visit, uint32_t need, uint32_t* take_eq,
                                               uint32_t* hist, uint32_t* scratch) {
+  uint32_t above, cnt, total;
   for (int i = threadIdx.x; i < kBins1; i += NT) hist[i] = 0;
   __syncthreads();
   visit([&](uint32_t key) { atomicAdd(&hist[key >> kShift1], 1u); });
   __syncthreads();
-  uint32_t above;
-  const uint32_t d1 = find_digit<NT>(hist, kBins1, need, &above, scratch);
+  const uint32_t d1 = block_digit<NT>(hist, kBins1, need, &above, &cnt, &total, scratch + NT / 64);
   need -= above;
+  __syncthreads();                              // every wave has read the histogram
   for (int i = threadIdx.x; i < kBins2; i += NT) hist[i] = 0;
   __syncthreads();
   visit([&](uint32_t key) {
     if ((key >> kShift1) == d1) atomicAdd(&hist[(key >> kShift2) & (kBins2 - 1)], 1u);
   });
   __syncthreads();
-  const uint32_t d2 = find_digit<NT>(hist, kBins2, need, &above, scratch);
+  const uint32_t d2 = block_digit<NT>(hist, kBins2, need, &above, &cnt, &total, scratch + NT / 64);
   need -= above;
   const uint32_t prefix = (d1 << (kShift1 - kShift2)) | d2;
   if (LEVELS == 2) {
     *take_eq = 0;
+    __syncthreads();                            // the histogram is free for the caller
     return prefix << kShift2;
   }
+  __syncthreads();
   for (int i = threadIdx.x; i < kBins3; i += NT) hist[i] = 0;
   __syncthreads();
   visit([&](uint32_t key) {
     if ((key >> kShift2) == prefix) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
   });
   __syncthreads();
-  const uint32_t d3 = find_digit<NT>(hist, kBins3, need, &above, scratch);
+  const uint32_t d3 = block_digit<NT>(hist, kBins3, need, &above, &cnt, &total, scratch + NT / 64);
   *take_eq = need - above;
+  __syncthreads();                              // the histogram is free for the caller
   return (prefix << kShift2) | d3;
+}
+
+// fn(ckey[i]) for i = threadIdx.x, threadIdx.x + NT, ... < C, the reads of
+// four iterations issued together (a loop that uses each LDS read at once
+// would wait for every read in turn).
+template <int NT, typename F>
+__device__ __forceinline__ void for_keys(const uint32_t* ckey, uint32_t C, F&& fn) {
+  constexpr int U = 4;
+  for (uint32_t i = threadIdx.x; i < C; i += U * NT) {
+    uint32_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = ckey[min(i + u * NT, C - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + u * NT < C) fn(x[u]);
+  }
 }
 
 // Exact `need`-th largest key (1 <= need <= C) of ckey[0..C) in LDS, with
@@ -166,50 +199,75 @@ __device__ __forceinline__ uint32_t radix_kth(V&& visit, uint32_t need, uint32_t
 // up to 11 bits are taken over [kmin, kmax] of the candidates; when the bin
 // holding the answer has at most 64 keys they are ranked by one wave.
 // `hist` holds kBins1 words, `bucket` 64 words.  select_kth_range takes the
-// range from the caller (every key must lie in [kmin, kmax]).
-template <int NT>
+// range from the caller: keys outside [kmin, kmax] are ignored.
+// With in_range, *in_range receives the number of keys in [kmin, kmax]; when
+// it is below `need` nothing more is done and the result is meaningless.
+// ZERO_FIRST = false: the caller has cleared hist[0..kBins1) and synchronised.
+template <int NT, bool ZERO_FIRST = true>
 __device__ __forceinline__ uint32_t select_kth_range(const uint32_t* ckey, uint32_t C, uint32_t need,
                                                      uint32_t kmin, uint32_t kmax,
                                                      uint32_t* take_eq, uint32_t* hist,
-                                                     uint32_t* bucket, uint32_t* scratch) {
+                                                     uint32_t* bucket, uint32_t* scratch,
+                                                     uint32_t* in_range = nullptr) {
   constexpr int NW = NT / 64;
-  uint32_t* sx = scratch + 2 * NW;              // bucket fill, K*, take
+  uint32_t* sx = scratch + 2 * NW;              // bucket fill, K*, take, count
   uint32_t base = kmin;
   int width = kmax == kmin ? 0 : 32 - __clz(kmax - kmin);   // keys in play: [base, base + 2^width)
+  if (in_range != nullptr && width == 0) {      // every key in play equals kmin: count them
+    if (threadIdx.x == 0) sx[3] = 0u;
+    __syncthreads();
+    uint32_t c = 0;
+    for_keys<NT>(ckey, C, [&](uint32_t x) { c += x == kmin; });
+    c = wave_sum(c);
+    if ((threadIdx.x & 63) == 0) atomicAdd(&sx[3], c);
+    __syncthreads();
+    *in_range = sx[3];
+    __syncthreads();
+  }
+  bool first = true;
   while (width > 0) {
     const int shift = width > 11 ? width - 11 : 0;
     const int nb = 1 << (width - shift);
-    for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0;
+    if (!first) __syncthreads();                // every wave is done with the last pass's bins
+    if (ZERO_FIRST || !first)
+      for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0;
     if (threadIdx.x == 0) sx[0] = 0u;
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < C; i += NT) {
-      const uint32_t x = ckey[i];
+    for_keys<NT>(ckey, C, [&](uint32_t x) {
       if (x >= base && ((uint64_t)(x - base) >> width) == 0) atomicAdd(&hist[(x - base) >> shift], 1u);
-    }
+    });
     __syncthreads();
-    uint32_t above, in_bin;
-    const uint32_t d = find_digit<NT>(hist, nb, need, &above, scratch, &in_bin);
+    uint32_t above, in_bin, total;
+    const uint32_t d = block_digit<NT>(hist, nb, need, &above, &in_bin, &total, scratch + NW);
+    if (first && in_range != nullptr) {
+      *in_range = total;
+      if (total < need) {                       // uniform: every thread has the same total
+        *take_eq = 0;
+        return base;
+      }
+    }
+    first = false;
     need -= above;
     base += d << shift;
     width = shift;
     if (width > 0 && in_bin <= 64) {            // rank the bin's keys in one wave
-      for (uint32_t i = threadIdx.x; i < C; i += NT) {
-        const uint32_t x = ckey[i];
+      for_keys<NT>(ckey, C, [&](uint32_t x) {
         if (x >= base && ((uint64_t)(x - base) >> width) == 0) {
           const uint32_t j = atomicAdd(&sx[0], 1u);
           if (j < 64u) bucket[j] = x;
         }
-      }
+      });
       __syncthreads();
-      if ((uint32_t)threadIdx.x < in_bin) {
-        const uint32_t x = bucket[threadIdx.x];
+      if (threadIdx.x < 64) {                   // wave 0: lane j holds bucket[j], ranks by readlane
+        const int lane = threadIdx.x;
+        const uint32_t x = (uint32_t)lane < in_bin ? bucket[lane] : 0u;
         uint32_t gt = 0, ge = 0;
-        for (uint32_t j = 0; j < in_bin; ++j) {
-          const uint32_t y = bucket[j];
+        for (int j = 0; j < (int)in_bin; ++j) {
+          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
           gt += y > x;
           ge += y >= x;
         }
-        if (gt < need && need <= ge) { sx[1] = x; sx[2] = need - gt; }
+        if ((uint32_t)lane < in_bin && gt < need && need <= ge) { sx[1] = x; sx[2] = need - gt; }
       }
       __syncthreads();
       base = sx[1];
@@ -236,11 +294,8 @@ __device__ __forceinline__ uint32_t select_kth(const uint32_t* ckey, uint32_t C,
     lo = min(lo, x);
     hi = max(hi, x);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
-  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
   if (threadIdx.x == 0) { sx[0] = 0xffffffffu; sx[1] = 0u; }
   __syncthreads();
   if (lane == 0) { atomicMin(&sx[0], lo); atomicMax(&sx[1], hi); }
@@ -256,11 +311,17 @@ __device__ __forceinline__ void emit_ordered(G&& get, uint32_t count, uint32_t k
                                              int k, int32_t* __restrict__ out, uint32_t* scratch) {
   const uint32_t per = (count + NT - 1) / NT;
   const uint32_t i0 = min(count, per * threadIdx.x), i1 = min(count, i0 + per);
+  constexpr int U = 4;                          // reads of four elements issued together
   uint32_t gt = 0, eq = 0;
-  for (uint32_t i = i0; i < i1; ++i) {
-    const uint32_t key = get(i).x;
-    gt += key > kstar;
-    eq += key == kstar;
+  for (uint32_t i = i0; i < i1; i += U) {
+    uint32_t key[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) key[u] = get(min(i + u, i1 - 1)).x;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      gt += i + u < i1 && key[u] > kstar;
+      eq += i + u < i1 && key[u] == kstar;
+    }
   }
   uint32_t gb, eb, gall, eall;
   if (count < 65536u) {                         // both counts fit 16 bits: one 32-bit scan
@@ -274,15 +335,21 @@ __device__ __forceinline__ void emit_ordered(G&& get, uint32_t count, uint32_t k
     gb = (uint32_t)pre; eb = (uint32_t)(pre >> 32);
     gall = (uint32_t)total; eall = (uint32_t)(total >> 32);
   }
-  for (uint32_t i = i0; i < i1; ++i) {
-    const uint2 kp = get(i);
-    if (kp.x > kstar) {
-      const uint32_t o = gb + min(eb, take_eq);
-      if (o < (uint32_t)k) out[o] = (int32_t)kp.y;
-      ++gb;
-    } else if (kp.x == kstar) {
-      if (eb < take_eq && gb + eb < (uint32_t)k) out[gb + eb] = (int32_t)kp.y;
-      ++eb;
+  for (uint32_t i = i0; i < i1; i += U) {
+    uint2 kp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kp[u] = get(min(i + u, i1 - 1));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i + u >= i1) break;
+      if (kp[u].x > kstar) {
+        const uint32_t o = gb + min(eb, take_eq);
+        if (o < (uint32_t)k) out[o] = (int32_t)kp[u].y;
+        ++gb;
+      } else if (kp[u].x == kstar) {
+        if (eb < take_eq && gb + eb < (uint32_t)k) out[gb + eb] = (int32_t)kp[u].y;
+        ++eb;
+      }
     }
   }
   const uint32_t written = min((uint32_t)k, gall + min(eall, take_eq));
@@ -345,17 +412,17 @@ __device__ __forceinline__ uint32_t sample_tau(const float* v, int ns, int n, in
 }
 
 // Ordered compaction of one batch: element (e, thread) sits at position
-// base + e*NT + threadIdx.x; those with pass[e] are appended to (ckey, cpos)
-// after `start` entries, in ascending position order (entries past `cap` are
-// counted, not stored).  `table` holds E*NT/64 <= 64 words of LDS.  There is
-// one barrier: every wave scans the per-(e, wave) counts itself.  So two
-// consecutive calls must not share a table (callers alternate two), and a
-// caller synchronises before it reads what was compacted into LDS.  Returns
-// the batch's number of passing elements.
-template <int NT, int E, typename Pos>
-__device__ __forceinline__ uint32_t compact_ordered(const uint32_t* key, const bool* pass, int base,
-                                                    uint32_t start, uint32_t* ckey, Pos* cpos,
-                                                    uint32_t cap, uint32_t* table) {
+// base + e*NT + threadIdx.x; those with pass[e] are handed to put(slot, key,
+// position) with slot = start + their rank in ascending position order (put
+// drops slots past its capacity; they are still counted).  `table` holds
+// E*NT/64 <= 64 words of LDS.  There is one barrier: every wave scans the
+// per-(e, wave) counts itself.  So two consecutive calls must not share a
+// table (callers alternate two), and a caller synchronises before it reads
+// what was compacted into LDS.  Returns the batch's number of passing
+// elements.
+template <int NT, int E, typename Put>
+__device__ __forceinline__ uint32_t compact_ordered_to(const uint32_t* key, const bool* pass, int base,
+                                                       uint32_t start, uint32_t* table, Put&& put) {
   constexpr int NW = NT / 64;
   static_assert(E * NW <= 64, "one count per lane");
   const int lane = threadIdx.x & 63;
@@ -369,24 +436,28 @@ __device__ __forceinline__ uint32_t compact_ordered(const uint32_t* key, const b
   __syncthreads();
   // exclusive prefix over the E*NW counts in (e, wave) order, lane i holding count i
   const uint32_t c = lane < E * NW ? table[lane] : 0u;
-  uint32_t incl = c;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
-    if (lane >= off) incl += y;
-  }
+  const uint32_t incl = wave_sum_incl(c);
   const uint32_t excl = incl - c;
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
   const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)excl, e * NW + wave);
-    if (pass[e]) {
-      const uint32_t slot = start + at + (uint32_t)__popcll(m[e] & below);
-      if (slot < cap) { ckey[slot] = key[e]; cpos[slot] = (Pos)(base + e * NT + (int)threadIdx.x); }
-    }
+    if (pass[e])
+      put(start + at + (uint32_t)__popcll(m[e] & below), key[e], base + e * NT + (int)threadIdx.x);
   }
   return total;
+}
+
+// The same into separate key and position arrays of `cap` entries.
+template <int NT, int E, typename Pos>
+__device__ __forceinline__ uint32_t compact_ordered(const uint32_t* key, const bool* pass, int base,
+                                                    uint32_t start, uint32_t* ckey, Pos* cpos,
+                                                    uint32_t cap, uint32_t* table) {
+  return compact_ordered_to<NT, E>(key, pass, base, start, table,
+                                   [&](uint32_t slot, uint32_t k, int pos) {
+                                     if (slot < cap) { ckey[slot] = k; cpos[slot] = (Pos)pos; }
+                                   });
 }
 
 }  // namespace idx

@@ -76,17 +76,46 @@ def oracle_batch(wl):
 
 
 def oracle_layer(wl, layer, reqs=None, with_new=True, fill=0xEE):
-    """The oracle's cache (only the requests in ``reqs``) and q8 / folded w."""
-    reqs = range(wl.num_reqs) if reqs is None else reqs
+    """The oracle's cache (only the requests in ``reqs``) and q8 / folded w.
+    Requests own disjoint blocks, so they are quantised and written in
+    parallel threads (numpy releases the GIL in the heavy steps)."""
+    reqs = list(range(wl.num_reqs) if reqs is None else reqs)
     cache = np.full((wl.num_blocks, 64, 132), fill, np.uint8)
-    for r in reqs:
+
+    def one(r):
         kb = wl.request_k(layer, r)
         L, n = int(wl.seq_lens[r]), int(wl.new_tokens[r])
         upto = L if with_new else L - n
         oquant.quant_write_k(cache, kb[:upto], wl.slots(r, np.arange(upto)))
+
+    with cf.ThreadPoolExecutor(workers()) as ex:
+        list(ex.map(one, reqs))
     q8, qs = oquant.quantize_q(wl.q_bits(layer))
     w = oquant.fold_weights(wl.w_raw(layer), qs)
     return dict(cache=cache, q8=q8, qs=qs, w=w)
+
+
+def oracle_rows(wl, orc, tokens):
+    """Oracle scores {t: fp64 row} for the given query tokens, in parallel
+    threads (one BLAS thread each)."""
+    ob = oracle_batch(wl)
+
+    def one(t):
+        r, p = ob.token_request(int(t)), ob.token_position(int(t))
+        return int(t), oracle.logits.logits_row(orc["q8"][t], orc["w"][t], orc["cache"],
+                                                 wl.block_table[r], p)
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except Exception:                              # pragma: no cover - optional
+        limit = None
+    try:
+        with cf.ThreadPoolExecutor(workers()) as ex:
+            return dict(ex.map(one, tokens))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
 
 
 # ------------------------------------------------------------- comparison --

@@ -457,6 +457,50 @@ def test_topk_threshold_fallbacks(env):
         check_topk_band(b[t], sc, wl.k, f"token {t}")
 
 
+def _scale_positions(m, torch, dev_cache, orc_cache, block_table_row, positions, factor):
+    """Multiply the stored fp32 scale of the given logical positions by a power
+    of two in both caches: their scores scale by exactly that factor."""
+    flat_d = dev_cache.tensor.view(dev_cache.num_blocks, -1)
+    flat_o = orc_cache.reshape(orc_cache.shape[0], -1)
+    for p in positions:
+        b = int(block_table_row[p // 64])
+        lo = 64 * 128 + (p % 64) * 4
+        sc = flat_o[b, lo:lo + 4].copy().view("<f4") * np.float32(factor)
+        flat_o[b, lo:lo + 4] = sc.view(np.uint8)
+        flat_d[b, lo:lo + 4] = torch.from_numpy(sc.view(np.uint8).copy()).cuda()
+
+
+def test_fused_rescore_fallback(env):
+    """Decode rows over long contexts are selected from per-chunk candidates
+    (each work-group keeps about its expected share of the row's top k plus a
+    margin).  Here 2048 consecutive positions of request 0 have their scores
+    scaled by 8, so the chunks there hold far more than their share: the row
+    must be rescored whole.  Fused equals idx_logits + idx_topk and the oracle,
+    through idx_score_topk and through an F layer that writes its K rows."""
+    m, torch = env
+    wl = random_batch(4010, [20000, 9000, 30000], 1, k=2048)
+    dev = device_layer(m, torch, wl, 0, with_new=True)
+    orc = oracle_layer(wl, 0)
+    hot = list(range(8192, 8192 + 2048))
+    _scale_positions(m, torch, dev["cache"], orc["cache"], wl.block_table[0], hot, 8.0)
+    batch = device_batch(m, wl)
+    lg = m.idx_logits(dev["q8"], dev["w"], dev["cache"], batch)
+    a = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+    b = m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], batch, wl.k).cpu().numpy()
+    assert np.array_equal(a, b)
+    want = oracle.logits.logits(orc["q8"], orc["w"], orc["cache"], oracle_batch(wl))
+    for t, sc in want.items():
+        check_topk_band(b[t], sc, wl.k, f"token {t}")
+    assert np.isin(hot, b[0]).sum() > 700, "the scaled positions should dominate row 0"
+    # the same through an F layer whose scoring kernel writes the new K rows
+    # (the new rows are already in the cache, so the bytes do not change)
+    topk = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
+    m.idx_indexcache_layer(dev["k_new"], dev["cache"], dev["q8"], dev["w"], True, True,
+                           dev["slots_new"], batch, wl.k, topk)
+    assert np.array_equal(topk.cpu().numpy(), a)
+    assert np.array_equal(dev["cache"].tensor.cpu().numpy(), orc["cache"])
+
+
 def test_layer_k_write_inside_scoring(env):
     """An F layer of a decode batch writes its new K rows from inside the decode
     scoring kernel.  The cache bytes and the top-k rows must equal the separate
