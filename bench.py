@@ -3,9 +3,27 @@
 A step is the whole hot path for one batch: one F layer of the IndexCache
 stack (idx_indexcache_layer), which quantises + scatters this step's new K
 rows, scores every causal position and selects the top-k into the persistent
-buffer.  Inputs are resident in HBM before timing starts.  The headline workload is the 128K decode batch
-(8 requests x 131072 positions, k = 2048); the 32K chunked prefill (24576
-cached + 8192 new tokens) is reported alongside in the same JSON line.
+buffer (on decode batches over long contexts the scores never leave the chip:
+fused score + top-k).  Inputs are resident in HBM before timing starts.
+
+The headline workload is the 128K decode batch (8 requests x 131072
+positions, k = 2048).  The JSON line also carries every other workload:
+
+  prefill-24k+8k     chunked prefill, 24576 cached + 8192 new tokens
+  decode-64x16k-32k  64 decode requests, contexts uniform in [16K, 32K]
+  prefill-1k         T = S = 1024 causal, k = 256
+  stack-16L-32x64k   16 layers, FSSS x4, 32 decode requests at 64K (a step is
+                     the whole stack; all-F is timed beside it)
+
+each with its step time, throughput, the step's per-kernel times and the
+dominant kernel's roofline.  Per-kernel times come from a separate traced loop
+(idx_trace_begin: HIP events on the kernels' stream around every launch), so
+the timed loop that gives `value` carries no extra events.  Algorithmic work
+per launch of the dominant kernel:
+
+  decode scoring   sum_t (p_t + 1) * 132 B of K + per token 8192 B of q,
+                   256 B of weights, 256 + 132 B of its new K row
+  prefill scoring  2 * 64 * 128 * sum_t (p_t + 1) fp8 flops (causal pairs)
 
 Decode steps rotate through several copies of the K cache so the 256 MB
 Infinity Cache cannot serve the K bytes across iterations.
@@ -16,15 +34,15 @@ Infinity Cache cannot serve the K bytes across iterations.
 `roofline.traffic` is the dominant kernel's HBM bytes per launch as the
 FETCH_SIZE / WRITE_SIZE counters saw them in a profiled run of this script,
 scaled by what the same counters read for a plain copy of known size.  It is
-read from the committed counter summary and reported only while the scoring
-sources are byte-identical to the ones that summary was taken on (else null).
+read from the committed counter summary and reported only while the kernel's
+sources are the ones that summary was taken on (else null).
 """
 
 import argparse
 import hashlib
-import re
 import json
 import os
+import re
 import sys
 import time
 
@@ -37,9 +55,17 @@ METRIC = "indexer query-tokens/s (128K decode, 32K prefill); % of HBM / fp8 MFMA
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 PROFILES = os.path.join(ROOT, "profiles")
-SCORE_SOURCES = ("sparse_attention_token_fp8_amd/csrc/score.hip",
-                 "sparse_attention_token_fp8_amd/csrc/score_device.hpp",
-                 "sparse_attention_token_fp8_amd/csrc/common.hpp")
+CSRC = "sparse_attention_token_fp8_amd/csrc/"
+HEADLINE = "decode-8x128k"
+SINGLE_LAYER = ("decode-8x128k", "prefill-24k+8k", "decode-64x16k-32k", "prefill-1k")
+STACK = "stack-16L-32x64k"
+# sources whose code the dominant kernels are built from (for the traffic digest)
+KERNEL_SOURCES = {
+    "score_keep_kernel": ("fused.hip", "score_device.hpp", "topk_device.hpp", "common.hpp",
+                          "quant_device.hpp"),
+    "score_prefill_kernel": ("score.hip", "score_device.hpp", "common.hpp", "quant_device.hpp"),
+}
+DECODE_KERNELS = ("score_keep_kernel", "score_decode_write_kernel", "score_decode_kernel")
 
 
 def log(*a):
@@ -49,32 +75,30 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="decode-8x128k")
-    p.add_argument("--secondary", default="prefill-24k+8k", help="'' to skip")
+    p.add_argument("--workloads", default=",".join(SINGLE_LAYER + (STACK,)),
+                   help="comma-separated; the headline " + HEADLINE + " always runs")
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-next-rows", action="store_true",
                    help="skip the q-fold / physical-conversion / mixed-batch / graph measurements")
-    p.add_argument("--cpu-sample", type=int, default=8, help="query tokens the oracle scores")
-    p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed oracle work")
-    p.add_argument("--stack", action="store_true",
-                   help="also time the 16-layer IndexCache stack at full size (FSSS x4 and all F)")
+    p.add_argument("--cpu-tokens", type=int, default=8, help="query tokens the oracle scores per pass")
+    p.add_argument("--cpu-seconds", type=float, default=5.0, help="minimum timed oracle work per workload")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain 1 GiB device copies (counter calibration)")
     return p.parse_args()
 
 
-def score_build_flags():
-    """The hipcc flags the scoring kernels are compiled with (read from build.py by path)."""
+def build_flags(src):
+    """The hipcc flags a source is compiled with (read from build.py by path)."""
     import importlib.util
     spec = importlib.util.spec_from_file_location(
         "_idx_build_flags", os.path.join(ROOT, "sparse_attention_token_fp8_amd", "build.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     return [os.path.basename(f) if f.startswith("-I") else f
-            for f in mod.COMMON + mod.EXTRA.get("score.hip", [])]
+            for f in mod.COMMON + mod.EXTRA.get(src, [])]
 
 
 def _code_only(text):
@@ -85,21 +109,22 @@ def _code_only(text):
     return " ".join(text.split())
 
 
-def sources_digest():
-    """Digest of the scoring kernels' code (comments aside) and their compile flags."""
+def sources_digest(kernel):
+    """Digest of a dominant kernel's code (comments aside) and its compile flags."""
+    files = KERNEL_SOURCES[kernel]
     h = hashlib.sha256()
-    for f in SCORE_SOURCES:
-        with open(os.path.join(ROOT, f)) as fh:
+    for f in files:
+        with open(os.path.join(ROOT, CSRC, f)) as fh:
             h.update(_code_only(fh.read()).encode())
-    h.update(" ".join(score_build_flags()).encode())
+    h.update(" ".join(build_flags(files[0])).encode())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter
-    summary, or None when there is none or the sources have changed since."""
+    summary, or None when there is none or the kernel's sources have changed."""
     path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.md")
-    if not os.path.exists(path):
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     fields = {}
     with open(path) as fh:
@@ -108,9 +133,20 @@ def measured_traffic(kernel, workload):
             if line.startswith(("traffic_bytes_per_launch:", "sources_digest:")):
                 key, val = line.split(":", 1)
                 fields[key] = val.strip()
-    if fields.get("sources_digest") != sources_digest():
+    if fields.get("sources_digest") != sources_digest(kernel):
         return None
     return int(fields["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in fields else None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def copy_calibration(torch, nbytes=1 << 30, launches=4):
@@ -126,7 +162,7 @@ def copy_calibration(torch, nbytes=1 << 30, launches=4):
 
 # ------------------------------------------------------------------ setup --
 
-def setup(m, torch, wl, replicas):
+def setup(m, torch, wl, replicas, layer=0):
     """Device state: cache replicas with the context K, q_fp8 / w, new K rows."""
     import concurrent.futures as cf
     t0 = time.time()
@@ -135,12 +171,12 @@ def setup(m, torch, wl, replicas):
     reqs = [r for r in range(wl.num_reqs) if wl.seq_lens[r] > wl.new_tokens[r]]
     nw = max(1, min(16, len(os.sched_getaffinity(0))))
     with cf.ThreadPoolExecutor(nw) as ex:
-        for kb, slots in ex.map(lambda r: wl.ctx_rows(0, [r]), reqs):
+        for kb, slots in ex.map(lambda r: wl.ctx_rows(layer, [r]), reqs):
             m.idx_quant_write_k(torch.from_numpy(kb.view(np.int16)).cuda(),
                                 torch.from_numpy(slots).cuda(), cache)
-    q8, w, _ = m.idx_quant_q_fold_w(torch.from_numpy(wl.q_bits(0).view(np.int16)).cuda(),
-                                    torch.from_numpy(wl.w_raw(0)).cuda())
-    nb, ns = wl.new_rows(0)
+    q8, w, _ = m.idx_quant_q_fold_w(torch.from_numpy(wl.q_bits(layer).view(np.int16)).cuda(),
+                                    torch.from_numpy(wl.w_raw(layer)).cuda())
+    nb, ns = wl.new_rows(layer)
     k_new = torch.from_numpy(nb.view(np.int16)).cuda()
     slots = torch.from_numpy(ns).cuda()
     caches = [cache] + [m.KCache(wl.num_blocks, tensor=cache.tensor.clone()) for _ in range(replicas - 1)]
@@ -150,21 +186,17 @@ def setup(m, torch, wl, replicas):
     return dict(batch=batch, caches=caches, q8=q8, w=w, k_new=k_new, slots=slots)
 
 
-def positions_sum(wl):
-    return int(np.sum(wl.token_pos() + 1))
-
-
 def algorithmic(wl):
-    """Per-step algorithmic work: K bytes scored, HBM bytes of the step, MFMA flops."""
-    P = positions_sum(wl)
+    """Per-step algorithmic work of one F layer (the measurement section's counts):
+    decode scoring bytes (K of every causal position, q, w, the new K row),
+    the step's bytes (plus the top-k indices written) and the MFMA flops of
+    the causal (token, position) pairs."""
+    P = int(np.sum(wl.token_pos() + 1))
     T = wl.num_tokens
-    step_bytes = P * 132 + T * (64 * 128 + 64 * 4 + 4 * wl.k + 256 + 132)
-    logits_bytes = P * (132 + 4) + T * (64 * 128 + 64 * 4)
-    # each byte once: every request's K, q codes and weights in, one score out per position
-    unique_bytes = int(np.sum(wl.seq_lens)) * 132 + T * (64 * 128 + 64 * 4) + P * 4
+    score_bytes = P * 132 + T * (64 * 128 + 64 * 4 + 256 + 132)
+    step_bytes = score_bytes + T * 4 * wl.k
     flops = 2 * 64 * 128 * P
-    return dict(positions=P, step_bytes=step_bytes, logits_bytes=logits_bytes,
-                unique_bytes=unique_bytes, flops=flops)
+    return dict(positions=P, score_bytes=score_bytes, step_bytes=step_bytes, flops=flops)
 
 
 def time_loop(torch, fn, steps, warmup):
@@ -180,22 +212,86 @@ def time_loop(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps   # ms
 
 
-def step_quantiles(torch, fn, steps, warmup):
-    """p10 / median / p90 of single steps, each bracketed by its own events on the
-    current stream (a separate loop from the mean, which uses one event pair)."""
+def step_quantiles(m, torch, fn, steps, warmup):
+    """p10 / median / p90 of single steps, each bracketed by its own timing events
+    (device-scope release) on the current stream; a separate loop from the mean,
+    which uses one event pair."""
     for i in range(warmup):
         fn(i)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    ev = [(m.HipEvent(), m.HipEvent()) for _ in range(steps)]
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(ev):
         a.record()
         fn(i)
         b.record()
     torch.cuda.synchronize()
-    t = np.sort(np.array([a.elapsed_time(b) for a, b in ev]))
+    t = np.sort(np.array([a.elapsed_ms(b) for a, b in ev]))
     q = lambda f: round(float(t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))]), 5)
     return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "steps": steps}
+
+
+def kernel_times(m, torch, fn, steps, warmup):
+    """Average time of each kernel the step launches, from a traced loop (the
+    library's idx_trace_begin: HIP events recorded on the kernels' stream
+    around every launch, recorded with a device-scope release so that they add
+    next to nothing to the kernels they bracket).  Returns {name: (mean ms,
+    launches)} in launch order."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    with m.KernelTrace(capacity=64 * steps) as tr:
+        for i in range(steps):
+            fn(i)
+    acc = {}
+    for name, ms in tr.kernels:
+        s, n = acc.get(name, (0.0, 0))
+        acc[name] = (s + ms, n + 1)
+    return {name: (s / n, n) for name, (s, n) in acc.items()}
+
+
+def dominant(kernels):
+    """The kernel that takes the most of the step's time in a trace."""
+    return max(kernels, key=lambda n: kernels[n][0] * kernels[n][1])
+
+
+def roofline(wl, name, kernel, ms, launches):
+    """Roofline entry of the dominant kernel from its measured time per launch."""
+    a = algorithmic(wl)
+    if kernel in DECODE_KERNELS:
+        ach = a["score_bytes"] / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kernel, name),
+                "kernel": kernel, "ms_per_launch": round(ms, 5), "launches_per_step": launches,
+                "bytes_per_launch": a["score_bytes"]}
+    ach = a["flops"] / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / FP8_PEAK_TFLOPS, 4), "traffic": measured_traffic(kernel, name),
+            "kernel": kernel, "ms_per_launch": round(ms, 5), "launches_per_step": launches,
+            "flops_per_launch": a["flops"]}
+
+
+def dominant_ms(m, torch, kernel, d, wl, reps, ws, steps, warmup):
+    """Time per launch of the step's dominant kernel, launched back to back on its
+    own through the entry point that runs exactly that launch: the fused
+    path's scoring (idx_score_candidates with the step's new K rows) or the
+    prefill scoring (idx_logits).  Events bracket the whole loop, so the
+    per-launch time carries one launch gap and no event overhead."""
+    B, k = d["batch"], wl.k
+    if kernel == "score_keep_kernel":
+        fn = lambda i: m.idx_score_candidates(d["q8"], d["w"], d["caches"][i % reps], B, k, ws,
+                                              d["k_new"], d["slots"])
+    elif kernel == "score_prefill_kernel":
+        logits = torch.empty((wl.num_tokens, wl.max_seq_len), dtype=torch.float32, device="cuda")
+        fn = lambda i: m.idx_logits(d["q8"], d["w"], d["caches"][i % reps], B, logits=logits)
+    else:
+        return None
+    return time_loop(torch, fn, steps, warmup)
+
+
+def config_of(wl, reps):
+    return {"workload": wl.name, "requests": wl.num_reqs, "query_tokens": wl.num_tokens,
+            "max_context": wl.max_seq_len, "index_topk": wl.k, "heads": 64, "head_dim": 128,
+            "block_size": 64, "layers": wl.num_layers, "cache_copies": reps}
 
 
 def run_workload(m, torch, name, args):
@@ -206,73 +302,43 @@ def run_workload(m, torch, name, args):
     d = setup(m, torch, wl, reps)
     B, k = d["batch"], wl.k
     topk = torch.empty((wl.num_tokens, k), dtype=torch.int32, device="cuda")
-    ws = torch.empty(m.idx_score_topk_workspace_size(B, k), dtype=torch.uint8, device="cuda")
-    logits = torch.empty((wl.num_tokens, wl.max_seq_len), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, m.idx_score_topk_workspace_size(B, k)), dtype=torch.uint8, device="cuda")
 
-    def step(i):                                       # one F layer: a1 + a4
-        c = d["caches"][i % reps]
-        m.idx_indexcache_layer(d["k_new"], c, d["q8"], d["w"], True, True, d["slots"], B, k, topk,
-                               workspace=ws)
-
-    def score_only(i):
-        m.idx_logits(d["q8"], d["w"], d["caches"][i % reps], B, logits=logits)
+    def step(i):                                       # one F layer: new K rows, scores, top-k
+        m.idx_indexcache_layer(d["k_new"], d["caches"][i % reps], d["q8"], d["w"], True, True,
+                               d["slots"], B, k, topk, workspace=ws)
 
     ms_step = time_loop(torch, step, args.steps, args.warmup)
-    ms_logits = time_loop(torch, score_only, args.steps, args.warmup)
-    quant = step_quantiles(torch, step, max(args.steps, 50), args.warmup)
+    quant = step_quantiles(m, torch, step, max(args.steps, 50), args.warmup)
+    kern = kernel_times(m, torch, step, min(args.steps, 20), 2)
+    dom = dominant(kern)
+    ms_dom = dominant_ms(m, torch, dom, d, wl, reps, ws, args.steps, args.warmup)
+    roof = roofline(wl, name, dom, ms_dom if ms_dom is not None else kern[dom][0], kern[dom][1])
     a = algorithmic(wl)
-    if decode:
-        ach = a["logits_bytes"] / (ms_logits * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("score_decode_kernel", name),
-                "kernel": "score_decode_kernel (idx_logits)", "ms_per_launch": round(ms_logits, 5),
-                "bytes_per_launch": a["logits_bytes"]}
-    else:
-        ach = a["flops"] / (ms_logits * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / FP8_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic("score_prefill_kernel", name),
-                "kernel": "score_prefill_kernel (idx_logits)", "ms_per_launch": round(ms_logits, 5),
-                "flops_per_launch": a["flops"]}
-    step_gbs = a["step_bytes"] / (ms_step * 1e-3) / 1e9
-    res = dict(workload=name, tokens=wl.num_tokens, ms_per_step=ms_step, step_ms_quantiles=quant,
-               value=wl.num_tokens / (ms_step * 1e-3), roofline=roof,
-               step_hbm_frac=round(step_gbs / HBM_PEAK_GBS, 4),
+    res = dict(workload=name, value=round(wl.num_tokens / (ms_step * 1e-3), 1),
+               ms_per_step=round(ms_step, 5), step_ms_quantiles=quant, roofline=roof,
+               kernels_ms={n: round(v[0], 5) for n, v in kern.items()},
+               step_hbm_frac=round(a["step_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                step_mfma_frac=round(a["flops"] / (ms_step * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-               config={"workload": name, "requests": wl.num_reqs, "query_tokens": wl.num_tokens,
-                       "max_context": wl.max_seq_len, "index_topk": k, "heads": 64, "head_dim": 128,
-                       "block_size": 64, "cache_copies": reps})
-    log(f"{name}: {ms_step * 1e3:.1f} us/step, logits kernel {ms_logits * 1e3:.1f} us "
-        f"({roof['frac'] * 100:.1f}% of {roof['bound']} peak)")
+               config=config_of(wl, reps))
+    log(f"{name}: {ms_step * 1e3:.1f} us/step; " +
+        ", ".join(f"{n} {v[0] * 1e3:.1f} us" for n, v in kern.items()) +
+        f"; {roof['kernel']} alone {roof['ms_per_launch'] * 1e3:.1f} us, "
+        f"{roof['frac'] * 100:.1f}% of {roof['bound']} peak")
+    del d, topk, ws
+    torch.cuda.empty_cache()
     return res, wl
 
 
-def _layers(m, torch, wl):
-    """Per-layer device state for a multi-layer workload (context K, q_fp8 / w, new K rows)."""
-    layers = []
-    reqs = [r for r in range(wl.num_reqs) if wl.seq_lens[r] > wl.new_tokens[r]]
-    for l in range(wl.num_layers):
-        cache = m.KCache(wl.num_blocks, fill=0)
-        for r in reqs:
-            kb, slots = wl.ctx_rows(l, [r])
-            m.idx_quant_write_k(torch.from_numpy(kb.view(np.int16)).cuda(),
-                                torch.from_numpy(slots).cuda(), cache)
-        q8, w, _ = m.idx_quant_q_fold_w(torch.from_numpy(wl.q_bits(l).view(np.int16)).cuda(),
-                                        torch.from_numpy(wl.w_raw(l)).cuda())
-        nb, ns = wl.new_rows(l)
-        layers.append((torch.from_numpy(nb.view(np.int16)).cuda(), cache, q8, w))
-    return layers, torch.from_numpy(ns).cuda()
-
-
-def run_stack(m, torch, steps=20, warmup=3):
+def run_stack(m, torch, args):
     """stack-16L-32x64k: the 16-layer stack (idx_indexcache_stack) with the FSSS x4
-    schedule and with every layer F.  Layer 0's context K is written once and copied
-    into 16 distinct caches, so every F layer reads its own 277 MB."""
+    schedule, the step, and with every layer F beside it.  Layer 0's context K
+    is written once and copied into 16 distinct caches, so every F layer reads
+    its own 277 MB."""
     import concurrent.futures as cf
     from synth import CONFIGS, make_workload
     t0 = time.time()
-    wl = make_workload(CONFIGS["stack-16L-32x64k"])
+    wl = make_workload(CONFIGS[STACK])
     batch = m.Batch(wl.seq_lens, wl.query_start_loc, wl.block_table)
     cache = m.KCache(wl.num_blocks, fill=0)
     nw = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -293,15 +359,34 @@ def run_stack(m, torch, steps=20, warmup=3):
     torch.cuda.synchronize()
     log(f"setup {wl.name}: {time.time() - t0:.1f}s, {wl.num_layers} caches")
     fsss = m.idx_layer_schedule(True, wl.pattern, 1, 2, wl.num_layers)
-    res = {}
-    for name, full in (("fsss", fsss), ("all_f", [True] * wl.num_layers)):
-        res[name] = time_loop(torch, lambda i: m.idx_indexcache_stack(
-            layers, full, True, slots, batch, wl.k, topk, workspace=ws), steps, warmup)
-    log(f"{wl.name}: FSSS x4 {res['fsss'] * 1e3:.1f} us, all F {res['all_f'] * 1e3:.1f} us per stack")
-    return {"workload": wl.name, "layers": wl.num_layers, "f_layers": [i for i, f in enumerate(fsss) if f],
-            "ms_fsss": round(res["fsss"], 5), "ms_all_f": round(res["all_f"], 5),
-            "speedup": round(res["all_f"] / res["fsss"], 3),
-            "query_tokens_per_s": round(wl.num_tokens / (res["fsss"] * 1e-3), 1)}
+
+    def stack(full):
+        return lambda i: m.idx_indexcache_stack(layers, full, True, slots, batch, wl.k, topk,
+                                                workspace=ws)
+
+    steps = max(5, args.steps // 2)
+    ms_fsss = time_loop(torch, stack(fsss), steps, 3)
+    ms_all_f = time_loop(torch, stack([True] * wl.num_layers), steps, 3)
+    quant = step_quantiles(m, torch, stack(fsss), max(steps, 20), 3)
+    kern = kernel_times(m, torch, stack(fsss), 5, 1)
+    kern = {n: (ms, cnt // 5) for n, (ms, cnt) in kern.items()}   # launches per stack
+    dom = dominant(kern)
+    f_layers = [l for l, f in enumerate(fsss) if f]
+    dom_state = {"batch": batch, "caches": [layers[l][1] for l in f_layers],
+                 "q8": layers[0][2], "w": layers[0][3], "k_new": layers[0][0], "slots": slots}
+    ms_dom = dominant_ms(m, torch, dom, dom_state, wl, len(f_layers), ws, steps, 3)
+    roof = roofline(wl, STACK, dom, ms_dom if ms_dom is not None else kern[dom][0], kern[dom][1])
+    log(f"{wl.name}: FSSS x4 {ms_fsss * 1e3:.1f} us, all F {ms_all_f * 1e3:.1f} us per stack; " +
+        ", ".join(f"{n} {v[0] * 1e3:.1f} us x{v[1]}" for n, v in kern.items()))
+    res = {"workload": wl.name, "value": round(wl.num_tokens / (ms_fsss * 1e-3), 1),
+           "ms_per_step": round(ms_fsss, 5), "step_ms_quantiles": quant, "roofline": roof,
+           "kernels_ms": {n: round(v[0], 5) for n, v in kern.items()},
+           "kernel_launches_per_step": {n: v[1] for n, v in kern.items()},
+           "f_layers": [i for i, f in enumerate(fsss) if f], "ms_all_f": round(ms_all_f, 5),
+           "all_f_over_fsss": round(ms_all_f / ms_fsss, 3), "config": config_of(wl, 1)}
+    del layers, cache, topk, ws
+    torch.cuda.empty_cache()
+    return res, wl
 
 
 def run_next_rows(m, torch, steps=20, warmup=3):
@@ -375,7 +460,7 @@ def run_next_rows(m, torch, steps=20, warmup=3):
     ms1, ms2 = min(r1), min(r2)
     a = algorithmic(mw)
     pos = mw.token_pos() + 1
-    dec_bytes = int(np.sum(pos[:64])) * 136 + 64 * (H * D + H * 4)
+    dec_bytes = int(np.sum(pos[:64])) * 132 + 64 * (H * D + H * 4)
     pre_flops = 2 * H * D * int(np.sum(pos[64:]))
     bound_ms = max(dec_bytes / (HBM_PEAK_GBS * 1e9), pre_flops / (FP8_PEAK_TFLOPS * 1e12)) * 1e3
     out["next3_mixed_batch"] = {
@@ -422,6 +507,8 @@ def run_next_rows(m, torch, steps=20, warmup=3):
     return out
 
 
+
+
 def _hbm_row(kernel, nbytes, ms, shape):
     ach = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": kernel, "shape": shape, "bound": "hbm", "bytes_per_launch": nbytes,
@@ -429,9 +516,11 @@ def _hbm_row(kernel, nbytes, ms, shape):
             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
 
 
-def cpu_baseline(wl, sample, min_seconds=10.0):
-    """The oracle, as it stands, on `sample` query tokens of the workload, repeated
-    until at least `min_seconds` of work has been timed."""
+def cpu_baseline(wl, sample, min_seconds=5.0):
+    """The oracle, as it stands, on `sample` query tokens of the workload (their
+    requests' new K rows written into each layer's cache, fp64 scores over the
+    full causal range, full-sort top-k on the F layers), repeated until at least
+    `min_seconds` of work has been timed.  Returns query-tokens/s of that work."""
     import concurrent.futures as cf
     import oracle
     from oracle import logits as olog, quant as oquant, topk as otopk
@@ -440,35 +529,49 @@ def cpu_baseline(wl, sample, min_seconds=10.0):
         blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         blas = None
-    tokens = np.linspace(0, wl.num_tokens - 1, min(sample, wl.num_tokens)).astype(int)
+    tokens = np.unique(np.linspace(0, wl.num_tokens - 1, min(sample, wl.num_tokens)).astype(int))
     reqs = sorted(set(int(r) for r in wl.token_req()[tokens]))
-    cache = np.zeros((wl.num_blocks, 64, 132), np.uint8)
-    new = {}
-    nw = max(1, min(16, len(os.sched_getaffinity(0))))
-    with cf.ThreadPoolExecutor(nw) as ex:               # context: setup, not timed
-        for r, kb in ex.map(lambda r: (r, wl.request_k(0, r)), reqs):
-            L, n = int(wl.seq_lens[r]), int(wl.new_tokens[r])
-            oquant.quant_write_k(cache, kb[:L - n], wl.slots(r, np.arange(L - n)))
-            new[r] = (kb[L - n:], wl.slots(r, np.arange(L - n, L)))
-    q8, qs = oquant.quantize_q(wl.q_bits(0))
-    w = oquant.fold_weights(wl.w_raw(0), qs)
+    full = [c == "F" for c in wl.pattern] if wl.num_layers > 1 else [True]
     ob = oracle.Batch(wl.seq_lens, wl.query_start_loc, wl.block_table)
+    nw = max(1, min(16, len(os.sched_getaffinity(0))))
+    layers = []
+    for layer, is_f in enumerate(full):                 # setup, not timed
+        cache = np.zeros((wl.num_blocks, 64, 132), np.uint8)
+        new = {}
+
+        def ctx(r, layer=layer, cache=cache, is_f=is_f):
+            kb = wl.request_k(layer, r)
+            L, n = int(wl.seq_lens[r]), int(wl.new_tokens[r])
+            if is_f:                                    # S layers score nothing: no context needed
+                oquant.quant_write_k(cache, kb[:L - n], wl.slots(r, np.arange(L - n)))
+            return r, (kb[L - n:], wl.slots(r, np.arange(L - n, L)))
+
+        with cf.ThreadPoolExecutor(nw) as ex:
+            new = dict(ex.map(ctx, reqs))
+        q8 = w = None
+        if is_f:
+            q8, qs = oquant.quantize_q(wl.q_bits(layer))
+            w = oquant.fold_weights(wl.w_raw(layer), qs)
+        layers.append((is_f, cache, new, q8, w))
     passes = 0
     t0 = time.time()
     while passes == 0 or time.time() - t0 < min_seconds:
-        for r in reqs:                                 # this step's K rows of the sampled requests
-            oquant.quant_write_k(cache, *new[r])
-        for t in tokens:
-            r, p = ob.token_request(int(t)), ob.token_position(int(t))
-            s = olog.logits_row(q8[t], w[t], cache, wl.block_table[r], p)
-            otopk.topk_row(s, wl.k)
+        for is_f, cache, new, q8, w in layers:
+            for r in reqs:                              # this step's K rows of the sampled requests
+                oquant.quant_write_k(cache, *new[r])
+            if is_f:
+                for t in tokens:
+                    r, p = ob.token_request(int(t)), ob.token_position(int(t))
+                    s = olog.logits_row(q8[t], w[t], cache, wl.block_table[r], p)
+                    otopk.topk_row(s, wl.k)
         passes += 1
     dt = time.time() - t0
     return {"value": round(passes * len(tokens) / dt, 3), "unit": "query-tokens/s",
-            "cores": len(os.sched_getaffinity(0)), "blas_threads": blas, "kind": "oracle",
+            "cores": len(os.sched_getaffinity(0)), "blas_threads": blas, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"{passes} pass(es) over {len(tokens)} of the {wl.num_tokens} query tokens of "
-                      f"{wl.name} (their new K rows, fp64 scores over the full causal range, "
-                      f"full-sort top-{wl.k}); {dt:.1f} s"}
+                      f"{wl.name} ({wl.num_layers} layer(s): their new K rows, fp64 scores over the "
+                      f"full causal range and a full-sort top-{wl.k} on F layers); {dt:.1f} s"}
 
 
 def main():
@@ -485,28 +588,36 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
         return
-    main_res, wl = run_workload(m, torch, args.workload, args)
-    out = {"metric": METRIC, "value": round(main_res["value"], 1), "unit": "query-tokens/s",
+    names = [HEADLINE] + [n for n in args.workloads.split(",") if n and n != HEADLINE]
+    results, wls = {}, {}
+    for name in names:
+        if name == STACK:
+            results[name], wls[name] = run_stack(m, torch, args)
+        else:
+            results[name], wls[name] = run_workload(m, torch, name, args)
+    head = results[HEADLINE]
+    out = {"metric": METRIC, "value": head["value"], "unit": "query-tokens/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(main_res["ms_per_step"], 5), "higher_is_better": True,
+           "ms_per_step": head["ms_per_step"], "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
-           "config": main_res["config"], "roofline": main_res["roofline"],
-           "step_ms_quantiles": main_res["step_ms_quantiles"],
-           "step_hbm_frac": main_res["step_hbm_frac"]}
-    if args.secondary:
-        sec, _ = run_workload(m, torch, args.secondary, args)
-        out["secondary"] = {k: sec[k] for k in ("workload", "value", "ms_per_step", "roofline",
-                                                 "step_mfma_frac", "step_ms_quantiles", "config")}
-        out["secondary"]["value"] = round(sec["value"], 1)
+           "config": head["config"], "roofline": head["roofline"],
+           "step_ms_quantiles": head["step_ms_quantiles"], "kernels_ms": head["kernels_ms"],
+           "step_hbm_frac": head["step_hbm_frac"],
+           "workloads": {n: r for n, r in results.items() if n != HEADLINE}}
     if not args.no_next_rows:
         try:
             out["next_rows"] = run_next_rows(m, torch)
         except Exception as e:                         # reported, never fatal to the bench line
             out["next_rows"] = {"error": f"{type(e).__name__}: {e}"}
-    if args.stack:
-        out["stack"] = run_stack(m, torch)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample, args.cpu_seconds)
+        for name in names:
+            t0 = time.time()
+            cb = cpu_baseline(wls[name], args.cpu_tokens if name != STACK else 2, args.cpu_seconds)
+            log(f"cpu baseline {name}: {cb['value']} query-tokens/s ({time.time() - t0:.1f} s)")
+            if name == HEADLINE:
+                out["cpu_baseline"] = cb
+            else:
+                out["workloads"][name]["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

@@ -178,14 +178,43 @@ idx_status_t idx_topk(const float* logits, int64_t logits_stride, const idx_batc
 size_t idx_score_topk_workspace_size(const idx_batch_t* batch, int32_t k);
 
 /*
- * idx_logits followed by idx_topk in one call; the scores live only in the
- * workspace.  The selected rows are identical to idx_logits + idx_topk on
- * the same inputs.
+ * idx_logits followed by idx_topk in one call, with the same rows as those
+ * two on the same inputs.  Decode batches over long rows (the fused path,
+ * below) never write their scores: each work-group keeps its chunk's scores on
+ * chip and passes on only the keys above a per-chunk threshold, and one exact
+ * select per row takes the top k from them.  Other batches keep the scores in
+ * the workspace between the scoring and the select.
  */
 idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
                             idx_kcache_t cache, const idx_batch_t* batch, int32_t k,
                             int32_t* topk, int64_t topk_stride,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The two launches of idx_score_topk's fused path, for callers that want to
+ * run or time them apart.  The fused path serves batches scored one token per
+ * work-group (every request has at most one new token, or num_decode_tokens
+ * == num_tokens) with fewer than 256 tokens and rows longer than 8192
+ * positions; for any other batch both calls return IDX_ERR_UNSUPPORTED.
+ * idx_score_candidates scores every causal position with the scores kept on
+ * chip and leaves, per chunk of positions, the keys at or above a per-chunk
+ * threshold (with the threshold and the chunk's largest key) in the
+ * workspace; with k_bf16 != NULL it also quantises this step's new K rows
+ * into the cache as idx_quant_write_k would (inside the scoring kernel when
+ * every request has at most 4 new tokens).  idx_select_candidates then writes
+ * each row's top k exactly as idx_score_topk (rescoring a row whose chunks
+ * held more than their share of its top k).  Between the two the workspace,
+ * q_fp8, w and the cache must not change.  Workspace: idx_score_topk_workspace_size.
+ */
+idx_status_t idx_score_candidates(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                  int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
+                                  int32_t k, const uint16_t* k_bf16, int64_t k_row_stride,
+                                  const int64_t* slot_mapping, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+idx_status_t idx_select_candidates(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                   int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
+                                   int32_t k, int32_t* topk, int64_t topk_stride, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph
@@ -279,6 +308,23 @@ idx_status_t idx_topk_to_physical(const int32_t* logical, int64_t logical_stride
                                   int32_t k, int64_t block_stride_rows,
                                   int32_t* physical, int64_t physical_stride,
                                   int32_t* valid_counts, hipStream_t stream);
+
+/*
+ * Per-kernel timing without a profiler (diagnostics; not part of the method).
+ * After idx_trace_begin(events, capacity), every kernel the library enqueues
+ * from the calling thread is bracketed by two of the caller's events:
+ * events[2i] is recorded on the kernel's stream just before kernel i and
+ * events[2i+1] just after it, until the events run out (later kernels are not
+ * bracketed).  idx_trace_end stops the trace and returns the number of kernels
+ * bracketed; with names != NULL, names[i] (static strings, i < max_names)
+ * receives kernel i's name.  The events belong to the caller (created with
+ * timing enabled).  Recording events adds work to the stream, so a traced call
+ * runs slightly slower than an untraced one, and a trace under graph capture
+ * records event nodes into the graph.  idx_trace_begin returns
+ * IDX_ERR_INVALID_ARG for a null array or a capacity below 2.
+ */
+idx_status_t idx_trace_begin(hipEvent_t* events, int32_t capacity);
+int32_t idx_trace_end(const char** names, int32_t max_names);
 
 #ifdef __cplusplus
 }

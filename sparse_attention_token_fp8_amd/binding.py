@@ -64,7 +64,13 @@ SIGNATURES = {
                                       _vp, _sz, _vp]),
     "idx_score_topk_noalloc": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _i32, _vp,
                                               _i64, _vp]),
+    "idx_score_candidates": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _i32, _vp, _i64,
+                                            _vp, _vp, _sz, _vp]),
+    "idx_select_candidates": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _i32, _vp,
+                                             _i64, _vp, _sz, _vp]),
     "idx_layer_schedule": (ctypes.c_int, [_i32, ctypes.c_char_p, _i32, _i32, _i32, _vp]),
+    "idx_trace_begin": (ctypes.c_int, [_vp, _i32]),
+    "idx_trace_end": (_i32, [_vp, _i32]),
     "idx_indexcache_layer": (ctypes.c_int, [ctypes.POINTER(LayerIOC), _i32, _i32, _vp, _PBatch,
                                             _i32, _vp, _i64, _vp, _sz, _vp]),
     "idx_indexcache_stack": (ctypes.c_int, [ctypes.POINTER(LayerIOC), _i32, _vp, _i32, _vp,
@@ -235,6 +241,29 @@ def idx_score_topk(q_fp8, w, cache, batch, k, topk=None, workspace=None, stream=
     return topk
 
 
+def idx_score_candidates(q_fp8, w, cache, batch, k, workspace, k_new=None, slot_mapping=None,
+                         stream=None):
+    """First launch of the fused path: scores kept on chip, per-chunk candidates into
+    `workspace`; with k_new / slot_mapping also this step's new K rows."""
+    kn = None if k_new is None else as_bf16_bits(k_new)
+    _check("idx_score_candidates",
+           _lib.idx_score_candidates(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(),
+                                     k, _ptr(kn), int(kn.stride(0)) if kn is not None else 0,
+                                     _ptr(slot_mapping), _ptr(workspace), workspace.numel(),
+                                     _stream(stream)))
+
+
+def idx_select_candidates(q_fp8, w, cache, batch, k, workspace, topk=None, stream=None):
+    """Second launch of the fused path: each row's top k from the candidates."""
+    if topk is None:
+        topk = torch.empty((batch.num_tokens, k), dtype=torch.int32, device=q_fp8.device)
+    _check("idx_select_candidates",
+           _lib.idx_select_candidates(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(),
+                                      k, _ptr(topk), int(topk.stride(0)), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)))
+    return topk
+
+
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -297,3 +326,82 @@ def idx_topk_to_physical(logical, batch, num_blocks, block_size=BLOCK_SIZE, bloc
                                      int(num_blocks), k, int(block_stride_rows), _ptr(physical),
                                      int(physical.stride(0)), _ptr(valid_counts), _stream(stream)))
     return physical, valid_counts
+
+
+def _hip_runtime():
+    """The HIP runtime this process already uses (torch's; libidx binds to it too)."""
+    for line in open("/proc/self/maps"):
+        path = line.split()[-1]
+        if os.path.basename(path).startswith("libamdhip64.so"):
+            lib = ctypes.CDLL(path)
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            return lib
+    raise RuntimeError("the HIP runtime is not loaded in this process")
+
+
+_hip = None
+# hipEventReleaseToDevice (a device-scope release when recorded), else
+# hipEventDisableSystemFence; the two together are refused when recorded
+_EVENT_FLAGS = (0x40000000, 0x20000000)
+
+
+class HipEvent:
+    """A HIP event for timing only, recorded with a device-scope release instead
+    of the system-scope fence of a default event (a cache write-back and
+    invalidate, which would add itself to every bracketed kernel)."""
+
+    def __init__(self):
+        global _hip
+        if _hip is None:
+            _hip = _hip_runtime()
+        self.handle = ctypes.c_void_p()
+        for flags in _EVENT_FLAGS:
+            if _hip.hipEventCreateWithFlags(ctypes.byref(self.handle), flags) == 0:
+                return
+        raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream=None):
+        s = torch.cuda.current_stream() if stream is None else stream
+        if _hip.hipEventRecord(self.handle, ctypes.c_void_p(s.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, end):
+        ms = ctypes.c_float()
+        if _hip.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        if _hip is not None and self.handle:
+            _hip.hipEventDestroy(self.handle)
+
+
+class KernelTrace:
+    """Per-kernel times of the library calls made inside a ``with`` block on this
+    thread (idx_trace_begin / idx_trace_end): ``kernels`` lists (name, ms) in
+    launch order after the block, once the work has finished.  ``capacity`` is
+    the number of kernels that can be timed."""
+
+    def __init__(self, capacity=256, stream=None):
+        self.capacity = int(capacity)
+        self.stream = torch.cuda.current_stream() if stream is None else stream
+        self.kernels = []
+
+    def __enter__(self):
+        self._events = [HipEvent() for _ in range(2 * self.capacity)]
+        self._arr = (ctypes.c_void_p * len(self._events))(*[e.handle.value for e in self._events])
+        _check("idx_trace_begin", _lib.idx_trace_begin(ctypes.cast(self._arr, ctypes.c_void_p),
+                                                      len(self._events)))
+        return self
+
+    def __exit__(self, *exc):
+        names = (ctypes.c_char_p * self.capacity)()
+        n = _lib.idx_trace_end(ctypes.cast(names, ctypes.c_void_p), self.capacity)
+        self.stream.synchronize()
+        self.kernels = [(names[i].decode(), self._events[2 * i].elapsed_ms(self._events[2 * i + 1]))
+                        for i in range(n)]
+        return False

@@ -99,6 +99,26 @@ idx_status_t check_k_rows(const uint16_t* k_bf16, int64_t k_row_stride, const in
   return IDX_OK;
 }
 
+// The fused path's first launch (scores kept on chip, each chunk's candidates
+// into the workspace); with kq set, this step's new K rows are quantised into
+// the cache first (by the scoring kernel itself when the batch allows it).
+hipError_t keep_candidates(const uint8_t* q_fp8, const float* w, const idx_kcache_t& cache,
+                           const idx_batch_t* batch, int32_t k, void* workspace,
+                           const uint16_t* kq, int64_t kq_stride, const int64_t* slots,
+                           hipStream_t stream) {
+  const BatchArgs b = to_args(batch);
+  KeepSlots ks;
+  keep_workspace_layout(b, workspace, &ks);
+  const bool fk = kq != nullptr && score_writes_k(b, batch->num_decode_tokens);
+  if (kq != nullptr && !fk) {
+    const hipError_t e = launch_quant_write_k(kq, batch->num_tokens, kq_stride, slots, cache.data,
+                                              cache.num_blocks * kBlock, stream);
+    if (e != hipSuccess) return e;
+  }
+  return launch_keep_candidates(q_fp8, w, CacheArgs{cache.data, cache.num_blocks}, b,
+                                fk ? kq : nullptr, kq_stride, slots, cache.data, k, ks, stream);
+}
+
 // Scores + top-k of one batch into `topk`; with kq set, this step's new K rows
 // are quantised into the cache first (by the decode scoring kernel itself
 // when it scores the whole batch).  Arguments are already checked.
@@ -107,18 +127,13 @@ hipError_t score_topk(const uint8_t* q_fp8, const float* w, const idx_kcache_t& 
                       void* workspace, const uint16_t* kq, int64_t kq_stride,
                       const int64_t* slots, hipStream_t stream) {
   if (keep_path(to_args(batch), batch->num_decode_tokens)) {
-    const BatchArgs b = to_args(batch);
-    const CacheArgs c{cache.data, cache.num_blocks};
+    hipError_t e = keep_candidates(q_fp8, w, cache, batch, k, workspace, kq, kq_stride, slots,
+                                   stream);
+    if (e != hipSuccess) return e;
     KeepSlots ks;
-    keep_workspace_layout(b, workspace, &ks);
-    const bool fk = kq != nullptr && score_writes_k(b, batch->num_decode_tokens);
-    if (kq != nullptr && !fk) {
-      const hipError_t e = launch_quant_write_k(kq, batch->num_tokens, kq_stride, slots, cache.data,
-                                                cache.num_blocks * kBlock, stream);
-      if (e != hipSuccess) return e;
-    }
-    return launch_score_topk_keep(q_fp8, w, c, b, fk ? kq : nullptr, kq_stride, slots, cache.data,
-                                  k, ks, topk, topk_stride, stream);
+    keep_workspace_layout(to_args(batch), workspace, &ks);
+    return launch_keep_select(q_fp8, w, CacheArgs{cache.data, cache.num_blocks}, to_args(batch), k,
+                              ks, topk, topk_stride, stream);
   }
   TopkWorkspace ws;
   fused_workspace(batch, workspace, &ws);
@@ -297,6 +312,46 @@ idx_status_t idx_score_topk_noalloc(const uint8_t* q_fp8, const float* w, int32_
   if (ws == nullptr) return IDX_ERR_LAUNCH;
   return launched(score_topk(q_fp8, w, cache, batch, k, topk, topk_stride, ws, nullptr, 0,
                              nullptr, stream));
+}
+
+idx_status_t idx_score_candidates(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                  int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
+                                  int32_t k, const uint16_t* k_bf16, int64_t k_row_stride,
+                                  const int64_t* slot_mapping, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  idx_status_t s = check_scoring(q_fp8, w, n_heads, head_dim, cache, batch);
+  if (s != IDX_OK) return s;
+  if (k < 1 || k > kMaxK) return IDX_ERR_UNSUPPORTED;
+  if (batch->num_tokens == 0) return IDX_OK;
+  if (!keep_path(to_args(batch), batch->num_decode_tokens)) return IDX_ERR_UNSUPPORTED;
+  if (k_bf16 != nullptr) {
+    s = check_k_rows(k_bf16, k_row_stride, slot_mapping, cache, batch->num_tokens);
+    if (s != IDX_OK) return s;
+  }
+  if (workspace == nullptr || workspace_bytes < idx_score_topk_workspace_size(batch, k) ||
+      !aligned(workspace, 256))
+    return IDX_ERR_WORKSPACE;
+  return launched(keep_candidates(q_fp8, w, cache, batch, k, workspace, k_bf16, k_row_stride,
+                                  slot_mapping, stream));
+}
+
+idx_status_t idx_select_candidates(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                   int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
+                                   int32_t k, int32_t* topk, int64_t topk_stride, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  idx_status_t s = check_scoring(q_fp8, w, n_heads, head_dim, cache, batch);
+  if (s != IDX_OK) return s;
+  s = check_k(k, topk_stride, topk, batch->num_tokens);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens == 0) return IDX_OK;
+  if (!keep_path(to_args(batch), batch->num_decode_tokens)) return IDX_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < idx_score_topk_workspace_size(batch, k) ||
+      !aligned(workspace, 256))
+    return IDX_ERR_WORKSPACE;
+  KeepSlots ks;
+  keep_workspace_layout(to_args(batch), workspace, &ks);
+  return launched(launch_keep_select(q_fp8, w, CacheArgs{cache.data, cache.num_blocks},
+                                     to_args(batch), k, ks, topk, topk_stride, stream));
 }
 
 idx_status_t idx_indexcache_layer(const idx_layer_io_t* layer, int32_t is_full, int32_t write_k,

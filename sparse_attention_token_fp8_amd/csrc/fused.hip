@@ -431,32 +431,38 @@ size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks) {
   return off;
 }
 
-hipError_t launch_score_topk_keep(const uint8_t* q8, const float* w, const CacheArgs& cache,
+hipError_t launch_keep_candidates(const uint8_t* q8, const float* w, const CacheArgs& cache,
                                   const BatchArgs& b, const uint16_t* kq, int64_t kq_stride,
                                   const int64_t* slots, uint8_t* cache_w, int k,
-                                  const KeepSlots& ks, int32_t* out, int64_t ldo,
-                                  hipStream_t stream) {
+                                  const KeepSlots& ks, hipStream_t stream) {
   if (b.num_tokens == 0) return hipSuccess;
   const int ident = b.num_reqs == b.num_tokens && b.max_query_len <= 1;
   if (b.max_seq_len > 0) {
     const dim3 grid((unsigned)ks.nslots, (unsigned)b.num_tokens);
     if (kq != nullptr) {
       const NewRows nk{kq, kq_stride, slots, cache_w, cache.num_blocks * kBlock};
-      hipLaunchKernelGGL((score_keep_kernel<IDX_DECODE_RING, true>), grid, dim3(kScoreThreads), 0,
-                         stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+      IDX_LAUNCH("score_keep_kernel", (score_keep_kernel<IDX_DECODE_RING, true>), grid,
+                 dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
     } else {
-      hipLaunchKernelGGL((score_keep_kernel<IDX_DECODE_RING, false>), grid, dim3(kScoreThreads), 0,
-                         stream, q8, w, cache, b, ks.chunk_blocks, ident, NewRows{}, k, ks);
+      IDX_LAUNCH("score_keep_kernel", (score_keep_kernel<IDX_DECODE_RING, false>), grid,
+                 dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, NewRows{},
+                 k, ks);
     }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  } else if (kq != nullptr) {
-    const hipError_t e = launch_quant_write_k(kq, b.num_tokens, kq_stride, slots, cache_w,
-                                              cache.num_blocks * kBlock, stream);
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(topk_keep_resolve_kernel, dim3((unsigned)b.num_tokens), dim3(kResThreads), 0,
-                     stream, q8, w, cache, b, ident, k, ks, out, ldo);
+  if (kq != nullptr)
+    return launch_quant_write_k(kq, b.num_tokens, kq_stride, slots, cache_w,
+                                cache.num_blocks * kBlock, stream);
+  return hipSuccess;
+}
+
+hipError_t launch_keep_select(const uint8_t* q8, const float* w, const CacheArgs& cache,
+                              const BatchArgs& b, int k, const KeepSlots& ks, int32_t* out,
+                              int64_t ldo, hipStream_t stream) {
+  if (b.num_tokens == 0) return hipSuccess;
+  const int ident = b.num_reqs == b.num_tokens && b.max_query_len <= 1;
+  IDX_LAUNCH("topk_keep_resolve_kernel", (topk_keep_resolve_kernel), dim3((unsigned)b.num_tokens),
+             dim3(kResThreads), stream, q8, w, cache, b, ident, k, ks, out, ldo);
   return hipGetLastError();
 }
 

@@ -6,6 +6,19 @@
 
 namespace idx {
 
+// Tracing (idx_trace_begin): records the next caller event on `stream`
+// before (after = false) or after (after = true) the kernel `name`; a no-op
+// unless the calling thread is tracing.
+void trace_mark(hipStream_t stream, const char* name, bool after);
+
+// Every kernel launch of the library goes through this, so a trace sees it.
+#define IDX_LAUNCH(NAME, KERNEL, GRID, BLOCK, STREAM, ...)                  \
+  do {                                                                      \
+    ::idx::trace_mark(STREAM, NAME, false);                                 \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);        \
+    ::idx::trace_mark(STREAM, NAME, true);                                  \
+  } while (0)
+
 hipError_t launch_quant_write_k(const uint16_t* k, int64_t num_rows, int64_t stride,
                                 const int64_t* slots, uint8_t* cache, int64_t num_slots,
                                 hipStream_t stream);
@@ -46,14 +59,19 @@ bool keep_path(const BatchArgs& b, int64_t dec_tokens);
 // Workspace of the fused path; returns its bytes and, with a base, fills `ks`.
 size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks);
 
-// Fused score + top-k (scores kept on chip, candidates compacted per chunk,
-// one exact select per row).  With kq, this step's new K rows are written to
-// the cache by the scoring kernel (score_writes_k must hold).
-hipError_t launch_score_topk_keep(const uint8_t* q8, const float* w, const CacheArgs& cache,
+// The fused path's two launches.  launch_keep_candidates scores the batch
+// with the scores kept on chip and leaves each chunk's candidates in `ks`; with
+// kq, this step's new K rows are written first (by the scoring kernel itself,
+// so score_writes_k must hold).  launch_keep_select takes each row's top k
+// from the candidates (rescoring a row whose chunks held more than their
+// share).
+hipError_t launch_keep_candidates(const uint8_t* q8, const float* w, const CacheArgs& cache,
                                   const BatchArgs& b, const uint16_t* kq, int64_t kq_stride,
                                   const int64_t* slots, uint8_t* cache_w, int k,
-                                  const KeepSlots& ks, int32_t* out, int64_t ldo,
-                                  hipStream_t stream);
+                                  const KeepSlots& ks, hipStream_t stream);
+hipError_t launch_keep_select(const uint8_t* q8, const float* w, const CacheArgs& cache,
+                              const BatchArgs& b, int k, const KeepSlots& ks, int32_t* out,
+                              int64_t ldo, hipStream_t stream);
 
 // Finish long rows from the candidate slots of `ws`.
 hipError_t launch_topk_resolve(const float* logits, int64_t ld, const BatchArgs& b,

@@ -114,12 +114,13 @@ hipError_t launch_topk_to_physical(const int32_t* logical, int64_t ldl, const Ba
   if (b.num_tokens == 0) return hipSuccess;
   CacheArgs c{nullptr, num_blocks};
   if ((block_size & (block_size - 1)) == 0)
-    hipLaunchKernelGGL(to_physical_kernel<true>, dim3((unsigned)b.num_tokens), dim3(256), 0, stream,
-                       logical, ldl, b, c, block_size, __builtin_ctz((unsigned)block_size), k,
-                       stride_rows, physical, ldp, valid);
+    IDX_LAUNCH("to_physical_kernel", (to_physical_kernel<true>), dim3((unsigned)b.num_tokens),
+               dim3(256), stream, logical, ldl, b, c, block_size,
+               __builtin_ctz((unsigned)block_size), k, stride_rows, physical, ldp, valid);
   else
-    hipLaunchKernelGGL(to_physical_kernel<false>, dim3((unsigned)b.num_tokens), dim3(256), 0, stream,
-                       logical, ldl, b, c, block_size, 0, k, stride_rows, physical, ldp, valid);
+    IDX_LAUNCH("to_physical_kernel", (to_physical_kernel<false>), dim3((unsigned)b.num_tokens),
+               dim3(256), stream, logical, ldl, b, c, block_size, 0, k, stride_rows, physical,
+               ldp, valid);
   return hipGetLastError();
 }
 

@@ -112,8 +112,8 @@ hipError_t launch_quant_write_k(const uint16_t* k, int64_t num_rows, int64_t str
                                 const int64_t* slots, uint8_t* cache, int64_t num_slots,
                                 hipStream_t stream) {
   const int64_t blocks = (num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(quant_write_k_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k,
-                     num_rows, stride, slots, cache, num_slots);
+  IDX_LAUNCH("quant_write_k_kernel", (quant_write_k_kernel), dim3((unsigned)blocks), dim3(256),
+             stream, k, num_rows, stride, slots, cache, num_slots);
   return hipGetLastError();
 }
 
@@ -122,13 +122,13 @@ hipError_t launch_quant_q_fold(const uint16_t* q, const float* w_raw, int64_t nu
                                float* qs_out, hipStream_t stream) {
   if ((reinterpret_cast<uintptr_t>(q) & 15) == 0) {
     const int64_t blocks = (num_rows + kFoldRows - 1) / kFoldRows;
-    hipLaunchKernelGGL(quant_q_fold16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q,
-                       w_raw, num_rows, softmax_scale, head_norm, q8, w_out, qs_out);
+    IDX_LAUNCH("quant_q_fold16_kernel", (quant_q_fold16_kernel), dim3((unsigned)blocks),
+               dim3(256), stream, q, w_raw, num_rows, softmax_scale, head_norm, q8, w_out, qs_out);
     return hipGetLastError();
   }
   const int64_t blocks = (num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(quant_q_fold_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, w_raw,
-                     num_rows, softmax_scale, head_norm, q8, w_out, qs_out);
+  IDX_LAUNCH("quant_q_fold_kernel", (quant_q_fold_kernel), dim3((unsigned)blocks), dim3(256),
+             stream, q, w_raw, num_rows, softmax_scale, head_norm, q8, w_out, qs_out);
   return hipGetLastError();
 }
 

@@ -315,8 +315,8 @@ hipError_t launch_score_write_k(const uint8_t* q8, const float* w, const CacheAr
   const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
   const NewRows nk{k, k_stride, slots, cache_w, cache.num_blocks * kBlock};
   const int ident = b.num_reqs == b.num_tokens && b.max_query_len <= 1;
-  hipLaunchKernelGGL(score_decode_write_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0,
-                     stream, q8, w, cache, b, logits, ld, cb, ident, nk, samp);
+  IDX_LAUNCH("score_decode_write_kernel", (score_decode_write_kernel<IDX_DECODE_RING>), grid,
+             dim3(kScoreThreads), stream, q8, w, cache, b, logits, ld, cb, ident, nk, samp);
   return hipGetLastError();
 }
 
@@ -329,9 +329,9 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
     const int cb = decode_chunk_blocks(b.max_seq_len, b.num_tokens);
     const int chunks = (b.max_seq_len + cb * kBlock - 1) / (cb * kBlock);
     const dim3 grid((unsigned)chunks, (unsigned)b.num_tokens);
-    hipLaunchKernelGGL(score_decode_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0, stream,
-                       q8, w, cache, b, logits, ld, cb,
-                       (int)(b.num_reqs == b.num_tokens && b.max_query_len <= 1), samp);
+    IDX_LAUNCH("score_decode_kernel", (score_decode_kernel<IDX_DECODE_RING>), grid,
+               dim3(kScoreThreads), stream, q8, w, cache, b, logits, ld, cb,
+               (int)(b.num_reqs == b.num_tokens && b.max_query_len <= 1), samp);
   } else {
     if (dec_tokens < 0) dec_tokens = 0;
     // groups numbered per request (gpr each) when that wastes little, else
@@ -348,12 +348,13 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
     const int pchunks = (b.max_seq_len + pcb * kBlock - 1) / (pcb * kBlock);
     if (dec_tokens == 0) {
       const dim3 grid((unsigned)pchunks, (unsigned)groups);
-      hipLaunchKernelGGL(score_prefill_kernel, grid, dim3(kScoreThreads), 0, stream, q8, w, cache, b,
-                         logits, ld, pcb, gpr, samp);
+      IDX_LAUNCH("score_prefill_kernel", (score_prefill_kernel), grid, dim3(kScoreThreads),
+                 stream, q8, w, cache, b, logits, ld, pcb, gpr, samp);
     } else {
       const dim3 grid((unsigned)std::max(dchunks, pchunks), (unsigned)(dec_tokens + groups));
-      hipLaunchKernelGGL(score_mixed_kernel<IDX_DECODE_RING>, grid, dim3(kScoreThreads), 0, stream,
-                         q8, w, cache, b, logits, ld, (int)dec_tokens, dcb, pcb, gpr, samp);
+      IDX_LAUNCH("score_mixed_kernel", (score_mixed_kernel<IDX_DECODE_RING>), grid,
+                 dim3(kScoreThreads), stream, q8, w, cache, b, logits, ld, (int)dec_tokens, dcb,
+                 pcb, gpr, samp);
     }
   }
   return hipGetLastError();

@@ -321,8 +321,8 @@ hipError_t launch_topk_resolve(const float* logits, int64_t ld, const BatchArgs&
                                const TopkWorkspace& ws, int k, int32_t* out, int64_t ldo,
                                hipStream_t stream) {
   if (b.num_tokens == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_resolve_kernel, dim3((unsigned)b.num_tokens), dim3(kResolveThreads), 0,
-                     stream, logits, ld, b, k, ws, out, ldo);
+  IDX_LAUNCH("topk_resolve_kernel", (topk_resolve_kernel), dim3((unsigned)b.num_tokens),
+             dim3(kResolveThreads), stream, logits, ld, b, k, ws, out, ldo);
   return hipGetLastError();
 }
 
@@ -333,11 +333,11 @@ hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, cons
     // the workspace layout fixed the chunking: one slot of slot_cap entries per chunk
     const dim3 grid((unsigned)std::max(1, ws.nslots), (unsigned)b.num_tokens);
     if (ws.slot_cap == kChunkSampled)
-      hipLaunchKernelGGL(topk_filter_kernel<kChunkSampled>, grid, dim3(kThreads), 0, stream, logits,
-                         ld, b, k, ws, out, ldo);
+      IDX_LAUNCH("topk_filter_kernel", (topk_filter_kernel<kChunkSampled>), grid, dim3(kThreads),
+                 stream, logits, ld, b, k, ws, out, ldo);
     else if (ws.slot_cap == kChunkPlain)
-      hipLaunchKernelGGL(topk_filter_kernel<kChunkPlain>, grid, dim3(kThreads), 0, stream, logits,
-                         ld, b, k, ws, out, ldo);
+      IDX_LAUNCH("topk_filter_kernel", (topk_filter_kernel<kChunkPlain>), grid, dim3(kThreads),
+                 stream, logits, ld, b, k, ws, out, ldo);
     else
       return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
@@ -345,11 +345,11 @@ hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, cons
     return launch_topk_resolve(logits, ld, b, ws, k, out, ldo, stream);
   } else {
     if (b.max_seq_len <= 65536)
-      hipLaunchKernelGGL(topk_rows_kernel<uint16_t>, dim3((unsigned)b.num_tokens), dim3(kRowThreads),
-                         0, stream, logits, ld, b, k, out, ldo);
+      IDX_LAUNCH("topk_rows_kernel", (topk_rows_kernel<uint16_t>), dim3((unsigned)b.num_tokens),
+                 dim3(kRowThreads), stream, logits, ld, b, k, out, ldo);
     else
-      hipLaunchKernelGGL(topk_rows_kernel<int32_t>, dim3((unsigned)b.num_tokens), dim3(kRowThreads),
-                         0, stream, logits, ld, b, k, out, ldo);
+      IDX_LAUNCH("topk_rows_kernel", (topk_rows_kernel<int32_t>), dim3((unsigned)b.num_tokens),
+                 dim3(kRowThreads), stream, logits, ld, b, k, out, ldo);
   }
   return hipGetLastError();
 }

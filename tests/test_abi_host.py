@@ -181,3 +181,35 @@ def test_physical_checks_table_width_against_its_block_size(m):
     assert L.idx_logits(FAKE, FAKE, 64, 128, _cache(m), B(_batch(m, max_seq_len=1024, stride=8,
                                                                  num_tokens=0, max_query_len=0)),
                         FAKE, 1024, S) == -1
+
+
+def test_trace_rejects_and_ends_empty(m):
+    L = m.lib()
+    assert L.idx_trace_begin(None, 8) == -1
+    assert L.idx_trace_begin(FAKE, 1) == -1
+    assert L.idx_trace_end(None, 0) == 0              # not tracing: nothing bracketed
+    # tracing, but every call below is rejected on the host: no kernel, no event recorded
+    assert L.idx_trace_begin(FAKE, 8) == 0
+    assert L.idx_quant_write_k(FAKE, 1, 64, 128, FAKE, _cache(m), S) == -2
+    assert L.idx_trace_end(None, 0) == 0
+
+
+def test_candidate_stages_reject_other_batches(m):
+    L = m.lib()
+    B = ctypes.byref
+    # a prefill batch (4 new tokens of one request): not the fused path
+    pre = _batch(m, num_tokens=4, max_seq_len=20000, max_query_len=4, stride=400)
+    assert L.idx_score_candidates(FAKE, FAKE, 64, 128, _cache(m), B(pre), 2048, None, 0, None,
+                                  FAKE, 1 << 30, S) == -2
+    assert L.idx_select_candidates(FAKE, FAKE, 64, 128, _cache(m), B(pre), 2048, FAKE, 2048,
+                                   FAKE, 1 << 30, S) == -2
+    # a decode batch over long rows is the fused path: a short workspace is refused
+    dec = _batch(m, num_tokens=1, max_seq_len=20000, max_query_len=1, stride=400)
+    need = L.idx_score_topk_workspace_size(B(dec), 2048)
+    assert need > 0
+    assert L.idx_score_candidates(FAKE, FAKE, 64, 128, _cache(m), B(dec), 2048, None, 0, None,
+                                  FAKE, need - 1, S) == -3
+    assert L.idx_select_candidates(FAKE, FAKE, 64, 128, _cache(m), B(dec), 2048, FAKE, 2048,
+                                   FAKE, need - 1, S) == -3
+    assert L.idx_score_candidates(FAKE, FAKE, 64, 128, _cache(m), B(dec), 0, None, 0, None,
+                                  FAKE, need, S) == -2

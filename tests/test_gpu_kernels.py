@@ -501,6 +501,61 @@ def test_fused_rescore_fallback(env):
     assert np.array_equal(dev["cache"].tensor.cpu().numpy(), orc["cache"])
 
 
+def test_kernel_trace_names_the_step_kernels(env):
+    """idx_trace_begin brackets every kernel of the traced calls with the
+    caller's events: a decode F layer over long rows runs the fused scoring
+    kernel and its resolve, a prefill F layer the K write, the scoring and the
+    row top-k; the bracketed times are positive and the results are those of
+    an untraced call."""
+    m, torch = env
+    for wl, want in ((random_batch(4020, [20000, 9000], 1, k=512),
+                      ["score_keep_kernel", "topk_keep_resolve_kernel"]),
+                     (random_batch(4021, [3000], [300], k=256),
+                      ["quant_write_k_kernel", "score_prefill_kernel", "topk_rows_kernel"])):
+        dev = device_layer(m, torch, wl, 0)
+        batch = device_batch(m, wl)
+        ref_cache = m.KCache(wl.num_blocks, tensor=dev["cache"].tensor.clone())
+        ref = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
+        m.idx_indexcache_layer(dev["k_new"], ref_cache, dev["q8"], dev["w"], True, True,
+                               dev["slots_new"], batch, wl.k, ref)
+        topk = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
+        with m.KernelTrace(capacity=8) as tr:
+            m.idx_indexcache_layer(dev["k_new"], dev["cache"], dev["q8"], dev["w"], True, True,
+                                   dev["slots_new"], batch, wl.k, topk)
+        say("trace", tr.kernels)
+        assert [n for n, _ in tr.kernels] == want
+        assert all(ms > 0 for _, ms in tr.kernels)
+        assert torch.equal(topk, ref)
+    with m.KernelTrace(capacity=1) as tr:         # events for one kernel: the first is timed
+        m.idx_indexcache_layer(dev["k_new"], dev["cache"], dev["q8"], dev["w"], True, True,
+                               dev["slots_new"], batch, wl.k, topk)
+    assert [n for n, _ in tr.kernels] == want[:1]
+
+
+def test_candidate_stages_equal_score_topk(env):
+    """idx_score_candidates + idx_select_candidates are the fused path's two
+    launches: the same rows as idx_score_topk, and with the new K rows the same
+    cache bytes and rows as the F layer."""
+    m, torch = env
+    wl = random_batch(4022, [20000, 9000, 30000], 1, k=2048)
+    dev = device_layer(m, torch, wl, 0)
+    batch = device_batch(m, wl)
+    ref_cache = m.KCache(wl.num_blocks, tensor=dev["cache"].tensor.clone())
+    ref = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
+    m.idx_indexcache_layer(dev["k_new"], ref_cache, dev["q8"], dev["w"], True, True,
+                           dev["slots_new"], batch, wl.k, ref)
+    ws = torch.empty(m.idx_score_topk_workspace_size(batch, wl.k), dtype=torch.uint8, device="cuda")
+    m.idx_score_candidates(dev["q8"], dev["w"], dev["cache"], batch, wl.k, ws, dev["k_new"],
+                           dev["slots_new"])
+    got = m.idx_select_candidates(dev["q8"], dev["w"], dev["cache"], batch, wl.k, ws)
+    assert torch.equal(dev["cache"].tensor, ref_cache.tensor)
+    assert torch.equal(got, ref)
+    m.idx_score_candidates(dev["q8"], dev["w"], dev["cache"], batch, wl.k, ws)   # no new rows
+    got = m.idx_select_candidates(dev["q8"], dev["w"], dev["cache"], batch, wl.k, ws)
+    assert torch.equal(got, m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], batch, wl.k))
+    assert torch.equal(got, ref)
+
+
 def test_layer_k_write_inside_scoring(env):
     """An F layer of a decode batch writes its new K rows from inside the decode
     scoring kernel.  The cache bytes and the top-k rows must equal the separate
