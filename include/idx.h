@@ -294,6 +294,49 @@ idx_status_t idx_indexcache_stack(const idx_layer_io_t* layers, int32_t num_laye
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The consumer's view of the top-k rows for the logical -> physical
+ * conversion ([group] SparseMLAIndexGroup: the physical top-k and the valid
+ * counts of an index group): rows are converted through the batch's block
+ * table with `block_size` positions per block, physical slot =
+ * block * block_stride_rows + offset (block_stride_rows 0 = block_size).
+ *   physical      device int32 rows of k entries, physical_stride >= k
+ *   valid_counts  device int32 [num_tokens] or NULL
+ *   num_blocks    the consumer's pool: a block id outside it gives -1
+ */
+typedef struct idx_physical {
+  int32_t* physical;
+  int64_t physical_stride;
+  int32_t* valid_counts;
+  int32_t block_size;
+  int64_t num_blocks;
+  int64_t block_stride_rows;
+} idx_physical_t;
+
+/*
+ * idx_indexcache_layer / idx_indexcache_stack with the group's physical rows
+ * ([group] SparseMLAIndexGroup._convert_once, SparseMLAIndexGroupBuilder: a
+ * group is the layer that produces the top-k and the layers that reuse it;
+ * its rows are converted once, after the producer).  An F layer converts its
+ * fresh top-k rows into phys (as idx_topk_to_physical would); an S layer
+ * leaves phys alone, so every layer of a group reads the physical rows of the
+ * group's F layer.  phys == NULL gives the plain calls.  The physical
+ * arguments are checked like idx_topk_to_physical's, before anything is
+ * enqueued.
+ */
+idx_status_t idx_indexcache_layer_physical(const idx_layer_io_t* layer, int32_t is_full,
+                                           int32_t write_k, const int64_t* slot_mapping,
+                                           const idx_batch_t* batch, int32_t k, int32_t* topk,
+                                           int64_t topk_stride, const idx_physical_t* phys,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+idx_status_t idx_indexcache_stack_physical(const idx_layer_io_t* layers, int32_t num_layers,
+                                           const uint8_t* is_full, int32_t write_k_on_s,
+                                           const int64_t* slot_mapping, const idx_batch_t* batch,
+                                           int32_t k, int32_t* topk, int64_t topk_stride,
+                                           const idx_physical_t* phys, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Logical -> physical top-k conversion ([group] SparseMLAIndexGroup,
  * convert_logical_to_physical_topk / _convert_once): for token t of request
  * r, physical = block_table[r][pos / block_size] * stride_rows + pos % block_size,

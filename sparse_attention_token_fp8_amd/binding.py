@@ -48,6 +48,12 @@ class LayerIOC(ctypes.Structure):
                 ("cache", KCacheC), ("q_fp8", ctypes.c_void_p), ("w", ctypes.c_void_p)]
 
 
+class PhysicalC(ctypes.Structure):
+    _fields_ = [("physical", ctypes.c_void_p), ("physical_stride", ctypes.c_int64),
+                ("valid_counts", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int64), ("block_stride_rows", ctypes.c_int64)]
+
+
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 _PBatch = ctypes.POINTER(BatchC)
 
@@ -75,6 +81,12 @@ SIGNATURES = {
                                             _i32, _vp, _i64, _vp, _sz, _vp]),
     "idx_indexcache_stack": (ctypes.c_int, [ctypes.POINTER(LayerIOC), _i32, _vp, _i32, _vp,
                                             _PBatch, _i32, _vp, _i64, _vp, _sz, _vp]),
+    "idx_indexcache_layer_physical": (ctypes.c_int, [ctypes.POINTER(LayerIOC), _i32, _i32, _vp,
+                                                     _PBatch, _i32, _vp, _i64,
+                                                     ctypes.POINTER(PhysicalC), _vp, _sz, _vp]),
+    "idx_indexcache_stack_physical": (ctypes.c_int, [ctypes.POINTER(LayerIOC), _i32, _vp, _i32,
+                                                     _vp, _PBatch, _i32, _vp, _i64,
+                                                     ctypes.POINTER(PhysicalC), _vp, _sz, _vp]),
     "idx_topk_to_physical": (ctypes.c_int, [_vp, _i64, _PBatch, _i32, _i64, _i32, _i64, _vp, _i64,
                                             _vp, _vp]),
 }
@@ -312,6 +324,54 @@ def idx_indexcache_stack(layers, is_full, write_k_on_s, slot_mapping, batch, k, 
            _lib.idx_indexcache_stack(arr, n, ctypes.cast(full, ctypes.c_void_p), int(write_k_on_s),
                                      _ptr(slot_mapping), batch.c(), k, _ptr(topk),
                                      int(topk.stride(0)), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+class Physical:
+    """The consumer's physical top-k rows and valid counts of an index group:
+    [num_tokens, k] int32 rows over a pool of num_blocks blocks of block_size
+    positions (physical slot = block * block_stride_rows + offset)."""
+
+    def __init__(self, num_tokens, k, num_blocks, block_size=BLOCK_SIZE, block_stride_rows=0,
+                 device="cuda", fill=None):
+        self.physical = torch.empty((num_tokens, k), dtype=torch.int32, device=device)
+        self.valid_counts = torch.empty((num_tokens,), dtype=torch.int32, device=device)
+        if fill is not None:
+            self.physical.fill_(fill)
+            self.valid_counts.fill_(fill)
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self.block_stride_rows = int(block_stride_rows)
+
+    def c(self):
+        return PhysicalC(_ptr(self.physical), int(self.physical.stride(0)), _ptr(self.valid_counts),
+                         self.block_size, self.num_blocks, self.block_stride_rows)
+
+
+def idx_indexcache_layer_physical(k_new, cache, q_fp8, w, is_full, write_k, slot_mapping, batch, k,
+                                  topk, physical, workspace=None, stream=None):
+    """idx_indexcache_layer that also converts an F layer's rows into `physical`
+    (a Physical); S layers leave it alone."""
+    io = _layer_io(k_new, cache, q_fp8, w)
+    ph = physical.c()
+    ws = _workspace(idx_score_topk_workspace_size(batch, k), topk.device, workspace)
+    _check("idx_indexcache_layer_physical",
+           _lib.idx_indexcache_layer_physical(ctypes.byref(io), int(is_full), int(write_k),
+                                              _ptr(slot_mapping), batch.c(), k, _ptr(topk),
+                                              int(topk.stride(0)), ctypes.byref(ph), _ptr(ws),
+                                              ws.numel(), _stream(stream)))
+
+
+def idx_indexcache_stack_physical(layers, is_full, write_k_on_s, slot_mapping, batch, k, topk,
+                                  physical, workspace=None, stream=None):
+    n = len(layers)
+    arr = (LayerIOC * n)(*[_layer_io(*lay) for lay in layers])
+    full = (ctypes.c_uint8 * n)(*[1 if f else 0 for f in is_full])
+    ph = physical.c()
+    ws = _workspace(idx_score_topk_workspace_size(batch, k), topk.device, workspace)
+    _check("idx_indexcache_stack_physical",
+           _lib.idx_indexcache_stack_physical(arr, n, ctypes.cast(full, ctypes.c_void_p),
+                                              int(write_k_on_s), _ptr(slot_mapping), batch.c(), k,
+                                              _ptr(topk), int(topk.stride(0)), ctypes.byref(ph),
+                                              _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def idx_topk_to_physical(logical, batch, num_blocks, block_size=BLOCK_SIZE, block_stride_rows=0,

@@ -154,6 +154,63 @@ hipError_t score_topk(const uint8_t* q_fp8, const float* w, const idx_kcache_t& 
   return e;
 }
 
+// Every layer of a stack, checked before anything is enqueued.
+idx_status_t check_stack(const idx_layer_io_t* layers, int32_t num_layers, const uint8_t* is_full,
+                         int32_t write_k_on_s, const int64_t* slot_mapping,
+                         const idx_batch_t* batch, int32_t k, const int32_t* topk,
+                         int64_t topk_stride, const void* workspace, size_t workspace_bytes) {
+  if (layers == nullptr || is_full == nullptr || num_layers < 1) return IDX_ERR_INVALID_ARG;
+  if (!is_full[0]) return IDX_ERR_INVALID_ARG;
+  idx_status_t s = check_batch(batch);
+  if (s != IDX_OK) return s;
+  for (int l = 0; l < num_layers; ++l) {
+    const idx_layer_io_t& L = layers[l];
+    s = check_cache(L.cache);
+    if (s != IDX_OK) return s;
+    if (is_full[l]) {
+      s = check_scoring(L.q_fp8, L.w, kHeads, kHeadDim, L.cache, batch);
+      if (s != IDX_OK) return s;
+    }
+    if ((is_full[l] || write_k_on_s) && batch->num_tokens > 0 &&
+        (L.k_bf16 == nullptr || L.k_row_stride < kHeadDim || (L.k_row_stride % 4) != 0 ||
+         !aligned(L.k_bf16, 8) || slot_mapping == nullptr || !aligned(slot_mapping, 8) ||
+         L.cache.data == nullptr))
+      return IDX_ERR_INVALID_ARG;
+  }
+  s = check_k(k, topk_stride, topk, batch->num_tokens);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens > 0 &&
+      (workspace == nullptr || workspace_bytes < idx_score_topk_workspace_size(batch, k) ||
+       !aligned(workspace, 256)))
+    return IDX_ERR_WORKSPACE;
+  return IDX_OK;
+}
+
+// The physical conversion's arguments (the consumer's block size, pool and
+// output rows) for rows of k entries.
+idx_status_t check_physical(const idx_batch_t* batch, int32_t k, const idx_physical_t* p) {
+  if (p->block_size < 1) return IDX_ERR_INVALID_ARG;
+  idx_status_t s = check_batch(batch, p->block_size);
+  if (s != IDX_OK) return s;
+  if (k < 1 || k > kMaxK) return IDX_ERR_UNSUPPORTED;
+  if (p->num_blocks < 0 || p->block_stride_rows < 0) return IDX_ERR_INVALID_ARG;
+  const int64_t stride_rows = p->block_stride_rows ? p->block_stride_rows : p->block_size;
+  if (stride_rows < p->block_size) return IDX_ERR_INVALID_ARG;
+  if (p->num_blocks * stride_rows > (int64_t)INT32_MAX) return IDX_ERR_UNSUPPORTED;
+  if (p->physical_stride < k) return IDX_ERR_INVALID_ARG;
+  if (batch->num_tokens > 0 && p->physical == nullptr) return IDX_ERR_INVALID_ARG;
+  if (!aligned(p->physical, 4) || !aligned(p->valid_counts, 4)) return IDX_ERR_INVALID_ARG;
+  return IDX_OK;
+}
+
+hipError_t to_physical(const int32_t* logical, int64_t logical_stride, const idx_batch_t* batch,
+                       int32_t k, const idx_physical_t& p, hipStream_t stream) {
+  const int64_t stride_rows = p.block_stride_rows ? p.block_stride_rows : p.block_size;
+  return launch_topk_to_physical(logical, logical_stride, to_args(batch), p.block_size,
+                                 p.num_blocks, k, stride_rows, p.physical, p.physical_stride,
+                                 p.valid_counts, stream);
+}
+
 }  // namespace
 
 // Workspace of idx_score_topk_noalloc, for callers that cannot allocate: one
@@ -386,37 +443,9 @@ idx_status_t idx_indexcache_stack(const idx_layer_io_t* layers, int32_t num_laye
                                   const int64_t* slot_mapping, const idx_batch_t* batch, int32_t k,
                                   int32_t* topk, int64_t topk_stride, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
-  if (layers == nullptr || is_full == nullptr || num_layers < 1) return IDX_ERR_INVALID_ARG;
-  if (!is_full[0]) return IDX_ERR_INVALID_ARG;
-  // check every layer before enqueueing anything
-  idx_status_t s = check_batch(batch);
-  if (s != IDX_OK) return s;
-  for (int l = 0; l < num_layers; ++l) {
-    const idx_layer_io_t& L = layers[l];
-    s = check_cache(L.cache);
-    if (s != IDX_OK) return s;
-    if (is_full[l]) {
-      s = check_scoring(L.q_fp8, L.w, kHeads, kHeadDim, L.cache, batch);
-      if (s != IDX_OK) return s;
-    }
-    if ((is_full[l] || write_k_on_s) && batch->num_tokens > 0 &&
-        (L.k_bf16 == nullptr || L.k_row_stride < kHeadDim || (L.k_row_stride % 4) != 0 ||
-         !aligned(L.k_bf16, 8) || slot_mapping == nullptr || !aligned(slot_mapping, 8) ||
-         L.cache.data == nullptr))
-      return IDX_ERR_INVALID_ARG;
-  }
-  s = check_k(k, topk_stride, topk, batch->num_tokens);
-  if (s != IDX_OK) return s;
-  if (batch->num_tokens > 0 &&
-      (workspace == nullptr || workspace_bytes < idx_score_topk_workspace_size(batch, k) ||
-       !aligned(workspace, 256)))
-    return IDX_ERR_WORKSPACE;
-  for (int l = 0; l < num_layers; ++l) {
-    s = idx_indexcache_layer(&layers[l], is_full[l], write_k_on_s, slot_mapping, batch, k, topk,
-                             topk_stride, workspace, workspace_bytes, stream);
-    if (s != IDX_OK) return s;
-  }
-  return IDX_OK;
+  return idx_indexcache_stack_physical(layers, num_layers, is_full, write_k_on_s, slot_mapping,
+                                       batch, k, topk, topk_stride, nullptr, workspace,
+                                       workspace_bytes, stream);
 }
 
 idx_status_t idx_topk_to_physical(const int32_t* logical, int64_t logical_stride,
@@ -424,22 +453,53 @@ idx_status_t idx_topk_to_physical(const int32_t* logical, int64_t logical_stride
                                   int32_t k, int64_t block_stride_rows, int32_t* physical,
                                   int64_t physical_stride, int32_t* valid_counts,
                                   hipStream_t stream) {
-  if (block_size < 1) return IDX_ERR_INVALID_ARG;
-  idx_status_t s = check_batch(batch, block_size);
+  const idx_physical_t ph{physical, physical_stride, valid_counts, block_size, num_blocks,
+                          block_stride_rows};
+  idx_status_t s = check_physical(batch, k, &ph);
   if (s != IDX_OK) return s;
-  if (k < 1 || k > kMaxK) return IDX_ERR_UNSUPPORTED;
-  if (num_blocks < 0 || block_stride_rows < 0) return IDX_ERR_INVALID_ARG;
-  const int64_t stride_rows = block_stride_rows ? block_stride_rows : block_size;
-  if (stride_rows < block_size) return IDX_ERR_INVALID_ARG;
-  if (num_blocks * stride_rows > (int64_t)INT32_MAX) return IDX_ERR_UNSUPPORTED;
-  if (logical_stride < k || physical_stride < k) return IDX_ERR_INVALID_ARG;
+  if (logical_stride < k) return IDX_ERR_INVALID_ARG;
   if (batch->num_tokens == 0) return IDX_OK;
-  if (logical == nullptr || physical == nullptr) return IDX_ERR_INVALID_ARG;
-  if (!aligned(logical, 4) || !aligned(physical, 4) || !aligned(valid_counts, 4))
-    return IDX_ERR_INVALID_ARG;
-  return launched(launch_topk_to_physical(logical, logical_stride, to_args(batch), block_size,
-                                          num_blocks, k, stride_rows, physical, physical_stride,
-                                          valid_counts, stream));
+  if (logical == nullptr || !aligned(logical, 4)) return IDX_ERR_INVALID_ARG;
+  return launched(to_physical(logical, logical_stride, batch, k, ph, stream));
+}
+
+idx_status_t idx_indexcache_layer_physical(const idx_layer_io_t* layer, int32_t is_full,
+                                           int32_t write_k, const int64_t* slot_mapping,
+                                           const idx_batch_t* batch, int32_t k, int32_t* topk,
+                                           int64_t topk_stride, const idx_physical_t* phys,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  if (phys != nullptr && is_full) {
+    const idx_status_t s = check_physical(batch, k, phys);
+    if (s != IDX_OK) return s;
+  }
+  const idx_status_t s = idx_indexcache_layer(layer, is_full, write_k, slot_mapping, batch, k,
+                                              topk, topk_stride, workspace, workspace_bytes,
+                                              stream);
+  if (s != IDX_OK || phys == nullptr || !is_full || batch->num_tokens == 0) return s;
+  return launched(to_physical(topk, topk_stride, batch, k, *phys, stream));
+}
+
+idx_status_t idx_indexcache_stack_physical(const idx_layer_io_t* layers, int32_t num_layers,
+                                           const uint8_t* is_full, int32_t write_k_on_s,
+                                           const int64_t* slot_mapping, const idx_batch_t* batch,
+                                           int32_t k, int32_t* topk, int64_t topk_stride,
+                                           const idx_physical_t* phys, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  if (phys != nullptr) {
+    const idx_status_t s = check_physical(batch, k, phys);
+    if (s != IDX_OK) return s;
+  }
+  idx_status_t s = check_stack(layers, num_layers, is_full, write_k_on_s, slot_mapping, batch, k,
+                               topk, topk_stride, workspace, workspace_bytes);
+  if (s != IDX_OK) return s;
+  for (int l = 0; l < num_layers; ++l) {
+    s = idx_indexcache_layer_physical(&layers[l], is_full[l], write_k_on_s, slot_mapping, batch,
+                                      k, topk, topk_stride, phys, workspace, workspace_bytes,
+                                      stream);
+    if (s != IDX_OK) return s;
+  }
+  return IDX_OK;
 }
 
 }  // extern "C"

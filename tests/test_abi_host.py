@@ -213,3 +213,35 @@ def test_candidate_stages_reject_other_batches(m):
                                    FAKE, need - 1, S) == -3
     assert L.idx_score_candidates(FAKE, FAKE, 64, 128, _cache(m), B(dec), 0, None, 0, None,
                                   FAKE, need, S) == -2
+
+
+def test_group_physical_rejects_before_any_work(m):
+    L = m.lib()
+    B = ctypes.byref
+    ok = _batch(m)
+    io = (m.binding.LayerIOC * 2)()
+    for lay in io:
+        lay.cache = _cache(m)
+        lay.k_bf16, lay.k_row_stride, lay.q_fp8, lay.w = 0x10000, 128, 0x10000, 0x10000
+    full = ctypes.cast((ctypes.c_uint8 * 2)(1, 0), ctypes.c_void_p)
+    P = m.binding.PhysicalC
+    bad = [P(0x10000, 8, None, 0, 10, 0),            # block size 0
+           P(0x10000, 4, None, 64, 10, 0),           # physical rows narrower than k
+           P(0x10000, 8, None, 64, 10, 32),          # block stride below the block size
+           P(None, 8, None, 64, 10, 0),              # no physical rows for a non-empty batch
+           P(0x10002, 8, None, 64, 10, 0)]           # misaligned rows
+    want = [-1, -1, -1, -1, -1]
+    for ph, w in zip(bad, want):
+        # an F layer checks the physical arguments before it scores anything
+        assert L.idx_indexcache_layer_physical(B(io[0]), 1, 1, FAKE, B(ok), 8, FAKE, 8, B(ph),
+                                               FAKE, 1 << 20, S) == w
+        assert L.idx_indexcache_stack_physical(io, 2, full, 1, FAKE, B(ok), 8, FAKE, 8, B(ph),
+                                               FAKE, 1 << 20, S) == w
+    huge = P(0x10000, 8, None, 64, 1 << 30, 64)          # pool beyond int32 slots
+    assert L.idx_indexcache_stack_physical(io, 2, full, 1, FAKE, B(ok), 8, FAKE, 8, B(huge),
+                                           FAKE, 1 << 20, S) == -2
+    # a good physical description does not let a bad stack through
+    good = P(0x10000, 8, None, 64, 10, 0)
+    io[1].cache = _cache(m, bs=32)
+    assert L.idx_indexcache_stack_physical(io, 2, full, 1, FAKE, B(ok), 8, FAKE, 8, B(good),
+                                           FAKE, 1 << 20, S) == -2

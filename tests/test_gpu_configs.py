@@ -14,13 +14,17 @@ oracle, recomputed on the host from the same raw draws:
 
 The 16-layer stack also compares the new K rows of every layer, S layers
 included, with oracle bytes, checks every row of each F layer against the
-oracle, and checks that S layers leave the last F layer's rows in the buffer.
+oracle, checks that S layers leave the last F layer's rows in the buffer,
+and runs each layer with the group's physical conversion: after an F layer
+the physical rows and valid counts equal the oracle's conversion of its
+top-k rows, and an S layer leaves them as they were.
 """
 
 import numpy as np
 import pytest
 
 from oracle import quant as oquant
+from oracle.physical import to_physical
 from synth import CONFIGS, make_workload
 from tests.gpu_helpers import (check_topk_band, device_batch, device_layer, oracle_layer,
                                oracle_rows, say)
@@ -120,14 +124,25 @@ def test_stack_16L_32x64k(env):
     batch = device_batch(m, wl)
     topk = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
     ws = torch.empty(m.idx_score_topk_workspace_size(batch, wl.k), dtype=torch.uint8, device="cuda")
+    # the group's physical rows: converted after each F layer, left alone by S layers
+    phys = m.Physical(wl.num_tokens, wl.k, wl.num_blocks, fill=-9)
     consumed = []
     for layer in range(wl.num_layers):
         say(f"[stack] layer {layer} {'F' if full[layer] else 'S'}")
         dev = device_layer(m, torch, wl, layer)
-        m.idx_indexcache_layer(dev["k_new"], dev["cache"], dev["q8"], dev["w"], full[layer], True,
-                               dev["slots_new"], batch, wl.k, topk, workspace=ws)
+        before = (phys.physical.cpu().numpy().copy(), phys.valid_counts.cpu().numpy().copy())
+        m.idx_indexcache_layer_physical(dev["k_new"], dev["cache"], dev["q8"], dev["w"], full[layer],
+                                        True, dev["slots_new"], batch, wl.k, topk, phys,
+                                        workspace=ws)
         torch.cuda.synchronize()
         consumed.append(topk.cpu().numpy().copy())
+        got_phys = (phys.physical.cpu().numpy(), phys.valid_counts.cpu().numpy())
+        if full[layer]:
+            want_phys = to_physical(consumed[-1], wl.token_req(), wl.block_table, 64)
+        else:
+            want_phys = before
+        assert np.array_equal(got_phys[0], want_phys[0]), f"layer {layer}: physical rows"
+        assert np.array_equal(got_phys[1], want_phys[1]), f"layer {layer}: valid counts"
         # this layer's new K rows (written inside scoring on F layers, by the
         # separate quantiser on S layers) against the oracle's bytes
         nb, ns = wl.new_rows(layer)

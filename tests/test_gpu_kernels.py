@@ -639,3 +639,35 @@ def test_topk_to_physical_block_shapes(env, block_size, stride, k):
     want, wv = oracle.physical.to_physical(logical, wl.token_req(), bt, block_size, stride or None)
     assert np.array_equal(phys.cpu().numpy(), want)
     assert np.array_equal(valid.cpu().numpy(), wv)
+
+@pytest.mark.parametrize("block_stride", [0, 80])
+def test_stack_physical_equals_stack_then_convert(env, block_stride):
+    """idx_indexcache_stack_physical gives the plain stack's top-k rows, and
+    physical rows equal to the oracle's conversion of the last F layer's rows
+    (the S layers after it leave them alone)."""
+    m, torch = env
+    pattern = "FSFSS"
+    wl = random_batch(5201, [3000, 9000, 700, 1500], [1, 1, 40, 1], k=256,
+                      num_layers=len(pattern), pattern=pattern)
+    say("stack physical", pattern, "block stride", block_stride)
+    full = m.idx_layer_schedule(True, pattern, 1, 2, len(pattern))
+    batch = device_batch(m, wl)
+    results = []
+    for with_phys in (False, True):
+        devs = [device_layer(m, torch, wl, l) for l in range(len(pattern))]
+        layers = [(d["k_new"], d["cache"], d["q8"], d["w"]) for d in devs]
+        topk = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
+        if with_phys:
+            phys = m.Physical(wl.num_tokens, wl.k, wl.num_blocks, block_stride_rows=block_stride,
+                              fill=-9)
+            m.idx_indexcache_stack_physical(layers, full, True, devs[0]["slots_new"], batch, wl.k,
+                                            topk, phys)
+        else:
+            m.idx_indexcache_stack(layers, full, True, devs[0]["slots_new"], batch, wl.k, topk)
+        torch.cuda.synchronize()
+        results.append(topk.cpu().numpy())
+    assert np.array_equal(results[0], results[1])
+    want, wv = oracle.physical.to_physical(results[1], wl.token_req(), wl.block_table, 64,
+                                           block_stride or None)
+    assert np.array_equal(phys.physical.cpu().numpy(), want)
+    assert np.array_equal(phys.valid_counts.cpu().numpy(), wv)
