@@ -12,6 +12,9 @@ pages compute it on an fp32 torch tensor.
 
 Modules
   e4m3      OCP 8-bit float E4M3 encode / decode
+  e2m1      OCP 4-bit float E2M1 encode / decode, E8M0 scales
+  fp4cache  the FP4 indexer K cache: per-32 quantiser, block layout,
+            scatter / gather and its score
   quant     ue8m0 per-128 quantisation, paged-cache scatter, q quantisation
             and weight fold
   paged     the byte layout of one paged K-cache block and gathers through
@@ -27,5 +30,5 @@ are silent the reading adopted is stated in the docstring.  Functions whose
 result no independent pin covers say "parity unpinned".
 """
 
-from . import e4m3, quant, paged, logits, topk, schedule, stack, physical  # noqa: F401
+from . import e4m3, e2m1, quant, paged, logits, fp4cache, topk, schedule, stack, physical  # noqa: F401
 from .batch import Batch  # noqa: F401
