@@ -217,6 +217,44 @@ idx_status_t idx_select_candidates(const uint8_t* q_fp8, const float* w, int32_t
                                    size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The FP4 indexer K cache ([blog] SparseAttnIndexer.forward_cuda passes
+ * use_fp4_cache to the op; the pages give no format, the one below is this
+ * library's: the OCP MX FP4 element E2M1 with E8M0 power-of-two scales per
+ * 32 dims, which gfx950's scaled matrix cores read directly).  Same
+ * idx_kcache_t, block_size 64, but each block holds 4352 bytes (68 per
+ * position, half the FP8 cache's codes plus four scale bytes):
+ *   codes   byte g*1024 + p*16 + i            dims 32g+2i (bits 0-3) and
+ *                                             32g+2i+1 (bits 4-7) of offset p
+ *   scales  byte 4096 + g*64 + (p%16)*4 + p/16  E8M0 byte e + 127 of group g
+ * for groups g = 0..3 of 32 dims and offsets p = 0..63; cache.data holds
+ * num_blocks * 4352 bytes, 16-byte aligned.
+ *
+ * idx_quant_write_k_fp4: per row and group, e = the smallest integer with
+ * max(amax_g, 1e-4) <= 6 * 2^e, code = E2M1(x / 2^e) to nearest, ties to
+ * even, sign of zero kept; arguments and skipped slots as idx_quant_write_k.
+ * Only the written slots' 68 bytes change.
+ *
+ * idx_logits_fp4: the scores of idx_logits with K decoded group by group,
+ *   I[t, s] = sum_h w[t, h] * max(0, sum_d q8[t, h, d] * c[s, d] * 2^e[s, d/32]),
+ * same arguments, causal rows and ReLU split (no separate per-position scale).
+ *
+ * idx_score_topk_fp4: idx_logits_fp4 then idx_topk's selection, the scores
+ * kept in the workspace (>= idx_score_topk_fp4_workspace_size bytes,
+ * 256-byte aligned) between the two.
+ */
+idx_status_t idx_quant_write_k_fp4(const uint16_t* k_bf16, int64_t num_tokens, int32_t head_dim,
+                                   int64_t k_row_stride, const int64_t* slot_mapping,
+                                   idx_kcache_t cache, hipStream_t stream);
+idx_status_t idx_logits_fp4(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
+                            idx_kcache_t cache, const idx_batch_t* batch, float* logits,
+                            int64_t logits_stride, hipStream_t stream);
+size_t idx_score_topk_fp4_workspace_size(const idx_batch_t* batch, int32_t k);
+idx_status_t idx_score_topk_fp4(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
+                                int32_t k, int32_t* topk, int64_t topk_stride, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation):
  * idx_score_topk with its workspace taken from a device array that the

@@ -74,6 +74,11 @@ SIGNATURES = {
                                             _vp, _vp, _sz, _vp]),
     "idx_select_candidates": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _i32, _vp,
                                              _i64, _vp, _sz, _vp]),
+    "idx_quant_write_k_fp4": (ctypes.c_int, [_vp, _i64, _i32, _i64, _vp, KCacheC, _vp]),
+    "idx_logits_fp4": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _vp, _i64, _vp]),
+    "idx_score_topk_fp4_workspace_size": (_sz, [_PBatch, _i32]),
+    "idx_score_topk_fp4": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _i32, _vp, _i64,
+                                          _vp, _sz, _vp]),
     "idx_layer_schedule": (ctypes.c_int, [_i32, ctypes.c_char_p, _i32, _i32, _i32, _vp]),
     "idx_trace_begin": (ctypes.c_int, [_vp, _i32]),
     "idx_trace_end": (_i32, [_vp, _i32]),
@@ -136,6 +141,24 @@ class KCache:
                 tensor = torch.empty((num_blocks, BLOCK_SIZE, TOKEN_BYTES), dtype=torch.uint8, device=device)
             else:
                 tensor = torch.full((num_blocks, BLOCK_SIZE, TOKEN_BYTES), fill, dtype=torch.uint8, device=device)
+        self.tensor = tensor
+        self.num_blocks = int(tensor.shape[0])
+
+    def c(self):
+        return KCacheC(self.tensor.data_ptr(), self.num_blocks, BLOCK_SIZE)
+
+
+FP4_BLOCK_BYTES = 4352        # 64 positions x (64 code bytes + 4 scale bytes)
+
+
+class KCacheFP4:
+    """A paged FP4 indexer K cache: uint8 [num_blocks, 4352] on the device."""
+
+    def __init__(self, num_blocks, device="cuda", fill=None, tensor=None):
+        if tensor is None:
+            shape = (num_blocks, FP4_BLOCK_BYTES)
+            tensor = (torch.empty(shape, dtype=torch.uint8, device=device) if fill is None
+                      else torch.full(shape, fill, dtype=torch.uint8, device=device))
         self.tensor = tensor
         self.num_blocks = int(tensor.shape[0])
 
@@ -250,6 +273,41 @@ def idx_score_topk(q_fp8, w, cache, batch, k, topk=None, workspace=None, stream=
            _lib.idx_score_topk(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(), k,
                                _ptr(topk), int(topk.stride(0)), _ptr(ws), ws.numel(),
                                _stream(stream)))
+    return topk
+
+
+def idx_quant_write_k_fp4(k, slot_mapping, cache, stream=None):
+    """Quantise K rows [N, >=128] (bf16) to the FP4 cache (a KCacheFP4)."""
+    k = as_bf16_bits(k)
+    n = int(k.shape[0])
+    _check("idx_quant_write_k_fp4",
+           _lib.idx_quant_write_k_fp4(_ptr(k), n, HEAD_DIM, int(k.stride(0)) if n else HEAD_DIM,
+                                      _ptr(slot_mapping), cache.c(), _stream(stream)))
+
+
+def idx_logits_fp4(q_fp8, w, cache, batch, logits=None, stream=None):
+    """Scores against an FP4 cache, as idx_logits."""
+    if logits is None:
+        logits = torch.empty((batch.num_tokens, max(batch.max_seq_len, 1)), dtype=torch.float32,
+                             device=q_fp8.device)
+    _check("idx_logits_fp4",
+           _lib.idx_logits_fp4(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(),
+                               _ptr(logits), int(logits.stride(0)), _stream(stream)))
+    return logits
+
+
+def idx_score_topk_fp4_workspace_size(batch, k):
+    return int(_lib.idx_score_topk_fp4_workspace_size(batch.c(), k))
+
+
+def idx_score_topk_fp4(q_fp8, w, cache, batch, k, topk=None, workspace=None, stream=None):
+    if topk is None:
+        topk = torch.empty((batch.num_tokens, k), dtype=torch.int32, device=q_fp8.device)
+    ws = _workspace(idx_score_topk_fp4_workspace_size(batch, k), q_fp8.device, workspace)
+    _check("idx_score_topk_fp4",
+           _lib.idx_score_topk_fp4(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(), k,
+                                   _ptr(topk), int(topk.stride(0)), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
     return topk
 
 

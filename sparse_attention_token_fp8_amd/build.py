@@ -36,6 +36,7 @@ SCORE_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA = {
     "score.hip": SCORE_FLAGS,
     "fused.hip": SCORE_FLAGS,
+    "fp4.hip": SCORE_FLAGS,
 }
 
 

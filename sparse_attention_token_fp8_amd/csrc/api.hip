@@ -338,6 +338,60 @@ size_t idx_score_topk_workspace_size(const idx_batch_t* batch, int32_t k) {
   return fused_workspace(batch, nullptr, nullptr);
 }
 
+idx_status_t idx_quant_write_k_fp4(const uint16_t* k_bf16, int64_t num_tokens, int32_t head_dim,
+                                   int64_t k_row_stride, const int64_t* slot_mapping,
+                                   idx_kcache_t cache, hipStream_t stream) {
+  if (head_dim != kHeadDim) return IDX_ERR_UNSUPPORTED;
+  idx_status_t s = check_cache(cache);
+  if (s != IDX_OK) return s;
+  if (num_tokens < 0) return IDX_ERR_INVALID_ARG;
+  if (num_tokens == 0) return IDX_OK;
+  s = check_k_rows(k_bf16, k_row_stride, slot_mapping, cache, num_tokens);
+  if (s != IDX_OK) return s;
+  return launched(launch_quant_write_k_fp4(k_bf16, num_tokens, k_row_stride, slot_mapping,
+                                           cache.data, cache.num_blocks * kBlock, stream));
+}
+
+idx_status_t idx_logits_fp4(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
+                            idx_kcache_t cache, const idx_batch_t* batch, float* logits,
+                            int64_t logits_stride, hipStream_t stream) {
+  idx_status_t s = check_scoring(q_fp8, w, n_heads, head_dim, cache, batch);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens == 0) return IDX_OK;
+  if (logits == nullptr || logits_stride < batch->max_seq_len || !aligned(logits, 4))
+    return IDX_ERR_INVALID_ARG;
+  return launched(launch_score_fp4(q_fp8, w, CacheArgs{cache.data, cache.num_blocks},
+                                   to_args(batch), batch->num_decode_tokens, logits, logits_stride,
+                                   nullptr, stream));
+}
+
+size_t idx_score_topk_fp4_workspace_size(const idx_batch_t* batch, int32_t k) {
+  if (batch == nullptr || batch->num_tokens <= 0 || k < 1) return 0;
+  if (check_batch(batch) != IDX_OK) return 0;
+  return fused_workspace(batch, nullptr, nullptr);
+}
+
+idx_status_t idx_score_topk_fp4(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
+                                int32_t k, int32_t* topk, int64_t topk_stride, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  idx_status_t s = check_scoring(q_fp8, w, n_heads, head_dim, cache, batch);
+  if (s != IDX_OK) return s;
+  s = check_k(k, topk_stride, topk, batch->num_tokens);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens == 0) return IDX_OK;
+  if (workspace == nullptr || workspace_bytes < idx_score_topk_fp4_workspace_size(batch, k) ||
+      !aligned(workspace, 256))
+    return IDX_ERR_WORKSPACE;
+  TopkWorkspace ws;
+  fused_workspace(batch, workspace, &ws);
+  const BatchArgs b = to_args(batch);
+  hipError_t e = launch_score_fp4(q_fp8, w, CacheArgs{cache.data, cache.num_blocks}, b,
+                                  batch->num_decode_tokens, ws.logits, ws.ld, ws.samp, stream);
+  if (e == hipSuccess) e = launch_topk(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
+  return launched(e);
+}
+
 idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
                             idx_kcache_t cache, const idx_batch_t* batch, int32_t k,
                             int32_t* topk, int64_t topk_stride, void* workspace,

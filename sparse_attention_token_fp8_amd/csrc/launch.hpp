@@ -35,6 +35,15 @@ hipError_t launch_score(const uint8_t* q8, const float* w, const CacheArgs& cach
                         const BatchArgs& b, int64_t dec_tokens, float* logits, int64_t ld,
                         float* samp, hipStream_t stream);
 
+// The FP4 cache (4352-byte blocks): quantise-and-scatter, and scores (decode
+// batches with the decode split, every other batch with the prefill split).
+hipError_t launch_quant_write_k_fp4(const uint16_t* k, int64_t num_rows, int64_t stride,
+                                    const int64_t* slots, uint8_t* cache, int64_t num_slots,
+                                    hipStream_t stream);
+hipError_t launch_score_fp4(const uint8_t* q8, const float* w, const CacheArgs& cache,
+                            const BatchArgs& b, int64_t dec_tokens, float* logits, int64_t ld,
+                            float* samp, hipStream_t stream);
+
 // Blocks per decode work-group for `tokens` rows of up to max_seq_len
 // positions (a multiple of 4, 8..64).
 int decode_chunk_blocks(int max_seq_len, int64_t tokens);

@@ -670,5 +670,97 @@ __device__ __forceinline__ void xcd_spread(int* chunk, int* row) {
 }
 
 
+// ----------------------------------------------------- prefill groups --
+// Prefill groups are numbered across the batch: request r holds
+// ceil(m_r / kPrefillTM) groups, m_r = its tokens at or above tok_lo (the
+// first of them starting its first group), so ceil(P / kPrefillTM) + num_reqs
+// groups cover any batch with P such tokens, and requests without prefill
+// tokens (the decodes of a mixed batch) take no work-groups.  Every wave finds
+// its group's request with a scan of the per-request group counts, 256
+// requests per round of loads.
+struct PrefillGroup {
+  int r;    // request
+  int q0;   // its first token (batch index), qsl[r]
+  int nq;   // its tokens, qsl[r+1] - qsl[r]
+  int len;  // its positions, seq_lens[r]
+  int t0;   // first token of the group (batch index)
+  int nt;   // tokens in the group, 1..kPrefillTM
+};
+
+__device__ __forceinline__ bool prefill_group(const BatchArgs& b, int G, int tok_lo, int gpr,
+                                              PrefillGroup* pg) {
+  constexpr int TM = kPrefillTM, U = 4;
+  if (gpr > 0) {                                // per-request numbering: gpr groups per request
+    const int r = G / gpr, g = G % gpr;
+    if (r >= b.num_reqs) return false;
+    pg->r = r;
+    pg->q0 = b.qsl[r];
+    pg->nq = b.qsl[r + 1] - pg->q0;
+    pg->len = b.seq_lens[r];
+    pg->t0 = pg->q0 + g * TM;
+    pg->nt = min(TM, pg->nq - g * TM);
+    return pg->nt > 0 && pg->t0 + pg->nt > tok_lo;
+  }
+  const int lane = threadIdx.x & 63;
+  int base = 0;                                 // groups of the requests already passed
+  for (int r0 = 0; r0 < b.num_reqs; r0 += 64 * U) {
+    int lo[U], hi[U], len[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {               // every load of the round first
+      const int r = r0 + 64 * u + lane;
+      lo[u] = r < b.num_reqs ? b.qsl[r] : 0;
+      hi[u] = r < b.num_reqs ? b.qsl[r + 1] : 0;
+      len[u] = r < b.num_reqs ? b.seq_lens[r] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int l = max(lo[u], tok_lo);
+      const int cnt = hi[u] > l ? (hi[u] - l + TM - 1) / TM : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const int total = __shfl(incl, 63, 64);
+      if (G < base + total) {
+        const uint64_t past = __ballot(G < base + incl);
+        const int L = __ffsll((unsigned long long)past) - 1;
+        const int excl = __builtin_amdgcn_readlane(incl - cnt, L);
+        const int lL = __builtin_amdgcn_readlane(l, L);
+        const int hL = __builtin_amdgcn_readlane(hi[u], L);
+        pg->r = r0 + 64 * u + L;
+        pg->q0 = __builtin_amdgcn_readlane(lo[u], L);
+        pg->nq = hL - pg->q0;
+        pg->len = __builtin_amdgcn_readlane(len[u], L);
+        pg->t0 = lL + (G - base - excl) * TM;
+        pg->nt = min(TM, hL - pg->t0);
+        return true;
+      }
+      base += total;
+    }
+  }
+  return false;
+}
+
+// Groups the prefill split launches for P tokens at or above tok_lo (at most
+// one partial group per request that holds such tokens).
+inline int64_t prefill_groups_bound(int64_t P, int num_reqs) {
+  return (P + kPrefillTM - 1) / kPrefillTM + std::min<int64_t>(num_reqs, P);
+}
+
+// Prefill chunk: halved from the maximum until the grid holds `target`
+// prefill work-groups, down to 4 blocks.  The target is 1024 (two per
+// work-group slot): smaller chunks add more per-work-group set-up than they
+// balance.  When a mixed launch's decode work-groups alone fill every slot,
+// the target is 2048, so that short prefill work-groups fill in around them.
+inline int prefill_chunk_blocks(const BatchArgs& b, int64_t groups, bool fill_around) {
+  const int64_t target = fill_around ? 2048 : 1024;
+  int cb = IDX_PREFILL_MAX_CHUNK;
+  while (cb > 4 && groups * ((b.max_seq_len + cb * kBlock - 1) / (cb * kBlock)) < target) cb >>= 1;
+  return cb;
+}
+
+
 }  // namespace
 }  // namespace idx

@@ -12,8 +12,8 @@ import oracle
 from oracle import quant as oquant, topk as otopk
 from synth import f32_to_bf16_bits, random_batch
 from tests.fp8_bruteforce import all_finite_bf16_bits
-from tests.gpu_helpers import (check_logits_row, check_topk_band, device_batch, device_layer,
-                               oracle_batch, oracle_layer, say)
+from tests.gpu_helpers import (adversarial_q_w, check_logits_row, check_topk_band, device_batch,
+                               device_layer, oracle_batch, oracle_layer, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -205,31 +205,6 @@ def test_decode_and_prefill_kernels_agree_bitwise(env):
     assert np.array_equal(a[0].cpu().numpy().view(np.uint32), b[2].cpu().numpy().view(np.uint32))
 
 
-def _adversarial_q_w(rng, T):
-    """q codes and folded weights chosen to stress the scores' linear half.
-
-    The scoring kernels split w*max(d, 0) into (w/2)|d| + (w/2)d and contract
-    the second half as u . k with u = sum_h (w_h/2) q_h held in four E4M3
-    pieces; these rows give u a wide dynamic range, saturated codes, exact
-    cancellation and weights over several decades.
-    """
-    H, D = 64, 128
-    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
-    q8 = rng.choice(finite, size=(T, H, D)).astype(np.uint8)
-    # four decades of weights, up to ~10x the folded weights of N(0,1) data (larger ones make
-    # the plain fp32 head sum itself miss the tolerance where the terms cancel)
-    w = (rng.choice([-1.0, 1.0], size=(T, H)) * 10.0 ** rng.uniform(-7, -3, size=(T, H))).astype(np.float32)
-    q8[0] = 0x7E                                  # every code +448: u is w-weighted sum of 448s
-    q8[1, :, :] = 0x01                            # smallest subnormal everywhere ...
-    q8[1, :, 0] = 0x7E                            # ... but one dimension at +448: u spans ~2^18
-    w[2, 1::2] = -w[2, 0::2]                      # pairs of heads with opposite weights ...
-    q8[2, 1::2] = q8[2, 0::2]                     # ... and equal q rows: every score is 0 (u = 0)
-    q8[3] = np.where(rng.random((H, D)) < 0.5, 0x80, q8[3])   # half the codes -0
-    w[4] = 0.0                                    # all weights zero
-    w[5] = np.float32(1e-30)                      # tiny weights (u far below the clamp range)
-    return q8, w
-
-
 def test_logits_linear_half_adversarial(env):
     """Scores from adversarial q / w stay within tolerance of the oracle, and the
     decode and prefill kernels give the same bits for them."""
@@ -240,7 +215,7 @@ def test_logits_linear_half_adversarial(env):
     orc = oracle_layer(wl, 0)
     assert np.array_equal(dev["cache"].tensor.cpu().numpy(), orc["cache"])
     rng = np.random.default_rng(2005)
-    q8, w = _adversarial_q_w(rng, T)
+    q8, w = adversarial_q_w(rng, T)
     batch = device_batch(m, wl)
     got = m.idx_logits(torch.from_numpy(q8).cuda(), torch.from_numpy(w).cuda(), dev["cache"], batch)
     got = got.cpu().numpy()
