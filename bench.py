@@ -14,6 +14,8 @@ positions, k = 2048).  The JSON line also carries every other workload:
   prefill-1k         T = S = 1024 causal, k = 256
   stack-16L-32x64k   16 layers, FSSS x4, 32 decode requests at 64K (a step is
                      the whole stack; all-F is timed beside it)
+  decode-8x128k-fp4  the headline batch over the FP4 indexer K cache (a step:
+                     idx_quant_write_k_fp4 of the new rows, idx_score_topk_fp4)
 
 each with its step time, throughput, the step's per-kernel times and the
 dominant kernel's roofline.  Per-kernel times come from a separate traced loop
@@ -23,6 +25,8 @@ per launch of the dominant kernel:
 
   decode scoring   sum_t (p_t + 1) * 132 B of K + per token 8192 B of q,
                    256 B of weights, 256 + 132 B of its new K row
+  FP4 decode       sum_t (p_t + 1) * 68 B of K + per token 8192 B of q and
+                   256 B of weights (the new rows are a separate launch)
   prefill scoring  2 * 64 * 128 * sum_t (p_t + 1) fp8 flops (causal pairs)
 
 Decode steps rotate through several copies of the K cache so the 256 MB
@@ -57,15 +61,20 @@ FP8_PEAK_TFLOPS = 5000.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = "sparse_attention_token_fp8_amd/csrc/"
 HEADLINE = "decode-8x128k"
-SINGLE_LAYER = ("decode-8x128k", "prefill-24k+8k", "decode-64x16k-32k", "prefill-1k")
+SINGLE_LAYER = ("decode-8x128k", "prefill-24k+8k", "decode-64x16k-32k", "prefill-1k",
+                "decode-8x128k-fp4")
+FP4_SUFFIX = "-fp4"
 STACK = "stack-16L-32x64k"
 # sources whose code the dominant kernels are built from (for the traffic digest)
 KERNEL_SOURCES = {
     "score_keep_kernel": ("fused.hip", "score_device.hpp", "topk_device.hpp", "common.hpp",
                           "quant_device.hpp"),
     "score_prefill_kernel": ("score.hip", "score_device.hpp", "common.hpp", "quant_device.hpp"),
+    "score_fp4_decode_kernel": ("fp4.hip", "score_device.hpp", "common.hpp", "quant_device.hpp"),
 }
-DECODE_KERNELS = ("score_keep_kernel", "score_decode_write_kernel", "score_decode_kernel")
+DECODE_KERNELS = ("score_keep_kernel", "score_decode_write_kernel", "score_decode_kernel",
+                  "score_fp4_decode_kernel")
+FP4_KERNELS = ("score_fp4_decode_kernel", "score_fp4_prefill_kernel")
 
 
 def log(*a):
@@ -162,39 +171,46 @@ def copy_calibration(torch, nbytes=1 << 30, launches=4):
 
 # ------------------------------------------------------------------ setup --
 
-def setup(m, torch, wl, replicas, layer=0):
-    """Device state: cache replicas with the context K, q_fp8 / w, new K rows."""
+def setup(m, torch, wl, replicas, layer=0, fp4=False):
+    """Device state: cache replicas with the context K (FP8, or FP4), q_fp8 / w,
+    new K rows."""
     import concurrent.futures as cf
     t0 = time.time()
     batch = m.Batch(wl.seq_lens, wl.query_start_loc, wl.block_table)
-    cache = m.KCache(wl.num_blocks, fill=0)
+    kind = m.KCacheFP4 if fp4 else m.KCache
+    write = m.idx_quant_write_k_fp4 if fp4 else m.idx_quant_write_k
+    cache = kind(wl.num_blocks, fill=0)
     reqs = [r for r in range(wl.num_reqs) if wl.seq_lens[r] > wl.new_tokens[r]]
     nw = max(1, min(16, len(os.sched_getaffinity(0))))
     with cf.ThreadPoolExecutor(nw) as ex:
         for kb, slots in ex.map(lambda r: wl.ctx_rows(layer, [r]), reqs):
-            m.idx_quant_write_k(torch.from_numpy(kb.view(np.int16)).cuda(),
-                                torch.from_numpy(slots).cuda(), cache)
+            write(torch.from_numpy(kb.view(np.int16)).cuda(), torch.from_numpy(slots).cuda(), cache)
     q8, w, _ = m.idx_quant_q_fold_w(torch.from_numpy(wl.q_bits(layer).view(np.int16)).cuda(),
                                     torch.from_numpy(wl.w_raw(layer)).cuda())
     nb, ns = wl.new_rows(layer)
     k_new = torch.from_numpy(nb.view(np.int16)).cuda()
     slots = torch.from_numpy(ns).cuda()
-    caches = [cache] + [m.KCache(wl.num_blocks, tensor=cache.tensor.clone()) for _ in range(replicas - 1)]
+    caches = [cache] + [kind(wl.num_blocks, tensor=cache.tensor.clone()) for _ in range(replicas - 1)]
     torch.cuda.synchronize()
     log(f"setup {wl.name}: {time.time() - t0:.1f}s, {replicas} cache copies of "
         f"{cache.tensor.numel() / 1e6:.1f} MB")
     return dict(batch=batch, caches=caches, q8=q8, w=w, k_new=k_new, slots=slots)
 
 
-def algorithmic(wl):
+def algorithmic(wl, fp4=False):
     """Per-step algorithmic work of one F layer (the measurement section's counts):
-    decode scoring bytes (K of every causal position, q, w, the new K row),
-    the step's bytes (plus the top-k indices written) and the MFMA flops of
-    the causal (token, position) pairs."""
+    decode scoring bytes (K of every causal position, q, w, the new K row; for
+    the FP4 cache 68 B per position and the new rows outside the scoring
+    launch), the step's bytes (plus the top-k indices written) and the MFMA
+    flops of the causal (token, position) pairs."""
     P = int(np.sum(wl.token_pos() + 1))
     T = wl.num_tokens
-    score_bytes = P * 132 + T * (64 * 128 + 64 * 4 + 256 + 132)
-    step_bytes = score_bytes + T * 4 * wl.k
+    if fp4:
+        score_bytes = P * 68 + T * (64 * 128 + 64 * 4)
+        step_bytes = score_bytes + T * (256 + 68) + T * 4 * wl.k
+    else:
+        score_bytes = P * 132 + T * (64 * 128 + 64 * 4 + 256 + 132)
+        step_bytes = score_bytes + T * 4 * wl.k
     flops = 2 * 64 * 128 * P
     return dict(positions=P, score_bytes=score_bytes, step_bytes=step_bytes, flops=flops)
 
@@ -256,7 +272,7 @@ def dominant(kernels):
 
 def roofline(wl, name, kernel, ms, launches):
     """Roofline entry of the dominant kernel from its measured time per launch."""
-    a = algorithmic(wl)
+    a = algorithmic(wl, fp4=kernel in FP4_KERNELS)
     if kernel in DECODE_KERNELS:
         ach = a["score_bytes"] / (ms * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -280,33 +296,42 @@ def dominant_ms(m, torch, kernel, d, wl, reps, ws, steps, warmup):
     if kernel == "score_keep_kernel":
         fn = lambda i: m.idx_score_candidates(d["q8"], d["w"], d["caches"][i % reps], B, k, ws,
                                               d["k_new"], d["slots"])
-    elif kernel == "score_prefill_kernel":
+    elif kernel in ("score_prefill_kernel",) + FP4_KERNELS:
         logits = torch.empty((wl.num_tokens, wl.max_seq_len), dtype=torch.float32, device="cuda")
-        fn = lambda i: m.idx_logits(d["q8"], d["w"], d["caches"][i % reps], B, logits=logits)
+        score = m.idx_logits if kernel == "score_prefill_kernel" else m.idx_logits_fp4
+        fn = lambda i: score(d["q8"], d["w"], d["caches"][i % reps], B, logits=logits)
     else:
         return None
     return time_loop(torch, fn, steps, warmup)
 
 
-def config_of(wl, reps):
-    return {"workload": wl.name, "requests": wl.num_reqs, "query_tokens": wl.num_tokens,
-            "max_context": wl.max_seq_len, "index_topk": wl.k, "heads": 64, "head_dim": 128,
-            "block_size": 64, "layers": wl.num_layers, "cache_copies": reps}
+def config_of(wl, reps, fp4=False):
+    return {"workload": wl.name + (FP4_SUFFIX if fp4 else ""), "requests": wl.num_reqs,
+            "query_tokens": wl.num_tokens, "max_context": wl.max_seq_len, "index_topk": wl.k,
+            "heads": 64, "head_dim": 128, "block_size": 64, "layers": wl.num_layers,
+            "cache_copies": reps, "k_cache": "fp4 e2m1 + e8m0 per 32" if fp4 else "fp8 e4m3 + fp32"}
 
 
 def run_workload(m, torch, name, args):
     from synth import CONFIGS, make_workload
-    wl = make_workload(CONFIGS[name])
+    fp4 = name.endswith(FP4_SUFFIX)
+    wl = make_workload(CONFIGS[name[:-len(FP4_SUFFIX)] if fp4 else name])
     decode = wl.max_query_len == 1
     reps = args.replicas if decode else 1
-    d = setup(m, torch, wl, reps)
+    d = setup(m, torch, wl, reps, fp4=fp4)
     B, k = d["batch"], wl.k
     topk = torch.empty((wl.num_tokens, k), dtype=torch.int32, device="cuda")
-    ws = torch.empty(max(256, m.idx_score_topk_workspace_size(B, k)), dtype=torch.uint8, device="cuda")
+    wsize = m.idx_score_topk_fp4_workspace_size(B, k) if fp4 else m.idx_score_topk_workspace_size(B, k)
+    ws = torch.empty(max(256, wsize), dtype=torch.uint8, device="cuda")
 
     def step(i):                                       # one F layer: new K rows, scores, top-k
-        m.idx_indexcache_layer(d["k_new"], d["caches"][i % reps], d["q8"], d["w"], True, True,
-                               d["slots"], B, k, topk, workspace=ws)
+        c = d["caches"][i % reps]
+        if fp4:
+            m.idx_quant_write_k_fp4(d["k_new"], d["slots"], c)
+            m.idx_score_topk_fp4(d["q8"], d["w"], c, B, k, topk, workspace=ws)
+        else:
+            m.idx_indexcache_layer(d["k_new"], c, d["q8"], d["w"], True, True, d["slots"], B, k,
+                                   topk, workspace=ws)
 
     ms_step = time_loop(torch, step, args.steps, args.warmup)
     quant = step_quantiles(m, torch, step, max(args.steps, 50), args.warmup)
@@ -314,19 +339,20 @@ def run_workload(m, torch, name, args):
     dom = dominant(kern)
     ms_dom = dominant_ms(m, torch, dom, d, wl, reps, ws, args.steps, args.warmup)
     roof = roofline(wl, name, dom, ms_dom if ms_dom is not None else kern[dom][0], kern[dom][1])
-    a = algorithmic(wl)
+    a = algorithmic(wl, fp4=fp4)
     res = dict(workload=name, value=round(wl.num_tokens / (ms_step * 1e-3), 1),
                ms_per_step=round(ms_step, 5), step_ms_quantiles=quant, roofline=roof,
                kernels_ms={n: round(v[0], 5) for n, v in kern.items()},
                step_hbm_frac=round(a["step_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                step_mfma_frac=round(a["flops"] / (ms_step * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-               config=config_of(wl, reps))
+               config=config_of(wl, reps, fp4))
     log(f"{name}: {ms_step * 1e3:.1f} us/step; " +
         ", ".join(f"{n} {v[0] * 1e3:.1f} us" for n, v in kern.items()) +
         f"; {roof['kernel']} alone {roof['ms_per_launch'] * 1e3:.1f} us, "
         f"{roof['frac'] * 100:.1f}% of {roof['bound']} peak")
     del d, topk, ws
     torch.cuda.empty_cache()
+    wl.fp4 = fp4
     return res, wl
 
 
@@ -523,7 +549,12 @@ def cpu_baseline(wl, sample, min_seconds=5.0):
     `min_seconds` of work has been timed.  Returns query-tokens/s of that work."""
     import concurrent.futures as cf
     import oracle
-    from oracle import logits as olog, quant as oquant, topk as otopk
+    from oracle import fp4cache, logits as olog, quant as oquant, topk as otopk
+    fp4 = getattr(wl, "fp4", False)
+    write = fp4cache.quant_write_k if fp4 else oquant.quant_write_k
+    score_row = fp4cache.logits_row if fp4 else olog.logits_row
+    new_cache = ((lambda: fp4cache.new_cache(wl.num_blocks)) if fp4 else
+                 (lambda: np.zeros((wl.num_blocks, 64, 132), np.uint8)))
     try:
         from threadpoolctl import threadpool_info
         blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
@@ -536,14 +567,14 @@ def cpu_baseline(wl, sample, min_seconds=5.0):
     nw = max(1, min(16, len(os.sched_getaffinity(0))))
     layers = []
     for layer, is_f in enumerate(full):                 # setup, not timed
-        cache = np.zeros((wl.num_blocks, 64, 132), np.uint8)
+        cache = new_cache()
         new = {}
 
         def ctx(r, layer=layer, cache=cache, is_f=is_f):
             kb = wl.request_k(layer, r)
             L, n = int(wl.seq_lens[r]), int(wl.new_tokens[r])
             if is_f:                                    # S layers score nothing: no context needed
-                oquant.quant_write_k(cache, kb[:L - n], wl.slots(r, np.arange(L - n)))
+                write(cache, kb[:L - n], wl.slots(r, np.arange(L - n)))
             return r, (kb[L - n:], wl.slots(r, np.arange(L - n, L)))
 
         with cf.ThreadPoolExecutor(nw) as ex:
@@ -558,11 +589,11 @@ def cpu_baseline(wl, sample, min_seconds=5.0):
     while passes == 0 or time.time() - t0 < min_seconds:
         for is_f, cache, new, q8, w in layers:
             for r in reqs:                              # this step's K rows of the sampled requests
-                oquant.quant_write_k(cache, *new[r])
+                write(cache, *new[r])
             if is_f:
                 for t in tokens:
                     r, p = ob.token_request(int(t)), ob.token_position(int(t))
-                    s = olog.logits_row(q8[t], w[t], cache, wl.block_table[r], p)
+                    s = score_row(q8[t], w[t], cache, wl.block_table[r], p)
                     otopk.topk_row(s, wl.k)
         passes += 1
     dt = time.time() - t0
@@ -570,7 +601,8 @@ def cpu_baseline(wl, sample, min_seconds=5.0):
             "cores": len(os.sched_getaffinity(0)), "blas_threads": blas, "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{passes} pass(es) over {len(tokens)} of the {wl.num_tokens} query tokens of "
-                      f"{wl.name} ({wl.num_layers} layer(s): their new K rows, fp64 scores over the "
+                      f"{wl.name}{FP4_SUFFIX if fp4 else ''} ({wl.num_layers} layer(s): their new K "
+                      f"rows{' (FP4 cache)' if fp4 else ''}, fp64 scores over the "
                       f"full causal range and a full-sort top-{wl.k} on F layers); {dt:.1f} s"}
 
 

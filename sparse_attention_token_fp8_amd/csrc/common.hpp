@@ -58,8 +58,9 @@ __host__ __device__ inline int sample_stride(int n) {
 __host__ __device__ inline int sample_pos(int j, int S) { return j * S + ((37 * j + 11) & (S - 1)); }
 
 // Top-k workspace (device, caller-owned).  The fused entry points keep the
-// scores in `logits` and, for long rows, each row's sampled scores in `samp`
-// (entry j = the score at sample_pos(j, S)), written by the scoring kernels.
+// scores in `logits` and, for every row long enough to be sampled, the row's
+// sampled scores in `samp` (entry j = the score at sample_pos(j, S)), written
+// by the scoring kernels.
 // Long rows keep their candidates in `nslots` slots of `slot_cap` entries per
 // row (`cand_key` / `cand_pos`, in position order across the slots; one slot
 // per chunk of topk_chunk() positions) with each slot's count in `counts`.
@@ -98,6 +99,7 @@ int topk_nchunks(int max_seq_len, bool sample_copy);
 int topk_max_seq_len();
 
 constexpr int kMaxSlots = 2048;                 // slots per row the resolve can index
+constexpr int kRowCap = 5120;                   // LDS candidates of the many-rows top-k; longer rows are sampled
 
 // Layout of the workspace for T rows of up to max_seq_len positions; returns
 // the total bytes.  When base is non-null also fills `ws`.  logits_ld is 0
@@ -105,7 +107,8 @@ constexpr int kMaxSlots = 2048;                 // slots per row the resolve can
 inline size_t topk_workspace_layout(int64_t T, int max_seq_len, int64_t logits_ld, void* base,
                                     TopkWorkspace* ws) {
   const bool lr = topk_uses_long_rows(T, max_seq_len);
-  const bool samp = lr && logits_ld > 0;
+  // the scoring kernels' compact sample copy, for every row a tau is sampled for
+  const bool samp = logits_ld > 0 && (lr || max_seq_len > kRowCap);
   const int64_t nslots = lr ? topk_nchunks(max_seq_len, samp) : 0;
   const int64_t cap = lr ? topk_chunk(samp) : 0;
   size_t off = 0;

@@ -21,7 +21,6 @@ namespace idx {
 namespace {
 
 constexpr int kRowThreads = 512;
-constexpr int kRowCap = 5120;        // LDS candidate capacity of the row kernel
 constexpr int kCandCap = 6144;       // LDS candidate capacity of the resolve
 constexpr int kBatch = 8;            // positions per thread per batch in the row kernel
 // Positions per filter work-group.  With the scoring kernel's compact sample
@@ -62,11 +61,15 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ row, int n,
 // One work-group per row.  Candidate positions are stored as Pos (16 bits
 // when every row fits in 65536 positions), which with 512 threads lets four
 // rows share a CU.
+// With `samp` (the scoring kernel's compact sample copy) the sample is one
+// contiguous read; without it the sampled positions are gathered from the row,
+// which touches every line of it once more before the pass over the row.
 template <typename Pos>
 __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __restrict__ logits,
                                                                 int64_t ld, BatchArgs b, int k,
                                                                 int32_t* __restrict__ topk,
-                                                                int64_t ldo) {
+                                                                int64_t ldo,
+                                                                const float* __restrict__ samp) {
   const int t = blockIdx.x;
   const int n = token_pos_wave(b, t).n;
   int32_t* out = topk + (size_t)t * ldo;
@@ -85,7 +88,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
   const bool sampled = n > kRowCap;             // else every position is a candidate
   float sv[sample_per<kRowThreads>()];
   int ns = 0;
-  if (sampled) ns = sample_load<kRowThreads>(row, n, sv);   // first: tau waits on these only
+  if (sampled)                                  // first: tau waits on these only
+    ns = samp ? sample_load_compact<kRowThreads>(samp + (size_t)t * kMaxSample, n, sv)
+              : sample_load<kRowThreads>(row, n, sv);
   // Two batches in flight: while one is compacted the next two are loading.
   // Loads past the row re-read its last position (the pass test drops them),
   // so no load sits behind a branch and the compiler waits only for the batch
@@ -346,10 +351,10 @@ hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, cons
   } else {
     if (b.max_seq_len <= 65536)
       IDX_LAUNCH("topk_rows_kernel", (topk_rows_kernel<uint16_t>), dim3((unsigned)b.num_tokens),
-                 dim3(kRowThreads), stream, logits, ld, b, k, out, ldo);
+                 dim3(kRowThreads), stream, logits, ld, b, k, out, ldo, ws.samp);
     else
       IDX_LAUNCH("topk_rows_kernel", (topk_rows_kernel<int32_t>), dim3((unsigned)b.num_tokens),
-                 dim3(kRowThreads), stream, logits, ld, b, k, out, ldo);
+                 dim3(kRowThreads), stream, logits, ld, b, k, out, ldo, ws.samp);
   }
   return hipGetLastError();
 }
