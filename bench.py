@@ -13,7 +13,9 @@ positions, k = 2048).  The JSON line also carries every other workload:
   decode-64x16k-32k  64 decode requests, contexts uniform in [16K, 32K]
   prefill-1k         T = S = 1024 causal, k = 256
   stack-16L-32x64k   16 layers, FSSS x4, 32 decode requests at 64K (a step is
-                     the whole stack; all-F is timed beside it)
+                     the whole stack; all-F, and FSSS with the index group's
+                     physical rows converted after each F layer, are timed
+                     beside it)
   decode-8x128k-fp4  the headline batch over the FP4 indexer K cache (a step:
                      idx_quant_write_k_fp4 of the new rows, idx_score_topk_fp4)
 
@@ -390,9 +392,17 @@ def run_stack(m, torch, args):
         return lambda i: m.idx_indexcache_stack(layers, full, True, slots, batch, wl.k, topk,
                                                 workspace=ws)
 
+    # the index group's physical rows (block size 64), converted once after each F layer
+    phys = m.Physical(wl.num_tokens, wl.k, wl.num_blocks)
+
+    def stack_physical(i):
+        m.idx_indexcache_stack_physical(layers, fsss, True, slots, batch, wl.k, topk, phys,
+                                        workspace=ws)
+
     steps = max(5, args.steps // 2)
     ms_fsss = time_loop(torch, stack(fsss), steps, 3)
     ms_all_f = time_loop(torch, stack([True] * wl.num_layers), steps, 3)
+    ms_phys = time_loop(torch, stack_physical, steps, 3)
     quant = step_quantiles(m, torch, stack(fsss), max(steps, 20), 3)
     kern = kernel_times(m, torch, stack(fsss), 5, 1)
     kern = {n: (ms, cnt // 5) for n, (ms, cnt) in kern.items()}   # launches per stack
@@ -409,10 +419,28 @@ def run_stack(m, torch, args):
            "kernels_ms": {n: round(v[0], 5) for n, v in kern.items()},
            "kernel_launches_per_step": {n: v[1] for n, v in kern.items()},
            "f_layers": [i for i, f in enumerate(fsss) if f], "ms_all_f": round(ms_all_f, 5),
+           "ms_fsss_with_physical_rows": round(ms_phys, 5),
            "all_f_over_fsss": round(ms_all_f / ms_fsss, 3), "config": config_of(wl, 1)}
-    del layers, cache, topk, ws
+    del layers, cache, topk, ws, phys
     torch.cuda.empty_cache()
     return res, wl
+
+
+def _layers(m, torch, wl):
+    """Per-layer device state for a multi-layer workload (context K, q_fp8 / w, new K rows)."""
+    layers = []
+    reqs = [r for r in range(wl.num_reqs) if wl.seq_lens[r] > wl.new_tokens[r]]
+    for l in range(wl.num_layers):
+        cache = m.KCache(wl.num_blocks, fill=0)
+        for r in reqs:
+            kb, slots = wl.ctx_rows(l, [r])
+            m.idx_quant_write_k(torch.from_numpy(kb.view(np.int16)).cuda(),
+                                torch.from_numpy(slots).cuda(), cache)
+        q8, w, _ = m.idx_quant_q_fold_w(torch.from_numpy(wl.q_bits(l).view(np.int16)).cuda(),
+                                        torch.from_numpy(wl.w_raw(l)).cuda())
+        nb, ns = wl.new_rows(l)
+        layers.append((torch.from_numpy(nb.view(np.int16)).cuda(), cache, q8, w))
+    return layers, torch.from_numpy(ns).cuda()
 
 
 def run_next_rows(m, torch, steps=20, warmup=3):

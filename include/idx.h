@@ -149,9 +149,12 @@ idx_status_t idx_quant_q_fold_w(const uint16_t* q_bf16, const float* w_raw, int6
  * Sums are fp32 (fp8 x fp8 products accumulated by the matrix cores).  The
  * kernels evaluate w * max(d, 0) as (w/2) |d| + (w/2) d, the second half
  * through sum_h (w_h/2) q8[t,h,:] held in four fp8 pieces (about 16
- * significant bits); the rounding stays below 1e-5 of the sum of the terms'
- * magnitudes.  A token's scores are the same bits whichever kernel, batch
- * composition or entry point computes them.
+ * significant bits; with exact dot products this split rounds to about 1e-7
+ * of sum_h |w_h| |d_h| ks).  The dot products come from gfx950's fp8 matrix
+ * cores, whose 128-product accumulation is not exact: up to about 2e-4 of
+ * sum_d |q_hd k_d| per product, which puts the scores within about 2e-5 of
+ * sum_h |w_h| |d_h| ks on N(0,1) data.  A token's scores are the same bits
+ * whichever kernel, batch composition or entry point computes them.
  */
 idx_status_t idx_logits(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
                         idx_kcache_t cache, const idx_batch_t* batch,
