@@ -17,7 +17,7 @@ positions, k = 2048).  The JSON line also carries every other workload:
                      physical rows converted after each F layer, are timed
                      beside it)
   decode-8x128k-fp4  the headline batch over the FP4 indexer K cache (a step:
-                     idx_quant_write_k_fp4 of the new rows, idx_score_topk_fp4)
+                     idx_indexcache_layer_fp4, the same F layer)
 
 each with its step time, throughput, the step's per-kernel times and the
 dominant kernel's roofline.  Per-kernel times come from a separate traced loop
@@ -27,8 +27,8 @@ per launch of the dominant kernel:
 
   decode scoring   sum_t (p_t + 1) * 132 B of K + per token 8192 B of q,
                    256 B of weights, 256 + 132 B of its new K row
-  FP4 decode       sum_t (p_t + 1) * 68 B of K + per token 8192 B of q and
-                   256 B of weights (the new rows are a separate launch)
+  FP4 decode       sum_t (p_t + 1) * 68 B of K + per token 8192 B of q,
+                   256 B of weights, 256 + 68 B of its new K row
   prefill scoring  2 * 64 * 128 * sum_t (p_t + 1) fp8 flops (causal pairs)
 
 Decode steps rotate through several copies of the K cache so the 256 MB
@@ -72,11 +72,14 @@ KERNEL_SOURCES = {
     "score_keep_kernel": ("fused.hip", "score_device.hpp", "topk_device.hpp", "common.hpp",
                           "quant_device.hpp"),
     "score_prefill_kernel": ("score.hip", "score_device.hpp", "common.hpp", "quant_device.hpp"),
-    "score_fp4_decode_kernel": ("fp4.hip", "score_device.hpp", "common.hpp", "quant_device.hpp"),
+    "score_fp4_decode_kernel": ("fp4.hip", "fp4_device.hpp", "score_device.hpp", "common.hpp",
+                                "quant_device.hpp"),
+    "score_keep_fp4_kernel": ("fused.hip", "fp4_device.hpp", "score_device.hpp", "topk_device.hpp",
+                              "common.hpp", "quant_device.hpp"),
 }
 DECODE_KERNELS = ("score_keep_kernel", "score_decode_write_kernel", "score_decode_kernel",
-                  "score_fp4_decode_kernel")
-FP4_KERNELS = ("score_fp4_decode_kernel", "score_fp4_prefill_kernel")
+                  "score_fp4_decode_kernel", "score_keep_fp4_kernel")
+FP4_KERNELS = ("score_fp4_decode_kernel", "score_fp4_prefill_kernel", "score_keep_fp4_kernel")
 
 
 def log(*a):
@@ -208,8 +211,8 @@ def algorithmic(wl, fp4=False):
     P = int(np.sum(wl.token_pos() + 1))
     T = wl.num_tokens
     if fp4:
-        score_bytes = P * 68 + T * (64 * 128 + 64 * 4)
-        step_bytes = score_bytes + T * (256 + 68) + T * 4 * wl.k
+        score_bytes = P * 68 + T * (64 * 128 + 64 * 4 + 256 + 68)
+        step_bytes = score_bytes + T * 4 * wl.k
     else:
         score_bytes = P * 132 + T * (64 * 128 + 64 * 4 + 256 + 132)
         step_bytes = score_bytes + T * 4 * wl.k
@@ -295,9 +298,9 @@ def dominant_ms(m, torch, kernel, d, wl, reps, ws, steps, warmup):
     prefill scoring (idx_logits).  Events bracket the whole loop, so the
     per-launch time carries one launch gap and no event overhead."""
     B, k = d["batch"], wl.k
-    if kernel == "score_keep_kernel":
-        fn = lambda i: m.idx_score_candidates(d["q8"], d["w"], d["caches"][i % reps], B, k, ws,
-                                              d["k_new"], d["slots"])
+    if kernel in ("score_keep_kernel", "score_keep_fp4_kernel"):
+        cand = m.idx_score_candidates if kernel == "score_keep_kernel" else m.idx_score_candidates_fp4
+        fn = lambda i: cand(d["q8"], d["w"], d["caches"][i % reps], B, k, ws, d["k_new"], d["slots"])
     elif kernel in ("score_prefill_kernel",) + FP4_KERNELS:
         logits = torch.empty((wl.num_tokens, wl.max_seq_len), dtype=torch.float32, device="cuda")
         score = m.idx_logits if kernel == "score_prefill_kernel" else m.idx_logits_fp4
@@ -329,8 +332,8 @@ def run_workload(m, torch, name, args):
     def step(i):                                       # one F layer: new K rows, scores, top-k
         c = d["caches"][i % reps]
         if fp4:
-            m.idx_quant_write_k_fp4(d["k_new"], d["slots"], c)
-            m.idx_score_topk_fp4(d["q8"], d["w"], c, B, k, topk, workspace=ws)
+            m.idx_indexcache_layer_fp4(d["k_new"], c, d["q8"], d["w"], True, True, d["slots"], B, k,
+                                       topk, workspace=ws)
         else:
             m.idx_indexcache_layer(d["k_new"], c, d["q8"], d["w"], True, True, d["slots"], B, k,
                                    topk, workspace=ws)

@@ -218,6 +218,17 @@ idx_status_t idx_select_candidates(const uint8_t* q_fp8, const float* w, int32_t
                                    int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
                                    int32_t k, int32_t* topk, int64_t topk_stride, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
+/* The same two launches over an FP4 cache (the fused path of idx_score_topk_fp4). */
+idx_status_t idx_score_candidates_fp4(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                      int32_t head_dim, idx_kcache_t cache,
+                                      const idx_batch_t* batch, int32_t k, const uint16_t* k_bf16,
+                                      int64_t k_row_stride, const int64_t* slot_mapping,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+idx_status_t idx_select_candidates_fp4(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                       int32_t head_dim, idx_kcache_t cache,
+                                       const idx_batch_t* batch, int32_t k, int32_t* topk,
+                                       int64_t topk_stride, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The FP4 indexer K cache ([blog] SparseAttnIndexer.forward_cuda passes
@@ -241,9 +252,11 @@ idx_status_t idx_select_candidates(const uint8_t* q_fp8, const float* w, int32_t
  *   I[t, s] = sum_h w[t, h] * max(0, sum_d q8[t, h, d] * c[s, d] * 2^e[s, d/32]),
  * same arguments, causal rows and ReLU split (no separate per-position scale).
  *
- * idx_score_topk_fp4: idx_logits_fp4 then idx_topk's selection, the scores
- * kept in the workspace (>= idx_score_topk_fp4_workspace_size bytes,
- * 256-byte aligned) between the two.
+ * idx_score_topk_fp4: idx_logits_fp4 then idx_topk's selection, with the
+ * same rows as those two on the same inputs; decode batches over long rows
+ * take the fused path of idx_score_topk (scores kept on chip, per-chunk
+ * candidates, one exact select per row), the others keep the scores in the
+ * workspace (>= idx_score_topk_fp4_workspace_size bytes, 256-byte aligned).
  */
 idx_status_t idx_quant_write_k_fp4(const uint16_t* k_bf16, int64_t num_tokens, int32_t head_dim,
                                    int64_t k_row_stride, const int64_t* slot_mapping,
@@ -322,6 +335,20 @@ idx_status_t idx_indexcache_layer(const idx_layer_io_t* layer, int32_t is_full, 
                                   const int64_t* slot_mapping, const idx_batch_t* batch, int32_t k,
                                   int32_t* topk, int64_t topk_stride,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * idx_indexcache_layer over an FP4 cache (layer->cache in the FP4 layout
+ * described with idx_quant_write_k_fp4): an F layer quantises this step's K
+ * rows into it (inside the fused scoring kernel when every request has at
+ * most 4 new tokens) and runs idx_score_topk_fp4 (workspace:
+ * idx_score_topk_fp4_workspace_size); an S layer writes the K rows (write_k)
+ * and nothing else.
+ */
+idx_status_t idx_indexcache_layer_fp4(const idx_layer_io_t* layer, int32_t is_full,
+                                      int32_t write_k, const int64_t* slot_mapping,
+                                      const idx_batch_t* batch, int32_t k, int32_t* topk,
+                                      int64_t topk_stride, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /*
  * A whole stack: idx_indexcache_layer for l = 0..num_layers-1 in order, with

@@ -79,6 +79,12 @@ SIGNATURES = {
     "idx_score_topk_fp4_workspace_size": (_sz, [_PBatch, _i32]),
     "idx_score_topk_fp4": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _i32, _vp, _i64,
                                           _vp, _sz, _vp]),
+    "idx_score_candidates_fp4": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _i32, _vp,
+                                                _i64, _vp, _vp, _sz, _vp]),
+    "idx_select_candidates_fp4": (ctypes.c_int, [_vp, _vp, _i32, _i32, KCacheC, _PBatch, _i32, _vp,
+                                                 _i64, _vp, _sz, _vp]),
+    "idx_indexcache_layer_fp4": (ctypes.c_int, [ctypes.POINTER(LayerIOC), _i32, _i32, _vp, _PBatch,
+                                                _i32, _vp, _i64, _vp, _sz, _vp]),
     "idx_layer_schedule": (ctypes.c_int, [_i32, ctypes.c_char_p, _i32, _i32, _i32, _vp]),
     "idx_trace_begin": (ctypes.c_int, [_vp, _i32]),
     "idx_trace_end": (_i32, [_vp, _i32]),
@@ -311,27 +317,47 @@ def idx_score_topk_fp4(q_fp8, w, cache, batch, k, topk=None, workspace=None, str
     return topk
 
 
-def idx_score_candidates(q_fp8, w, cache, batch, k, workspace, k_new=None, slot_mapping=None,
-                         stream=None):
-    """First launch of the fused path: scores kept on chip, per-chunk candidates into
-    `workspace`; with k_new / slot_mapping also this step's new K rows."""
+def _score_candidates(name, q_fp8, w, cache, batch, k, workspace, k_new, slot_mapping, stream):
     kn = None if k_new is None else as_bf16_bits(k_new)
-    _check("idx_score_candidates",
-           _lib.idx_score_candidates(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(),
+    _check(name, getattr(_lib, name)(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(),
                                      k, _ptr(kn), int(kn.stride(0)) if kn is not None else 0,
                                      _ptr(slot_mapping), _ptr(workspace), workspace.numel(),
                                      _stream(stream)))
 
 
-def idx_select_candidates(q_fp8, w, cache, batch, k, workspace, topk=None, stream=None):
-    """Second launch of the fused path: each row's top k from the candidates."""
+def _select_candidates(name, q_fp8, w, cache, batch, k, workspace, topk, stream):
     if topk is None:
         topk = torch.empty((batch.num_tokens, k), dtype=torch.int32, device=q_fp8.device)
-    _check("idx_select_candidates",
-           _lib.idx_select_candidates(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(),
-                                      k, _ptr(topk), int(topk.stride(0)), _ptr(workspace),
-                                      workspace.numel(), _stream(stream)))
+    _check(name, getattr(_lib, name)(_ptr(q_fp8), _ptr(w), N_HEADS, HEAD_DIM, cache.c(), batch.c(),
+                                     k, _ptr(topk), int(topk.stride(0)), _ptr(workspace),
+                                     workspace.numel(), _stream(stream)))
     return topk
+
+
+def idx_score_candidates(q_fp8, w, cache, batch, k, workspace, k_new=None, slot_mapping=None,
+                         stream=None):
+    """First launch of the fused path: scores kept on chip, per-chunk candidates into
+    `workspace`; with k_new / slot_mapping also this step's new K rows."""
+    _score_candidates("idx_score_candidates", q_fp8, w, cache, batch, k, workspace, k_new,
+                      slot_mapping, stream)
+
+
+def idx_select_candidates(q_fp8, w, cache, batch, k, workspace, topk=None, stream=None):
+    """Second launch of the fused path: each row's top k from the candidates."""
+    return _select_candidates("idx_select_candidates", q_fp8, w, cache, batch, k, workspace, topk,
+                              stream)
+
+
+def idx_score_candidates_fp4(q_fp8, w, cache, batch, k, workspace, k_new=None, slot_mapping=None,
+                             stream=None):
+    """idx_score_candidates over an FP4 cache (a KCacheFP4)."""
+    _score_candidates("idx_score_candidates_fp4", q_fp8, w, cache, batch, k, workspace, k_new,
+                      slot_mapping, stream)
+
+
+def idx_select_candidates_fp4(q_fp8, w, cache, batch, k, workspace, topk=None, stream=None):
+    return _select_candidates("idx_select_candidates_fp4", q_fp8, w, cache, batch, k, workspace,
+                              topk, stream)
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -369,6 +395,17 @@ def idx_indexcache_layer(k_new, cache, q_fp8, w, is_full, write_k, slot_mapping,
            _lib.idx_indexcache_layer(ctypes.byref(io), int(is_full), int(write_k), _ptr(slot_mapping),
                                      batch.c(), k, _ptr(topk), int(topk.stride(0)), _ptr(ws),
                                      ws.numel(), _stream(stream)))
+
+
+def idx_indexcache_layer_fp4(k_new, cache, q_fp8, w, is_full, write_k, slot_mapping, batch, k,
+                             topk, workspace=None, stream=None):
+    """idx_indexcache_layer over an FP4 cache (a KCacheFP4)."""
+    io = _layer_io(k_new, cache, q_fp8, w)
+    ws = _workspace(idx_score_topk_fp4_workspace_size(batch, k), topk.device, workspace)
+    _check("idx_indexcache_layer_fp4",
+           _lib.idx_indexcache_layer_fp4(ctypes.byref(io), int(is_full), int(write_k),
+                                         _ptr(slot_mapping), batch.c(), k, _ptr(topk),
+                                         int(topk.stride(0)), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def idx_indexcache_stack(layers, is_full, write_k_on_s, slot_mapping, batch, k, topk,

@@ -105,18 +105,21 @@ idx_status_t check_k_rows(const uint16_t* k_bf16, int64_t k_row_stride, const in
 hipError_t keep_candidates(const uint8_t* q_fp8, const float* w, const idx_kcache_t& cache,
                            const idx_batch_t* batch, int32_t k, void* workspace,
                            const uint16_t* kq, int64_t kq_stride, const int64_t* slots,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool fp4 = false) {
   const BatchArgs b = to_args(batch);
   KeepSlots ks;
   keep_workspace_layout(b, workspace, &ks);
   const bool fk = kq != nullptr && score_writes_k(b, batch->num_decode_tokens);
   if (kq != nullptr && !fk) {
-    const hipError_t e = launch_quant_write_k(kq, batch->num_tokens, kq_stride, slots, cache.data,
-                                              cache.num_blocks * kBlock, stream);
+    const int64_t ns = cache.num_blocks * kBlock;
+    const hipError_t e =
+        fp4 ? launch_quant_write_k_fp4(kq, batch->num_tokens, kq_stride, slots, cache.data, ns, stream)
+            : launch_quant_write_k(kq, batch->num_tokens, kq_stride, slots, cache.data, ns, stream);
     if (e != hipSuccess) return e;
   }
   return launch_keep_candidates(q_fp8, w, CacheArgs{cache.data, cache.num_blocks}, b,
-                                fk ? kq : nullptr, kq_stride, slots, cache.data, k, ks, stream);
+                                fk ? kq : nullptr, kq_stride, slots, cache.data, k, ks, stream,
+                                fp4);
 }
 
 // Scores + top-k of one batch into `topk`; with kq set, this step's new K rows
@@ -368,8 +371,48 @@ idx_status_t idx_logits_fp4(const uint8_t* q_fp8, const float* w, int32_t n_head
 size_t idx_score_topk_fp4_workspace_size(const idx_batch_t* batch, int32_t k) {
   if (batch == nullptr || batch->num_tokens <= 0 || k < 1) return 0;
   if (check_batch(batch) != IDX_OK) return 0;
+  if (keep_path(to_args(batch), batch->num_decode_tokens))
+    return keep_workspace_layout(to_args(batch), nullptr, nullptr);
   return fused_workspace(batch, nullptr, nullptr);
 }
+
+}  // extern "C"
+
+namespace {
+
+// idx_score_topk_fp4's work (arguments already checked): decode batches over
+// long rows take the fused path with the FP4 scoring kernel (the new K rows,
+// with kq, written inside it when the batch allows), the others the FP4 scores
+// into the workspace and the unfused top-k.
+hipError_t score_topk_fp4(const uint8_t* q_fp8, const float* w, const idx_kcache_t& cache,
+                          const idx_batch_t* batch, int32_t k, int32_t* topk, int64_t topk_stride,
+                          void* workspace, const uint16_t* kq, int64_t kq_stride,
+                          const int64_t* slots, hipStream_t stream) {
+  const BatchArgs b = to_args(batch);
+  const CacheArgs c{cache.data, cache.num_blocks};
+  if (keep_path(b, batch->num_decode_tokens)) {
+    hipError_t e = keep_candidates(q_fp8, w, cache, batch, k, workspace, kq, kq_stride, slots,
+                                   stream, true);
+    if (e != hipSuccess) return e;
+    KeepSlots ks;
+    keep_workspace_layout(b, workspace, &ks);
+    return launch_keep_select(q_fp8, w, c, b, k, ks, topk, topk_stride, stream, true);
+  }
+  hipError_t e = hipSuccess;
+  if (kq != nullptr)
+    e = launch_quant_write_k_fp4(kq, batch->num_tokens, kq_stride, slots, cache.data,
+                                 cache.num_blocks * kBlock, stream);
+  if (e != hipSuccess) return e;
+  TopkWorkspace ws;
+  fused_workspace(batch, workspace, &ws);
+  e = launch_score_fp4(q_fp8, w, c, b, batch->num_decode_tokens, ws.logits, ws.ld, ws.samp, stream);
+  if (e == hipSuccess) e = launch_topk(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
 
 idx_status_t idx_score_topk_fp4(const uint8_t* q_fp8, const float* w, int32_t n_heads,
                                 int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
@@ -383,13 +426,37 @@ idx_status_t idx_score_topk_fp4(const uint8_t* q_fp8, const float* w, int32_t n_
   if (workspace == nullptr || workspace_bytes < idx_score_topk_fp4_workspace_size(batch, k) ||
       !aligned(workspace, 256))
     return IDX_ERR_WORKSPACE;
-  TopkWorkspace ws;
-  fused_workspace(batch, workspace, &ws);
-  const BatchArgs b = to_args(batch);
-  hipError_t e = launch_score_fp4(q_fp8, w, CacheArgs{cache.data, cache.num_blocks}, b,
-                                  batch->num_decode_tokens, ws.logits, ws.ld, ws.samp, stream);
-  if (e == hipSuccess) e = launch_topk(ws.logits, ws.ld, b, ws, k, topk, topk_stride, stream);
-  return launched(e);
+  return launched(score_topk_fp4(q_fp8, w, cache, batch, k, topk, topk_stride, workspace, nullptr,
+                                 0, nullptr, stream));
+}
+
+idx_status_t idx_indexcache_layer_fp4(const idx_layer_io_t* layer, int32_t is_full,
+                                      int32_t write_k, const int64_t* slot_mapping,
+                                      const idx_batch_t* batch, int32_t k, int32_t* topk,
+                                      int64_t topk_stride, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  if (layer == nullptr) return IDX_ERR_INVALID_ARG;
+  idx_status_t s = check_batch(batch);
+  if (s != IDX_OK) return s;
+  if (!is_full) {
+    if (!write_k) return IDX_OK;
+    return idx_quant_write_k_fp4(layer->k_bf16, batch->num_tokens, kHeadDim, layer->k_row_stride,
+                                 slot_mapping, layer->cache, stream);
+  }
+  s = check_scoring(layer->q_fp8, layer->w, kHeads, kHeadDim, layer->cache, batch);
+  if (s != IDX_OK) return s;
+  s = check_k(k, topk_stride, topk, batch->num_tokens);
+  if (s != IDX_OK) return s;
+  s = check_k_rows(layer->k_bf16, layer->k_row_stride, slot_mapping, layer->cache,
+                   batch->num_tokens);
+  if (s != IDX_OK) return s;
+  if (batch->num_tokens == 0) return IDX_OK;
+  if (workspace == nullptr || workspace_bytes < idx_score_topk_fp4_workspace_size(batch, k) ||
+      !aligned(workspace, 256))
+    return IDX_ERR_WORKSPACE;
+  return launched(score_topk_fp4(layer->q_fp8, layer->w, layer->cache, batch, k, topk, topk_stride,
+                                 workspace, layer->k_bf16, layer->k_row_stride, slot_mapping,
+                                 stream));
 }
 
 idx_status_t idx_score_topk(const uint8_t* q_fp8, const float* w, int32_t n_heads, int32_t head_dim,
@@ -425,11 +492,15 @@ idx_status_t idx_score_topk_noalloc(const uint8_t* q_fp8, const float* w, int32_
                              nullptr, stream));
 }
 
-idx_status_t idx_score_candidates(const uint8_t* q_fp8, const float* w, int32_t n_heads,
-                                  int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
-                                  int32_t k, const uint16_t* k_bf16, int64_t k_row_stride,
-                                  const int64_t* slot_mapping, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+idx_status_t score_candidates(bool fp4, const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                              int32_t head_dim, const idx_kcache_t& cache, const idx_batch_t* batch,
+                              int32_t k, const uint16_t* k_bf16, int64_t k_row_stride,
+                              const int64_t* slot_mapping, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
   idx_status_t s = check_scoring(q_fp8, w, n_heads, head_dim, cache, batch);
   if (s != IDX_OK) return s;
   if (k < 1 || k > kMaxK) return IDX_ERR_UNSUPPORTED;
@@ -439,30 +510,70 @@ idx_status_t idx_score_candidates(const uint8_t* q_fp8, const float* w, int32_t 
     s = check_k_rows(k_bf16, k_row_stride, slot_mapping, cache, batch->num_tokens);
     if (s != IDX_OK) return s;
   }
-  if (workspace == nullptr || workspace_bytes < idx_score_topk_workspace_size(batch, k) ||
+  if (workspace == nullptr || workspace_bytes < keep_workspace_layout(to_args(batch), nullptr, nullptr) ||
       !aligned(workspace, 256))
     return IDX_ERR_WORKSPACE;
   return launched(keep_candidates(q_fp8, w, cache, batch, k, workspace, k_bf16, k_row_stride,
-                                  slot_mapping, stream));
+                                  slot_mapping, stream, fp4));
 }
 
-idx_status_t idx_select_candidates(const uint8_t* q_fp8, const float* w, int32_t n_heads,
-                                   int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
-                                   int32_t k, int32_t* topk, int64_t topk_stride, void* workspace,
-                                   size_t workspace_bytes, hipStream_t stream) {
+idx_status_t select_candidates(bool fp4, const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                               int32_t head_dim, const idx_kcache_t& cache,
+                               const idx_batch_t* batch, int32_t k, int32_t* topk,
+                               int64_t topk_stride, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   idx_status_t s = check_scoring(q_fp8, w, n_heads, head_dim, cache, batch);
   if (s != IDX_OK) return s;
   s = check_k(k, topk_stride, topk, batch->num_tokens);
   if (s != IDX_OK) return s;
   if (batch->num_tokens == 0) return IDX_OK;
   if (!keep_path(to_args(batch), batch->num_decode_tokens)) return IDX_ERR_UNSUPPORTED;
-  if (workspace == nullptr || workspace_bytes < idx_score_topk_workspace_size(batch, k) ||
+  if (workspace == nullptr || workspace_bytes < keep_workspace_layout(to_args(batch), nullptr, nullptr) ||
       !aligned(workspace, 256))
     return IDX_ERR_WORKSPACE;
   KeepSlots ks;
   keep_workspace_layout(to_args(batch), workspace, &ks);
   return launched(launch_keep_select(q_fp8, w, CacheArgs{cache.data, cache.num_blocks},
-                                     to_args(batch), k, ks, topk, topk_stride, stream));
+                                     to_args(batch), k, ks, topk, topk_stride, stream, fp4));
+}
+
+}  // namespace
+
+extern "C" {
+
+idx_status_t idx_score_candidates(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                  int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
+                                  int32_t k, const uint16_t* k_bf16, int64_t k_row_stride,
+                                  const int64_t* slot_mapping, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return score_candidates(false, q_fp8, w, n_heads, head_dim, cache, batch, k, k_bf16,
+                          k_row_stride, slot_mapping, workspace, workspace_bytes, stream);
+}
+
+idx_status_t idx_select_candidates(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                   int32_t head_dim, idx_kcache_t cache, const idx_batch_t* batch,
+                                   int32_t k, int32_t* topk, int64_t topk_stride, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  return select_candidates(false, q_fp8, w, n_heads, head_dim, cache, batch, k, topk, topk_stride,
+                           workspace, workspace_bytes, stream);
+}
+
+idx_status_t idx_score_candidates_fp4(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                      int32_t head_dim, idx_kcache_t cache,
+                                      const idx_batch_t* batch, int32_t k, const uint16_t* k_bf16,
+                                      int64_t k_row_stride, const int64_t* slot_mapping,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return score_candidates(true, q_fp8, w, n_heads, head_dim, cache, batch, k, k_bf16,
+                          k_row_stride, slot_mapping, workspace, workspace_bytes, stream);
+}
+
+idx_status_t idx_select_candidates_fp4(const uint8_t* q_fp8, const float* w, int32_t n_heads,
+                                       int32_t head_dim, idx_kcache_t cache,
+                                       const idx_batch_t* batch, int32_t k, int32_t* topk,
+                                       int64_t topk_stride, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  return select_candidates(true, q_fp8, w, n_heads, head_dim, cache, batch, k, topk, topk_stride,
+                           workspace, workspace_bytes, stream);
 }
 
 idx_status_t idx_indexcache_layer(const idx_layer_io_t* layer, int32_t is_full, int32_t write_k,

@@ -28,37 +28,14 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "score_device.hpp"
+#include "fp4_device.hpp"
+
+#ifndef IDX_FP4_DECODE_RING
+#define IDX_FP4_DECODE_RING 4
+#endif
 
 namespace idx {
 namespace {
-
-constexpr int kFp4CodeBytes = kBlock * kHeadDim / 2;          // 4096
-constexpr int kFp4BlockBytes = kFp4CodeBytes + kBlock * 4;     // 4352
-constexpr int kFp4Plane = kBlock * 16;                          // one group's codes: 1024
-
-// ---------------------------------------------------------- quantiser --
-
-// Group exponent: the smallest e with max(amax, 1e-4) <= 6 * 2^e.  `amag` is
-// the bf16 magnitude pattern of the group's amax: amax = (1 + m/128) 2^(E-127)
-// and 6 = 1.5 * 2^2.
-__device__ __forceinline__ int fp4_exponent(uint32_t amag) {
-  const float a = __uint_as_float(amag << 16);
-  if (!(a >= 1e-4f)) return -15;                 // the floor: 1e-4 <= 6 * 2^-15
-  const int E = (int)(amag >> 7);
-  const int m = (int)(amag & 0x7F);
-  return (E - 127) - 2 + (m > 64 ? 1 : 0);
-}
-
-// E2M1 code of bf16 value x times s = 2^-e (exact in fp32; |x s| <= 6): the
-// number of rounding boundaries at or below |x s|, each boundary open or
-// closed so that a tie goes to the even code, plus the sign bit.
-__device__ __forceinline__ uint32_t encode_e2m1(uint32_t x, float s) {
-  const float y = fabsf(__uint_as_float(x << 16) * s);
-  const uint32_t c = (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
-                     (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
-                     (uint32_t)(y > 5.f);
-  return c | ((x >> 12) & 8u);
-}
 
 // 32 lanes per row, lane q owns dims 4q..4q+3 (group q/8).
 constexpr int kFp4QuantRows = 8;                 // rows per 256-thread work-group
@@ -87,129 +64,6 @@ __global__ __launch_bounds__(256) void quant_write_k_fp4_kernel(const uint16_t* 
   uint8_t* base = cache + blk * kFp4BlockBytes;
   *reinterpret_cast<uint16_t*>(base + g * kFp4Plane + p * 16 + 2 * (q & 7)) = (uint16_t)codes;
   if ((q & 7) == 0) base[kFp4CodeBytes + g * 64 + (p & 15) * 4 + (p >> 4)] = (uint8_t)(e + 127);
-}
-
-// ------------------------------------------------------------ scoring --
-
-// One block's B operands for this lane: tile tl's 16 code bytes (position
-// 16 tl + lane%16, group lane/16) and the dword of that position's group
-// scales for the four tiles (byte tl).
-struct KBlock4 {
-  uint4 b[4];
-  uint32_t sc;
-};
-
-// A buffer resource of `bytes` = 0 (absent block, or past the run) loads
-// zeros: codes 0 score 0.
-template <int AUX>
-__device__ __forceinline__ void fp4_block_load(KBlock4& kb, const uint8_t* base, int bytes, int lane) {
-  const __amdgpu_buffer_rsrc_t rs = byte_rsrc(base, bytes);
-  const int c = lane & 15, G = lane >> 4;
-#pragma unroll
-  for (int tl = 0; tl < 4; ++tl) {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, G * kFp4Plane + (16 * tl + c) * 16, 0, AUX);
-    kb.b[tl] = make_uint4(x[0], x[1], x[2], x[3]);
-  }
-  kb.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, kFp4CodeBytes + G * 64 + c * 4, 0, AUX);
-}
-
-template <int TL>
-__device__ __forceinline__ v4f mfma_fp4(const v8i& a, const uint4& b, uint32_t sc) {
-  const v8i bb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  // A: E4M3 (format 0), scale 2^0; B: E2M1 (format 4), scale byte TL of sc
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, zero, 0, 4, 0, 127, TL, (int)sc);
-}
-
-// Tile TL of a block for NT tokens: this lane's partial (its 16 heads, its
-// share of the linear half) into part[t][TL], in the FP8 path's order.
-template <int TL, int NT>
-__device__ __forceinline__ void fp4_tile(const QFrag* f, const LinFrag& lf, const KBlock4& kb,
-                                         float (&part)[NT][4]) {
-  const v4f lin = mfma_fp4<TL>(lf.a, kb.b[TL], kb.sc);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    TileAcc acc;
-#pragma unroll
-    for (int hg = 0; hg < 4; ++hg) acc.d[hg] = mfma_fp4<TL>(f[t].a[hg], kb.b[TL], kb.sc);
-    part[t][TL] = fmaf(lin[t], lf.sc[t], tile_epilogue(f[t], acc));
-  }
-}
-
-// Scores of one block for NT tokens: out[t] is token t's score at position
-// lane_pos(lane).
-template <int NT>
-__device__ __forceinline__ void fp4_block_scores(const QFrag* f, const LinFrag& lf, const KBlock4& kb,
-                                                 float* out) {
-  float part[NT][4];
-  fp4_tile<0, NT>(f, lf, kb, part);
-  fp4_tile<1, NT>(f, lf, kb, part);
-  fp4_tile<2, NT>(f, lf, kb, part);
-  fp4_tile<3, NT>(f, lf, kb, part);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) out[t] = reduce_block(part[t][0], part[t][1], part[t][2], part[t][3]);
-}
-
-// Stores a score at position s of a row of n (and its sampled copy).
-__device__ __forceinline__ void fp4_emit(float* __restrict__ out, float* __restrict__ srow, int s,
-                                         int n, int sS, int sSh, float v) {
-  if (s < n) out[s] = v;
-  if (srow != nullptr) {
-    const int sj = s >> sSh;
-    if (s < n && (s & (sS - 1)) == ((37 * sj + 11) & (sS - 1))) srow[sj] = v;
-  }
-}
-
-// Decode split: one query token per work-group, `chunk_blocks` blocks of its
-// causal range split into four runs, one per wave.  The K stream is read
-// once: each wave keeps NB-1 blocks' operand loads in flight, straight into
-// the MFMA registers (non-temporal).
-template <int NB>
-__device__ __forceinline__ void fp4_decode_body(int bx, int t, const uint8_t* __restrict__ q8,
-                                                const float* __restrict__ w, const CacheArgs& cache,
-                                                const BatchArgs& b, float* __restrict__ logits,
-                                                int64_t ld, int chunk_blocks, uint8_t* lds,
-                                                float* __restrict__ samp) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const TokenPos tp = token_pos_wave(b, t);
-  QFrag f[1];
-  load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
-  const int n = tp.n;
-  const int lb0 = bx * chunk_blocks;
-  if (lb0 * kBlock >= n) return;
-  const int nblk = min(chunk_blocks, (n - lb0 * kBlock + kBlock - 1) / kBlock);
-  const int per = (nblk + 3) / 4;
-  const int mine = max(0, min(per, nblk - wave * per));        // <= 16 blocks
-  if (mine == 0) return;
-  auto blk = [&](int j) { return lb0 + wave * per + j; };
-  const int pbl = lane < mine ? (int)phys_block(b, cache, tp.r, blk(lane)) : -1;
-  auto load = [&](KBlock4& kb, int j) {                       // j <= mine + NB - 2 < 64
-    const int pb = __builtin_amdgcn_readlane(pbl, j);
-    fp4_block_load<kLoadStream>(kb, cache.data + (int64_t)max(pb, 0) * kFp4BlockBytes,
-                                (j < mine && pb >= 0) ? kFp4BlockBytes : 0, lane);
-  };
-  KBlock4 ring[NB];
-#pragma unroll
-  for (int u = 0; u < NB - 1; ++u) load(ring[u], u);
-  LinFrag lf;
-  make_lin<1>(lf, f, lds + wave * kLinScratch, lane);
-  float* out = logits + (size_t)t * ld;
-  float* srow = samp ? samp + (size_t)t * kMaxSample : nullptr;
-  const int sS = sample_stride(n), sSh = 31 - __clz(sS);
-  const int lp = lane_pos(lane);
-  const int iters = (mine + NB - 1) / NB * NB;
-  for (int j0 = 0; j0 < iters; j0 += NB) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int j = j0 + u;
-      load(ring[(u + NB - 1) % NB], j + NB - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      float v;
-      fp4_block_scores<1>(f, lf, ring[u], &v);
-      if (j < mine) fp4_emit(out, srow, blk(j) * kBlock + lp, n, sS, sSh, v);
-    }
-  }
 }
 
 // Prefill split: kPrefillTM consecutive query tokens of one request per
@@ -295,9 +149,6 @@ __device__ __forceinline__ void fp4_prefill_body(int bx, int gy, const uint8_t* 
   }
 }
 
-#ifndef IDX_FP4_DECODE_RING
-#define IDX_FP4_DECODE_RING 4
-#endif
 #ifndef IDX_FP4_PREFILL_RING
 #define IDX_FP4_PREFILL_RING 2
 #endif
@@ -310,7 +161,8 @@ void score_fp4_decode_kernel(const uint8_t* __restrict__ q8, const float* __rest
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kLinScratch];
   int cx, ry;
   xcd_spread(&cx, &ry);
-  fp4_decode_body<NB>(cx, ry, q8, w, cache, b, logits, ld, chunk_blocks, lds, samp);
+  fp4_decode_body<NB>(cx, ry, q8, w, cache, b, logits, ld, chunk_blocks,
+                      b.num_reqs == b.num_tokens && b.max_query_len <= 1, lds, NewRows{}, samp);
 }
 
 template <int NB>

@@ -1,0 +1,277 @@
+// Device code of the FP4 indexer K cache (internal), shared by its
+// quantise-and-scatter and scoring kernels (fp4.hip) and the fused score +
+// top-k kernels (fused.hip).  The format and the scoring method are
+// described in fp4.hip.
+#pragma once
+
+#include "common.hpp"
+#include "quant_device.hpp"
+#include "score_device.hpp"
+
+namespace idx {
+namespace {
+
+constexpr int kFp4CodeBytes = kBlock * kHeadDim / 2;          // 4096
+constexpr int kFp4BlockBytes = kFp4CodeBytes + kBlock * 4;     // 4352
+constexpr int kFp4Plane = kBlock * 16;                          // one group's codes: 1024
+
+// ---------------------------------------------------------- quantiser --
+
+// Group exponent: the smallest e with max(amax, 1e-4) <= 6 * 2^e.  `amag` is
+// the bf16 magnitude pattern of the group's amax: amax = (1 + m/128) 2^(E-127)
+// and 6 = 1.5 * 2^2.
+__device__ __forceinline__ int fp4_exponent(uint32_t amag) {
+  const float a = __uint_as_float(amag << 16);
+  if (!(a >= 1e-4f)) return -15;                 // the floor: 1e-4 <= 6 * 2^-15
+  const int E = (int)(amag >> 7);
+  const int m = (int)(amag & 0x7F);
+  return (E - 127) - 2 + (m > 64 ? 1 : 0);
+}
+
+// E2M1 code of bf16 value x times s = 2^-e (exact in fp32; |x s| <= 6): the
+// number of rounding boundaries at or below |x s|, each boundary open or
+// closed so that a tie goes to the even code, plus the sign bit.
+__device__ __forceinline__ uint32_t encode_e2m1(uint32_t x, float s) {
+  const float y = fabsf(__uint_as_float(x << 16) * s);
+  const uint32_t c = (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
+                     (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
+                     (uint32_t)(y > 5.f);
+  return c | ((x >> 12) & 8u);
+}
+
+// ------------------------------------------------------------ scoring --
+
+// One block's B operands for this lane: tile tl's 16 code bytes (position
+// 16 tl + lane%16, group lane/16) and the dword of that position's group
+// scales for the four tiles (byte tl).
+struct KBlock4 {
+  uint4 b[4];
+  uint32_t sc;
+};
+
+// A buffer resource of `bytes` = 0 (absent block, or past the run) loads
+// zeros: codes 0 score 0.
+template <int AUX>
+__device__ __forceinline__ void fp4_block_load(KBlock4& kb, const uint8_t* base, int bytes, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = byte_rsrc(base, bytes);
+  const int c = lane & 15, G = lane >> 4;
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, G * kFp4Plane + (16 * tl + c) * 16, 0, AUX);
+    kb.b[tl] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+  kb.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, kFp4CodeBytes + G * 64 + c * 4, 0, AUX);
+}
+
+template <int TL>
+__device__ __forceinline__ v4f mfma_fp4(const v8i& a, const uint4& b, uint32_t sc) {
+  const v8i bb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  // A: E4M3 (format 0), scale 2^0; B: E2M1 (format 4), scale byte TL of sc
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, zero, 0, 4, 0, 127, TL, (int)sc);
+}
+
+// Tile TL of a block for NT tokens: this lane's partial (its 16 heads, its
+// share of the linear half) into part[t][TL], in the FP8 path's order.
+template <int TL, int NT>
+__device__ __forceinline__ void fp4_tile(const QFrag* f, const LinFrag& lf, const KBlock4& kb,
+                                         float (&part)[NT][4]) {
+  const v4f lin = mfma_fp4<TL>(lf.a, kb.b[TL], kb.sc);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    TileAcc acc;
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) acc.d[hg] = mfma_fp4<TL>(f[t].a[hg], kb.b[TL], kb.sc);
+    part[t][TL] = fmaf(lin[t], lf.sc[t], tile_epilogue(f[t], acc));
+  }
+}
+
+// Scores of one block for NT tokens: out[t] is token t's score at position
+// lane_pos(lane).
+template <int NT>
+__device__ __forceinline__ void fp4_block_scores(const QFrag* f, const LinFrag& lf, const KBlock4& kb,
+                                                 float* out) {
+  float part[NT][4];
+  fp4_tile<0, NT>(f, lf, kb, part);
+  fp4_tile<1, NT>(f, lf, kb, part);
+  fp4_tile<2, NT>(f, lf, kb, part);
+  fp4_tile<3, NT>(f, lf, kb, part);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) out[t] = reduce_block(part[t][0], part[t][1], part[t][2], part[t][3]);
+}
+
+// Stores a score at position s of a row of n (and its sampled copy).
+__device__ __forceinline__ void fp4_emit(float* __restrict__ out, float* __restrict__ srow, int s,
+                                         int n, int sS, int sSh, float v) {
+  if (s < n) out[s] = v;
+  if (srow != nullptr) {
+    const int sj = s >> sSh;
+    if (s < n && (s & (sS - 1)) == ((37 * sj + 11) & (sS - 1))) srow[sj] = v;
+  }
+}
+
+// Decode split: one query token per work-group, `chunk_blocks` blocks of its
+// causal range split into four runs, one per wave.  The K stream is read
+// once: each wave keeps NB-1 blocks' operand loads in flight, straight into
+// the MFMA registers (non-temporal).  `ident`: token t is request t.
+//
+// With FK the step's new K rows of the token's request that fall in this
+// wave's blocks and causal range are quantised here (each lane its group's 32
+// values, with the quantiser of quant_write_k_fp4_kernel), patched into the
+// loaded operands of their block (where their slot is the block-table slot of
+// their position) and the token's own row written to the cache.  With KEEP
+// the scores go to `kept` (LDS) with their key histogram and largest key, as
+// decode_body does for the fused path.  Returns the token's causal count, or
+// -1 when the chunk holds none of its positions.
+template <int NB, bool FK = false, bool KEEP = false>
+__device__ __forceinline__ int fp4_decode_body(int bx, int t, const uint8_t* __restrict__ q8,
+                                               const float* __restrict__ w, const CacheArgs& cache,
+                                               const BatchArgs& b, float* __restrict__ logits,
+                                               int64_t ld, int chunk_blocks, bool ident,
+                                               uint8_t* lds, const NewRows& nk,
+                                               float* __restrict__ samp, float* kept = nullptr,
+                                               uint32_t* khist = nullptr, uint32_t* khi = nullptr) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  TokenPos tp;
+  if (ident) {
+    tp.r = t;
+    tp.q0 = t;
+    tp.nq = 1;
+    tp.len = b.seq_lens[t];
+    tp.n = min(max(tp.len, 0), b.max_seq_len);
+  } else {
+    tp = token_pos_wave(b, t);
+  }
+  QFrag f[1];
+  load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
+  const int n = tp.n;
+  const int lb0 = bx * chunk_blocks;
+  if (lb0 * kBlock >= n) return -1;
+  const int nblk = min(chunk_blocks, (n - lb0 * kBlock + kBlock - 1) / kBlock);
+  const int per = (nblk + 3) / 4;
+  const int mine = max(0, min(per, nblk - wave * per));        // <= 16 blocks
+  if (mine == 0) return n;
+  auto blk = [&](int j) { return lb0 + wave * per + j; };
+  const int pbl = lane < mine ? (int)phys_block(b, cache, tp.r, blk(lane)) : -1;
+  auto load = [&](KBlock4& kb, int j) {                       // j <= mine + NB - 2 < 64
+    const int pb = __builtin_amdgcn_readlane(pbl, j);
+    fp4_block_load<kLoadStream>(kb, cache.data + (int64_t)max(pb, 0) * kFp4BlockBytes,
+                                (j < mine && pb >= 0) ? kFp4BlockBytes : 0, lane);
+  };
+  KBlock4 ring[NB];
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u) load(ring[u], u);
+  LinFrag lf;
+  make_lin<1>(lf, f, lds + wave * kLinScratch, lane);
+
+  const int G = lane >> 4;
+  uint4 fcode[kMaxFusedRows];
+  uint32_t fexp[kMaxFusedRows];
+  int fpos0 = 0, nfix = 0;
+  if (FK) {
+    const int newlo = tp.len - tp.nq;
+    const int lo = max(newlo, blk(0) * kBlock);
+    const int hi = min(n - 1, (blk(mine - 1) + 1) * kBlock - 1);
+    nfix = min(kMaxFusedRows, max(0, hi - lo + 1));
+    fpos0 = lo;
+#pragma unroll
+    for (int i = 0; i < kMaxFusedRows; ++i) {
+      fcode[i] = make_uint4(0u, 0u, 0u, 0u);
+      fexp[i] = 0xFFFFFFFFu;
+      if (i < nfix) {
+        const int P = lo + i;
+        const int row = tp.q0 + (P - newlo);
+        const uint16_t* kr = nk.k + (int64_t)row * nk.stride + 32 * G;
+        uint32_t x[16];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const uint2 p2 = *reinterpret_cast<const uint2*>(kr + 4 * v);
+          x[2 * v] = p2.x;
+          x[2 * v + 1] = p2.y;
+        }
+        uint32_t am = 0u;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) am = max(am, max(x[v] & 0x7FFFu, (x[v] >> 16) & 0x7FFFu));
+        const int e = fp4_exponent(am);
+        const float sc = pow2f(-e);
+        uint32_t c[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          c[d] = 0u;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t wv = x[4 * d + m];
+            c[d] |= encode_e2m1(wv & 0xFFFFu, sc) << (8 * m);
+            c[d] |= encode_e2m1(wv >> 16, sc) << (8 * m + 4);
+          }
+        }
+        fcode[i] = make_uint4(c[0], c[1], c[2], c[3]);
+        const int64_t want = nk.slots[row];
+        const int pb = __builtin_amdgcn_readlane(pbl, P / kBlock - blk(0));
+        const bool patch = pb >= 0 && want == (int64_t)pb * kBlock + P % kBlock;
+        if (patch) fexp[i] = (uint32_t)(e + 127);
+        if (row == t && want >= 0 && want < nk.num_slots) {   // the token's own row: to the cache
+          uint8_t* cb = nk.cache + (want / kBlock) * kFp4BlockBytes;
+          const int p = (int)(want % kBlock);
+          if ((lane & 15) == 0) {
+            *reinterpret_cast<uint4*>(cb + G * kFp4Plane + p * 16) = fcode[i];
+            cb[kFp4CodeBytes + G * 64 + (p & 15) * 4 + (p >> 4)] = (uint8_t)(e + 127);
+          }
+        }
+      }
+    }
+  }
+
+  float* out = logits + (size_t)t * ld;
+  float* srow = samp ? samp + (size_t)t * kMaxSample : nullptr;
+  const int sS = sample_stride(n), sSh = 31 - __clz(sS);
+  const int lp = lane_pos(lane);
+  uint32_t hik = 0u;                            // KEEP: largest key of this lane
+  const int iters = (mine + NB - 1) / NB * NB;
+  for (int j0 = 0; j0 < iters; j0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int j = j0 + u;
+      load(ring[(u + NB - 1) % NB], j + NB - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      KBlock4& kb = ring[u];
+      if (FK) {
+#pragma unroll
+        for (int i = 0; i < kMaxFusedRows; ++i) {
+          const int P = fpos0 + i;
+          if (i < nfix && fexp[i] != 0xFFFFFFFFu && P / kBlock == blk(j)) {
+            const int r = P % kBlock, tl = r >> 4;
+            if ((lane & 15) == (r & 15)) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (q == tl) kb.b[q] = fcode[i];
+              kb.sc = (kb.sc & ~(0xFFu << (8 * tl))) | (fexp[i] << (8 * tl));
+            }
+          }
+        }
+      }
+      float v;
+      fp4_block_scores<1>(f, lf, kb, &v);
+      const int s = blk(j) * kBlock + lp;
+      if (KEEP) {
+        if (j < mine && s < n) {
+          kept[s - lb0 * kBlock] = v;
+          const uint32_t key = order_key(v);
+          atomicAdd(&khist[key >> kKeepHistShift], 1u);
+          hik = max(hik, key);
+        }
+      } else if (j < mine) {
+        fp4_emit(out, srow, s, n, sS, sSh, v);
+      }
+    }
+  }
+  if (KEEP) {
+    const uint32_t m = wave_max(hik);
+    if (lane == 0) atomicMax(khi, m);
+  }
+  return n;
+}
+
+}  // namespace
+}  // namespace idx

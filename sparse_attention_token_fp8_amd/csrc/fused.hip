@@ -32,6 +32,11 @@
 #include "launch.hpp"
 #include "score_device.hpp"
 #include "topk_device.hpp"
+#include "fp4_device.hpp"
+
+#ifndef IDX_FP4_DECODE_RING
+#define IDX_FP4_DECODE_RING 4
+#endif
 
 #include <algorithm>
 
@@ -147,13 +152,14 @@ __device__ __forceinline__ void chunk_filter(const float* kept, int t, int cx, i
 }
 
 // Decode scoring that keeps each chunk's candidates (step 1).  With FK it also
-// writes this step's new K rows, as score_decode_write_kernel does.
-template <int NB, bool FK>
-__global__ __launch_bounds__(kScoreThreads)
-__attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_keep_kernel(
-    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    int chunk_blocks, int ident, NewRows nk, int k, KeepSlots ks) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
+// writes this step's new K rows, as score_decode_write_kernel does.  FP4:
+// the cache is the FP4 one (fp4_decode_body, no LDS staging of K).
+template <int NB, bool FK, bool FP4>
+__device__ __forceinline__ void keep_body(const uint8_t* __restrict__ q8,
+                                          const float* __restrict__ w, const CacheArgs& cache,
+                                          const BatchArgs& b, int chunk_blocks, int ident,
+                                          const NewRows& nk, int k, const KeepSlots& ks,
+                                          uint8_t* lds) {
   __shared__ float kept[kMaxChunkPos];
   __shared__ __attribute__((aligned(16))) uint32_t hist[kTauBins];
   __shared__ __attribute__((aligned(16))) uint32_t hist2[kTau2Bins];
@@ -167,11 +173,34 @@ __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_keep_ke
   __syncthreads();
   int cx, ry;
   xcd_spread(&cx, &ry);
-  const int n = decode_body<NB, FK, false, true>(cx, ry, q8, w, cache, b, nullptr, 0, chunk_blocks,
-                                                 ident != 0, lds, nk, nullptr, kept, hist, table);
+  int n;
+  if constexpr (FP4)
+    n = fp4_decode_body<NB, FK, true>(cx, ry, q8, w, cache, b, nullptr, 0, chunk_blocks, ident != 0,
+                                      lds, nk, nullptr, kept, hist, table);
+  else
+    n = decode_body<NB, FK, false, true>(cx, ry, q8, w, cache, b, nullptr, 0, chunk_blocks,
+                                         ident != 0, lds, nk, nullptr, kept, hist, table);
   if (n <= k) return;                           // nothing here, or a row the resolve takes whole
   __syncthreads();                              // every wave's scores are in `kept`
   chunk_filter(kept, ry, cx, chunk_blocks, n, k, ks, hist, hist2, table);
+}
+
+template <int NB, bool FK>
+__global__ __launch_bounds__(kScoreThreads)
+__attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_keep_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
+    int chunk_blocks, int ident, NewRows nk, int k, KeepSlots ks) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
+  keep_body<NB, FK, false>(q8, w, cache, b, chunk_blocks, ident, nk, k, ks, lds);
+}
+
+template <int NB, bool FK>
+__global__ __launch_bounds__(kScoreThreads)
+__attribute__((amdgpu_waves_per_eu(2))) void score_keep_fp4_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
+    int chunk_blocks, int ident, NewRows nk, int k, KeepSlots ks) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kLinScratch];
+  keep_body<NB, FK, true>(q8, w, cache, b, chunk_blocks, ident, nk, k, ks, lds);
 }
 
 // ------------------------------------------------------------- resolve --
@@ -201,6 +230,7 @@ constexpr size_t kResolveSmem = sizeof(ResolveLds) > sizeof(RescoreLds) ? sizeof
 // Step 3: keys of all n positions of token t's row into keys[0..n), by
 // kRescoreWaves waves of the work-group (the others idle), with the scoring
 // kernels' per-block operations.
+template <bool FP4>
 __device__ __forceinline__ void rescore_row(const uint8_t* __restrict__ q8,
                                             const float* __restrict__ w, const CacheArgs& cache,
                                             const BatchArgs& b, int t, int r, int n,
@@ -217,6 +247,16 @@ __device__ __forceinline__ void rescore_row(const uint8_t* __restrict__ q8,
   const int nb = (n + kBlock - 1) / kBlock;
   for (int lb = wave; lb < nb; lb += kRescoreWaves) {
     const int64_t pb = phys_block(b, cache, r, lb);
+    if constexpr (FP4) {
+      KBlock4 kb;
+      fp4_block_load<kLoadStream>(kb, cache.data + (pb >= 0 ? pb : 0) * kFp4BlockBytes,
+                                  pb >= 0 ? kFp4BlockBytes : 0, lane);
+      float v;
+      fp4_block_scores<1>(f, lf, kb, &v);
+      const int s = lb * kBlock + lp;
+      if (s < n) keys[s] = order_key(v);
+      continue;
+    }
     WaveStage st;
     wave_stage_load(st, cache.data + (pb >= 0 ? pb : 0) * kBlockBytes, pb >= 0 ? kBlockBytes : 0,
                     lane);
@@ -236,6 +276,7 @@ __device__ __forceinline__ void rescore_row(const uint8_t* __restrict__ q8,
 // counts, thresholds and maxima and (for rows of up to kSpecSlots slots) the
 // first entries of every slot are loaded at once, so the gather costs one
 // round trip to memory.
+template <bool FP4>
 __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     int ident, int k, KeepSlots ks, int32_t* __restrict__ topk, int64_t ldo) {
@@ -384,7 +425,7 @@ __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
   // nslots * cap) take its rescored keys as one flat array of n words.
   __syncthreads();                              // the candidates' LDS is reused
   uint32_t* keys = reinterpret_cast<uint32_t*>(ks.cand + rbase * cap);
-  rescore_row(q8, w, cache, b, t, r, n, keys, reinterpret_cast<RescoreLds*>(smem));
+  rescore_row<FP4>(q8, w, cache, b, t, r, n, keys, reinterpret_cast<RescoreLds*>(smem));
   __syncthreads();                              // every key written before any is read
   uint32_t take;
   const uint32_t kstar = radix_kth<NT, 3>([&](auto&& fn) {
@@ -434,35 +475,48 @@ size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks) {
 hipError_t launch_keep_candidates(const uint8_t* q8, const float* w, const CacheArgs& cache,
                                   const BatchArgs& b, const uint16_t* kq, int64_t kq_stride,
                                   const int64_t* slots, uint8_t* cache_w, int k,
-                                  const KeepSlots& ks, hipStream_t stream) {
+                                  const KeepSlots& ks, hipStream_t stream, bool fp4) {
   if (b.num_tokens == 0) return hipSuccess;
   const int ident = b.num_reqs == b.num_tokens && b.max_query_len <= 1;
   if (b.max_seq_len > 0) {
     const dim3 grid((unsigned)ks.nslots, (unsigned)b.num_tokens);
-    if (kq != nullptr) {
-      const NewRows nk{kq, kq_stride, slots, cache_w, cache.num_blocks * kBlock};
+    const NewRows nk = kq != nullptr ? NewRows{kq, kq_stride, slots, cache_w, cache.num_blocks * kBlock}
+                                     : NewRows{};
+    if (fp4 && kq != nullptr)
+      IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_DECODE_RING, true>), grid,
+                 dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+    else if (fp4)
+      IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_DECODE_RING, false>), grid,
+                 dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+    else if (kq != nullptr)
       IDX_LAUNCH("score_keep_kernel", (score_keep_kernel<IDX_DECODE_RING, true>), grid,
                  dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
-    } else {
+    else
       IDX_LAUNCH("score_keep_kernel", (score_keep_kernel<IDX_DECODE_RING, false>), grid,
-                 dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, NewRows{},
-                 k, ks);
-    }
+                 dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
     return hipGetLastError();
   }
   if (kq != nullptr)
-    return launch_quant_write_k(kq, b.num_tokens, kq_stride, slots, cache_w,
-                                cache.num_blocks * kBlock, stream);
+    return fp4 ? launch_quant_write_k_fp4(kq, b.num_tokens, kq_stride, slots, cache_w,
+                                          cache.num_blocks * kBlock, stream)
+               : launch_quant_write_k(kq, b.num_tokens, kq_stride, slots, cache_w,
+                                      cache.num_blocks * kBlock, stream);
   return hipSuccess;
 }
 
 hipError_t launch_keep_select(const uint8_t* q8, const float* w, const CacheArgs& cache,
                               const BatchArgs& b, int k, const KeepSlots& ks, int32_t* out,
-                              int64_t ldo, hipStream_t stream) {
+                              int64_t ldo, hipStream_t stream, bool fp4) {
   if (b.num_tokens == 0) return hipSuccess;
   const int ident = b.num_reqs == b.num_tokens && b.max_query_len <= 1;
-  IDX_LAUNCH("topk_keep_resolve_kernel", (topk_keep_resolve_kernel), dim3((unsigned)b.num_tokens),
-             dim3(kResThreads), stream, q8, w, cache, b, ident, k, ks, out, ldo);
+  if (fp4)
+    IDX_LAUNCH("topk_keep_resolve_kernel", (topk_keep_resolve_kernel<true>),
+               dim3((unsigned)b.num_tokens), dim3(kResThreads), stream, q8, w, cache, b, ident, k, ks,
+               out, ldo);
+  else
+    IDX_LAUNCH("topk_keep_resolve_kernel", (topk_keep_resolve_kernel<false>),
+               dim3((unsigned)b.num_tokens), dim3(kResThreads), stream, q8, w, cache, b, ident, k, ks,
+               out, ldo);
   return hipGetLastError();
 }
 

@@ -5,8 +5,9 @@ within the scoring tolerance of the oracle's fp64 scores on the same decoded
 K; the decode and prefill scoring kernels give the same bits; top-k rows
 equal idx_topk over idx_logits_fp4 and fall inside the oracle's tie band.
 The full-size case runs the FP4 step of 8 decode tokens over 128K positions
-(new K rows quantised, then scores and top-k) and checks the whole cache and
-every row.
+(idx_indexcache_layer_fp4: the fused scoring kernel writes the new K rows,
+keeps its scores on chip and passes per-chunk candidates to the exact
+select) and checks the whole cache and every row.
 """
 
 import numpy as np
@@ -214,10 +215,113 @@ def test_fp4_score_topk(env, lengths, new, k):
         check_topk_band(g[t], want[t], k, f"fp4 token {t}")
 
 
+def _fp4_scale_positions(dev_cache, orc_cache, block_table_row, positions, add):
+    """Add `add` to the four E8M0 group exponents of the given logical positions in
+    both FP4 caches: their scores scale by exactly 2^add."""
+    import torch
+    p = np.asarray(positions, np.int64)
+    b = np.asarray(block_table_row, np.int64)[p // 64].repeat(4)
+    q = (p % 64).repeat(4)
+    g = np.tile(np.arange(4), p.size)
+    off = 4096 + g * 64 + (q % 16) * 4 + q // 16
+    orc_cache[b, off] = (orc_cache[b, off].astype(np.int64) + add).astype(np.uint8)
+    dev_cache.tensor[torch.from_numpy(b).cuda(), torch.from_numpy(off).cuda()] = \
+        torch.from_numpy(orc_cache[b, off].copy()).cuda()
+
+
+def test_fp4_fused_rescore_fallback(env):
+    """Decode rows over long contexts take the fused path over the FP4 cache
+    too.  2048 consecutive positions of request 0 scaled by 8 (their group
+    exponents + 3) hold far more than their chunks' share of the top k, so the
+    row is rescored whole; the rows equal idx_logits_fp4 + idx_topk and the
+    oracle's band."""
+    m, torch = env
+    wl = random_batch(7401, [20000, 9000, 30000], 1, k=2048)
+    dev = device_layer(m, torch, wl, 0, with_new=True, fmt="fp4")
+    orc = oracle_layer(wl, 0, fmt="fp4")
+    hot = list(range(8192, 8192 + 2048))
+    _fp4_scale_positions(dev["cache"], orc["cache"], wl.block_table[0], hot, 3)
+    assert np.array_equal(dev["cache"].tensor.cpu().numpy(), orc["cache"])
+    batch = device_batch(m, wl)
+    lg = m.idx_logits_fp4(dev["q8"], dev["w"], dev["cache"], batch)
+    a = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+    with m.KernelTrace(capacity=8) as tr:
+        b = m.idx_score_topk_fp4(dev["q8"], dev["w"], dev["cache"], batch, wl.k)
+    assert [n for n, _ in tr.kernels] == ["score_keep_fp4_kernel", "topk_keep_resolve_kernel"]
+    b = b.cpu().numpy()
+    assert np.array_equal(a, b)
+    want = oracle_rows(wl, orc, range(wl.num_tokens))
+    for t in range(wl.num_tokens):
+        check_topk_band(b[t], want[t], wl.k, f"fp4 fallback token {t}")
+    assert np.isin(hot, b[0]).sum() > 700, "the scaled positions should dominate row 0"
+
+
+def test_fp4_layer_k_write_inside_scoring(env):
+    """idx_indexcache_layer_fp4 on an F layer: the cache bytes and the top-k rows
+    equal the separate idx_quant_write_k_fp4 + idx_logits_fp4 + idx_topk on a
+    copy of the cache: decode batches over long rows (the fused kernel writes
+    the new rows itself) with a padding token, requests of three new tokens
+    with the decode split (fused, rows written inside scoring) and without it
+    (prefill split, rows written first), and many short requests (unfused)."""
+    m, torch = env
+    many = np.random.default_rng(7403).integers(1, 6000, 40).tolist()
+    cases = [(random_batch(7401, [3000, 9000, 20000, 700, 1500], 1, k=512), [0], [3]),
+             (random_batch(7402, [2500, 9000, 4000], 3, k=256), [9, 0], []),
+             (random_batch(7403, many, 1, k=256), [0], [5])]
+    for wl, splits, pad in cases:
+        for nd in splits:
+            say("fp4 layer K write", wl.seq_lens.tolist(), wl.new_tokens.tolist(), "decode tokens", nd)
+            dev = device_layer(m, torch, wl, 0, fmt="fp4")
+            slots = dev["slots_new"].clone()
+            for p in pad:
+                slots[p] = -1
+            batch = m.Batch(wl.seq_lens, wl.query_start_loc, wl.block_table, num_decode_tokens=nd)
+            ref_cache = m.KCacheFP4(wl.num_blocks, tensor=dev["cache"].tensor.clone())
+            m.idx_quant_write_k_fp4(dev["k_new"], slots, ref_cache)
+            lg = m.idx_logits_fp4(dev["q8"], dev["w"], ref_cache, batch)
+            want = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+            topk = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
+            m.idx_indexcache_layer_fp4(dev["k_new"], dev["cache"], dev["q8"], dev["w"], True, True,
+                                       slots, batch, wl.k, topk)
+            assert torch.equal(dev["cache"].tensor, ref_cache.tensor)
+            assert np.array_equal(topk.cpu().numpy(), want)
+    # an S layer writes the rows and nothing else
+    wl = random_batch(7404, [3000, 9000], 1, k=256)
+    dev = device_layer(m, torch, wl, 0, fmt="fp4")
+    batch = device_batch(m, wl)
+    ref_cache = m.KCacheFP4(wl.num_blocks, tensor=dev["cache"].tensor.clone())
+    m.idx_quant_write_k_fp4(dev["k_new"], dev["slots_new"], ref_cache)
+    topk = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
+    m.idx_indexcache_layer_fp4(dev["k_new"], dev["cache"], dev["q8"], dev["w"], False, True,
+                               dev["slots_new"], batch, wl.k, topk)
+    assert torch.equal(dev["cache"].tensor, ref_cache.tensor)
+    assert bool((topk == -7).all())
+
+
+def test_fp4_candidate_stages(env):
+    """idx_score_candidates_fp4 + idx_select_candidates_fp4 are the FP4 fused
+    path's two launches: the same cache bytes and rows as the F layer."""
+    m, torch = env
+    wl = random_batch(7405, [20000, 9000, 30000], 1, k=2048)
+    dev = device_layer(m, torch, wl, 0, fmt="fp4")
+    batch = device_batch(m, wl)
+    ref_cache = m.KCacheFP4(wl.num_blocks, tensor=dev["cache"].tensor.clone())
+    ref = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
+    m.idx_indexcache_layer_fp4(dev["k_new"], ref_cache, dev["q8"], dev["w"], True, True,
+                               dev["slots_new"], batch, wl.k, ref)
+    ws = torch.empty(m.idx_score_topk_fp4_workspace_size(batch, wl.k), dtype=torch.uint8,
+                     device="cuda")
+    m.idx_score_candidates_fp4(dev["q8"], dev["w"], dev["cache"], batch, wl.k, ws, dev["k_new"],
+                               dev["slots_new"])
+    got = m.idx_select_candidates_fp4(dev["q8"], dev["w"], dev["cache"], batch, wl.k, ws)
+    assert torch.equal(dev["cache"].tensor, ref_cache.tensor)
+    assert torch.equal(got, ref)
+
+
 def test_fp4_decode_8x128k_step(env):
-    """The FP4 step at full size: 8 decode tokens over 128K positions, the new K
-    rows quantised into the FP4 cache, then scores and top-2048.  The whole
-    cache against the oracle's bytes, every row against its fp64 scores."""
+    """The FP4 step at full size, as bench.py times it: 8 decode tokens over
+    128K positions through idx_indexcache_layer_fp4.  The whole cache against
+    the oracle's bytes, every row against its fp64 scores."""
     m, torch = env
     wl = make_workload(CONFIGS["decode-8x128k"])
     say(f"[fp4 decode-8x128k] tokens {wl.num_tokens} pool {wl.num_blocks}")
@@ -226,8 +330,8 @@ def test_fp4_decode_8x128k_step(env):
     topk = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
     ws = torch.empty(m.idx_score_topk_fp4_workspace_size(batch, wl.k), dtype=torch.uint8,
                      device="cuda")
-    m.idx_quant_write_k_fp4(dev["k_new"], dev["slots_new"], dev["cache"])
-    m.idx_score_topk_fp4(dev["q8"], dev["w"], dev["cache"], batch, wl.k, topk, workspace=ws)
+    m.idx_indexcache_layer_fp4(dev["k_new"], dev["cache"], dev["q8"], dev["w"], True, True,
+                               dev["slots_new"], batch, wl.k, topk, workspace=ws)
     torch.cuda.synchronize()
     say("[fp4 decode-8x128k] oracle cache")
     orc = oracle_layer(wl, 0, fmt="fp4")
