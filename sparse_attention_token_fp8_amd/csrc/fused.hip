@@ -37,6 +37,9 @@
 #ifndef IDX_FP4_DECODE_RING
 #define IDX_FP4_DECODE_RING 4
 #endif
+#ifndef IDX_FP4_KEEP_RING
+#define IDX_FP4_KEEP_RING 2
+#endif
 
 #include <algorithm>
 
@@ -194,9 +197,12 @@ __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_keep_ke
   keep_body<NB, FK, false>(q8, w, cache, b, chunk_blocks, ident, nk, k, ks, lds);
 }
 
+#ifndef IDX_FP4_KEEP_WAVES_PER_EU
+#define IDX_FP4_KEEP_WAVES_PER_EU 2
+#endif
 template <int NB, bool FK>
 __global__ __launch_bounds__(kScoreThreads)
-__attribute__((amdgpu_waves_per_eu(2))) void score_keep_fp4_kernel(
+__attribute__((amdgpu_waves_per_eu(IDX_FP4_KEEP_WAVES_PER_EU))) void score_keep_fp4_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     int chunk_blocks, int ident, NewRows nk, int k, KeepSlots ks) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kLinScratch];
@@ -483,10 +489,10 @@ hipError_t launch_keep_candidates(const uint8_t* q8, const float* w, const Cache
     const NewRows nk = kq != nullptr ? NewRows{kq, kq_stride, slots, cache_w, cache.num_blocks * kBlock}
                                      : NewRows{};
     if (fp4 && kq != nullptr)
-      IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_DECODE_RING, true>), grid,
+      IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_KEEP_RING, true>), grid,
                  dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
     else if (fp4)
-      IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_DECODE_RING, false>), grid,
+      IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_KEEP_RING, false>), grid,
                  dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
     else if (kq != nullptr)
       IDX_LAUNCH("score_keep_kernel", (score_keep_kernel<IDX_DECODE_RING, true>), grid,
