@@ -104,11 +104,13 @@ __device__ __forceinline__ uint32_t wave_find_bin(const uint32_t* h, uint32_t ne
 // past the scoring loop; hist2 is zero.  tau is the lower edge of the level-2
 // bin holding the m-th largest key (so at least m keys are >= tau, and at most
 // the bin's other keys besides them); every wave finds it on its own from the
-// shared histograms.  `table` holds 65 words.
+// shared histograms.  NT threads, NT >= 256, for chunks of up to MAXPOS
+// positions; `table` holds 65 words, 129 when MAXPOS / 64 > 64.
+template <int NT, int MAXPOS = kMaxChunkPos>
 __device__ __forceinline__ void chunk_filter(const float* kept, int t, int cx, int chunk_blocks,
                                              int n, int k, const KeepSlots& ks, uint32_t* hist,
                                              uint32_t* hist2, uint32_t* table) {
-  constexpr int NT = kScoreThreads, E = kKeepPer;
+  constexpr int E = MAXPOS / NT;
   const int lane = threadIdx.x & 63;
   const int base = cx * chunk_blocks * kBlock;
   const int nvalid = min(n - base, chunk_blocks * kBlock);
@@ -143,10 +145,17 @@ __device__ __forceinline__ void chunk_filter(const float* kept, int t, int cx, i
   const size_t slot = (size_t)t * ks.nslots + cx;
   uint2* dst = ks.cand + slot * ks.cap;
   const uint32_t cap = (uint32_t)ks.cap;
-  const uint32_t cnt = compact_ordered_to<NT, E>(key, pass, base, 0u, table + 1,
-                                                 [&](uint32_t i, uint32_t kk, int pos) {
-                                                   if (i < cap) dst[i] = make_uint2(kk, (uint32_t)pos);
-                                                 });
+  auto put = [&](uint32_t i, uint32_t kk, int pos) {
+    if (i < cap) dst[i] = make_uint2(kk, (uint32_t)pos);
+  };
+  uint32_t cnt;
+  if constexpr (E * (NT / 64) <= 64) {
+    cnt = compact_ordered_to<NT, E>(key, pass, base, 0u, table + 1, put);
+  } else {                                      // two halves in position order, own count tables
+    constexpr int H = E / 2;
+    const uint32_t c1 = compact_ordered_to<NT, H>(key, pass, base, 0u, table + 1, put);
+    cnt = c1 + compact_ordered_to<NT, H>(key + H, pass + H, base + H * NT, c1, table + 65, put);
+  }
   if (threadIdx.x == 0) {
     ks.counts[slot] = cnt;
     ks.taus[slot] = tau;
@@ -185,7 +194,7 @@ __device__ __forceinline__ void keep_body(const uint8_t* __restrict__ q8,
                                          ident != 0, lds, nk, nullptr, kept, hist, table);
   if (n <= k) return;                           // nothing here, or a row the resolve takes whole
   __syncthreads();                              // every wave's scores are in `kept`
-  chunk_filter(kept, ry, cx, chunk_blocks, n, k, ks, hist, hist2, table);
+  chunk_filter<kScoreThreads>(kept, ry, cx, chunk_blocks, n, k, ks, hist, hist2, table);
 }
 
 template <int NB, bool FK>
@@ -209,13 +218,228 @@ __attribute__((amdgpu_waves_per_eu(IDX_FP4_KEEP_WAVES_PER_EU))) void score_keep_
   keep_body<NB, FK, true>(q8, w, cache, b, chunk_blocks, ident, nk, k, ks, lds);
 }
 
+// ------------------------------------------------- one work-group a CU --
+// The same step 1 with one work-group of kDynWaves waves per CU, whose waves
+// take the chunk's blocks one at a time from a work-group counter: the CU's
+// two SIMD slots no longer hold two work-groups of which the younger is
+// served later and ends last, waves that the SIMDs serve faster take more
+// blocks, and the chunk's threshold and compaction run once per CU.
+constexpr int kDynWaves = 8;
+constexpr int kDynThreads = 64 * kDynWaves;
+constexpr int kDynMaxBlocks = 128;              // a chunk's blocks: two block ids per lane
+
+// Scores one token's chunk (up to kDynMaxBlocks blocks) into kept/khist/khi, as
+// decode_body does with KEEP; *next is the LDS block counter, set to
+// kDynWaves * (NB - 1) before the call (each wave's first NB - 1 blocks are
+// wave, wave + kDynWaves, ...).  With FK every wave quantises the chunk's new
+// rows, the wave that scores a row's block patches it into its staged copy,
+// and wave 0 writes the token's own row to the cache.  Returns the token's
+// causal count n, or -1 when the chunk holds none of its positions.
+template <int NB, bool FK>
+__device__ __forceinline__ int dyn_body(int cx, int t, const uint8_t* __restrict__ q8,
+                                        const float* __restrict__ w, const CacheArgs& cache,
+                                        const BatchArgs& b, int chunk_blocks, bool ident,
+                                        uint8_t* lds, const NewRows& nk, float* kept,
+                                        uint32_t* khist, uint32_t* khi, uint32_t* next) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lb0 = cx * chunk_blocks;
+  int bt_full[2] = {-1, -1};                    // raw ids; checked only once they are needed
+  if (ident) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (lane + 64 * h < chunk_blocks)
+        bt_full[h] = b.bt[(int64_t)t * b.bt_stride + min(lb0 + lane + 64 * h, (int)b.bt_stride - 1)];
+  }
+  TokenPos tp;
+  if (ident) {                                  // one new token per request: token t is request t
+    tp.r = t;
+    tp.q0 = t;
+    tp.nq = 1;
+    tp.len = b.seq_lens[t];
+    tp.n = min(max(tp.len, 0), b.max_seq_len);
+  } else {
+    tp = token_pos_wave(b, t);
+  }
+  QFrag f[1];
+  load_q(f[0], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
+  const int n = tp.n;
+  if (lb0 * kBlock >= n) return -1;
+  const int nblk = min(chunk_blocks, (n - lb0 * kBlock + kBlock - 1) / kBlock);
+  const int lp = lane_pos(lane);
+  uint32_t hi = 0u;                             // largest key of this lane
+  auto emit = [&](int j, float v) {             // j: the chunk's block, < nblk
+    const int s = (lb0 + j) * kBlock + lp;
+    if (s < n) {
+      kept[s - lb0 * kBlock] = v;
+      const uint32_t key = order_key(v);
+      atomicAdd(&khist[key >> kKeepHistShift], 1u);
+      hi = max(hi, key);
+    }
+  };
+  auto keep_max = [&]() {
+    const uint32_t m = wave_max(hi);
+    if (lane == 0) atomicMax(khi, m);
+  };
+  if (cache.num_blocks == 0) {                  // no K at all: every score is 0
+    for (int j = wave; j < nblk; j += kDynWaves) emit(j, 0.f);
+    keep_max();
+    return n;
+  }
+  // lane j holds the physical blocks of the chunk's blocks j and 64 + j
+  int pbl[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane + 64 * h;
+    if (ident && nblk == chunk_blocks)
+      pbl[h] = (j < chunk_blocks && lb0 + j < b.bt_stride && bt_full[h] >= 0 &&
+                bt_full[h] < cache.num_blocks) ? bt_full[h] : -1;
+    else
+      pbl[h] = j < nblk ? (int)phys_block(b, cache, tp.r, lb0 + j) : -1;
+  }
+  auto pblock = [&](int j) {                    // j uniform, < kDynMaxBlocks
+    return __builtin_amdgcn_readlane(j < 64 ? pbl[0] : pbl[1], j & 63);
+  };
+  // block j of the chunk (uniform); from nblk on it loads nothing
+  auto stage = [&](WaveStage& st, int j) {
+    const int pb = pblock(min(j, kDynMaxBlocks - 1));
+    wave_stage_load(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes,
+                    (j < nblk && pb >= 0) ? kBlockBytes : 0, lane);
+  };
+  auto grab = [&]() {
+    uint32_t j = 0u;
+    if (lane == 0) j = atomicAdd(next, 1u);
+    return __builtin_amdgcn_readfirstlane((int)j);
+  };
+  uint8_t* slot = lds + wave * kBlockBytes;
+  int jr[NB];                                   // the block each ring entry holds
+  WaveStage ring[NB];
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u) {
+    jr[u] = wave + u * kDynWaves;
+    stage(ring[u], jr[u]);
+  }
+  LinFrag lf;
+  make_lin<1>(lf, f, slot, lane);
+
+  uint32_t fcode[kMaxFusedRows];
+  uint32_t fscale[kMaxFusedRows];
+  int fpos0 = 0, nfix = 0;
+  if (FK) {                                     // the chunk's new rows, as decode_body
+    const int newlo = tp.len - tp.nq;
+    const int lo = max(newlo, lb0 * kBlock);
+    const int hi2 = min(n - 1, (lb0 + nblk) * kBlock - 1);
+    nfix = min(kMaxFusedRows, max(0, hi2 - lo + 1));
+    fpos0 = lo;
+#pragma unroll
+    for (int i = 0; i < kMaxFusedRows; ++i) {
+      fcode[i] = 0u;
+      fscale[i] = 0u;
+      if (i < nfix) {
+        const int P = lo + i;
+        const int row = tp.q0 + (P - newlo);
+        const uint2 v = *reinterpret_cast<const uint2*>(nk.k + (int64_t)row * nk.stride + (lane & 31) * 4);
+        const int64_t want = nk.slots[row];
+        int e;
+        const uint32_t code = quant_row_lane(v, &e);
+        const uint32_t sc = __float_as_uint(pow2f(e));
+        const int pb = pblock(P / kBlock - lb0);
+        const bool patch = pb >= 0 && want == (int64_t)pb * kBlock + P % kBlock;
+        fcode[i] = code;
+        fscale[i] = patch ? sc : 0xFFFFFFFFu;   // all ones: leave the row as the cache has it
+        if (wave == 0 && row == t && want >= 0 && want < nk.num_slots) {
+          uint8_t* cb = nk.cache + (want / kBlock) * kBlockBytes;
+          if (lane < 32) *reinterpret_cast<uint32_t*>(cb + (want % kBlock) * kHeadDim + lane * 4) = code;
+          if (lane == 0) *reinterpret_cast<uint32_t*>(cb + kCodeBytes + (want % kBlock) * 4) = sc;
+        }
+      }
+    }
+  }
+
+  // Each step takes the next block for the ring entry just consumed, then
+  // scores the oldest entry; a wave stops at its first block past the chunk
+  // (the counter only grows, so every later one is past it too).
+  for (;;) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int s = (u + NB - 1) % NB;
+      jr[s] = grab();
+      stage(ring[s], jr[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int j = jr[u];
+      if (j >= nblk) {
+        keep_max();
+        return n;
+      }
+      wave_stage_store(ring[u], slot, lane);
+      if (FK) {
+#pragma unroll
+        for (int i = 0; i < kMaxFusedRows; ++i) {
+          const int P = fpos0 + i;
+          if (i < nfix && fscale[i] != 0xFFFFFFFFu && P / kBlock == lb0 + j) {
+            const int rr = P % kBlock;
+            if (lane < 32)
+              *reinterpret_cast<uint32_t*>(slot + rr * kHeadDim + (((lane >> 2) ^ (rr & 7)) << 4) +
+                                           (lane & 3) * 4) = fcode[i];
+            if (lane == 0) *reinterpret_cast<uint32_t*>(slot + kCodeBytes + rr * 4) = fscale[i];
+          }
+        }
+      }
+      wave_sync_lds();
+      KBlock kb;
+      lds_kblock(kb, slot, lane);
+      wave_sync_lds();                          // reads done before the slot is rewritten
+      float v;
+      block_scores<1>(f, lf, kb, &v);
+      emit(j, v);
+    }
+  }
+}
+
+#ifndef IDX_DYN_RING
+#define IDX_DYN_RING 2
+#endif
+// MAXB: the largest chunk it takes (64 or kDynMaxBlocks blocks), which sizes
+// `kept` and the filter's registers.
+template <int NB, bool FK, int MAXB>
+__global__ __launch_bounds__(kDynThreads) void score_keep_dyn_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
+    int chunk_blocks, int ident, NewRows nk, int k, KeepSlots ks) {
+  static_assert(MAXB <= kDynMaxBlocks, "two block ids per lane");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDynWaves * kBlockBytes];
+  __shared__ float kept[MAXB * kBlock];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kTauBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist2[kTau2Bins];
+  __shared__ uint32_t table[1 + MAXB];
+  __shared__ uint32_t next;
+  for (int i = threadIdx.x; i < kTauBins / 4; i += kDynThreads)
+    reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = threadIdx.x; i < kTau2Bins / 4; i += kDynThreads)
+    reinterpret_cast<uint4*>(hist2)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) {
+    table[0] = 0u;
+    next = (uint32_t)(kDynWaves * (NB - 1));
+  }
+  __syncthreads();
+  int cx, ry;
+  xcd_spread(&cx, &ry);
+  const int n = dyn_body<NB, FK>(cx, ry, q8, w, cache, b, chunk_blocks, ident != 0, lds, nk, kept,
+                                 hist, table, &next);
+  if (n <= k) return;                           // nothing here, or a row the resolve takes whole
+  __syncthreads();                              // every wave's scores are in `kept`
+  chunk_filter<kDynThreads, MAXB * kBlock>(kept, ry, cx, chunk_blocks, n, k, ks, hist, hist2, table);
+}
+
 // ------------------------------------------------------------- resolve --
 
-constexpr int kResThreads = 1024;
+#ifndef IDX_RES_THREADS
+#define IDX_RES_THREADS 1024
+#endif
+constexpr int kResThreads = IDX_RES_THREADS;
 constexpr int kResCap = 8192;                   // candidates a row can hold in LDS
-constexpr int kRescoreWaves = 8;
+constexpr int kRescoreWaves = kResThreads / 64 < 8 ? kResThreads / 64 : 8;
 constexpr int kSpecSlots = 128;                 // rows of up to 128 slots preload candidates
-constexpr int kSpecPer = 8;                     // entries each thread preloads
+constexpr int kSpecPer = 8192 / kResThreads;    // entries each thread preloads
 
 struct ResolveLds {
   uint32_t ckey[kResCap];
@@ -224,7 +448,8 @@ struct ResolveLds {
   uint32_t pre[kMaxSlots + 1];
   uint32_t bucket[64];
   uint32_t scratch[scratch_words<kResThreads>()];
-  uint32_t misc[4];                             // T, largest key, candidates >= T
+  uint32_t emit[2 * (kResThreads / 64)];        // per-wave counts of the row's writer
+  uint32_t misc[4];                             // T, largest key, in-place count, bucket fill
 };
 struct RescoreLds {
   uint8_t stage[kRescoreWaves][kBlockBytes];
@@ -278,6 +503,88 @@ __device__ __forceinline__ void rescore_row(const uint8_t* __restrict__ q8,
   }
 }
 
+// A wave's run of the row's candidates, held in registers: wave w owns
+// candidates [w R, (w+1) R) of ckey/cpos[0..C) (ascending position order),
+// R a multiple of 64 and at most 64 E, lane l entries l, l + 64, ...
+template <int NT>
+struct RowRun {
+  static constexpr int E = kResCap / NT;
+  uint32_t key[E];
+  int32_t pos[E];
+  uint32_t a0, a1;                              // the run, clipped to C
+  int ne;                                       // iterations holding any of it
+  __device__ __forceinline__ void load(const uint32_t* ckey, const int32_t* cpos, uint32_t C) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const uint32_t R = (C + 64 * NW - 1) / (64 * NW) * 64;
+    a0 = min(C, wave * R);
+    a1 = min(C, a0 + R);
+    ne = (int)((a1 - a0 + 63u) / 64u);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {               // every read issued together (in bounds)
+      const uint32_t j = min(a0 + 64u * e + lane, C - 1u);
+      key[e] = ckey[j];
+      pos[e] = cpos[j];
+    }
+  }
+  __device__ __forceinline__ bool valid(int e) const {
+    return a0 + 64u * e + (threadIdx.x & 63) < a1;
+  }
+};
+
+// The row's k entries from the candidates of every wave's run: keys > kstar
+// are taken, and the first take_eq keys == kstar; slots past those get -1.
+// Each wave counts its run with ballots, one barrier exchanges the counts,
+// and each taken key's position goes to
+// #(earlier keys > kstar) + min(#(earlier keys == kstar), take_eq).
+template <int NT>
+__device__ __forceinline__ void emit_row_waves(const RowRun<NT>& run, uint32_t kstar,
+                                               uint32_t take_eq, int k, int32_t* __restrict__ out,
+                                               uint32_t* counts) {
+  constexpr int NW = NT / 64, E = RowRun<NT>::E;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  uint32_t ng = 0u, nq = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e >= run.ne) break;                     // uniform
+    const bool v = run.valid(e);
+    ng += (uint32_t)__popcll(__ballot(v && run.key[e] > kstar));
+    nq += (uint32_t)__popcll(__ballot(v && run.key[e] == kstar));
+  }
+  if (lane == 0) { counts[2 * wave] = ng; counts[2 * wave + 1] = nq; }
+  __syncthreads();
+  uint32_t gb = 0u, eb = 0u, gall = 0u, eall = 0u;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const uint32_t g = counts[2 * v], q = counts[2 * v + 1];
+    gb += v < wave ? g : 0u;
+    eb += v < wave ? q : 0u;
+    gall += g;
+    eall += q;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e >= run.ne) break;
+    const bool v = run.valid(e);
+    const bool g = v && run.key[e] > kstar, q = v && run.key[e] == kstar;
+    const uint64_t bg = __ballot(g), be = __ballot(q);
+    const uint32_t pg = __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
+    const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+    uint32_t o = 0xffffffffu;
+    if (g) o = gb + pg + min(eb + pe, take_eq);
+    else if (q && eb + pe < take_eq) o = gb + pg + eb + pe;
+    if (o < (uint32_t)k) out[o] = run.pos[e];
+    gb += (uint32_t)__popcll(bg);
+    eb += (uint32_t)__popcll(be);
+  }
+  const uint32_t written = min((uint32_t)k, gall + min(eall, take_eq));
+  for (uint32_t i = written + threadIdx.x; i < (uint32_t)k; i += NT) out[i] = -1;
+}
+
 // Steps 2 and 3 for one row per work-group.  The row's length, the slot
 // counts, thresholds and maxima and (for rows of up to kSpecSlots slots) the
 // first entries of every slot are loaded at once, so the gather costs one
@@ -306,18 +613,18 @@ __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
 #pragma unroll
     for (int u = 0; u < kSpecPer; ++u) sc[u] = ks.cand[sb + min((uint32_t)(my_lane + tps * u), cap - 1u)];
   }
-  // slot summaries of the first 64 slots, one per lane of wave 0
-  const int c0 = threadIdx.x;
-  uint32_t v0 = 0u, tv0 = 0u, mx0 = 0u;
-  if (c0 < 64 && c0 < ks.nslots) {
-    v0 = ks.counts[rbase + c0];
-    tv0 = ks.taus[rbase + c0];
-    mx0 = ks.maxes[rbase + c0];
-  }
+  // Slot summaries of the first 64 slots (lane c of every wave reads slot c;
+  // wave 0 uses them) and, for one token per request, the row's length: all
+  // issued with the preload, unconditionally, so the row costs one round trip.
+  const int c0 = min((int)threadIdx.x & 63, ks.nslots - 1);
+  const uint32_t v0 = ks.counts[rbase + c0];
+  const uint32_t tv0 = ks.taus[rbase + c0];
+  const uint32_t mx0 = ks.maxes[rbase + c0];
+  const int len_t = b.seq_lens[min(t, b.num_reqs - 1)];
   int r, n;
   if (ident) {                                  // one new token per request: token t is request t
     r = t;
-    n = min(max(b.seq_lens[t], 0), b.max_seq_len);
+    n = min(max(len_t, 0), b.max_seq_len);
   } else {
     const TokenPos tp = token_pos_wave(b, t);
     r = tp.r;
@@ -329,7 +636,8 @@ __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
     return;
   }
   const int nsl = min((n + ks.cap - 1) / ks.cap, ks.nslots);
-  for (int i = threadIdx.x; i < kBins1; i += NT) sm->hist[i] = 0u;   // for the select's first pass
+  for (int i = threadIdx.x; i < kBins1; i += NT) sm->hist[i] = 0u;   // counted during the gather
+  if (threadIdx.x == 0) sm->misc[3] = 0u;
   // slot offsets, T = the largest threshold, the largest key
   if (nsl <= 64) {
     if (threadIdx.x < 64) {
@@ -371,36 +679,74 @@ __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
   };
   bool decided = false;                         // step 2 settled the row
   if (C <= (uint32_t)kResCap) {
+    // The gather also counts the keys >= T in a histogram of up to 2048 bins
+    // of (key - T) >> shift, which spans [T, kmax].
+    const int width = kmax == T ? 0 : 32 - __clz(kmax - T);
+    const int shift = width > 11 ? width - 11 : 0;
+    auto put = [&](uint32_t i, uint2 e) {
+      sm->ckey[i] = e.x;
+      sm->cpos[i] = (int32_t)e.y;
+      if (e.x >= T) atomicAdd(&sm->hist[(e.x - T) >> shift], 1u);
+    };
     if (nsl <= nsp) {                           // every slot of the row was preloaded
       const uint32_t cnt = sm->pre[my_slot + 1] - sm->pre[my_slot], at0 = sm->pre[my_slot];
       if (my_ok && my_slot < nsl) {
 #pragma unroll
         for (int u = 0; u < kSpecPer; ++u) {
           const uint32_t j = (uint32_t)(my_lane + tps * u);
-          if (j < cnt) { sm->ckey[at0 + j] = sc[u].x; sm->cpos[at0 + j] = (int32_t)sc[u].y; }
+          if (j < cnt) put(at0 + j, sc[u]);
         }
         const size_t sb = (rbase + my_slot) * cap;   // entries beyond the preloaded ones
-        for (uint32_t j = (uint32_t)(my_lane + tps * kSpecPer); j < cnt; j += (uint32_t)tps) {
-          const uint2 e = ks.cand[sb + j];
-          sm->ckey[at0 + j] = e.x;
-          sm->cpos[at0 + j] = (int32_t)e.y;
-        }
+        for (uint32_t j = (uint32_t)(my_lane + tps * kSpecPer); j < cnt; j += (uint32_t)tps)
+          put(at0 + j, ks.cand[sb + j]);
       }
     } else {
-      for (uint32_t i = threadIdx.x; i < C; i += NT) {
-        const size_t a = at(i);
-        const uint2 e = ks.cand[a];
-        sm->ckey[i] = e.x;
-        sm->cpos[i] = (int32_t)e.y;
-      }
+      for (uint32_t i = threadIdx.x; i < C; i += NT) put(i, ks.cand[at(i)]);
     }
     __syncthreads();
-    uint32_t take, in_range;
-    const uint32_t kstar = select_kth_range<NT, false>(sm->ckey, C, (uint32_t)k, T, kmax, &take,
-                                                       sm->hist, sm->bucket, sm->scratch, &in_range);
+    RowRun<NT> run;                             // this wave's run of the candidates
+    run.load(sm->ckey, sm->cpos, C);
+    // Every wave finds the bin of the k-th largest key on its own.
+    uint32_t above, in_bin, in_range;
+    const uint32_t d = wave_digit(sm->hist, 1 << (width - shift), (uint32_t)k, &above, &in_bin,
+                                  &in_range);
     if (in_range >= (uint32_t)k) {              // at least k candidates at or above T
-      emit_ordered<NT>([&](uint32_t i) { return make_uint2(sm->ckey[i], (uint32_t)sm->cpos[i]); },
-                       C, kstar, take, k, out, sm->scratch);
+      const uint32_t need = (uint32_t)k - above;
+      const uint32_t base = T + (d << shift);
+      uint32_t kstar, take;
+      if (shift == 0) {                         // the bin is one key
+        kstar = base;
+        take = need;
+      } else if (in_bin <= 64u) {               // rank the bin's keys: collected, then per wave
+#pragma unroll
+        for (int e = 0; e < RowRun<NT>::E; ++e) {
+          if (e >= run.ne) break;
+          const uint32_t x = run.key[e];
+          if (run.valid(e) && x >= base && ((x - base) >> shift) == 0u) {
+            const uint32_t j = atomicAdd(&sm->misc[3], 1u);
+            if (j < 64u) sm->bucket[j] = x;
+          }
+        }
+        __syncthreads();
+        const int lane = threadIdx.x & 63;
+        const uint32_t x = (uint32_t)lane < in_bin ? sm->bucket[lane] : 0u;
+        uint32_t gt = 0u, ge = 0u;
+        for (int j = 0; j < (int)in_bin; ++j) {
+          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
+          gt += y > x;
+          ge += y >= x;
+        }
+        const int L = __ffsll((unsigned long long)__ballot((uint32_t)lane < in_bin && gt < need &&
+                                                           need <= ge)) - 1;
+        kstar = (uint32_t)__builtin_amdgcn_readlane((int)x, L);
+        take = need - (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
+      } else {                                  // a crowded bin: the general select within it
+        __syncthreads();                        // every wave has read the histogram
+        const uint32_t top = (uint32_t)min((uint64_t)kmax, (uint64_t)base + ((1ull << shift) - 1ull));
+        kstar = select_kth_range<NT>(sm->ckey, C, need, base, top, &take, sm->hist, sm->bucket,
+                                     sm->scratch);
+      }
+      emit_row_waves<NT>(run, kstar, take, k, out, sm->emit);
       decided = true;
     }
   } else {                                      // too many for LDS: select in place
@@ -443,16 +789,30 @@ __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
 
 }  // namespace
 
-bool keep_path(const BatchArgs& b, int64_t dec_tokens) {
+#ifndef IDX_KEEP_DYN
+#define IDX_KEEP_DYN 1
+#endif
+
+// Blocks per chunk of the fused path: the FP8 cache is scored by one
+// kDynWaves-wave work-group per CU (about one chunk per CU over the batch, 8
+// to kDynMaxBlocks blocks), the FP4 cache by decode_chunk_blocks' two per CU.
+static int keep_chunk_blocks(const BatchArgs& b, bool fp4) {
+  if (fp4 || !IDX_KEEP_DYN) return decode_chunk_blocks(b.max_seq_len, b.num_tokens);
+  const int64_t blocks_per_row = (b.max_seq_len + kBlock - 1) / kBlock;
+  const int64_t cb = (blocks_per_row * b.num_tokens + 255) / 256;
+  return (int)std::min<int64_t>(kDynMaxBlocks, std::max<int64_t>(8, cb));
+}
+
+bool keep_path(const BatchArgs& b, int64_t dec_tokens, bool fp4) {
   const bool decode_split = b.max_query_len <= 1 || dec_tokens >= b.num_tokens;
   if (!decode_split || !topk_uses_long_rows(b.num_tokens, b.max_seq_len)) return false;
-  const int cb = decode_chunk_blocks(b.max_seq_len, b.num_tokens);
+  const int cb = keep_chunk_blocks(b, fp4);
   const int64_t nslots = (b.max_seq_len + (int64_t)cb * kBlock - 1) / ((int64_t)cb * kBlock);
   return nslots <= kMaxSlots;
 }
 
-size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks) {
-  const int cb = decode_chunk_blocks(b.max_seq_len, b.num_tokens);
+size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks, bool fp4) {
+  const int cb = keep_chunk_blocks(b, fp4);
   const int64_t cap = (int64_t)cb * kBlock;
   const int64_t nslots = std::max<int64_t>(1, (b.max_seq_len + cap - 1) / cap);
   const size_t T = (size_t)b.num_tokens;
@@ -494,6 +854,18 @@ hipError_t launch_keep_candidates(const uint8_t* q8, const float* w, const Cache
     else if (fp4)
       IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_KEEP_RING, false>), grid,
                  dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+    else if (IDX_KEEP_DYN && kq != nullptr && ks.chunk_blocks <= 64)
+      IDX_LAUNCH("score_keep_kernel", (score_keep_dyn_kernel<IDX_DYN_RING, true, 64>), grid,
+                 dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+    else if (IDX_KEEP_DYN && kq != nullptr)
+      IDX_LAUNCH("score_keep_kernel", (score_keep_dyn_kernel<IDX_DYN_RING, true, kDynMaxBlocks>),
+                 grid, dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+    else if (IDX_KEEP_DYN && ks.chunk_blocks <= 64)
+      IDX_LAUNCH("score_keep_kernel", (score_keep_dyn_kernel<IDX_DYN_RING, false, 64>), grid,
+                 dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+    else if (IDX_KEEP_DYN)
+      IDX_LAUNCH("score_keep_kernel", (score_keep_dyn_kernel<IDX_DYN_RING, false, kDynMaxBlocks>),
+                 grid, dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
     else if (kq != nullptr)
       IDX_LAUNCH("score_keep_kernel", (score_keep_kernel<IDX_DECODE_RING, true>), grid,
                  dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);

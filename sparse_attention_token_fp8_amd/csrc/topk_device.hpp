@@ -89,10 +89,14 @@ __device__ __forceinline__ uint32_t wave_digit(const uint32_t* h, int nb, uint32
   const int active = nb >= 64 ? 64 : nb;
   uint32_t sum = 0u;
   if (lane < active) {
+    // all kBins1/64 reads unconditional (indices wrap inside the lane's bins),
+    // so they are issued together whatever `per` is
     const uint32_t* hb = h + nb - per * (lane + 1);
+    uint32_t v[kBins1 / 64];
 #pragma unroll
-    for (int i = 0; i < kBins1 / 64; ++i)
-      if (i < per) sum += hb[(i + lane) & (per - 1)];
+    for (int i = 0; i < kBins1 / 64; ++i) v[i] = hb[(i + lane) & (per - 1)];
+#pragma unroll
+    for (int i = 0; i < kBins1 / 64; ++i) sum += i < per ? v[i] : 0u;
   }
   const uint32_t incl = wave_sum_incl(sum);
   const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);

@@ -476,6 +476,45 @@ def test_fused_rescore_fallback(env):
     assert np.array_equal(dev["cache"].tensor.cpu().numpy(), orc["cache"])
 
 
+def test_fused_resolve_coarse_scores(env):
+    """K rows repeat a few patterns, so each row's scores take few distinct
+    values and the k-th largest is shared by hundreds of positions: with 40
+    patterns the bin of the k-th largest candidate is crowded (more than 64
+    keys) and is narrowed further; with 2 the candidates at or above the
+    largest chunk threshold can all be one key.  Fused equals idx_logits +
+    idx_topk and the oracle's tie band (lowest positions among equals)."""
+    import synth.gen as sg
+    m, torch = env
+
+    def coarse(P):
+        class Coarse(sg.Workload):
+            def request_k(self, layer, r):
+                kb = super().request_k(layer, r)
+                idx = (np.arange(kb.shape[0]) * 7919 + 13) % P
+                return kb[:P][idx].copy()
+        return Coarse
+
+    for P in (40, 2):
+        base = random_batch(4011 + P, [20000, 9000, 30000], 1, k=2048)
+        wl = coarse(P)(base.name, base.seed, base.seq_lens, base.new_tokens, base.block_table,
+                       base.num_blocks, base.k)
+        say("coarse scores", P, wl.seq_lens.tolist())
+        dev = device_layer(m, torch, wl, 0, with_new=True)
+        orc = oracle_layer(wl, 0)
+        batch = device_batch(m, wl)
+        lg = m.idx_logits(dev["q8"], dev["w"], dev["cache"], batch)
+        a = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+        b = m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], batch, wl.k).cpu().numpy()
+        assert np.array_equal(a, b), f"P={P}"
+        lgn = lg.cpu().numpy()
+        for t in range(wl.num_tokens):
+            n = int(wl.seq_lens[t])
+            assert len(np.unique(lgn[t, :n])) <= P + 1, "scores should take few values"
+        want = oracle.logits.logits(orc["q8"], orc["w"], orc["cache"], oracle_batch(wl))
+        for t, sc in want.items():
+            check_topk_band(b[t], sc, wl.k, f"P={P} token {t}")
+
+
 def test_kernel_trace_names_the_step_kernels(env):
     """idx_trace_begin brackets every kernel of the traced calls with the
     caller's events: a decode F layer over long rows runs the fused scoring

@@ -49,12 +49,14 @@ def test_topk_longest_rows(env):
         assert np.array_equal(got[t], want), f"row {t} n={n}"
 
 
-def test_score_topk_long_row_past_preload(env):
-    """The fused path on one request of 300 000 positions (147 slots of 2048,
-    gathered after the counts) and one of 70 000: equal to idx_logits +
-    idx_topk (74 and 18 slots of 4096) and within the oracle's tie band."""
+@pytest.mark.parametrize("lengths", [[300_000], [300_000, 70_000]])
+def test_score_topk_long_row_past_preload(env, lengths):
+    """The fused path on one request of 300 000 positions alone (chunks of 19
+    blocks: 247 slots, more than the resolve preloads, gathered after the
+    counts) and beside one of 70 000 (127 and 30 slots of 37 blocks): equal to
+    idx_logits + idx_topk and within the oracle's tie band."""
     m, torch = env
-    wl = random_batch(3102, [300_000, 70_000], 1, k=2048)
+    wl = random_batch(3102, lengths, 1, k=2048)
     say("fused long rows", wl.seq_lens.tolist())
     dev = device_layer(m, torch, wl, 0, with_new=True)
     batch = device_batch(m, wl)
