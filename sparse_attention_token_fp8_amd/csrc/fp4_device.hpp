@@ -123,6 +123,68 @@ __device__ __forceinline__ void fp4_emit(float* __restrict__ out, float* __restr
 // the scores go to `kept` (LDS) with their key histogram and largest key, as
 // decode_body does for the fused path.  Returns the token's causal count, or
 // -1 when the chunk holds none of its positions.
+// A new K row quantised as the cache stores it, for this lane's group
+// G = lane / 16 (dims 32G .. 32G+31 at kr): its 32 E2M1 codes, low nibble
+// first, and the group's exponent e (scale byte e + 127).
+__device__ __forceinline__ uint4 fp4_quant_group(const uint16_t* __restrict__ kr, int* e_out) {
+  uint32_t x[16];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const uint2 p2 = *reinterpret_cast<const uint2*>(kr + 4 * v);
+    x[2 * v] = p2.x;
+    x[2 * v + 1] = p2.y;
+  }
+  uint32_t am = 0u;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) am = max(am, max(x[v] & 0x7FFFu, (x[v] >> 16) & 0x7FFFu));
+  const int e = fp4_exponent(am);
+  const float sc = pow2f(-e);
+  uint32_t c[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    c[d] = 0u;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t wv = x[4 * d + m];
+      c[d] |= encode_e2m1(wv & 0xFFFFu, sc) << (8 * m);
+      c[d] |= encode_e2m1(wv >> 16, sc) << (8 * m + 4);
+    }
+  }
+  *e_out = e;
+  return make_uint4(c[0], c[1], c[2], c[3]);
+}
+
+// Row `slot` of the FP4 cache from each group's codes and exponent (lane
+// 16G writes group G).
+__device__ __forceinline__ void fp4_write_row(uint8_t* cache, int64_t slot, uint4 code, int e,
+                                              int lane) {
+  uint8_t* cb = cache + (slot / kBlock) * kFp4BlockBytes;
+  const int p = (int)(slot % kBlock), G = lane >> 4;
+  if ((lane & 15) == 0) {
+    *reinterpret_cast<uint4*>(cb + G * kFp4Plane + p * 16) = code;
+    cb[kFp4CodeBytes + G * 64 + (p & 15) * 4 + (p >> 4)] = (uint8_t)(e + 127);
+  }
+}
+
+// The staged block's row r (lane (r % 16) of each group holds it) replaced by
+// a new row's codes and exponent byte.
+__device__ __forceinline__ void fp4_patch_row(KBlock4& kb, int r, uint4 code, uint32_t ebyte,
+                                              int lane) {
+  const int tl = r >> 4;
+  const bool mine = (lane & 15) == (r & 15);
+  // element-wise selects: an index into kb.b would put the block in scratch
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bool put = mine && q == tl;
+    kb.b[q].x = put ? code.x : kb.b[q].x;
+    kb.b[q].y = put ? code.y : kb.b[q].y;
+    kb.b[q].z = put ? code.z : kb.b[q].z;
+    kb.b[q].w = put ? code.w : kb.b[q].w;
+  }
+  const uint32_t mask = 0xFFu << (8 * tl);
+  kb.sc = mine ? (kb.sc & ~mask) | (ebyte << (8 * tl)) : kb.sc;
+}
+
 template <int NB, bool FK = false, bool KEEP = false>
 __device__ __forceinline__ int fp4_decode_body(int bx, int t, const uint8_t* __restrict__ q8,
                                                const float* __restrict__ w, const CacheArgs& cache,
@@ -182,43 +244,14 @@ __device__ __forceinline__ int fp4_decode_body(int bx, int t, const uint8_t* __r
       if (i < nfix) {
         const int P = lo + i;
         const int row = tp.q0 + (P - newlo);
-        const uint16_t* kr = nk.k + (int64_t)row * nk.stride + 32 * G;
-        uint32_t x[16];
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const uint2 p2 = *reinterpret_cast<const uint2*>(kr + 4 * v);
-          x[2 * v] = p2.x;
-          x[2 * v + 1] = p2.y;
-        }
-        uint32_t am = 0u;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) am = max(am, max(x[v] & 0x7FFFu, (x[v] >> 16) & 0x7FFFu));
-        const int e = fp4_exponent(am);
-        const float sc = pow2f(-e);
-        uint32_t c[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          c[d] = 0u;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint32_t wv = x[4 * d + m];
-            c[d] |= encode_e2m1(wv & 0xFFFFu, sc) << (8 * m);
-            c[d] |= encode_e2m1(wv >> 16, sc) << (8 * m + 4);
-          }
-        }
-        fcode[i] = make_uint4(c[0], c[1], c[2], c[3]);
+        int e;
+        fcode[i] = fp4_quant_group(nk.k + (int64_t)row * nk.stride + 32 * G, &e);
         const int64_t want = nk.slots[row];
         const int pb = __builtin_amdgcn_readlane(pbl, P / kBlock - blk(0));
         const bool patch = pb >= 0 && want == (int64_t)pb * kBlock + P % kBlock;
         if (patch) fexp[i] = (uint32_t)(e + 127);
-        if (row == t && want >= 0 && want < nk.num_slots) {   // the token's own row: to the cache
-          uint8_t* cb = nk.cache + (want / kBlock) * kFp4BlockBytes;
-          const int p = (int)(want % kBlock);
-          if ((lane & 15) == 0) {
-            *reinterpret_cast<uint4*>(cb + G * kFp4Plane + p * 16) = fcode[i];
-            cb[kFp4CodeBytes + G * 64 + (p & 15) * 4 + (p >> 4)] = (uint8_t)(e + 127);
-          }
-        }
+        if (row == t && want >= 0 && want < nk.num_slots)   // the token's own row: to the cache
+          fp4_write_row(nk.cache, want, fcode[i], e, lane);
       }
     }
   }
@@ -240,15 +273,8 @@ __device__ __forceinline__ int fp4_decode_body(int bx, int t, const uint8_t* __r
 #pragma unroll
         for (int i = 0; i < kMaxFusedRows; ++i) {
           const int P = fpos0 + i;
-          if (i < nfix && fexp[i] != 0xFFFFFFFFu && P / kBlock == blk(j)) {
-            const int r = P % kBlock, tl = r >> 4;
-            if ((lane & 15) == (r & 15)) {
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (q == tl) kb.b[q] = fcode[i];
-              kb.sc = (kb.sc & ~(0xFFu << (8 * tl))) | (fexp[i] << (8 * tl));
-            }
-          }
+          if (i < nfix && fexp[i] != 0xFFFFFFFFu && P / kBlock == blk(j))
+            fp4_patch_row(kb, P % kBlock, fcode[i], fexp[i], lane);
         }
       }
       float v;

@@ -42,6 +42,7 @@
 #endif
 
 #include <algorithm>
+#include <type_traits>
 
 namespace idx {
 namespace {
@@ -235,7 +236,10 @@ constexpr int kDynMaxBlocks = 128;              // a chunk's blocks: two block i
 // rows, the wave that scores a row's block patches it into its staged copy,
 // and wave 0 writes the token's own row to the cache.  Returns the token's
 // causal count n, or -1 when the chunk holds none of its positions.
-template <int NB, bool FK>
+// FP4: the cache is the FP4 one, its blocks loaded straight into the MFMA
+// layout as fp4_decode_body does (`lds`: kLinScratch per wave); else each
+// block passes through the wave's LDS slot (`lds`: kBlockBytes per wave).
+template <int NB, bool FK, bool FP4>
 __device__ __forceinline__ int dyn_body(int cx, int t, const uint8_t* __restrict__ q8,
                                         const float* __restrict__ w, const CacheArgs& cache,
                                         const BatchArgs& b, int chunk_blocks, bool ident,
@@ -300,20 +304,25 @@ __device__ __forceinline__ int dyn_body(int cx, int t, const uint8_t* __restrict
   auto pblock = [&](int j) {                    // j uniform, < kDynMaxBlocks
     return __builtin_amdgcn_readlane(j < 64 ? pbl[0] : pbl[1], j & 63);
   };
+  using Ring = std::conditional_t<FP4, KBlock4, WaveStage>;
   // block j of the chunk (uniform); from nblk on it loads nothing
-  auto stage = [&](WaveStage& st, int j) {
+  auto stage = [&](Ring& st, int j) {
     const int pb = pblock(min(j, kDynMaxBlocks - 1));
-    wave_stage_load(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes,
-                    (j < nblk && pb >= 0) ? kBlockBytes : 0, lane);
+    if constexpr (FP4)
+      fp4_block_load<kLoadStream>(st, cache.data + (int64_t)max(pb, 0) * kFp4BlockBytes,
+                                  (j < nblk && pb >= 0) ? kFp4BlockBytes : 0, lane);
+    else
+      wave_stage_load(st, cache.data + (int64_t)max(pb, 0) * kBlockBytes,
+                      (j < nblk && pb >= 0) ? kBlockBytes : 0, lane);
   };
   auto grab = [&]() {
     uint32_t j = 0u;
     if (lane == 0) j = atomicAdd(next, 1u);
     return __builtin_amdgcn_readfirstlane((int)j);
   };
-  uint8_t* slot = lds + wave * kBlockBytes;
+  uint8_t* slot = lds + wave * (FP4 ? kLinScratch : kBlockBytes);
   int jr[NB];                                   // the block each ring entry holds
-  WaveStage ring[NB];
+  Ring ring[NB];
 #pragma unroll
   for (int u = 0; u < NB - 1; ++u) {
     jr[u] = wave + u * kDynWaves;
@@ -322,7 +331,11 @@ __device__ __forceinline__ int dyn_body(int cx, int t, const uint8_t* __restrict
   LinFrag lf;
   make_lin<1>(lf, f, slot, lane);
 
+  // FP8: a row is 32 lanes' 4-byte codes and a 4-byte scale (all ones: leave
+  // the row as the cache has it); FP4: each group's 16 code bytes and its
+  // exponent byte (all ones: leave it).
   uint32_t fcode[kMaxFusedRows];
+  uint4 fcode4[kMaxFusedRows];
   uint32_t fscale[kMaxFusedRows];
   int fpos0 = 0, nfix = 0;
   if (FK) {                                     // the chunk's new rows, as decode_body
@@ -334,23 +347,32 @@ __device__ __forceinline__ int dyn_body(int cx, int t, const uint8_t* __restrict
 #pragma unroll
     for (int i = 0; i < kMaxFusedRows; ++i) {
       fcode[i] = 0u;
-      fscale[i] = 0u;
+      fcode4[i] = make_uint4(0u, 0u, 0u, 0u);
+      fscale[i] = 0xFFFFFFFFu;
       if (i < nfix) {
         const int P = lo + i;
         const int row = tp.q0 + (P - newlo);
-        const uint2 v = *reinterpret_cast<const uint2*>(nk.k + (int64_t)row * nk.stride + (lane & 31) * 4);
         const int64_t want = nk.slots[row];
-        int e;
-        const uint32_t code = quant_row_lane(v, &e);
-        const uint32_t sc = __float_as_uint(pow2f(e));
         const int pb = pblock(P / kBlock - lb0);
         const bool patch = pb >= 0 && want == (int64_t)pb * kBlock + P % kBlock;
-        fcode[i] = code;
-        fscale[i] = patch ? sc : 0xFFFFFFFFu;   // all ones: leave the row as the cache has it
-        if (wave == 0 && row == t && want >= 0 && want < nk.num_slots) {
-          uint8_t* cb = nk.cache + (want / kBlock) * kBlockBytes;
-          if (lane < 32) *reinterpret_cast<uint32_t*>(cb + (want % kBlock) * kHeadDim + lane * 4) = code;
-          if (lane == 0) *reinterpret_cast<uint32_t*>(cb + kCodeBytes + (want % kBlock) * 4) = sc;
+        const bool own = wave == 0 && row == t && want >= 0 && want < nk.num_slots;
+        if constexpr (FP4) {
+          int e;
+          fcode4[i] = fp4_quant_group(nk.k + (int64_t)row * nk.stride + 32 * (lane >> 4), &e);
+          if (patch) fscale[i] = (uint32_t)(e + 127);
+          if (own) fp4_write_row(nk.cache, want, fcode4[i], e, lane);
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(nk.k + (int64_t)row * nk.stride + (lane & 31) * 4);
+          int e;
+          const uint32_t code = quant_row_lane(v, &e);
+          const uint32_t sc = __float_as_uint(pow2f(e));
+          fcode[i] = code;
+          if (patch) fscale[i] = sc;
+          if (own) {
+            uint8_t* cb = nk.cache + (want / kBlock) * kBlockBytes;
+            if (lane < 32) *reinterpret_cast<uint32_t*>(cb + (want % kBlock) * kHeadDim + lane * 4) = code;
+            if (lane == 0) *reinterpret_cast<uint32_t*>(cb + kCodeBytes + (want % kBlock) * 4) = sc;
+          }
         }
       }
     }
@@ -371,26 +393,39 @@ __device__ __forceinline__ int dyn_body(int cx, int t, const uint8_t* __restrict
         keep_max();
         return n;
       }
-      wave_stage_store(ring[u], slot, lane);
-      if (FK) {
+      float v;
+      if constexpr (FP4) {
+        KBlock4& kb = ring[u];
+        if (FK) {
 #pragma unroll
-        for (int i = 0; i < kMaxFusedRows; ++i) {
-          const int P = fpos0 + i;
-          if (i < nfix && fscale[i] != 0xFFFFFFFFu && P / kBlock == lb0 + j) {
-            const int rr = P % kBlock;
-            if (lane < 32)
-              *reinterpret_cast<uint32_t*>(slot + rr * kHeadDim + (((lane >> 2) ^ (rr & 7)) << 4) +
-                                           (lane & 3) * 4) = fcode[i];
-            if (lane == 0) *reinterpret_cast<uint32_t*>(slot + kCodeBytes + rr * 4) = fscale[i];
+          for (int i = 0; i < kMaxFusedRows; ++i) {
+            const int P = fpos0 + i;
+            if (i < nfix && fscale[i] != 0xFFFFFFFFu && P / kBlock == lb0 + j)
+              fp4_patch_row(kb, P % kBlock, fcode4[i], fscale[i], lane);
           }
         }
+        fp4_block_scores<1>(f, lf, kb, &v);
+      } else {
+        wave_stage_store(ring[u], slot, lane);
+        if (FK) {
+#pragma unroll
+          for (int i = 0; i < kMaxFusedRows; ++i) {
+            const int P = fpos0 + i;
+            if (i < nfix && fscale[i] != 0xFFFFFFFFu && P / kBlock == lb0 + j) {
+              const int rr = P % kBlock;
+              if (lane < 32)
+                *reinterpret_cast<uint32_t*>(slot + rr * kHeadDim + (((lane >> 2) ^ (rr & 7)) << 4) +
+                                             (lane & 3) * 4) = fcode[i];
+              if (lane == 0) *reinterpret_cast<uint32_t*>(slot + kCodeBytes + rr * 4) = fscale[i];
+            }
+          }
+        }
+        wave_sync_lds();
+        KBlock kb;
+        lds_kblock(kb, slot, lane);
+        wave_sync_lds();                        // reads done before the slot is rewritten
+        block_scores<1>(f, lf, kb, &v);
       }
-      wave_sync_lds();
-      KBlock kb;
-      lds_kblock(kb, slot, lane);
-      wave_sync_lds();                          // reads done before the slot is rewritten
-      float v;
-      block_scores<1>(f, lf, kb, &v);
       emit(j, v);
     }
   }
@@ -400,13 +435,13 @@ __device__ __forceinline__ int dyn_body(int cx, int t, const uint8_t* __restrict
 #define IDX_DYN_RING 2
 #endif
 // MAXB: the largest chunk it takes (64 or kDynMaxBlocks blocks), which sizes
-// `kept` and the filter's registers.
-template <int NB, bool FK, int MAXB>
+// `kept` and the filter's registers.  FP4: the FP4 cache.
+template <int NB, bool FK, int MAXB, bool FP4>
 __global__ __launch_bounds__(kDynThreads) void score_keep_dyn_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     int chunk_blocks, int ident, NewRows nk, int k, KeepSlots ks) {
   static_assert(MAXB <= kDynMaxBlocks, "two block ids per lane");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kDynWaves * kBlockBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDynWaves * (FP4 ? kLinScratch : kBlockBytes)];
   __shared__ float kept[MAXB * kBlock];
   __shared__ __attribute__((aligned(16))) uint32_t hist[kTauBins];
   __shared__ __attribute__((aligned(16))) uint32_t hist2[kTau2Bins];
@@ -423,8 +458,8 @@ __global__ __launch_bounds__(kDynThreads) void score_keep_dyn_kernel(
   __syncthreads();
   int cx, ry;
   xcd_spread(&cx, &ry);
-  const int n = dyn_body<NB, FK>(cx, ry, q8, w, cache, b, chunk_blocks, ident != 0, lds, nk, kept,
-                                 hist, table, &next);
+  const int n = dyn_body<NB, FK, FP4>(cx, ry, q8, w, cache, b, chunk_blocks, ident != 0, lds, nk,
+                                      kept, hist, table, &next);
   if (n <= k) return;                           // nothing here, or a row the resolve takes whole
   __syncthreads();                              // every wave's scores are in `kept`
   chunk_filter<kDynThreads, MAXB * kBlock>(kept, ry, cx, chunk_blocks, n, k, ks, hist, hist2, table);
@@ -792,12 +827,19 @@ __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
 #ifndef IDX_KEEP_DYN
 #define IDX_KEEP_DYN 1
 #endif
+#ifndef IDX_KEEP_DYN_FP4
+#define IDX_KEEP_DYN_FP4 1
+#endif
 
-// Blocks per chunk of the fused path: the FP8 cache is scored by one
-// kDynWaves-wave work-group per CU (about one chunk per CU over the batch, 8
-// to kDynMaxBlocks blocks), the FP4 cache by decode_chunk_blocks' two per CU.
+// Whether the fused path scores with one kDynWaves-wave work-group per CU
+// (score_keep_dyn_kernel) rather than two four-wave ones.
+static bool keep_dyn(bool fp4) { return fp4 ? IDX_KEEP_DYN_FP4 : IDX_KEEP_DYN; }
+
+// Blocks per chunk of the fused path: about one chunk per CU over the batch,
+// 8 to kDynMaxBlocks blocks, for the one-per-CU kernel; decode_chunk_blocks'
+// two per CU otherwise.
 static int keep_chunk_blocks(const BatchArgs& b, bool fp4) {
-  if (fp4 || !IDX_KEEP_DYN) return decode_chunk_blocks(b.max_seq_len, b.num_tokens);
+  if (!keep_dyn(fp4)) return decode_chunk_blocks(b.max_seq_len, b.num_tokens);
   const int64_t blocks_per_row = (b.max_seq_len + kBlock - 1) / kBlock;
   const int64_t cb = (blocks_per_row * b.num_tokens + 255) / 256;
   return (int)std::min<int64_t>(kDynMaxBlocks, std::max<int64_t>(8, cb));
@@ -838,6 +880,27 @@ size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks, bool
   return off;
 }
 
+template <bool FP4>
+hipError_t launch_keep_dyn(const dim3& grid, const uint8_t* q8, const float* w,
+                           const CacheArgs& cache, const BatchArgs& b, int ident, const NewRows& nk,
+                           bool fk, int k, const KeepSlots& ks, hipStream_t stream) {
+  const bool big = ks.chunk_blocks > 64;
+  const char* name = FP4 ? "score_keep_fp4_kernel" : "score_keep_kernel";   // the step's trace names
+  if (fk && !big)
+    IDX_LAUNCH(name, (score_keep_dyn_kernel<IDX_DYN_RING, true, 64, FP4>), grid,
+               dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+  else if (fk)
+    IDX_LAUNCH(name, (score_keep_dyn_kernel<IDX_DYN_RING, true, kDynMaxBlocks, FP4>),
+               grid, dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+  else if (!big)
+    IDX_LAUNCH(name, (score_keep_dyn_kernel<IDX_DYN_RING, false, 64, FP4>), grid,
+               dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+  else
+    IDX_LAUNCH(name, (score_keep_dyn_kernel<IDX_DYN_RING, false, kDynMaxBlocks, FP4>),
+               grid, dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
+  return hipGetLastError();
+}
+
 hipError_t launch_keep_candidates(const uint8_t* q8, const float* w, const CacheArgs& cache,
                                   const BatchArgs& b, const uint16_t* kq, int64_t kq_stride,
                                   const int64_t* slots, uint8_t* cache_w, int k,
@@ -848,24 +911,15 @@ hipError_t launch_keep_candidates(const uint8_t* q8, const float* w, const Cache
     const dim3 grid((unsigned)ks.nslots, (unsigned)b.num_tokens);
     const NewRows nk = kq != nullptr ? NewRows{kq, kq_stride, slots, cache_w, cache.num_blocks * kBlock}
                                      : NewRows{};
+    if (keep_dyn(fp4))
+      return fp4 ? launch_keep_dyn<true>(grid, q8, w, cache, b, ident, nk, kq != nullptr, k, ks, stream)
+                 : launch_keep_dyn<false>(grid, q8, w, cache, b, ident, nk, kq != nullptr, k, ks, stream);
     if (fp4 && kq != nullptr)
       IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_KEEP_RING, true>), grid,
                  dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
     else if (fp4)
       IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_KEEP_RING, false>), grid,
                  dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
-    else if (IDX_KEEP_DYN && kq != nullptr && ks.chunk_blocks <= 64)
-      IDX_LAUNCH("score_keep_kernel", (score_keep_dyn_kernel<IDX_DYN_RING, true, 64>), grid,
-                 dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
-    else if (IDX_KEEP_DYN && kq != nullptr)
-      IDX_LAUNCH("score_keep_kernel", (score_keep_dyn_kernel<IDX_DYN_RING, true, kDynMaxBlocks>),
-                 grid, dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
-    else if (IDX_KEEP_DYN && ks.chunk_blocks <= 64)
-      IDX_LAUNCH("score_keep_kernel", (score_keep_dyn_kernel<IDX_DYN_RING, false, 64>), grid,
-                 dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
-    else if (IDX_KEEP_DYN)
-      IDX_LAUNCH("score_keep_kernel", (score_keep_dyn_kernel<IDX_DYN_RING, false, kDynMaxBlocks>),
-                 grid, dim3(kDynThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
     else if (kq != nullptr)
       IDX_LAUNCH("score_keep_kernel", (score_keep_kernel<IDX_DECODE_RING, true>), grid,
                  dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
