@@ -45,14 +45,40 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
+# Scratch memory a kernel may use per lane: a few spilled registers outside
+# its loops (the prefill scoring kernel holds 256 VGPRs and spills two before
+# its block loop); more means a register array was put in memory.
+SCRATCH_LIMIT = 16
+
+
+def _scratch_kernels(remarks):
+    """Kernels whose resource-usage remarks report more than SCRATCH_LIMIT
+    bytes of scratch memory per lane."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in line:
+            n = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if n > SCRATCH_LIMIT and name is not None:
+                bad.append(f"{name} ({n} bytes/lane)")
+    return bad
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []),
+           "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{r.stderr}")
+    # every kernel keeps its state in registers and LDS: scratch memory in a
+    # hot loop costs more than the kernel's whole K stream
+    bad = _scratch_kernels(r.stderr)
+    if bad:
+        raise RuntimeError(f"{os.path.basename(src)}: kernels using scratch memory: " + ", ".join(bad))
     return obj
 
 
