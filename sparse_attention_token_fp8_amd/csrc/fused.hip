@@ -484,7 +484,7 @@ struct ResolveLds {
   uint32_t bucket[64];
   uint32_t scratch[scratch_words<kResThreads>()];
   uint32_t emit[2 * (kResThreads / 64)];        // per-wave counts of the row's writer
-  uint32_t misc[4];                             // T, largest key, in-place count, bucket fill
+  uint32_t misc[4];                             // T, largest key, in-place count or K*, bucket fill or take
 };
 struct RescoreLds {
   uint8_t stage[kRescoreWaves][kBlockBytes];
@@ -741,10 +741,12 @@ __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
     __syncthreads();
     RowRun<NT> run;                             // this wave's run of the candidates
     run.load(sm->ckey, sm->cpos, C);
-    // Every wave finds the bin of the k-th largest key on its own.
+    // The bin of the k-th largest key: wave 0 finds it and passes it on (with
+    // 16 waves per CU, every wave searching on its own costs more issue time
+    // than the barrier).
     uint32_t above, in_bin, in_range;
-    const uint32_t d = wave_digit(sm->hist, 1 << (width - shift), (uint32_t)k, &above, &in_bin,
-                                  &in_range);
+    const uint32_t d = block_digit<NT>(sm->hist, 1 << (width - shift), (uint32_t)k, &above, &in_bin,
+                                       &in_range, sm->scratch + NT / 64);
     if (in_range >= (uint32_t)k) {              // at least k candidates at or above T
       const uint32_t need = (uint32_t)k - above;
       const uint32_t base = T + (d << shift);
@@ -752,7 +754,7 @@ __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
       if (shift == 0) {                         // the bin is one key
         kstar = base;
         take = need;
-      } else if (in_bin <= 64u) {               // rank the bin's keys: collected, then per wave
+      } else if (in_bin <= 64u) {               // rank the bin's keys: collected, then by wave 0
 #pragma unroll
         for (int e = 0; e < RowRun<NT>::E; ++e) {
           if (e >= run.ne) break;
@@ -763,18 +765,25 @@ __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
           }
         }
         __syncthreads();
-        const int lane = threadIdx.x & 63;
-        const uint32_t x = (uint32_t)lane < in_bin ? sm->bucket[lane] : 0u;
-        uint32_t gt = 0u, ge = 0u;
-        for (int j = 0; j < (int)in_bin; ++j) {
-          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
-          gt += y > x;
-          ge += y >= x;
+        if (threadIdx.x < 64) {
+          const int lane = threadIdx.x;
+          const uint32_t x = (uint32_t)lane < in_bin ? sm->bucket[lane] : 0u;
+          uint32_t gt = 0u, ge = 0u;
+          for (int j = 0; j < (int)in_bin; ++j) {
+            const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
+            gt += y > x;
+            ge += y >= x;
+          }
+          const int L = __ffsll((unsigned long long)__ballot((uint32_t)lane < in_bin && gt < need &&
+                                                             need <= ge)) - 1;
+          if (lane == 0) {
+            sm->misc[2] = (uint32_t)__builtin_amdgcn_readlane((int)x, L);
+            sm->misc[3] = need - (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
+          }
         }
-        const int L = __ffsll((unsigned long long)__ballot((uint32_t)lane < in_bin && gt < need &&
-                                                           need <= ge)) - 1;
-        kstar = (uint32_t)__builtin_amdgcn_readlane((int)x, L);
-        take = need - (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
+        __syncthreads();
+        kstar = sm->misc[2];
+        take = sm->misc[3];
       } else {                                  // a crowded bin: the general select within it
         __syncthreads();                        // every wave has read the histogram
         const uint32_t top = (uint32_t)min((uint64_t)kmax, (uint64_t)base + ((1ull << shift) - 1ull));
