@@ -69,8 +69,8 @@ FP4_SUFFIX = "-fp4"
 STACK = "stack-16L-32x64k"
 # sources whose code the dominant kernels are built from (for the traffic digest)
 KERNEL_SOURCES = {
-    "score_keep_kernel": ("fused.hip", "score_device.hpp", "topk_device.hpp", "common.hpp",
-                          "quant_device.hpp"),
+    "score_keep_kernel": ("fused.hip", "score_device.hpp", "fp4_device.hpp", "topk_device.hpp",
+                          "common.hpp", "quant_device.hpp"),
     "score_prefill_kernel": ("score.hip", "score_device.hpp", "common.hpp", "quant_device.hpp"),
     "score_fp4_decode_kernel": ("fp4.hip", "fp4_device.hpp", "score_device.hpp", "common.hpp",
                                 "quant_device.hpp"),

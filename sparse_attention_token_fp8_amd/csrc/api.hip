@@ -108,7 +108,7 @@ hipError_t keep_candidates(const uint8_t* q_fp8, const float* w, const idx_kcach
                            hipStream_t stream, bool fp4 = false) {
   const BatchArgs b = to_args(batch);
   KeepSlots ks;
-  keep_workspace_layout(b, workspace, &ks, fp4);
+  keep_workspace_layout(b, workspace, &ks);
   const bool fk = kq != nullptr && score_writes_k(b, batch->num_decode_tokens);
   if (kq != nullptr && !fk) {
     const int64_t ns = cache.num_blocks * kBlock;
@@ -371,8 +371,8 @@ idx_status_t idx_logits_fp4(const uint8_t* q_fp8, const float* w, int32_t n_head
 size_t idx_score_topk_fp4_workspace_size(const idx_batch_t* batch, int32_t k) {
   if (batch == nullptr || batch->num_tokens <= 0 || k < 1) return 0;
   if (check_batch(batch) != IDX_OK) return 0;
-  if (keep_path(to_args(batch), batch->num_decode_tokens, true))
-    return keep_workspace_layout(to_args(batch), nullptr, nullptr, true);
+  if (keep_path(to_args(batch), batch->num_decode_tokens))
+    return keep_workspace_layout(to_args(batch), nullptr, nullptr);
   return fused_workspace(batch, nullptr, nullptr);
 }
 
@@ -390,12 +390,12 @@ hipError_t score_topk_fp4(const uint8_t* q_fp8, const float* w, const idx_kcache
                           const int64_t* slots, hipStream_t stream) {
   const BatchArgs b = to_args(batch);
   const CacheArgs c{cache.data, cache.num_blocks};
-  if (keep_path(b, batch->num_decode_tokens, true)) {
+  if (keep_path(b, batch->num_decode_tokens)) {
     hipError_t e = keep_candidates(q_fp8, w, cache, batch, k, workspace, kq, kq_stride, slots,
                                    stream, true);
     if (e != hipSuccess) return e;
     KeepSlots ks;
-    keep_workspace_layout(b, workspace, &ks, true);
+    keep_workspace_layout(b, workspace, &ks);
     return launch_keep_select(q_fp8, w, c, b, k, ks, topk, topk_stride, stream, true);
   }
   hipError_t e = hipSuccess;
@@ -505,13 +505,13 @@ idx_status_t score_candidates(bool fp4, const uint8_t* q_fp8, const float* w, in
   if (s != IDX_OK) return s;
   if (k < 1 || k > kMaxK) return IDX_ERR_UNSUPPORTED;
   if (batch->num_tokens == 0) return IDX_OK;
-  if (!keep_path(to_args(batch), batch->num_decode_tokens, fp4)) return IDX_ERR_UNSUPPORTED;
+  if (!keep_path(to_args(batch), batch->num_decode_tokens)) return IDX_ERR_UNSUPPORTED;
   if (k_bf16 != nullptr) {
     s = check_k_rows(k_bf16, k_row_stride, slot_mapping, cache, batch->num_tokens);
     if (s != IDX_OK) return s;
   }
   if (workspace == nullptr ||
-      workspace_bytes < keep_workspace_layout(to_args(batch), nullptr, nullptr, fp4) ||
+      workspace_bytes < keep_workspace_layout(to_args(batch), nullptr, nullptr) ||
       !aligned(workspace, 256))
     return IDX_ERR_WORKSPACE;
   return launched(keep_candidates(q_fp8, w, cache, batch, k, workspace, k_bf16, k_row_stride,
@@ -528,13 +528,13 @@ idx_status_t select_candidates(bool fp4, const uint8_t* q_fp8, const float* w, i
   s = check_k(k, topk_stride, topk, batch->num_tokens);
   if (s != IDX_OK) return s;
   if (batch->num_tokens == 0) return IDX_OK;
-  if (!keep_path(to_args(batch), batch->num_decode_tokens, fp4)) return IDX_ERR_UNSUPPORTED;
+  if (!keep_path(to_args(batch), batch->num_decode_tokens)) return IDX_ERR_UNSUPPORTED;
   if (workspace == nullptr ||
-      workspace_bytes < keep_workspace_layout(to_args(batch), nullptr, nullptr, fp4) ||
+      workspace_bytes < keep_workspace_layout(to_args(batch), nullptr, nullptr) ||
       !aligned(workspace, 256))
     return IDX_ERR_WORKSPACE;
   KeepSlots ks;
-  keep_workspace_layout(to_args(batch), workspace, &ks, fp4);
+  keep_workspace_layout(to_args(batch), workspace, &ks);
   return launched(launch_keep_select(q_fp8, w, CacheArgs{cache.data, cache.num_blocks},
                                      to_args(batch), k, ks, topk, topk_stride, stream, fp4));
 }

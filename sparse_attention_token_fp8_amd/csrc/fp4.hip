@@ -162,7 +162,7 @@ void score_fp4_decode_kernel(const uint8_t* __restrict__ q8, const float* __rest
   int cx, ry;
   xcd_spread(&cx, &ry);
   fp4_decode_body<NB>(cx, ry, q8, w, cache, b, logits, ld, chunk_blocks,
-                      b.num_reqs == b.num_tokens && b.max_query_len <= 1, lds, NewRows{}, samp);
+                      b.num_reqs == b.num_tokens && b.max_query_len <= 1, lds, samp);
 }
 
 template <int NB>

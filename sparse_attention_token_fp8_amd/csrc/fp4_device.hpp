@@ -110,19 +110,6 @@ __device__ __forceinline__ void fp4_emit(float* __restrict__ out, float* __restr
   }
 }
 
-// Decode split: one query token per work-group, `chunk_blocks` blocks of its
-// causal range split into four runs, one per wave.  The K stream is read
-// once: each wave keeps NB-1 blocks' operand loads in flight, straight into
-// the MFMA registers (non-temporal).  `ident`: token t is request t.
-//
-// With FK the step's new K rows of the token's request that fall in this
-// wave's blocks and causal range are quantised here (each lane its group's 32
-// values, with the quantiser of quant_write_k_fp4_kernel), patched into the
-// loaded operands of their block (where their slot is the block-table slot of
-// their position) and the token's own row written to the cache.  With KEEP
-// the scores go to `kept` (LDS) with their key histogram and largest key, as
-// decode_body does for the fused path.  Returns the token's causal count, or
-// -1 when the chunk holds none of its positions.
 // A new K row quantised as the cache stores it, for this lane's group
 // G = lane / 16 (dims 32G .. 32G+31 at kr): its 32 E2M1 codes, low nibble
 // first, and the group's exponent e (scale byte e + 127).
@@ -185,14 +172,18 @@ __device__ __forceinline__ void fp4_patch_row(KBlock4& kb, int r, uint4 code, ui
   kb.sc = mine ? (kb.sc & ~mask) | (ebyte << (8 * tl)) : kb.sc;
 }
 
-template <int NB, bool FK = false, bool KEEP = false>
+// Decode split: one query token per work-group, `chunk_blocks` blocks of its
+// causal range split into four runs, one per wave.  The K stream is read
+// once: each wave keeps NB-1 blocks' operand loads in flight, straight into
+// the MFMA registers (non-temporal).  `ident`: token t is request t.
+// Returns the token's causal count, or -1 when the chunk holds none of its
+// positions.
+template <int NB>
 __device__ __forceinline__ int fp4_decode_body(int bx, int t, const uint8_t* __restrict__ q8,
                                                const float* __restrict__ w, const CacheArgs& cache,
                                                const BatchArgs& b, float* __restrict__ logits,
                                                int64_t ld, int chunk_blocks, bool ident,
-                                               uint8_t* lds, const NewRows& nk,
-                                               float* __restrict__ samp, float* kept = nullptr,
-                                               uint32_t* khist = nullptr, uint32_t* khi = nullptr) {
+                                               uint8_t* lds, float* __restrict__ samp) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   TokenPos tp;
@@ -227,40 +218,10 @@ __device__ __forceinline__ int fp4_decode_body(int bx, int t, const uint8_t* __r
   LinFrag lf;
   make_lin<1>(lf, f, lds + wave * kLinScratch, lane);
 
-  const int G = lane >> 4;
-  uint4 fcode[kMaxFusedRows];
-  uint32_t fexp[kMaxFusedRows];
-  int fpos0 = 0, nfix = 0;
-  if (FK) {
-    const int newlo = tp.len - tp.nq;
-    const int lo = max(newlo, blk(0) * kBlock);
-    const int hi = min(n - 1, (blk(mine - 1) + 1) * kBlock - 1);
-    nfix = min(kMaxFusedRows, max(0, hi - lo + 1));
-    fpos0 = lo;
-#pragma unroll
-    for (int i = 0; i < kMaxFusedRows; ++i) {
-      fcode[i] = make_uint4(0u, 0u, 0u, 0u);
-      fexp[i] = 0xFFFFFFFFu;
-      if (i < nfix) {
-        const int P = lo + i;
-        const int row = tp.q0 + (P - newlo);
-        int e;
-        fcode[i] = fp4_quant_group(nk.k + (int64_t)row * nk.stride + 32 * G, &e);
-        const int64_t want = nk.slots[row];
-        const int pb = __builtin_amdgcn_readlane(pbl, P / kBlock - blk(0));
-        const bool patch = pb >= 0 && want == (int64_t)pb * kBlock + P % kBlock;
-        if (patch) fexp[i] = (uint32_t)(e + 127);
-        if (row == t && want >= 0 && want < nk.num_slots)   // the token's own row: to the cache
-          fp4_write_row(nk.cache, want, fcode[i], e, lane);
-      }
-    }
-  }
-
   float* out = logits + (size_t)t * ld;
   float* srow = samp ? samp + (size_t)t * kMaxSample : nullptr;
   const int sS = sample_stride(n), sSh = 31 - __clz(sS);
   const int lp = lane_pos(lane);
-  uint32_t hik = 0u;                            // KEEP: largest key of this lane
   const int iters = (mine + NB - 1) / NB * NB;
   for (int j0 = 0; j0 < iters; j0 += NB) {
 #pragma unroll
@@ -269,32 +230,11 @@ __device__ __forceinline__ int fp4_decode_body(int bx, int t, const uint8_t* __r
       load(ring[(u + NB - 1) % NB], j + NB - 1);
       __builtin_amdgcn_sched_barrier(0);
       KBlock4& kb = ring[u];
-      if (FK) {
-#pragma unroll
-        for (int i = 0; i < kMaxFusedRows; ++i) {
-          const int P = fpos0 + i;
-          if (i < nfix && fexp[i] != 0xFFFFFFFFu && P / kBlock == blk(j))
-            fp4_patch_row(kb, P % kBlock, fcode[i], fexp[i], lane);
-        }
-      }
       float v;
       fp4_block_scores<1>(f, lf, kb, &v);
       const int s = blk(j) * kBlock + lp;
-      if (KEEP) {
-        if (j < mine && s < n) {
-          kept[s - lb0 * kBlock] = v;
-          const uint32_t key = order_key(v);
-          atomicAdd(&khist[key >> kKeepHistShift], 1u);
-          hik = max(hik, key);
-        }
-      } else if (j < mine) {
-        fp4_emit(out, srow, s, n, sS, sSh, v);
-      }
+      if (j < mine) fp4_emit(out, srow, s, n, sS, sSh, v);
     }
-  }
-  if (KEEP) {
-    const uint32_t m = wave_max(hik);
-    if (lane == 0) atomicMax(khi, m);
   }
   return n;
 }

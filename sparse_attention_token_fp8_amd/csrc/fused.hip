@@ -6,7 +6,8 @@
 // positions in topk_indices_buffer; no score tensor crosses its boundary.
 //
 // Method.  A row of n causal positions is scored by work-groups that each own
-// a chunk of positions (the decode work split of score_device.hpp).
+// a chunk of consecutive blocks (about one chunk per CU over the batch; the
+// chunk's eight waves take its blocks one at a time).
 //  1. Each work-group keeps its chunk's scores in LDS.  It places a threshold
 //     tau_c with at least m_c keys of the chunk at or above it, where m_c is
 //     the chunk's expected share of the row's top k plus a wide margin
@@ -34,12 +35,6 @@
 #include "topk_device.hpp"
 #include "fp4_device.hpp"
 
-#ifndef IDX_FP4_DECODE_RING
-#define IDX_FP4_DECODE_RING 4
-#endif
-#ifndef IDX_FP4_KEEP_RING
-#define IDX_FP4_KEEP_RING 2
-#endif
 
 #include <algorithm>
 #include <type_traits>
@@ -47,8 +42,6 @@
 namespace idx {
 namespace {
 
-constexpr int kMaxChunkPos = 64 * kBlock;       // decode chunks are at most 64 blocks
-constexpr int kKeepPer = kMaxChunkPos / kScoreThreads;   // 16 positions per thread
 
 // Keys a chunk of `nvalid` of a row's n positions keeps at least: its expected
 // share e of the row's top k plus 6 sqrt(e) + 8.  The number of top-k keys in
@@ -66,7 +59,7 @@ __device__ __forceinline__ uint32_t chunk_keep(int k, int nvalid, int n) {
 // scoring loop), then the next 10 bits of the keys in the bin that holds the
 // m-th largest.
 constexpr int kTauBins = 4096;
-constexpr int kTauShift = kKeepHistShift;
+constexpr int kTauShift = 20;
 constexpr int kTau2Bins = 1024;
 constexpr int kTau2Shift = 10;
 
@@ -107,7 +100,7 @@ __device__ __forceinline__ uint32_t wave_find_bin(const uint32_t* h, uint32_t ne
 // the bin's other keys besides them); every wave finds it on its own from the
 // shared histograms.  NT threads, NT >= 256, for chunks of up to MAXPOS
 // positions; `table` holds 65 words, 129 when MAXPOS / 64 > 64.
-template <int NT, int MAXPOS = kMaxChunkPos>
+template <int NT, int MAXPOS>
 __device__ __forceinline__ void chunk_filter(const float* kept, int t, int cx, int chunk_blocks,
                                              int n, int k, const KeepSlots& ks, uint32_t* hist,
                                              uint32_t* hist2, uint32_t* table) {
@@ -162,61 +155,6 @@ __device__ __forceinline__ void chunk_filter(const float* kept, int t, int cx, i
     ks.taus[slot] = tau;
     ks.maxes[slot] = kmax;
   }
-}
-
-// Decode scoring that keeps each chunk's candidates (step 1).  With FK it also
-// writes this step's new K rows, as score_decode_write_kernel does.  FP4:
-// the cache is the FP4 one (fp4_decode_body, no LDS staging of K).
-template <int NB, bool FK, bool FP4>
-__device__ __forceinline__ void keep_body(const uint8_t* __restrict__ q8,
-                                          const float* __restrict__ w, const CacheArgs& cache,
-                                          const BatchArgs& b, int chunk_blocks, int ident,
-                                          const NewRows& nk, int k, const KeepSlots& ks,
-                                          uint8_t* lds) {
-  __shared__ float kept[kMaxChunkPos];
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kTauBins];
-  __shared__ __attribute__((aligned(16))) uint32_t hist2[kTau2Bins];
-  __shared__ uint32_t table[1 + kKeepPer * kScoreThreads / 64];
-  // the scoring loop counts into hist and maximises into table[0]
-  for (int i = threadIdx.x; i < kTauBins / 4; i += kScoreThreads)
-    reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-  for (int i = threadIdx.x; i < kTau2Bins / 4; i += kScoreThreads)
-    reinterpret_cast<uint4*>(hist2)[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (threadIdx.x == 0) table[0] = 0u;
-  __syncthreads();
-  int cx, ry;
-  xcd_spread(&cx, &ry);
-  int n;
-  if constexpr (FP4)
-    n = fp4_decode_body<NB, FK, true>(cx, ry, q8, w, cache, b, nullptr, 0, chunk_blocks, ident != 0,
-                                      lds, nk, nullptr, kept, hist, table);
-  else
-    n = decode_body<NB, FK, false, true>(cx, ry, q8, w, cache, b, nullptr, 0, chunk_blocks,
-                                         ident != 0, lds, nk, nullptr, kept, hist, table);
-  if (n <= k) return;                           // nothing here, or a row the resolve takes whole
-  __syncthreads();                              // every wave's scores are in `kept`
-  chunk_filter<kScoreThreads>(kept, ry, cx, chunk_blocks, n, k, ks, hist, hist2, table);
-}
-
-template <int NB, bool FK>
-__global__ __launch_bounds__(kScoreThreads)
-__attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_keep_kernel(
-    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    int chunk_blocks, int ident, NewRows nk, int k, KeepSlots ks) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kScoreLds];
-  keep_body<NB, FK, false>(q8, w, cache, b, chunk_blocks, ident, nk, k, ks, lds);
-}
-
-#ifndef IDX_FP4_KEEP_WAVES_PER_EU
-#define IDX_FP4_KEEP_WAVES_PER_EU 2
-#endif
-template <int NB, bool FK>
-__global__ __launch_bounds__(kScoreThreads)
-__attribute__((amdgpu_waves_per_eu(IDX_FP4_KEEP_WAVES_PER_EU))) void score_keep_fp4_kernel(
-    const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
-    int chunk_blocks, int ident, NewRows nk, int k, KeepSlots ks) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kLinScratch];
-  keep_body<NB, FK, true>(q8, w, cache, b, chunk_blocks, ident, nk, k, ks, lds);
 }
 
 // ------------------------------------------------- one work-group a CU --
@@ -277,7 +215,7 @@ __device__ __forceinline__ int dyn_body(int cx, int t, const uint8_t* __restrict
     if (s < n) {
       kept[s - lb0 * kBlock] = v;
       const uint32_t key = order_key(v);
-      atomicAdd(&khist[key >> kKeepHistShift], 1u);
+      atomicAdd(&khist[key >> kTauShift], 1u);
       hi = max(hi, key);
     }
   };
@@ -833,37 +771,24 @@ __global__ __launch_bounds__(kResThreads) void topk_keep_resolve_kernel(
 
 }  // namespace
 
-#ifndef IDX_KEEP_DYN
-#define IDX_KEEP_DYN 1
-#endif
-#ifndef IDX_KEEP_DYN_FP4
-#define IDX_KEEP_DYN_FP4 1
-#endif
-
-// Whether the fused path scores with one kDynWaves-wave work-group per CU
-// (score_keep_dyn_kernel) rather than two four-wave ones.
-static bool keep_dyn(bool fp4) { return fp4 ? IDX_KEEP_DYN_FP4 : IDX_KEEP_DYN; }
-
 // Blocks per chunk of the fused path: about one chunk per CU over the batch,
-// 8 to kDynMaxBlocks blocks, for the one-per-CU kernel; decode_chunk_blocks'
-// two per CU otherwise.
-static int keep_chunk_blocks(const BatchArgs& b, bool fp4) {
-  if (!keep_dyn(fp4)) return decode_chunk_blocks(b.max_seq_len, b.num_tokens);
+// 8 to kDynMaxBlocks blocks.
+static int keep_chunk_blocks(const BatchArgs& b) {
   const int64_t blocks_per_row = (b.max_seq_len + kBlock - 1) / kBlock;
   const int64_t cb = (blocks_per_row * b.num_tokens + 255) / 256;
   return (int)std::min<int64_t>(kDynMaxBlocks, std::max<int64_t>(8, cb));
 }
 
-bool keep_path(const BatchArgs& b, int64_t dec_tokens, bool fp4) {
+bool keep_path(const BatchArgs& b, int64_t dec_tokens) {
   const bool decode_split = b.max_query_len <= 1 || dec_tokens >= b.num_tokens;
   if (!decode_split || !topk_uses_long_rows(b.num_tokens, b.max_seq_len)) return false;
-  const int cb = keep_chunk_blocks(b, fp4);
+  const int cb = keep_chunk_blocks(b);
   const int64_t nslots = (b.max_seq_len + (int64_t)cb * kBlock - 1) / ((int64_t)cb * kBlock);
   return nslots <= kMaxSlots;
 }
 
-size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks, bool fp4) {
-  const int cb = keep_chunk_blocks(b, fp4);
+size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks) {
+  const int cb = keep_chunk_blocks(b);
   const int64_t cap = (int64_t)cb * kBlock;
   const int64_t nslots = std::max<int64_t>(1, (b.max_seq_len + cap - 1) / cap);
   const size_t T = (size_t)b.num_tokens;
@@ -920,22 +845,8 @@ hipError_t launch_keep_candidates(const uint8_t* q8, const float* w, const Cache
     const dim3 grid((unsigned)ks.nslots, (unsigned)b.num_tokens);
     const NewRows nk = kq != nullptr ? NewRows{kq, kq_stride, slots, cache_w, cache.num_blocks * kBlock}
                                      : NewRows{};
-    if (keep_dyn(fp4))
-      return fp4 ? launch_keep_dyn<true>(grid, q8, w, cache, b, ident, nk, kq != nullptr, k, ks, stream)
-                 : launch_keep_dyn<false>(grid, q8, w, cache, b, ident, nk, kq != nullptr, k, ks, stream);
-    if (fp4 && kq != nullptr)
-      IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_KEEP_RING, true>), grid,
-                 dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
-    else if (fp4)
-      IDX_LAUNCH("score_keep_fp4_kernel", (score_keep_fp4_kernel<IDX_FP4_KEEP_RING, false>), grid,
-                 dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
-    else if (kq != nullptr)
-      IDX_LAUNCH("score_keep_kernel", (score_keep_kernel<IDX_DECODE_RING, true>), grid,
-                 dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
-    else
-      IDX_LAUNCH("score_keep_kernel", (score_keep_kernel<IDX_DECODE_RING, false>), grid,
-                 dim3(kScoreThreads), stream, q8, w, cache, b, ks.chunk_blocks, ident, nk, k, ks);
-    return hipGetLastError();
+    return fp4 ? launch_keep_dyn<true>(grid, q8, w, cache, b, ident, nk, kq != nullptr, k, ks, stream)
+               : launch_keep_dyn<false>(grid, q8, w, cache, b, ident, nk, kq != nullptr, k, ks, stream);
   }
   if (kq != nullptr)
     return fp4 ? launch_quant_write_k_fp4(kq, b.num_tokens, kq_stride, slots, cache_w,

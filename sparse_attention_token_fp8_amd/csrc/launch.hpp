@@ -63,10 +63,10 @@ hipError_t launch_score_write_k(const uint8_t* q8, const float* w, const CacheAr
 
 // Whether idx_score_topk takes the fused path for this batch: every token
 // scored with the decode split, rows long enough for the long-row top-k.
-bool keep_path(const BatchArgs& b, int64_t dec_tokens, bool fp4 = false);
+bool keep_path(const BatchArgs& b, int64_t dec_tokens);
 
 // Workspace of the fused path; returns its bytes and, with a base, fills `ks`.
-size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks, bool fp4 = false);
+size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks);
 
 // The fused path's two launches.  launch_keep_candidates scores the batch
 // with the scores kept on chip and leaves each chunk's candidates in `ks`; with

@@ -475,25 +475,14 @@ constexpr int kMaxFusedRows = 4;
 // at once, in parallel with the request metadata.  With SPEC (the decode
 // rows of a mixed batch, decodes first) request t's slice is read alongside
 // the token lookup and kept if the lookup finds request t.
-//
-// With KEEP the scores are not stored to `logits` but kept in LDS for the
-// work-group's own top-k filter: position s of the chunk goes to
-// kept[s - first position of the chunk], its order key is counted in
-// khist[key >> kKeepHistShift] (LDS, zeroed before the call) and the largest
-// key of the work-group is accumulated in *khi (LDS) with atomicMax, while the
-// K stream is still in flight.
 // Returns the token's causal count n, or -1 when the chunk holds none of its
 // positions (then every wave of the work-group returns -1).
-constexpr int kKeepHistShift = 20;              // 4096 bins: sign, exponent, 3 mantissa bits
-
-template <int NB, bool FK, bool SPEC = false, bool KEEP = false>
+template <int NB, bool FK, bool SPEC = false>
 __device__ __forceinline__ int decode_body(int bx, int t, const uint8_t* __restrict__ q8,
                                            const float* __restrict__ w, const CacheArgs& cache,
                                            const BatchArgs& b, float* __restrict__ logits,
                                            int64_t ld, int chunk_blocks, bool ident, uint8_t* lds,
-                                           const NewRows& nk, float* __restrict__ samp,
-                                           float* kept = nullptr, uint32_t* khist = nullptr,
-                                           uint32_t* khi = nullptr) {
+                                           const NewRows& nk, float* __restrict__ samp) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
   const int lb0 = bx * chunk_blocks;
@@ -527,34 +516,17 @@ __device__ __forceinline__ int decode_body(int bx, int t, const uint8_t* __restr
   // the row's sampled scores also go to their compact copy (see sample_pos)
   float* srow = samp ? samp + (size_t)t * kMaxSample : nullptr;
   const int sS = sample_stride(n), sSh = 31 - __clz(sS);
-  uint32_t hi = 0u;                             // KEEP: largest key of this lane
   auto emit = [&](int j, float v) {
     const int s = blk(j) * kBlock + lp;
     const bool in = j < mine && s < n;
-    if (KEEP) {
-      if (in) {
-        kept[s - lb0 * kBlock] = v;
-        const uint32_t key = order_key(v);
-        atomicAdd(&khist[key >> kKeepHistShift], 1u);
-        hi = max(hi, key);
-      }
-      return;
-    }
     if (in) out[s] = v;
     if (srow != nullptr) {
       const int sj = s >> sSh;
       if (in && (s & (sS - 1)) == ((37 * sj + 11) & (sS - 1))) srow[sj] = v;
     }
   };
-  auto keep_max = [&]() {
-    if (KEEP) {
-      const uint32_t m = wave_max(hi);
-      if (lane == 0) atomicMax(khi, m);
-    }
-  };
   if (cache.num_blocks == 0) {                  // no K at all: every score is 0
     for (int j = 0; j < mine; ++j) emit(j, 0.f);
-    keep_max();
     return n;
   }
   // lane j holds the physical block of this wave's j-th block, so no K load
@@ -656,7 +628,6 @@ __device__ __forceinline__ int decode_body(int bx, int t, const uint8_t* __restr
       emit(j, v);
     }
   }
-  keep_max();
   return n;
 }
 
