@@ -157,18 +157,20 @@ __device__ __forceinline__ void chunk_filter(const float* kept, int t, int cx, i
   }
 }
 
-// ------------------------------------------------- one work-group a CU --
-// The same step 1 with one work-group of kDynWaves waves per CU, whose waves
-// take the chunk's blocks one at a time from a work-group counter: the CU's
-// two SIMD slots no longer hold two work-groups of which the younger is
-// served later and ends last, waves that the SIMDs serve faster take more
-// blocks, and the chunk's threshold and compaction run once per CU.
+// ---------------------------------------------------------- scoring --
+// Step 1 by one work-group of kDynWaves waves per CU, whose waves take the
+// chunk's blocks one at a time from a work-group counter: no CU holds two
+// work-groups of which the younger is served later and ends last, waves that
+// the SIMDs serve faster take more blocks, and the chunk's threshold and
+// compaction run once per CU.
 constexpr int kDynWaves = 8;
 constexpr int kDynThreads = 64 * kDynWaves;
 constexpr int kDynMaxBlocks = 128;              // a chunk's blocks: two block ids per lane
 
-// Scores one token's chunk (up to kDynMaxBlocks blocks) into kept/khist/khi, as
-// decode_body does with KEEP; *next is the LDS block counter, set to
+// Scores one token's chunk (up to kDynMaxBlocks blocks): position s of the
+// chunk's scores goes to kept[s - its first position] (LDS), its order key is
+// counted in khist[key >> kTauShift] (LDS, zeroed before the call) and the
+// largest key is accumulated in *khi; *next is the LDS block counter, set to
 // kDynWaves * (NB - 1) before the call (each wave's first NB - 1 blocks are
 // wave, wave + kDynWaves, ...).  With FK every wave quantises the chunk's new
 // rows, the wave that scores a row's block patches it into its staged copy,

@@ -73,8 +73,8 @@ size_t keep_workspace_layout(const BatchArgs& b, void* base, KeepSlots* ks);
 // kq, this step's new K rows are written first (by the scoring kernel itself,
 // so score_writes_k must hold).  launch_keep_select takes each row's top k
 // from the candidates (rescoring a row whose chunks held more than their
-// share).  fp4: the cache is the FP4 one (the same method, with
-// score_keep_fp4_kernel).
+// share).  fp4: the cache is the FP4 one (the same method and kernels, FP4
+// block loads).
 hipError_t launch_keep_candidates(const uint8_t* q8, const float* w, const CacheArgs& cache,
                                   const BatchArgs& b, const uint16_t* kq, int64_t kq_stride,
                                   const int64_t* slots, uint8_t* cache_w, int k,
