@@ -135,6 +135,178 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
   }
 }
 
+// The same work with each K block copied by the memory system straight into
+// LDS (buffer loads to LDS): no staging registers, LDS stores or masking in
+// the loop.  Two slots of 12 KiB (every wave issues three 1 KiB copies;
+// lanes past the block's 528 chunks read past the buffer and write zeros into
+// the slot's tail).  Iteration j: barrier (block j is in its slot for every
+// wave), the copies of block j+1 into the other slot (read last in iteration
+// j-1, before the barrier), block j scored, then each wave waits for all of
+// its memory operations (block j+1's copies and block j-1's score stores,
+// both issued a block's compute earlier) before it stores block j's scores
+// (range-checked buffer stores, no branch).  The copies are issued in inline
+// assembly (m0 holds the LDS address), so the compiler, which does not see
+// them, does not drain every memory operation at each barrier as it does for
+// the builtin form (that version took 2.68 ms against 1.51).
+constexpr int kDmaSlot = 12 * 1024;
+constexpr int kPrefillDmaLds = 2 * kDmaSlot + 4 * kLinScratch;
+
+// A buffer descriptor built from wave-uniform values, so that it sits in
+// SGPRs (a descriptor the compiler cannot prove uniform gets a loop around
+// every access that uses it).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return byte_rsrc(reinterpret_cast<const void*>((uintptr_t)(((uint64_t)hi << 32) | lo)),
+                   __builtin_amdgcn_readfirstlane(bytes));
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from rsrc + voff into LDS at m0 + 16 * lane (m0 is saved
+// and restored around the copy; a write of m0 needs one wait state before an
+// LDS copy reads it, as the compiler itself places).  The load has no VGPR
+// result, so nothing of the wave's registers is written while it is in flight.
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(voff), "s"(rs)
+      : "memory");
+}
+
+__device__ __forceinline__ void prefill_body_dma(int bx, int gy, const uint8_t* __restrict__ q8,
+                                                 const float* __restrict__ w, const CacheArgs& cache,
+                                                 const BatchArgs& b, float* __restrict__ logits,
+                                                 int64_t ld, int chunk_blocks, int gpr,
+                                                 uint8_t* lds, float* __restrict__ samp) {
+  constexpr int TPW = kPrefillTPW, NW = 4;
+  PrefillGroup pg;
+  if (!prefill_group(b, gy, 0, gpr, &pg)) return;
+  const int r = pg.r;
+  const int q0 = pg.q0;
+  const int nq = pg.nq;
+  const int tb = pg.t0 - q0;
+  const int L = pg.len;
+  auto count = [&](int i) {
+    int n = L - nq + i + 1;
+    n = n < 0 ? 0 : n;
+    return n > b.max_seq_len ? b.max_seq_len : n;
+  };
+  const int n_max = count(tb + pg.nt - 1);
+  const int lb0 = bx * chunk_blocks;
+  if (lb0 * kBlock >= n_max) return;
+  const int nblk = min(chunk_blocks, (n_max - lb0 * kBlock + kBlock - 1) / kBlock);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lp = lane_pos(lane);
+  int pbl[kPrefillWin];
+#pragma unroll
+  for (int w = 0; w < kPrefillWin; ++w)
+    pbl[w] = 64 * w + lane < nblk ? (int)phys_block(b, cache, r, lb0 + 64 * w + lane) : -1;
+
+  QFrag f[TPW];
+  int nt[TPW];
+  int tk[TPW];
+  int sS[TPW], sSh[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int i = tb + wave * TPW + j;
+    const int t = q0 + i;
+    if (i < tb + pg.nt && t < b.num_tokens) {
+      load_q(f[j], q8 + (size_t)t * kHeads * kHeadDim, w + (size_t)t * kHeads, lane);
+      nt[j] = count(i);
+      tk[j] = t;
+    } else {
+      zero_q(f[j]);
+      nt[j] = 0;
+      tk[j] = 0;
+    }
+    sS[j] = sample_stride(nt[j]);
+    sSh[j] = 31 - __clz(sS[j]);
+  }
+  if (cache.num_blocks == 0) {                  // no K at all: every score is 0
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj)
+      for (int j = 0; j < nblk; ++j) {
+        const int s = (lb0 + j) * kBlock + lp;
+        float* o = logits + (size_t)tk[jj] * ld;
+        if (s < nt[jj]) o[s] = 0.f;
+        if (samp != nullptr) {
+          const int sj = s >> sSh[jj];
+          if (s < nt[jj] && (s & (sS[jj] - 1)) == ((37 * sj + 11) & (sS[jj] - 1)))
+            samp[(size_t)tk[jj] * kMaxSample + sj] = 0.f;
+        }
+      }
+    return;
+  }
+  // the token rows and their sample copies as range-checked buffers: a
+  // position past the token's causal range, or not sampled, is stored past
+  // the buffer's end and dropped
+  __amdgpu_buffer_rsrc_t orow[TPW], srs[TPW];
+#pragma unroll
+  for (int jj = 0; jj < TPW; ++jj) {
+    orow[jj] = uniform_rsrc(logits + (size_t)tk[jj] * ld, nt[jj] * 4);
+    srs[jj] = uniform_rsrc(samp != nullptr ? samp + (size_t)tk[jj] * kMaxSample : logits,
+                           samp != nullptr && nt[jj] > 0 ? kMaxSample * 4 : 0);
+  }
+  LinFrag lf;
+  make_lin<TPW>(lf, f, lds + 2 * kDmaSlot + wave * kLinScratch, lane);
+
+  // block j of the chunk into `slot` (from nblk on, or absent: zeros)
+  auto copy_block = [&](int j, uint8_t* slot) {
+    const int jc = min(j, nblk - 1);
+    int v = pbl[0];
+#pragma unroll
+    for (int w = 1; w < kPrefillWin; ++w) v = (jc >> 6) == w ? pbl[w] : v;
+    const int pb = __builtin_amdgcn_readlane(v, jc & 63);
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(cache.data + (int64_t)max(pb, 0) * kBlockBytes,
+                                                   (j < nblk && pb >= 0) ? kBlockBytes : 0);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int u = wave + NW * i;
+      const int ci = 64 * u + lane;
+      const uint32_t voff = ci < kBlockBytes / 16 ? (uint32_t)stage_src<NW>(ci) : (uint32_t)kPastBlock;
+      copy_to_lds(rs, voff, __builtin_amdgcn_readfirstlane(lds_address(slot + u * 1024)));
+    }
+  };
+  uint8_t* cur = lds;
+  uint8_t* nxt = lds + kDmaSlot;
+  copy_block(0, cur);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int j = 0; j < nblk; ++j) {
+    __syncthreads();                            // block j in `cur` for every wave; `nxt` free
+    if (j + 1 < nblk) copy_block(j + 1, nxt);
+    const float ks = *reinterpret_cast<const float*>(cur + kCodeBytes + lp * 4);
+    float v[TPW];
+    block_scores_with<TPW>(f, lf, [&](int tl) { return lds_tile(cur, tl, lane); }, ks, v);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block j+1 landed; earlier stores done
+    const int s = (lb0 + j) * kBlock + lp;
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[jj]), orow[jj], (uint32_t)s * 4u, 0,
+                                            kLoadStream);
+      const int sj = s >> sSh[jj];
+      const bool sampled = (s & (sS[jj] - 1)) == ((37 * sj + 11) & (sS[jj] - 1));
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[jj]), srs[jj],
+                                            sampled && s < nt[jj] ? (uint32_t)sj * 4u : (uint32_t)kPastBlock * 16u,
+                                            0, 0);
+    }
+    uint8_t* const t0 = cur;
+    cur = nxt;
+    nxt = t0;
+  }
+}
+
 // ------------------------------------------------------------ kernels --
 template <int NB>
 __global__ __launch_bounds__(kScoreThreads)
@@ -162,14 +334,22 @@ __attribute__((amdgpu_waves_per_eu(IDX_DECODE_WAVES_PER_EU))) void score_decode_
 }
 
 // two work-groups per CU: the register budget is 256 VGPRs
+#ifndef IDX_PREFILL_DMA
+#define IDX_PREFILL_DMA 1
+#endif
 __global__ __launch_bounds__(kScoreThreads)
 __attribute__((amdgpu_waves_per_eu(2))) void score_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ w, CacheArgs cache, BatchArgs b,
     float* __restrict__ logits, int64_t ld, int chunk_blocks, int gpr, float* samp) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kPrefillLds];
   int cx, ry;
   xcd_spread(&cx, &ry);
-  prefill_body(cx, ry, 0, q8, w, cache, b, logits, ld, chunk_blocks, gpr, lds, samp);
+  if constexpr (IDX_PREFILL_DMA) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kPrefillDmaLds];
+    prefill_body_dma(cx, ry, q8, w, cache, b, logits, ld, chunk_blocks, gpr, lds, samp);
+  } else {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kPrefillLds];
+    prefill_body(cx, ry, 0, q8, w, cache, b, logits, ld, chunk_blocks, gpr, lds, samp);
+  }
 }
 
 // Mixed batch in one launch: rows y < dec_tokens are tokens scored with the
