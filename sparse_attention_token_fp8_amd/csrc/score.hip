@@ -137,19 +137,23 @@ __device__ __forceinline__ void prefill_body(int bx, int gy, int tok_lo,
 
 // The same work with each K block copied by the memory system straight into
 // LDS (buffer loads to LDS): no staging registers, LDS stores or masking in
-// the loop.  Two slots of 12 KiB (every wave issues three 1 KiB copies;
+// the loop.  Three slots of 12 KiB (every wave issues three 1 KiB copies;
 // lanes past the block's 528 chunks read past the buffer and write zeros into
-// the slot's tail).  Iteration j: barrier (block j is in its slot for every
-// wave), the copies of block j+1 into the other slot (read last in iteration
-// j-1, before the barrier), block j scored, then each wave waits for all of
-// its memory operations (block j+1's copies and block j-1's score stores,
-// both issued a block's compute earlier) before it stores block j's scores
-// (range-checked buffer stores, no branch).  The copies are issued in inline
-// assembly (m0 holds the LDS address), so the compiler, which does not see
-// them, does not drain every memory operation at each barrier as it does for
-// the builtin form (that version took 2.68 ms against 1.51).
+// the slot's tail), so in iteration j block j is scored while blocks j+1 and
+// j+2 are in flight: two blocks of compute hide the copies even when K comes
+// from HBM (after the top-k has streamed the scores through the caches; with
+// one block of look-ahead the step took 2.07 ms against 1.80).
+// The copies are issued in inline assembly (m0 holds the LDS address), so the
+// compiler, which does not see them, does not drain every memory operation at
+// each barrier as it does for the builtin form.  The waits are placed by
+// count instead: per iteration each wave issues exactly three copies and then
+// exactly 2 * TPW stores (range-checked buffer stores, none behind a branch),
+// and before block j is read each wave waits until only the operations it
+// issued after block j's copies may be in flight (a wave's vector memory
+// operations complete in issue order, which the compiler's own waits rely on
+// too).  Copies of blocks past the chunk read nothing and fill unused slots.
 constexpr int kDmaSlot = 12 * 1024;
-constexpr int kPrefillDmaLds = 2 * kDmaSlot + 4 * kLinScratch;
+constexpr int kPrefillDmaLds = 3 * kDmaSlot + 4 * kLinScratch;
 
 // A buffer descriptor built from wave-uniform values, so that it sits in
 // SGPRs (a descriptor the compiler cannot prove uniform gets a loop around
@@ -260,7 +264,7 @@ __device__ __forceinline__ void prefill_body_dma(int bx, int gy, const uint8_t* 
                            samp != nullptr && nt[jj] > 0 ? kMaxSample * 4 : 0);
   }
   LinFrag lf;
-  make_lin<TPW>(lf, f, lds + 2 * kDmaSlot + wave * kLinScratch, lane);
+  make_lin<TPW>(lf, f, lds + 3 * kDmaSlot + wave * kLinScratch, lane);
 
   // block j of the chunk into `slot` (from nblk on, or absent: zeros)
   auto copy_block = [&](int j, uint8_t* slot) {
@@ -279,17 +283,24 @@ __device__ __forceinline__ void prefill_body_dma(int bx, int gy, const uint8_t* 
       copy_to_lds(rs, voff, __builtin_amdgcn_readfirstlane(lds_address(slot + u * 1024)));
     }
   };
-  uint8_t* cur = lds;
-  uint8_t* nxt = lds + kDmaSlot;
-  copy_block(0, cur);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint8_t* slot0 = lds;
+  uint8_t* slot1 = lds + kDmaSlot;
+  uint8_t* slot2 = lds + 2 * kDmaSlot;
+  copy_block(0, slot0);
+  copy_block(1, slot1);
+  static_assert(TPW == 2, "the waits below count 2 * TPW stores per iteration");
   for (int j = 0; j < nblk; ++j) {
-    __syncthreads();                            // block j in `cur` for every wave; `nxt` free
-    if (j + 1 < nblk) copy_block(j + 1, nxt);
+    // operations after block j's copies: block j+1's copies and the stores
+    // of the iterations in between
+    if (j == 0) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else if (j == 1) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");    // 3 + 2 * TPW
+    else asm volatile("s_waitcnt vmcnt(11)" ::: "memory");               // 3 + 4 * TPW
+    __syncthreads();                            // block j in slot0; slot2 read last in j-1
+    copy_block(j + 2, slot2);
+    const uint8_t* cur = slot0;
     const float ks = *reinterpret_cast<const float*>(cur + kCodeBytes + lp * 4);
     float v[TPW];
     block_scores_with<TPW>(f, lf, [&](int tl) { return lds_tile(cur, tl, lane); }, ks, v);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block j+1 landed; earlier stores done
     const int s = (lb0 + j) * kBlock + lp;
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj) {
@@ -301,10 +312,12 @@ __device__ __forceinline__ void prefill_body_dma(int bx, int gy, const uint8_t* 
                                             sampled && s < nt[jj] ? (uint32_t)sj * 4u : (uint32_t)kPastBlock * 16u,
                                             0, 0);
     }
-    uint8_t* const t0 = cur;
-    cur = nxt;
-    nxt = t0;
+    uint8_t* const t0 = slot0;
+    slot0 = slot1;
+    slot1 = slot2;
+    slot2 = t0;
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy lands after the work-group ends
 }
 
 // ------------------------------------------------------------ kernels --
