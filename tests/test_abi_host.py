@@ -245,3 +245,25 @@ def test_group_physical_rejects_before_any_work(m):
     io[1].cache = _cache(m, bs=32)
     assert L.idx_indexcache_stack_physical(io, 2, full, 1, FAKE, B(ok), 8, FAKE, 8, B(good),
                                            FAKE, 1 << 20, S) == -2
+
+
+@pytest.mark.parametrize("tokens,max_len", [(8, 131072), (64, 32768), (32, 65536), (1, 300000),
+                                             (2, 9000), (255, 8193)])
+def test_fused_workspace_follows_the_chunking(m, tokens, max_len):
+    """Decode batches over long rows (fewer than 256 tokens, rows past 8192
+    positions) take the fused path, whose workspace holds per (row, chunk) a
+    candidate slot of chunk-size (key, position) pairs and three words of
+    summary.  Chunks cover about one CU's share of the batch's blocks, 8 to
+    128 blocks of 64 positions; the FP4 cache uses the same layout."""
+    L = m.lib()
+    B = ctypes.byref
+    bpr = -(-max_len // 64)
+    cb = min(128, max(8, -(-bpr * tokens // 256)))
+    cap = cb * 64
+    nslots = -(-max_len // cap)
+    up = lambda x: -(-x // 256) * 256
+    want = up(8 * tokens * nslots * cap) + 3 * up(4 * tokens * nslots)
+    dec = _batch(m, num_reqs=tokens, num_tokens=tokens, max_seq_len=max_len, max_query_len=1,
+                 stride=bpr)
+    assert L.idx_score_topk_workspace_size(B(dec), 2048) == want
+    assert L.idx_score_topk_fp4_workspace_size(B(dec), 2048) == want
