@@ -64,7 +64,7 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ row, int n,
 // With `samp` (the scoring kernel's compact sample copy) the sample is one
 // contiguous read; without it the sampled positions are gathered from the row,
 // which touches every line of it once more before the pass over the row.
-template <typename Pos>
+template <typename Pos, bool RANGES>
 __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __restrict__ logits,
                                                                 int64_t ld, BatchArgs b, int k,
                                                                 int32_t* __restrict__ topk,
@@ -99,28 +99,111 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
 #pragma unroll
     for (int e = 0; e < kBatch; ++e) v[e] = row[min(base + e * kRowThreads + (int)threadIdx.x, n - 1)];
   };
-  float va[kBatch], vb[kBatch];
-  load_batch(va, 0);
-  load_batch(vb, kStep);
-  const uint32_t tau = sampled ? sample_tau<kRowThreads>(sv, ns, n, k, hist, scratch) : 0u;
-  uint32_t C = 0;
-  auto batch = [&](float* v, int base, uint32_t* tab) {
-    uint32_t key[kBatch];
-    bool pass[kBatch];
+  if constexpr (RANGES) {
+    // Each wave streams its own contiguous range of the row (a multiple of 64
+    // positions) and compacts its candidates into its own part of the LDS list
+    // with ballots: no barrier until the row has been read.  The parts are then
+    // moved together in wave order, which is position order.
+    constexpr int NW = kRowThreads / 64, U = kBatch, kWaveCap = kRowCap / NW;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int seg = (n + 64 * NW - 1) / (64 * NW) * 64;
+    const int p0 = wave * seg, p1 = min(n, p0 + seg);
+    // past its range a wave re-reads the range's last position (the pass test
+    // drops it), so no load sits behind a branch and no line is fetched twice
+    const int last = max(p1 - 1, 0);
+    auto load_run = [&](float* v, int base) {
 #pragma unroll
-    for (int e = 0; e < kBatch; ++e) {
-      key[e] = order_key(v[e]);
-      pass[e] = base + e * kRowThreads + (int)threadIdx.x < n && key[e] >= tau;
+      for (int u = 0; u < U; ++u) v[u] = row[min(base + 64 * u + lane, last)];
+    };
+    float va[U], vb[U];
+    load_run(va, p0);
+    load_run(vb, p0 + 64 * U);
+    const uint32_t tau = sampled ? sample_tau<kRowThreads>(sv, ns, n, k, hist, scratch) : 0u;
+    uint32_t* wkey = ckey + wave * kWaveCap;
+    Pos* wpos = cpos + wave * kWaveCap;
+    uint32_t cnt = 0;                             // the wave's candidates so far (uniform)
+    auto run = [&](float* v, int base) {
+      uint32_t key[U];
+      bool pass[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        key[u] = order_key(v[u]);
+        pass[u] = base + 64 * u + lane < p1 && key[u] >= tau;
+      }
+      load_run(v, base + 2 * 64 * U);             // two runs ahead
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t mk = __ballot(pass[u]);
+        const uint32_t at = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+        if (pass[u] && at < (uint32_t)kWaveCap) {
+          wkey[at] = key[u];
+          wpos[at] = (Pos)(base + 64 * u + lane);
+        }
+        cnt += (uint32_t)__popcll(mk);
+      }
+    };
+    for (int base = p0; base < p1; base += 2 * 64 * U) {
+      run(va, base);
+      if (base + 64 * U < p1) run(vb, base + 64 * U);
     }
-    load_batch(v, base + 2 * kStep);            // two batches ahead
-    C += compact_ordered<kRowThreads, kBatch>(key, pass, base, C, ckey, cpos, kRowCap, tab);
-  };
-  for (int base = 0; base < n; base += 2 * kStep) {
-    batch(va, base, table[0]);
-    if (base + kStep < n) batch(vb, base + kStep, table[1]);
+    __shared__ uint32_t wcnt[NW];
+    if (lane == 0) wcnt[wave] = cnt;
+    __syncthreads();
+    uint32_t C = 0, before = 0;
+    bool fits = true;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const uint32_t c = wcnt[v];
+      fits = fits && c <= (uint32_t)kWaveCap;
+      before += v < wave ? c : 0u;
+      C += c;
+    }
+    if (!fits) C = kRowCap + 1;                   // a part overflowed: the whole row is selected
+    if (fits && C >= (uint32_t)k) {               // move the parts together (all reads first)
+      constexpr int R = kWaveCap / 64;
+      uint32_t rk[R];
+      Pos rp[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t i = min((uint32_t)(64 * r + lane), cnt - (cnt > 0 ? 1u : 0u));
+        rk[r] = wkey[i];
+        rp[r] = wpos[i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t i = (uint32_t)(64 * r + lane);
+        if (i < cnt) { ckey[before + i] = rk[r]; cpos[before + i] = rp[r]; }
+      }
+    }
+    __syncthreads();                              // the candidates, before the select reads them
+    finish_row<kRowThreads>(row, n, k, C, kRowCap, ckey, cpos, out, hist, bucket, scratch);
+  } else {
+    float va[kBatch], vb[kBatch];
+    load_batch(va, 0);
+    load_batch(vb, kStep);
+    const uint32_t tau = sampled ? sample_tau<kRowThreads>(sv, ns, n, k, hist, scratch) : 0u;
+    uint32_t C = 0;
+    auto batch = [&](float* v, int base, uint32_t* tab) {
+      uint32_t key[kBatch];
+      bool pass[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        key[e] = order_key(v[e]);
+        pass[e] = base + e * kRowThreads + (int)threadIdx.x < n && key[e] >= tau;
+      }
+      load_batch(v, base + 2 * kStep);            // two batches ahead
+      C += compact_ordered<kRowThreads, kBatch>(key, pass, base, C, ckey, cpos, kRowCap, tab);
+    };
+    for (int base = 0; base < n; base += 2 * kStep) {
+      batch(va, base, table[0]);
+      if (base + kStep < n) batch(vb, base + kStep, table[1]);
+    }
+    __syncthreads();                              // the compacted candidates, before the select reads them
+    finish_row<kRowThreads>(row, n, k, C, kRowCap, ckey, cpos, out, hist, bucket, scratch);
   }
-  __syncthreads();                              // the compacted candidates, before the select reads them
-  finish_row<kRowThreads>(row, n, k, C, kRowCap, ckey, cpos, out, hist, bucket, scratch);
 }
 
 // ---------------------------------------------------------- long rows --
@@ -349,11 +432,21 @@ hipError_t launch_topk(const float* logits, int64_t ld, const BatchArgs& b, cons
     if (e != hipSuccess) return e;
     return launch_topk_resolve(logits, ld, b, ws, k, out, ldo, stream);
   } else {
-    if (b.max_seq_len <= 65536)
-      IDX_LAUNCH("topk_rows_kernel", (topk_rows_kernel<uint16_t>), dim3((unsigned)b.num_tokens),
+    // rows whose sample the scoring kernel copied out are read once, each wave
+    // its own range; rows whose sample is gathered first keep the interleaved
+    // pass (faster there: the gather has just touched every line of the row)
+    const bool small = b.max_seq_len <= 65536;
+    if (small && ws.samp != nullptr)
+      IDX_LAUNCH("topk_rows_kernel", (topk_rows_kernel<uint16_t, true>), dim3((unsigned)b.num_tokens),
+                 dim3(kRowThreads), stream, logits, ld, b, k, out, ldo, ws.samp);
+    else if (small)
+      IDX_LAUNCH("topk_rows_kernel", (topk_rows_kernel<uint16_t, false>), dim3((unsigned)b.num_tokens),
+                 dim3(kRowThreads), stream, logits, ld, b, k, out, ldo, ws.samp);
+    else if (ws.samp != nullptr)
+      IDX_LAUNCH("topk_rows_kernel", (topk_rows_kernel<int32_t, true>), dim3((unsigned)b.num_tokens),
                  dim3(kRowThreads), stream, logits, ld, b, k, out, ldo, ws.samp);
     else
-      IDX_LAUNCH("topk_rows_kernel", (topk_rows_kernel<int32_t>), dim3((unsigned)b.num_tokens),
+      IDX_LAUNCH("topk_rows_kernel", (topk_rows_kernel<int32_t, false>), dim3((unsigned)b.num_tokens),
                  dim3(kRowThreads), stream, logits, ld, b, k, out, ldo, ws.samp);
   }
   return hipGetLastError();

@@ -373,6 +373,46 @@ def test_score_topk_fused_equals_unfused(env):
         assert np.array_equal(a, b)
 
 
+def test_row_topk_wave_ranges_overflow(env):
+    """Rows of a prefill batch whose sample the scoring kernel copies out are
+    read by the row top-k one contiguous range per wave, each wave compacting
+    its candidates into its own 640-entry part of the LDS list.  Here the K
+    rows of positions 4000..7999 are scaled by 4, so about half of them (those
+    with positive scores) rise above the threshold; in rows of 26k and 30k
+    positions one wave's range then holds over a thousand candidates and the
+    row is selected from the whole score row, while in the 20k rows the hot
+    positions are split over three waves and fit.  idx_score_topk (compact
+    sample) must equal idx_logits + idx_topk (sample gathered from the row,
+    interleaved pass) and the oracle."""
+    import synth.gen as sg
+    m, torch = env
+
+    class HotRun(sg.Workload):
+        def request_k(self, layer, r):
+            kb = super().request_k(layer, r)
+            x = (kb.astype(np.uint32) << 16).view(np.float32).copy()
+            x[4000:8000] *= np.float32(4.0)
+            return f32_to_bf16_bits(x)
+
+    for lengths, new in (([30000], [64]), ([20000, 26000], [40, 24])):
+        base = random_batch(4030 + len(lengths), lengths, new, k=2048)
+        wl = HotRun(base.name, base.seed, base.seq_lens, base.new_tokens, base.block_table,
+                    base.num_blocks, base.k)
+        say("row top-k wave ranges", wl.seq_lens.tolist(), wl.new_tokens.tolist())
+        dev = device_layer(m, torch, wl, 0, with_new=True)
+        batch = device_batch(m, wl)
+        lg = m.idx_logits(dev["q8"], dev["w"], dev["cache"], batch)
+        a = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+        b = m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], batch, wl.k).cpu().numpy()
+        assert np.array_equal(a, b)
+        assert np.isin(np.arange(4000, 8000), b[-1]).sum() > 1000, "the scaled positions should lead"
+        orc = oracle_layer(wl, 0)
+        rows = list(range(0, wl.num_tokens, 13)) + [wl.num_tokens - 1]
+        want = oracle.logits.logits(orc["q8"], orc["w"], orc["cache"], oracle_batch(wl), rows=rows)
+        for t, sc in want.items():
+            check_topk_band(b[t], sc, wl.k, f"token {t}")
+
+
 def test_score_topk_vs_oracle(env):
     m, torch = env
     for wl in (random_batch(4003, [70, 2100, 5000, 9000], 1, k=2048),
