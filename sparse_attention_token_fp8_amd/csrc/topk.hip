@@ -58,6 +58,48 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ row, int n,
   }
 }
 
+// tau from the loaded sample (as sample_tau: at or below the sample_rank-th
+// largest sampled key) with one histogram: its kBins1 bins of 2^kNearShift
+// keys each reach from the largest sampled key M down over four octaves, so
+// the bin of the rank-th key gives a threshold within 1/512 of an octave of
+// it.  Samples whose rank-th key lies further below M take sample_tau.
+constexpr int kNearShift = 14;
+
+template <int NT>
+__device__ __forceinline__ uint32_t sample_tau_near_max(const float* v, int ns, int n, int k,
+                                                        uint32_t* hist, uint32_t* scratch) {
+  constexpr int NW = NT / 64, E = sample_per<NT>();
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  uint32_t key[E];
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    key[e] = (int)threadIdx.x + e * NT < ns ? order_key(v[e]) : 0u;
+    mx = max(mx, key[e]);
+  }
+  mx = wave_max(mx);
+  for (int i = threadIdx.x; i < kBins1; i += NT) hist[i] = 0u;
+  if ((threadIdx.x & 63) == 0) scratch[wave] = mx;
+  __syncthreads();
+  uint32_t M = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = max(M, scratch[w]);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t d = (M - key[e]) >> kNearShift;   // key <= M: bins ascend towards M
+    if ((int)threadIdx.x + e * NT < ns && d < (uint32_t)kBins1) atomicAdd(&hist[kBins1 - 1 - d], 1u);
+  }
+  __syncthreads();
+  const uint32_t rank = sample_rank(n, ns, k);
+  uint32_t above, cnt, total;
+  const uint32_t dig = block_digit<NT>(hist, kBins1, rank, &above, &cnt, &total, scratch + NW);
+  __syncthreads();                              // every wave is done with hist and scratch
+  if (total < rank) return sample_tau<NT>(v, ns, n, k, hist, scratch);   // uniform
+  // the bin's keys: M - (d + 1) 2^s < key <= M - d 2^s, d = kBins1 - 1 - dig
+  const uint64_t below = (uint64_t)(kBins1 - dig) << kNearShift;
+  return (uint64_t)M + 1u > below ? (uint32_t)((uint64_t)M + 1u - below) : 0u;
+}
+
 // One work-group per row.  Candidate positions are stored as Pos (16 bits
 // when every row fits in 65536 positions), which with 512 threads lets four
 // rows share a CU.
@@ -71,6 +113,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
                                                                 int64_t ldo,
                                                                 const float* __restrict__ samp) {
   const int t = blockIdx.x;
+  float sv[sample_per<kRowThreads>()];
+  if constexpr (RANGES) {
+    // the compact copy is read whole before the row's length is known, so the
+    // two round trips overlap; entries past the row's sample are never used
+#pragma unroll
+    for (int e = 0; e < sample_per<kRowThreads>(); ++e)
+      sv[e] = samp[(size_t)t * kMaxSample + threadIdx.x + e * kRowThreads];
+  }
   const int n = token_pos_wave(b, t).n;
   int32_t* out = topk + (size_t)t * ldo;
   if (n <= k) {
@@ -86,11 +136,16 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
   const float* row = logits + (size_t)t * ld;
   constexpr int kStep = kRowThreads * kBatch;
   const bool sampled = n > kRowCap;             // else every position is a candidate
-  float sv[sample_per<kRowThreads>()];
   int ns = 0;
-  if (sampled)                                  // first: tau waits on these only
-    ns = samp ? sample_load_compact<kRowThreads>(samp + (size_t)t * kMaxSample, n, sv)
-              : sample_load<kRowThreads>(row, n, sv);
+  if (sampled) {
+    if constexpr (RANGES) {                     // the sample's size (its values are loaded)
+      const int S = sample_stride(n);
+      ns = (n + S - 1) / S;
+      if (ns > 0 && sample_pos(ns - 1, S) >= n) --ns;
+    } else {
+      ns = sample_load<kRowThreads>(row, n, sv);   // first: tau waits on these only
+    }
+  }
   // Two batches in flight: while one is compacted the next two are loading.
   // Loads past the row re-read its last position (the pass test drops them),
   // so no load sits behind a branch and the compiler waits only for the batch
@@ -119,7 +174,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
     float va[U], vb[U];
     load_run(va, p0);
     load_run(vb, p0 + 64 * U);
-    const uint32_t tau = sampled ? sample_tau<kRowThreads>(sv, ns, n, k, hist, scratch) : 0u;
+    const uint32_t tau = sampled ? sample_tau_near_max<kRowThreads>(sv, ns, n, k, hist, scratch) : 0u;
     uint32_t* wkey = ckey + wave * kWaveCap;
     Pos* wpos = cpos + wave * kWaveCap;
     uint32_t cnt = 0;                             // the wave's candidates so far (uniform)

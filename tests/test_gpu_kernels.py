@@ -413,6 +413,46 @@ def test_row_topk_wave_ranges_overflow(env):
             check_topk_band(b[t], sc, wl.k, f"token {t}")
 
 
+def test_row_topk_threshold_outliers(env):
+    """The row top-k over the compact sample places its threshold with one
+    histogram spanning four octaves of keys below the largest sampled key, and
+    falls back to the two-level search when the sample's rank-th key lies
+    further down.  Here the K rows of four sampled positions (11, 16, 37, 58:
+    the first sample entries of every row) are scaled by 128, so for tokens
+    whose scores there are positive the largest sampled key sits seven octaves
+    above the rest and the fallback runs.  The fused result must equal
+    idx_logits + idx_topk and the oracle."""
+    import synth.gen as sg
+    m, torch = env
+    hot = [11, 16, 37, 58]
+
+    class Outliers(sg.Workload):
+        def request_k(self, layer, r):
+            kb = super().request_k(layer, r)
+            x = (kb.astype(np.uint32) << 16).view(np.float32).copy()
+            x[hot] *= np.float32(128.0)
+            return f32_to_bf16_bits(x)
+
+    base = random_batch(4040, [9000, 12000], [50, 30], k=512)
+    wl = Outliers(base.name, base.seed, base.seq_lens, base.new_tokens, base.block_table,
+                  base.num_blocks, base.k)
+    say("row top-k threshold outliers", wl.seq_lens.tolist(), wl.new_tokens.tolist())
+    dev = device_layer(m, torch, wl, 0, with_new=True)
+    batch = device_batch(m, wl)
+    lg = m.idx_logits(dev["q8"], dev["w"], dev["cache"], batch)
+    a = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+    b = m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], batch, wl.k).cpu().numpy()
+    assert np.array_equal(a, b)
+    lgn = lg.cpu().numpy()
+    outl = sum(int(lgn[t, hot].max() > 0) for t in range(wl.num_tokens))
+    assert outl > 10, "some rows should hold a scaled positive score"
+    orc = oracle_layer(wl, 0)
+    rows = list(range(0, wl.num_tokens, 7)) + [wl.num_tokens - 1]
+    want = oracle.logits.logits(orc["q8"], orc["w"], orc["cache"], oracle_batch(wl), rows=rows)
+    for t, sc in want.items():
+        check_topk_band(b[t], sc, wl.k, f"token {t}")
+
+
 def test_score_topk_vs_oracle(env):
     m, torch = env
     for wl in (random_batch(4003, [70, 2100, 5000, 9000], 1, k=2048),
