@@ -767,6 +767,41 @@ def test_stack_physical_equals_stack_then_convert(env, block_stride):
     assert np.array_equal(phys.valid_counts.cpu().numpy(), wv)
 
 
+@pytest.mark.parametrize("alias", [False, True])
+def test_stack_equals_layer_calls(env, alias):
+    """idx_indexcache_stack equals idx_indexcache_layer called layer by layer:
+    every layer's cache bytes and the top-k rows, with distinct caches and
+    with an S layer writing into an F layer's cache (alias), where the
+    layers' order decides what the F layer scored and what the cache holds."""
+    m, torch = env
+    pattern = "FSSSFSS"
+    wl = random_batch(5301, [20000, 9000, 40000, 3000], 1, k=512,
+                      num_layers=len(pattern), pattern=pattern)
+    say("stack vs layer calls", pattern, "alias", alias)
+    full = [c == "F" for c in pattern]
+    batch = device_batch(m, wl)
+    outs = []
+    for use_stack in (True, False):
+        devs = [device_layer(m, torch, wl, l) for l in range(len(pattern))]
+        caches = [d["cache"] for d in devs]
+        if alias:
+            caches[2] = caches[0]               # S layer 2 writes into F layer 0's cache
+        layers = [(d["k_new"], c, d["q8"], d["w"]) for d, c in zip(devs, caches)]
+        topk = torch.full((wl.num_tokens, wl.k), -7, dtype=torch.int32, device="cuda")
+        slots = devs[0]["slots_new"]
+        if use_stack:
+            m.idx_indexcache_stack(layers, full, True, slots, batch, wl.k, topk)
+        else:
+            for lay, f in zip(layers, full):
+                m.idx_indexcache_layer(lay[0], lay[1], lay[2], lay[3], bool(f), True, slots, batch,
+                                       wl.k, topk)
+        torch.cuda.synchronize()
+        outs.append((topk.cpu().numpy(), [c.tensor.cpu().numpy() for c in caches]))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    for l in range(len(pattern)):
+        assert np.array_equal(outs[0][1][l], outs[1][1][l]), f"layer {l} cache"
+
+
 def test_relu_split_unscaled_weights_diagnostic(env):
     """Stress diagnostic: weights drawn N(0,1) and passed as they are (not
     folded, so scores reach ~1e4 and heads cancel heavily).  The kernel's
