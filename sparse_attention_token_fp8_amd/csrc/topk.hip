@@ -13,6 +13,8 @@
 // Neither shape uses device-scope atomics or fences: work-groups meet only at
 // kernel boundaries.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "topk_device.hpp"
@@ -31,6 +33,15 @@ constexpr int kChunkSampled = 2048;
 constexpr int kChunkPlain = 4096;
 constexpr int kMaxLongRow = 1 << 22;                 // rows up to 4M positions
 static_assert(kMaxLongRow / kChunkSampled <= kMaxSlots, "one slot per chunk");
+
+// byte_rsrc from wave-uniform values, so that the descriptor sits in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p, int bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return byte_rsrc(reinterpret_cast<const void*>((uintptr_t)(((uint64_t)hi << 32) | lo)),
+                   __builtin_amdgcn_readfirstlane(bytes));
+}
 
 template <int NT>
 __device__ __forceinline__ void write_all(int32_t* out, int n, int k) {
@@ -164,12 +175,15 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int seg = (n + 64 * NW - 1) / (64 * NW) * 64;
     const int p0 = wave * seg, p1 = min(n, p0 + seg);
-    // past its range a wave re-reads the range's last position (the pass test
-    // drops it), so no load sits behind a branch and no line is fetched twice
-    const int last = max(p1 - 1, 0);
+    // the row through a buffer that ends at the wave's range: a load past it
+    // returns 0.0 and fetches nothing, so no load sits behind a branch and no
+    // line is fetched twice
+    const __amdgpu_buffer_rsrc_t rrs = wave_rsrc(row, p1 * 4);
     auto load_run = [&](float* v, int base) {
+      const uint32_t voff = (uint32_t)(base + lane) * 4u;
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = row[min(base + 64 * u + lane, last)];
+      for (int u = 0; u < U; ++u)
+        v[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rrs, voff, 256 * u, 0));
     };
     float va[U], vb[U];
     load_run(va, p0);
@@ -178,31 +192,50 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
     uint32_t* wkey = ckey + wave * kWaveCap;
     Pos* wpos = cpos + wave * kWaveCap;
     uint32_t cnt = 0;                             // the wave's candidates so far (uniform)
-    auto run = [&](float* v, int base) {
+    // With a positive threshold (the usual case) a key at or above it is a
+    // float whose bits, read as a signed integer, are at or above the
+    // threshold's without its sign bit (negative values and negative NaNs
+    // fall below, positive NaNs above, as with keys): the pass compares the
+    // raw bits and stores them, and they become keys only for the candidates,
+    // as the parts are moved.  The 0.0 read past the range fails that test,
+    // so only the key test needs the position check.
+    const bool raw = tau > 0x80000000u;           // uniform
+    const int32_t tau_bits = (int32_t)(tau & 0x7fffffffu);
+    auto run = [&](auto raw_bits, float* v, int base) {
+      constexpr bool RAW = decltype(raw_bits)::value;
       uint32_t key[U];
       bool pass[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        key[u] = order_key(v[u]);
-        pass[u] = base + 64 * u + lane < p1 && key[u] >= tau;
+        key[u] = RAW ? __float_as_uint(v[u]) : order_key(v[u]);
+        pass[u] = RAW ? (int32_t)key[u] >= tau_bits : base + 64 * u + lane < p1 && key[u] >= tau;
       }
       load_run(v, base + 2 * 64 * U);             // two runs ahead
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint64_t mk = __ballot(pass[u]);
-        const uint32_t at = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-        if (pass[u] && at < (uint32_t)kWaveCap) {
+        // past the part's end every store lands on its last entry: the part
+        // has overflowed and the row is selected whole, so nothing reads it
+        const uint32_t at = min(cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u)),
+                                (uint32_t)kWaveCap - 1u);
+        if (pass[u]) {
           wkey[at] = key[u];
           wpos[at] = (Pos)(base + 64 * u + lane);
         }
         cnt += (uint32_t)__popcll(mk);
       }
     };
-    for (int base = p0; base < p1; base += 2 * 64 * U) {
-      run(va, base);
-      if (base + 64 * U < p1) run(vb, base + 64 * U);
-    }
+    auto pass_range = [&](auto raw_bits) {
+      for (int base = p0; base < p1; base += 2 * 64 * U) {
+        run(raw_bits, va, base);
+        if (base + 64 * U < p1) run(raw_bits, vb, base + 64 * U);
+      }
+    };
+    if (raw)
+      pass_range(std::integral_constant<bool, true>());
+    else
+      pass_range(std::integral_constant<bool, false>());
     __shared__ uint32_t wcnt[NW];
     if (lane == 0) wcnt[wave] = cnt;
     __syncthreads();
@@ -225,6 +258,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
         const uint32_t i = min((uint32_t)(64 * r + lane), cnt - (cnt > 0 ? 1u : 0u));
         rk[r] = wkey[i];
         rp[r] = wpos[i];
+      }
+      if (raw) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) rk[r] = order_key(__uint_as_float(rk[r]));
       }
       __syncthreads();
 #pragma unroll
