@@ -48,6 +48,72 @@ __device__ __forceinline__ void write_all(int32_t* out, int n, int k) {
   for (int j = threadIdx.x; j < k; j += NT) out[j] = j < n ? j : -1;
 }
 
+// The ordered write-out of one row from C candidates in LDS (ascending
+// positions), by waves: wave w takes a contiguous run of them into registers,
+// counts its keys > kstar and == kstar with ballots, one barrier exchanges
+// the counts (`counts`: 2 * NT / 64 words of LDS used by nothing else), and
+// each taken key's position goes
+// to #(earlier keys > kstar) + min(#(earlier keys == kstar), take_eq).  Keys
+// > kstar are taken, and the first take_eq keys == kstar; the rest of the k
+// slots get -1.
+template <int NT, typename Pos>
+__device__ __forceinline__ void emit_by_waves(const uint32_t* ckey, const Pos* cpos, uint32_t C,
+                                              uint32_t kstar, uint32_t take_eq, int k,
+                                              int32_t* __restrict__ out, uint32_t* counts) {
+  constexpr int NW = NT / 64, E = kRowCap / NT;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const uint32_t run = (C + 64 * NW - 1) / (64 * NW) * 64;
+  const uint32_t a0 = min(C, (uint32_t)wave * run), a1 = min(C, a0 + run);
+  const int ne = (int)((a1 - a0 + 63u) / 64u);  // uniform
+  uint32_t key[E];
+  int32_t pos[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {                 // every read issued together (in bounds)
+    const uint32_t j = min(a0 + 64u * e + lane, C - 1u);
+    key[e] = ckey[j];
+    pos[e] = (int32_t)cpos[j];
+  }
+  auto valid = [&](int e) { return a0 + 64u * e + lane < a1; };
+  uint32_t ng = 0u, nq = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e < ne) {                               // uniform
+      ng += (uint32_t)__popcll(__ballot(valid(e) && key[e] > kstar));
+      nq += (uint32_t)__popcll(__ballot(valid(e) && key[e] == kstar));
+    }
+  }
+  if (lane == 0) { counts[2 * wave] = ng; counts[2 * wave + 1] = nq; }
+  __syncthreads();
+  uint32_t gb = 0u, eb = 0u, gall = 0u, eall = 0u;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const uint32_t g = counts[2 * v], q = counts[2 * v + 1];
+    gb += v < wave ? g : 0u;
+    eb += v < wave ? q : 0u;
+    gall += g;
+    eall += q;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e >= ne) continue;                      // uniform
+    const bool g = valid(e) && key[e] > kstar, q = valid(e) && key[e] == kstar;
+    const uint64_t bg = __ballot(g), be = __ballot(q);
+    const uint32_t pg = __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
+    const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+    uint32_t o = 0xffffffffu;
+    if (g) o = gb + pg + min(eb + pe, take_eq);
+    else if (q && eb + pe < take_eq) o = gb + pg + eb + pe;
+    if (o < (uint32_t)k) out[o] = pos[e];
+    gb += (uint32_t)__popcll(bg);
+    eb += (uint32_t)__popcll(be);
+  }
+  const uint32_t written = min((uint32_t)k, gall + min(eall, take_eq));
+  for (uint32_t i = written + threadIdx.x; i < (uint32_t)k; i += NT) out[i] = -1;
+}
+
 // Exact select over the `C` candidates in LDS (k <= C <= cap, ascending
 // positions), else over the whole row, then the ordered write-out.
 template <int NT, typename Pos>
@@ -249,7 +315,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
       C += c;
     }
     if (!fits) C = kRowCap + 1;                   // a part overflowed: the whole row is selected
-    if (fits && C >= (uint32_t)k) {               // move the parts together (all reads first)
+    const bool in_lds = fits && C >= (uint32_t)k; // uniform
+    __shared__ uint32_t wmax[NW];
+    if (in_lds) {                                 // move the parts together (all reads first)
       constexpr int R = kWaveCap / 64;
       uint32_t rk[R];
       Pos rp[R];
@@ -259,10 +327,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
         rk[r] = wkey[i];
         rp[r] = wpos[i];
       }
-      if (raw) {
+      uint32_t hi = 0u;                           // the part's largest key
 #pragma unroll
-        for (int r = 0; r < R; ++r) rk[r] = order_key(__uint_as_float(rk[r]));
+      for (int r = 0; r < R; ++r) {
+        if (raw) rk[r] = order_key(__uint_as_float(rk[r]));
+        hi = max(hi, cnt > 0 ? rk[r] : 0u);       // entries past cnt repeat the last one
       }
+      hi = wave_max(hi);
+      if (lane == 0) wmax[wave] = hi;
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -271,7 +343,19 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
       }
     }
     __syncthreads();                              // the candidates, before the select reads them
-    finish_row<kRowThreads>(row, n, k, C, kRowCap, ckey, cpos, out, hist, bucket, scratch);
+    if (in_lds) {
+      // every candidate lies in [tau, the largest part maximum]
+      uint32_t kmax = 0u;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) kmax = max(kmax, wmax[v]);
+      uint32_t take;
+      const uint32_t kstar = select_kth_range<kRowThreads>(ckey, C, (uint32_t)k, tau, kmax, &take, hist,
+                                                           bucket, scratch);
+      __shared__ uint32_t ecnt[2 * NW];
+      emit_by_waves<kRowThreads>(ckey, cpos, C, kstar, take, k, out, ecnt);
+    } else {
+      finish_row<kRowThreads>(row, n, k, C, kRowCap, ckey, cpos, out, hist, bucket, scratch);
+    }
   } else {
     float va[kBatch], vb[kBatch];
     load_batch(va, 0);
