@@ -508,56 +508,12 @@ struct RowRun {
   }
 };
 
-// The row's k entries from the candidates of every wave's run: keys > kstar
-// are taken, and the first take_eq keys == kstar; slots past those get -1.
-// Each wave counts its run with ballots, one barrier exchanges the counts,
-// and each taken key's position goes to
-// #(earlier keys > kstar) + min(#(earlier keys == kstar), take_eq).
+// The row's k entries from the candidates of every wave's run (emit_runs).
 template <int NT>
 __device__ __forceinline__ void emit_row_waves(const RowRun<NT>& run, uint32_t kstar,
                                                uint32_t take_eq, int k, int32_t* __restrict__ out,
                                                uint32_t* counts) {
-  constexpr int NW = NT / 64, E = RowRun<NT>::E;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  uint32_t ng = 0u, nq = 0u;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (e >= run.ne) break;                     // uniform
-    const bool v = run.valid(e);
-    ng += (uint32_t)__popcll(__ballot(v && run.key[e] > kstar));
-    nq += (uint32_t)__popcll(__ballot(v && run.key[e] == kstar));
-  }
-  if (lane == 0) { counts[2 * wave] = ng; counts[2 * wave + 1] = nq; }
-  __syncthreads();
-  uint32_t gb = 0u, eb = 0u, gall = 0u, eall = 0u;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    const uint32_t g = counts[2 * v], q = counts[2 * v + 1];
-    gb += v < wave ? g : 0u;
-    eb += v < wave ? q : 0u;
-    gall += g;
-    eall += q;
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (e >= run.ne) break;
-    const bool v = run.valid(e);
-    const bool g = v && run.key[e] > kstar, q = v && run.key[e] == kstar;
-    const uint64_t bg = __ballot(g), be = __ballot(q);
-    const uint32_t pg = __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
-    const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
-    uint32_t o = 0xffffffffu;
-    if (g) o = gb + pg + min(eb + pe, take_eq);
-    else if (q && eb + pe < take_eq) o = gb + pg + eb + pe;
-    if (o < (uint32_t)k) out[o] = run.pos[e];
-    gb += (uint32_t)__popcll(bg);
-    eb += (uint32_t)__popcll(be);
-  }
-  const uint32_t written = min((uint32_t)k, gall + min(eall, take_eq));
-  for (uint32_t i = written + threadIdx.x; i < (uint32_t)k; i += NT) out[i] = -1;
+  emit_runs<NT, RowRun<NT>::E>(run.key, run.pos, run.a0, run.a1, kstar, take_eq, k, out, counts);
 }
 
 // Steps 2 and 3 for one row per work-group.  The row's length, the slot

@@ -49,13 +49,9 @@ __device__ __forceinline__ void write_all(int32_t* out, int n, int k) {
 }
 
 // The ordered write-out of one row from C candidates in LDS (ascending
-// positions), by waves: wave w takes a contiguous run of them into registers,
-// counts its keys > kstar and == kstar with ballots, one barrier exchanges
-// the counts (`counts`: 2 * NT / 64 words of LDS used by nothing else), and
-// each taken key's position goes
-// to #(earlier keys > kstar) + min(#(earlier keys == kstar), take_eq).  Keys
-// > kstar are taken, and the first take_eq keys == kstar; the rest of the k
-// slots get -1.
+// positions), by waves: wave w takes a contiguous run of them into registers
+// and emit_runs writes the row (`counts`: 2 * NT / 64 words of LDS used by
+// nothing else).
 template <int NT, typename Pos>
 __device__ __forceinline__ void emit_by_waves(const uint32_t* ckey, const Pos* cpos, uint32_t C,
                                               uint32_t kstar, uint32_t take_eq, int k,
@@ -65,7 +61,6 @@ __device__ __forceinline__ void emit_by_waves(const uint32_t* ckey, const Pos* c
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const uint32_t run = (C + 64 * NW - 1) / (64 * NW) * 64;
   const uint32_t a0 = min(C, (uint32_t)wave * run), a1 = min(C, a0 + run);
-  const int ne = (int)((a1 - a0 + 63u) / 64u);  // uniform
   uint32_t key[E];
   int32_t pos[E];
 #pragma unroll
@@ -74,44 +69,7 @@ __device__ __forceinline__ void emit_by_waves(const uint32_t* ckey, const Pos* c
     key[e] = ckey[j];
     pos[e] = (int32_t)cpos[j];
   }
-  auto valid = [&](int e) { return a0 + 64u * e + lane < a1; };
-  uint32_t ng = 0u, nq = 0u;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (e < ne) {                               // uniform
-      ng += (uint32_t)__popcll(__ballot(valid(e) && key[e] > kstar));
-      nq += (uint32_t)__popcll(__ballot(valid(e) && key[e] == kstar));
-    }
-  }
-  if (lane == 0) { counts[2 * wave] = ng; counts[2 * wave + 1] = nq; }
-  __syncthreads();
-  uint32_t gb = 0u, eb = 0u, gall = 0u, eall = 0u;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    const uint32_t g = counts[2 * v], q = counts[2 * v + 1];
-    gb += v < wave ? g : 0u;
-    eb += v < wave ? q : 0u;
-    gall += g;
-    eall += q;
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (e >= ne) continue;                      // uniform
-    const bool g = valid(e) && key[e] > kstar, q = valid(e) && key[e] == kstar;
-    const uint64_t bg = __ballot(g), be = __ballot(q);
-    const uint32_t pg = __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
-    const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
-    uint32_t o = 0xffffffffu;
-    if (g) o = gb + pg + min(eb + pe, take_eq);
-    else if (q && eb + pe < take_eq) o = gb + pg + eb + pe;
-    if (o < (uint32_t)k) out[o] = pos[e];
-    gb += (uint32_t)__popcll(bg);
-    eb += (uint32_t)__popcll(be);
-  }
-  const uint32_t written = min((uint32_t)k, gall + min(eall, take_eq));
-  for (uint32_t i = written + threadIdx.x; i < (uint32_t)k; i += NT) out[i] = -1;
+  emit_runs<NT, E>(key, pos, a0, a1, kstar, take_eq, k, out, counts);
 }
 
 // Exact select over the `C` candidates in LDS (k <= C <= cap, ascending

@@ -361,6 +361,62 @@ __device__ __forceinline__ void emit_ordered(G&& get, uint32_t count, uint32_t k
   __syncthreads();
 }
 
+// The row's k entries from runs of candidates held in registers: wave w
+// holds candidates a0 + 64 e + lane < a1 of the row's candidate order
+// (ascending positions), the runs of the waves following each other in wave
+// order.  Keys > kstar are taken, and the first take_eq keys == kstar; slots
+// past those get -1.  Each wave counts its run with ballots, one barrier
+// exchanges the counts (`counts`: 2 * NT / 64 words of LDS no other wave is
+// reading), and each taken key's position goes to
+// #(earlier keys > kstar) + min(#(earlier keys == kstar), take_eq).
+template <int NT, int E>
+__device__ __forceinline__ void emit_runs(const uint32_t (&key)[E], const int32_t (&pos)[E], uint32_t a0,
+                                          uint32_t a1, uint32_t kstar, uint32_t take_eq, int k,
+                                          int32_t* __restrict__ out, uint32_t* counts) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int ne = (int)((a1 - a0 + 63u) / 64u);  // uniform
+  auto valid = [&](int e) { return a0 + 64u * e + lane < a1; };
+  uint32_t ng = 0u, nq = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e < ne) {                               // uniform
+      ng += (uint32_t)__popcll(__ballot(valid(e) && key[e] > kstar));
+      nq += (uint32_t)__popcll(__ballot(valid(e) && key[e] == kstar));
+    }
+  }
+  if (lane == 0) { counts[2 * wave] = ng; counts[2 * wave + 1] = nq; }
+  __syncthreads();
+  uint32_t gb = 0u, eb = 0u, gall = 0u, eall = 0u;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const uint32_t g = counts[2 * v], q = counts[2 * v + 1];
+    gb += v < wave ? g : 0u;
+    eb += v < wave ? q : 0u;
+    gall += g;
+    eall += q;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e >= ne) continue;                      // uniform
+    const bool g = valid(e) && key[e] > kstar, q = valid(e) && key[e] == kstar;
+    const uint64_t bg = __ballot(g), be = __ballot(q);
+    const uint32_t pg = __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
+    const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+    uint32_t o = 0xffffffffu;
+    if (g) o = gb + pg + min(eb + pe, take_eq);
+    else if (q && eb + pe < take_eq) o = gb + pg + eb + pe;
+    if (o < (uint32_t)k) out[o] = pos[e];
+    gb += (uint32_t)__popcll(bg);
+    eb += (uint32_t)__popcll(be);
+  }
+  const uint32_t written = min((uint32_t)k, gall + min(eall, take_eq));
+  for (uint32_t i = written + threadIdx.x; i < (uint32_t)k; i += NT) out[i] = -1;
+}
+
 // Rank (1-based) of the sample key used as tau: about 1.5k of the n keys are
 // expected at or above it, plus a margin of 16 sample steps (the count stays
 // several standard deviations above k for samples of a few hundred keys).
