@@ -4,7 +4,11 @@
 //   many rows     one 512-thread work-group per row: tau from the row's
 //                 sample, candidates (key >= tau) compacted into LDS in
 //                 position order, exact select, ordered write-out.  No global
-//                 scratch and no atomics outside LDS.
+//                 scratch and no atomics outside LDS.  Rows whose sample the
+//                 scoring kernel copied out are streamed one contiguous range
+//                 per wave (each wave compacting into its own part of the
+//                 list); rows whose sample is gathered here are streamed by
+//                 the whole work-group, batch by batch.
 //   few long rows filter: work-groups of 2048 or 4096 positions compact their
 //                 candidates, in order, into a private slot of the workspace
 //                 (no atomics, nothing to clear); resolve: one work-group per
