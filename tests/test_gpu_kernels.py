@@ -703,11 +703,14 @@ def test_topk_to_physical(env):
 
 
 
-@pytest.mark.parametrize("block_size,stride,k", [(48, 0, 64), (32, 100, 64), (64, 96, 64), (64, 0, 30)])
+@pytest.mark.parametrize("block_size,stride,k", [(48, 0, 64), (32, 100, 64), (64, 96, 64), (64, 0, 30),
+                                                   (128, 0, 64)])
 def test_topk_to_physical_block_shapes(env, block_size, stride, k):
-    """Block sizes other than the cache's 64 (a power of two or not) and block
-    strides wider than the block give the oracle's slots and counts; k = 30
-    makes rows of 120 bytes, so every other row takes the unaligned path."""
+    """Block sizes other than the cache's 64 (a power of two or not, and 128,
+    whose block table is narrower than 64-position blocks would need) and
+    block strides wider than the block give the oracle's slots and counts;
+    k = 30 makes rows of 120 bytes, so every other row takes the unaligned
+    path."""
     m, torch = env
     rng = np.random.default_rng(5100 + block_size)
     wl = random_batch(5003, [100, 700, 64, 1500], [2, 1, 3, 40], k=k)
