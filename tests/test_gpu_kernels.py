@@ -453,6 +453,42 @@ def test_row_topk_threshold_outliers(env):
         check_topk_band(b[t], sc, wl.k, f"token {t}")
 
 
+def test_row_topk_signs(env):
+    """The row top-k over the compact sample compares raw float bits when the
+    threshold is positive and order keys otherwise.  Tokens whose weights are
+    all negative score <= 0 everywhere and take the key path; tokens whose
+    weights are all positive take the raw path.  idx_score_topk must equal idx_logits + idx_topk and the
+    oracle."""
+    import synth.gen as sg
+    m, torch = env
+
+    class Signed(sg.Workload):
+        def w_raw(self, layer):
+            w = np.abs(super().w_raw(layer))
+            w[0::2] *= np.float32(-1.0)            # even tokens: every weight negative
+            return w
+
+    base = random_batch(4050, [9000, 12000], [40, 24], k=512)
+    wl = Signed(base.name, base.seed, base.seq_lens, base.new_tokens, base.block_table,
+                base.num_blocks, base.k)
+    say("row top-k signs", wl.seq_lens.tolist(), wl.new_tokens.tolist())
+    dev = device_layer(m, torch, wl, 0, with_new=True)
+    batch = device_batch(m, wl)
+    lg = m.idx_logits(dev["q8"], dev["w"], dev["cache"], batch)
+    lgn = lg.cpu().numpy()
+    pos = wl.token_pos()
+    assert all(lgn[t, :pos[t] + 1].max() <= 0 for t in range(0, wl.num_tokens, 2))
+    assert all(lgn[t, :pos[t] + 1].min() >= 0 for t in range(1, wl.num_tokens, 2))
+    a = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+    b = m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], batch, wl.k).cpu().numpy()
+    assert np.array_equal(a, b)
+    orc = oracle_layer(wl, 0)
+    rows = list(range(0, wl.num_tokens, 5)) + [wl.num_tokens - 2, wl.num_tokens - 1]
+    want = oracle.logits.logits(orc["q8"], orc["w"], orc["cache"], oracle_batch(wl), rows=rows)
+    for t, sc in want.items():
+        check_topk_band(b[t], sc, wl.k, f"token {t}")
+
+
 def test_score_topk_vs_oracle(env):
     m, torch = env
     for wl in (random_batch(4003, [70, 2100, 5000, 9000], 1, k=2048),
