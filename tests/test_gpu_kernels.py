@@ -489,6 +489,48 @@ def test_row_topk_signs(env):
         check_topk_band(b[t], sc, wl.k, f"token {t}")
 
 
+def _sample_positions(n):
+    """The fixed sample of a row of n positions, j*S + ((37j + 11) mod S) with
+    S the power of two >= 16 that keeps at most 2048 of them; returns the
+    positions and S."""
+    S = 16
+    while -(-n // S) > 2048:
+        S *= 2
+    j = np.arange(-(-n // S))
+    pos = j * S + ((37 * j + 11) & (S - 1))
+    return pos[pos < n], S
+
+
+def test_prefill_sample_copy(env):
+    """The prefill scoring kernel's compact sample copy (read by the row top-k
+    instead of gathering the sample from the row) holds, for every row, the
+    row's own scores at the sample positions, bit for bit: rows with sample
+    strides 16 and 32, read back from a caller-provided workspace."""
+    m, torch = env
+    wl = random_batch(4060, [9000, 40000], [300, 64], k=512)
+    say("prefill sample copy", wl.seq_lens.tolist(), wl.new_tokens.tolist())
+    dev = device_layer(m, torch, wl, 0, with_new=True)
+    batch = device_batch(m, wl)
+    T = wl.num_tokens
+    ld = -(-int(wl.max_seq_len) // 64) * 64
+    size = m.idx_score_topk_workspace_size(batch, wl.k)
+    ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+    m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], batch, wl.k, workspace=ws)
+    torch.cuda.synchronize()
+    o_samp = -(-(4 * ld * T) // 256) * 256
+    assert size >= o_samp + 4 * 2048 * T
+    raw = ws.cpu().numpy()
+    scores = raw[:4 * ld * T].view(np.uint32).reshape(T, ld)
+    samp = raw[o_samp:o_samp + 4 * 2048 * T].view(np.uint32).reshape(T, 2048)
+    pos = wl.token_pos()
+    strides = set()
+    for t in range(T):
+        sp, S = _sample_positions(int(pos[t]) + 1)
+        strides.add(S)
+        assert np.array_equal(samp[t, :sp.size], scores[t, sp]), f"token {t}"
+    assert strides == {16, 32}
+
+
 def test_score_topk_vs_oracle(env):
     m, torch = env
     for wl in (random_batch(4003, [70, 2100, 5000, 9000], 1, k=2048),
