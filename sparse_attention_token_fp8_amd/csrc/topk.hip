@@ -264,7 +264,26 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
       pass_range(std::integral_constant<bool, true>());
     else
       pass_range(std::integral_constant<bool, false>());
+    constexpr int R = kWaveCap / 64;
     __shared__ uint32_t wcnt[NW];
+    __shared__ uint32_t wmax[NW];
+    __shared__ uint32_t ecnt[2 * NW];
+    if (raw) {
+      // Each wave turns its part's raw bits into keys where they lie, takes
+      // its largest key and pads the rest of the part with key 0, below the
+      // (positive) threshold, which the select ignores: the parts need no
+      // moving, and each wave writes out its own.
+      uint32_t hi = 0u;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t i = (uint32_t)(64 * r + lane);
+        const uint32_t x = i < cnt ? order_key(__uint_as_float(wkey[i])) : 0u;
+        wkey[i] = x;
+        hi = max(hi, x);
+      }
+      hi = wave_max(hi);
+      if (lane == 0) wmax[wave] = hi;
+    }
     if (lane == 0) wcnt[wave] = cnt;
     __syncthreads();
     uint32_t C = 0, before = 0;
@@ -278,9 +297,24 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
     }
     if (!fits) C = kRowCap + 1;                   // a part overflowed: the whole row is selected
     const bool in_lds = fits && C >= (uint32_t)k; // uniform
-    __shared__ uint32_t wmax[NW];
-    if (in_lds) {                                 // move the parts together (all reads first)
-      constexpr int R = kWaveCap / 64;
+    if (raw && in_lds) {
+      // every candidate lies in [tau, the largest part maximum]
+      uint32_t kmax = 0u;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) kmax = max(kmax, wmax[v]);
+      uint32_t take;
+      const uint32_t kstar = select_kth_range<kRowThreads>(ckey, (uint32_t)kRowCap, (uint32_t)k, tau, kmax,
+                                                           &take, hist, bucket, scratch);
+      uint32_t key[R];
+      int32_t pos[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        key[r] = wkey[64 * r + lane];
+        pos[r] = (int32_t)wpos[64 * r + lane];
+      }
+      const uint32_t a0 = (uint32_t)(wave * kWaveCap);
+      emit_runs<kRowThreads, R>(key, pos, a0, a0 + cnt, kstar, take, k, out, ecnt);
+    } else if (in_lds) {                          // keys: move the parts together (all reads first)
       uint32_t rk[R];
       Pos rp[R];
 #pragma unroll
@@ -291,10 +325,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
       }
       uint32_t hi = 0u;                           // the part's largest key
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (raw) rk[r] = order_key(__uint_as_float(rk[r]));
-        hi = max(hi, cnt > 0 ? rk[r] : 0u);       // entries past cnt repeat the last one
-      }
+      for (int r = 0; r < R; ++r) hi = max(hi, cnt > 0 ? rk[r] : 0u);   // entries past cnt repeat the last one
       hi = wave_max(hi);
       if (lane == 0) wmax[wave] = hi;
       __syncthreads();
@@ -303,17 +334,13 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
         const uint32_t i = (uint32_t)(64 * r + lane);
         if (i < cnt) { ckey[before + i] = rk[r]; cpos[before + i] = rp[r]; }
       }
-    }
-    __syncthreads();                              // the candidates, before the select reads them
-    if (in_lds) {
-      // every candidate lies in [tau, the largest part maximum]
+      __syncthreads();                            // the candidates, before the select reads them
       uint32_t kmax = 0u;
 #pragma unroll
       for (int v = 0; v < NW; ++v) kmax = max(kmax, wmax[v]);
       uint32_t take;
       const uint32_t kstar = select_kth_range<kRowThreads>(ckey, C, (uint32_t)k, tau, kmax, &take, hist,
                                                            bucket, scratch);
-      __shared__ uint32_t ecnt[2 * NW];
       emit_by_waves<kRowThreads>(ckey, cpos, C, kstar, take, k, out, ecnt);
     } else {
       finish_row<kRowThreads>(row, n, k, C, kRowCap, ckey, cpos, out, hist, bucket, scratch);
