@@ -531,6 +531,28 @@ def test_prefill_sample_copy(env):
     assert strides == {16, 32}
 
 
+@pytest.mark.parametrize("k", [1, 7, 2048])
+def test_row_topk_edges(env, k):
+    """Prefill rows around the row top-k's 5120-entry candidate list (5119,
+    5120 and 5121 positions: the last two just below and above the sampled
+    form, whose wave ranges then end mid-wave), rows whose length is no
+    multiple of 64, and an absent block whose 64 positions all score 0:
+    idx_score_topk (compact sample, ranged pass) equals idx_logits +
+    idx_topk for k = 1, 7 and 2048."""
+    m, torch = env
+    wl = random_batch(4070 + k, [5121, 5633, 6000], [3, 2, 300], k=k)
+    say("row top-k edges", wl.seq_lens.tolist(), wl.new_tokens.tolist(), "k", k)
+    dev = device_layer(m, torch, wl, 0, with_new=True)
+    bt = wl.block_table.copy()
+    bt[2, 10] = -1                              # positions 640..703 of the third request
+    batch = m.Batch(wl.seq_lens, wl.query_start_loc, bt)
+    lg = m.idx_logits(dev["q8"], dev["w"], dev["cache"], batch)
+    a = m.idx_topk(lg, batch, wl.k).cpu().numpy()
+    b = m.idx_score_topk(dev["q8"], dev["w"], dev["cache"], batch, wl.k).cpu().numpy()
+    assert sorted(int(p) + 1 for p in wl.token_pos()[:3]) == [5119, 5120, 5121]
+    assert np.array_equal(a, b)
+
+
 def test_score_topk_vs_oracle(env):
     m, torch = env
     for wl in (random_batch(4003, [70, 2100, 5000, 9000], 1, k=2048),
