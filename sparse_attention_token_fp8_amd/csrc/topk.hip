@@ -196,8 +196,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
   if constexpr (RANGES) {
     // Each wave streams its own contiguous range of the row (a multiple of 64
     // positions) and compacts its candidates into its own part of the LDS list
-    // with ballots: no barrier until the row has been read.  The parts are then
-    // moved together in wave order, which is position order.
+    // with ballots: no barrier until the row has been read.  The parts follow
+    // each other in wave order, which is position order; after the select each
+    // wave writes out its own part's share of the row.
     constexpr int NW = kRowThreads / 64, U = kBatch, kWaveCap = kRowCap / NW;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -225,8 +226,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(const float* __r
     // threshold's without its sign bit (negative values and negative NaNs
     // fall below, positive NaNs above, as with keys): the pass compares the
     // raw bits and stores them, and they become keys only for the candidates,
-    // as the parts are moved.  The 0.0 read past the range fails that test,
-    // so only the key test needs the position check.
+    // after the pass.  The 0.0 read past the range fails that test, so only
+    // the key test needs the position check.
     const bool raw = tau > 0x80000000u;           // uniform
     const int32_t tau_bits = (int32_t)(tau & 0x7fffffffu);
     auto run = [&](auto raw_bits, float* v, int base) {
