@@ -54,14 +54,11 @@ __device__ __forceinline__ uint32_t chunk_keep(int k, int nvalid, int n) {
   return (uint32_t)ceilf(e + 6.f * sqrtf(e)) + 8u;
 }
 
-// Threshold histograms: the top 12 bits of the order key (sign, exponent and
-// three mantissa bits, so bins are an eighth of an octave wide; counted by the
-// scoring loop), then the next 10 bits of the keys in the bin that holds the
-// m-th largest.
+// Threshold histogram: the top 12 bits of the order key (sign, exponent and
+// three mantissa bits, so bins are an eighth of an octave wide), counted by
+// the scoring loop.
 constexpr int kTauBins = 4096;
 constexpr int kTauShift = 20;
-constexpr int kTau2Bins = 1024;
-constexpr int kTau2Shift = 10;
 
 // In the histogram h[0..64*PER) of one work-group, the bin holding the
 // need-th largest entry (1 <= need <= total), found by one wave on its own:
@@ -94,16 +91,15 @@ __device__ __forceinline__ uint32_t wave_find_bin(const uint32_t* h, uint32_t ne
 }
 
 // Step 1, after the work-group's scores are in `kept` (position order), their
-// level-1 histogram in `hist` and their largest key in table[0], every wave
-// past the scoring loop; hist2 is zero.  tau is the lower edge of the level-2
-// bin holding the m-th largest key (so at least m keys are >= tau, and at most
-// the bin's other keys besides them); every wave finds it on its own from the
-// shared histograms.  NT threads, NT >= 256, for chunks of up to MAXPOS
+// histogram in `hist` and their largest key in table[0], every wave past the
+// scoring loop.  tau is the lower edge of the bin holding the m-th largest key
+// (so at least m keys are >= tau, and at most the bin's other keys besides
+// them); every wave finds it on its own from the shared histogram.  NT threads, NT >= 256, for chunks of up to MAXPOS
 // positions; `table` holds 65 words, 129 when MAXPOS / 64 > 64.
 template <int NT, int MAXPOS>
 __device__ __forceinline__ void chunk_filter(const float* kept, int t, int cx, int chunk_blocks,
                                              int n, int k, const KeepSlots& ks, uint32_t* hist,
-                                             uint32_t* hist2, uint32_t* table) {
+                                             uint32_t* table) {
   constexpr int E = MAXPOS / NT;
   const int lane = threadIdx.x & 63;
   const int base = cx * chunk_blocks * kBlock;
@@ -124,15 +120,7 @@ __device__ __forceinline__ void chunk_filter(const float* kept, int t, int cx, i
   uint32_t tau = 0u;
   if (cut) {                                      // uniform over the work-group
     uint32_t above;
-    const uint32_t d1 = wave_find_bin<kTauBins / 64>(hist, m, &above, lane);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (pass[e] && (key[e] >> kTauShift) == d1)
-        atomicAdd(&hist2[(key[e] >> kTau2Shift) & (kTau2Bins - 1)], 1u);
-    __syncthreads();
-    uint32_t above2;
-    const uint32_t d2 = wave_find_bin<kTau2Bins / 64>(hist2, m - above, &above2, lane);
-    tau = (d1 << kTauShift) | (d2 << kTau2Shift);
+    tau = wave_find_bin<kTauBins / 64>(hist, m, &above, lane) << kTauShift;
 #pragma unroll
     for (int e = 0; e < E; ++e) pass[e] = pass[e] && key[e] >= tau;
   }
@@ -384,13 +372,10 @@ __global__ __launch_bounds__(kDynThreads) void score_keep_dyn_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDynWaves * (FP4 ? kLinScratch : kBlockBytes)];
   __shared__ float kept[MAXB * kBlock];
   __shared__ __attribute__((aligned(16))) uint32_t hist[kTauBins];
-  __shared__ __attribute__((aligned(16))) uint32_t hist2[kTau2Bins];
   __shared__ uint32_t table[1 + MAXB];
   __shared__ uint32_t next;
   for (int i = threadIdx.x; i < kTauBins / 4; i += kDynThreads)
     reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-  for (int i = threadIdx.x; i < kTau2Bins / 4; i += kDynThreads)
-    reinterpret_cast<uint4*>(hist2)[i] = make_uint4(0u, 0u, 0u, 0u);
   if (threadIdx.x == 0) {
     table[0] = 0u;
     next = (uint32_t)(kDynWaves * (NB - 1));
@@ -402,7 +387,7 @@ __global__ __launch_bounds__(kDynThreads) void score_keep_dyn_kernel(
                                       kept, hist, table, &next);
   if (n <= k) return;                           // nothing here, or a row the resolve takes whole
   __syncthreads();                              // every wave's scores are in `kept`
-  chunk_filter<kDynThreads, MAXB * kBlock>(kept, ry, cx, chunk_blocks, n, k, ks, hist, hist2, table);
+  chunk_filter<kDynThreads, MAXB * kBlock>(kept, ry, cx, chunk_blocks, n, k, ks, hist, table);
 }
 
 // ------------------------------------------------------------- resolve --
